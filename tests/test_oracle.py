@@ -1,0 +1,281 @@
+"""Pins for the fp64 oracle (CPU only).
+
+None of these re-derives the oracle's own formula. Each checks the oracle against
+something independent of it:
+
+* a literal brute force (pure-Python loops, no log-sum-exp shift, full-vocabulary
+  teacher distribution, math.fsum);
+* central finite differences of the loss;
+* torch autograd;
+* torch's cross_entropy and kl_div special cases;
+* closed forms;
+* invariants that hold for any correct implementation.
+
+Together they catch a dropped term, a wrong sign or index, a transposed operand and a
+missing temperature factor.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+
+def rand_problem(N, d, V, K, seed, scale=1.0, tscale=1.5):
+    g = np.random.default_rng(seed)
+    H = g.standard_normal((N, d)) * scale
+    W = g.standard_normal((V, d)) / math.sqrt(d)
+    idx = np.stack([g.choice(V, K, replace=False) for _ in range(N)]).astype(np.int32)
+    t = g.standard_normal((N, K)) * tscale
+    return H, W, idx, t
+
+
+# ---------------------------------------------------------------- brute force
+
+def brute(H, W, idx, t, T, n_norm, g):
+    """Literal definition with Python floats: full-vocabulary teacher distribution p,
+    student q_v = exp(u_v) / sum_w exp(u_w) without any shift, KL = sum_v p_v log(p_v/q_v)."""
+    N, d = len(H), len(H[0])
+    V = len(W)
+    K = len(idx[0])
+    loss_terms, row_kl, lse_out, zk_out = [], [], [], []
+    G = [[0.0] * V for _ in range(N)]
+    for n in range(N):
+        z = [math.fsum(H[n][j] * W[v][j] for j in range(d)) for v in range(V)]
+        e = [math.exp(z[v] / T) for v in range(V)]
+        Z = math.fsum(e)
+        q = [ev / Z for ev in e]
+        et = [math.exp(t[n][k] / T) for k in range(K)]
+        Zt = math.fsum(et)
+        p = [0.0] * V
+        for k in range(K):
+            p[idx[n][k]] = et[k] / Zt
+        kl = math.fsum(p[v] * math.log(p[v] / q[v]) for v in range(V) if p[v] > 0)
+        row_kl.append(kl)
+        lse_out.append(math.log(Z))
+        zk_out.append([z[idx[n][k]] for k in range(K)])
+        for v in range(V):
+            G[n][v] = g * T / n_norm * (q[v] - p[v])
+    loss = g * T * T / n_norm * math.fsum(row_kl)
+    dH = [[math.fsum(G[n][v] * W[v][j] for v in range(V)) for j in range(d)] for n in range(N)]
+    dW = [[math.fsum(G[n][v] * H[n][j] for n in range(N)) for j in range(d)] for v in range(V)]
+    return dict(loss=loss, row_kl=np.array(row_kl), lse=np.array(lse_out), zk=np.array(zk_out),
+                dH=np.array(dH), dW=np.array(dW))
+
+
+@pytest.mark.parametrize("N,d,V,K,T,g,seed", [
+    (3, 4, 7, 3, 1.0, 1.0, 0),
+    (4, 5, 9, 4, 2.0, 0.7, 1),
+    (2, 3, 5, 1, 0.5, -1.3, 2),
+    (4, 5, 9, 2, 1.7, 1.0, 3),
+])
+def test_brute_force(N, d, V, K, T, g, seed):
+    H, W, idx, t = rand_problem(N, d, V, K, seed)
+    ref = brute(H.tolist(), W.tolist(), idx.tolist(), t.tolist(), T, N, g)
+    for fn in (lambda: oracle.kl_dense(H, W, idx, t, T, g=g),
+               lambda: oracle.kl_chunked(H, W, idx, t, T, chunk=2, g=g),
+               lambda: oracle.kl_fused(H, W, idx, t, T, chunk=3, vtile=4, g=g)):
+        out = fn()
+        assert abs(out["loss"] - ref["loss"]) <= 1e-13 * max(1.0, abs(ref["loss"]))
+        for key in ("row_kl", "lse", "zk", "dH", "dW"):
+            np.testing.assert_allclose(out[key], ref[key], rtol=1e-12, atol=1e-13, err_msg=key)
+    rk = oracle.kl_rows(H, W, idx, t, T, rows=[N - 1, 0], n_norm=N, g=g)
+    np.testing.assert_allclose(rk["dH"], ref["dH"][[N - 1, 0]], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(rk["row_kl"], ref["row_kl"][[N - 1, 0]], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------- finite differences
+
+@pytest.mark.parametrize("T", [1.0, 2.0])
+def test_finite_differences(T):
+    N, d, V, K = 6, 8, 23, 5
+    H, W, idx, t = rand_problem(N, d, V, K, 10)
+    g = 0.9
+    out = oracle.kl_dense(H, W, idx, t, T, g=g)
+    rng = np.random.default_rng(11)
+    h = 1e-6
+
+    def loss(Hx, Wx):
+        return oracle.kl_dense(Hx, Wx, idx, t, T, g=g)["loss"]
+
+    for _ in range(20):
+        i, j = rng.integers(N), rng.integers(d)
+        Hp, Hm = H.copy(), H.copy()
+        Hp[i, j] += h
+        Hm[i, j] -= h
+        fd = (loss(Hp, W) - loss(Hm, W)) / (2 * h)
+        assert abs(fd - out["dH"][i, j]) <= 1e-7 * max(1e-3, abs(out["dH"][i, j])) + 1e-9
+        v, j = rng.integers(V), rng.integers(d)
+        Wp, Wm = W.copy(), W.copy()
+        Wp[v, j] += h
+        Wm[v, j] -= h
+        fd = (loss(H, Wp) - loss(H, Wm)) / (2 * h)
+        assert abs(fd - out["dW"][v, j]) <= 1e-7 * max(1e-3, abs(out["dW"][v, j])) + 1e-9
+
+
+# ------------------------------------------------------------- torch autograd
+
+@pytest.mark.parametrize("T", [1.0, 2.5])
+def test_autograd_general_k(T):
+    """torch differentiates the KL term; its gradients must equal the closed form."""
+    N, d, V, K = 7, 6, 31, 4
+    H, W, idx, t = rand_problem(N, d, V, K, 20)
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    logq = torch.log_softmax(Ht @ Wt.T / T, dim=1)
+    logp = torch.log_softmax(torch.tensor(t) / T, dim=1)
+    it = torch.tensor(idx, dtype=torch.long)
+    kl = (logp.exp() * (logp - logq.gather(1, it))).sum(1)
+    loss = T * T * kl.mean()
+    loss.backward()
+    out = oracle.kl_fused(H, W, idx, t, T, chunk=3, vtile=7)
+    assert abs(out["loss"] - loss.item()) <= 1e-12
+    np.testing.assert_allclose(out["dH"], Ht.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(out["dW"], Wt.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+# ------------------------------------------------------------ library special cases
+
+@pytest.mark.parametrize("T", [1.0, 3.0])
+def test_k1_is_cross_entropy(T):
+    """With one cached entry the teacher is one-hot and the loss is T^2 * cross entropy."""
+    N, d, V = 9, 5, 17
+    H, W, idx, t = rand_problem(N, d, V, 1, 30)
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    ce = torch.nn.functional.cross_entropy(Ht @ Wt.T / T, torch.tensor(idx[:, 0], dtype=torch.long))
+    (T * T * ce).backward()
+    out = oracle.kl_dense(H, W, idx, t, T)
+    assert abs(out["loss"] - T * T * ce.item()) <= 1e-12
+    np.testing.assert_allclose(out["dH"], Ht.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(out["dW"], Wt.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+@pytest.mark.parametrize("T", [1.0, 2.0])
+def test_k_equals_v_is_kl_div(T):
+    """With every token cached the teacher is a full softmax and torch's kl_div applies."""
+    N, d, V = 5, 4, 11
+    g = np.random.default_rng(40)
+    H = g.standard_normal((N, d))
+    W = g.standard_normal((V, d))
+    idx = np.stack([g.permutation(V) for _ in range(N)]).astype(np.int32)
+    t = g.standard_normal((N, V)) * 2
+    full_t = np.empty((N, V))
+    np.put_along_axis(full_t, idx.astype(np.int64), t, axis=1)
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    kd = torch.nn.functional.kl_div(torch.log_softmax(Ht @ Wt.T / T, 1),
+                                    torch.softmax(torch.tensor(full_t) / T, 1), reduction="batchmean")
+    (T * T * kd).backward()
+    out = oracle.kl_fused(H, W, idx, t, T, chunk=2, vtile=3)
+    assert abs(out["loss"] - T * T * kd.item()) <= 1e-12
+    np.testing.assert_allclose(out["dH"], Ht.grad.numpy(), rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(out["dW"], Wt.grad.numpy(), rtol=1e-10, atol=1e-13)
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_uniform_student_closed_form():
+    """W = 0 makes the student uniform: KL_n = log V + sum_k p_t log p_t; a flat teacher
+    then gives log(V/K)."""
+    N, d, V, K = 6, 4, 50, 7
+    H, W, idx, t = rand_problem(N, d, V, K, 50)
+    W0 = np.zeros_like(W)
+    out = oracle.kl_dense(H, W0, idx, t, 1.3)
+    a = t / 1.3
+    p = np.exp(a) / np.exp(a).sum(1, keepdims=True)
+    np.testing.assert_allclose(out["row_kl"], math.log(V) + (p * np.log(p)).sum(1), rtol=1e-13)
+    flat = oracle.kl_fused(H, W0, idx, np.full_like(t, 0.25), 1.0, chunk=4, vtile=9)
+    np.testing.assert_allclose(flat["row_kl"], math.log(V / K), rtol=1e-13)
+
+
+def test_zero_when_student_equals_teacher():
+    """Student logits equal to the cached logits at idx and -inf elsewhere give KL = 0."""
+    N, V, K = 8, 40, 6
+    g = np.random.default_rng(60)
+    idx = np.stack([g.choice(V, K, replace=False) for _ in range(N)]).astype(np.int32)
+    for T in (1.0, 0.7, 2.0):
+        t = g.standard_normal((N, K)) * 3
+        z = np.full((N, V), -np.inf)
+        np.put_along_axis(z, idx.astype(np.int64), t, axis=1)
+        row_kl, lse, zk = oracle.kl_from_logits(z, idx, t, T)
+        assert np.all(np.abs(row_kl) <= 1e-15)
+        np.testing.assert_array_equal(zk, t)
+
+
+def test_gibbs_inequality():
+    for seed in range(5):
+        H, W, idx, t = rand_problem(16, 8, 60, 9, 70 + seed, scale=2.0, tscale=3.0)
+        out = oracle.kl_dense(H, W, idx, t, 1.0)
+        assert np.all(out["row_kl"] >= 0)
+
+
+# --------------------------------------------------------- formulation equality
+
+@pytest.mark.parametrize("chunk", [1, 7, 19])
+@pytest.mark.parametrize("vtile", [1, 13, 41])
+def test_formulations_agree(chunk, vtile):
+    """Dense, forward-chunked and fused chunked give the same numbers."""
+    N, d, V, K = 19, 6, 41, 5
+    H, W, idx, t = rand_problem(N, d, V, K, 80)
+    T, gg = 1.6, 0.8
+    a = oracle.kl_dense(H, W, idx, t, T, g=gg)
+    b = oracle.kl_chunked(H, W, idx, t, T, chunk=chunk, g=gg)
+    c = oracle.kl_fused(H, W, idx, t, T, chunk=chunk, vtile=vtile, g=gg)
+    for o in (b, c):
+        assert abs(o["loss"] - a["loss"]) <= 1e-12 * abs(a["loss"])
+        for key in ("lse", "row_kl", "zk", "dH", "dW"):
+            np.testing.assert_allclose(o[key], a[key], rtol=1e-12, atol=1e-14, err_msg=key)
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_shift_invariance():
+    """Every row of G sums to zero: sum_v dW[v,:] = 0, and adding the same vector to every
+    row of W leaves the loss and dH unchanged."""
+    N, d, V, K = 12, 7, 33, 6
+    H, W, idx, t = rand_problem(N, d, V, K, 90)
+    a = oracle.kl_dense(H, W, idx, t, 1.4)
+    np.testing.assert_allclose(a["dW"].sum(axis=0), 0.0, atol=1e-14)
+    c = np.random.default_rng(91).standard_normal(d)
+    b = oracle.kl_fused(H, W + c[None, :], idx, t, 1.4, chunk=5, vtile=8)
+    assert abs(a["loss"] - b["loss"]) <= 1e-12 * a["loss"]
+    np.testing.assert_allclose(a["dH"], b["dH"], rtol=1e-10, atol=1e-14)
+
+
+def test_linear_in_upstream_gradient():
+    N, d, V, K = 5, 4, 21, 3
+    H, W, idx, t = rand_problem(N, d, V, K, 100)
+    a = oracle.kl_dense(H, W, idx, t, 1.0, g=1.0)
+    b = oracle.kl_dense(H, W, idx, t, 1.0, g=-2.5)
+    np.testing.assert_allclose(b["dH"], -2.5 * a["dH"], rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(b["dW"], -2.5 * a["dW"], rtol=1e-14, atol=1e-16)
+    c = oracle.kl_dense(H, W, idx, t, 1.0, n_norm=2 * N)
+    np.testing.assert_allclose(c["dW"], 0.5 * a["dW"], rtol=1e-14, atol=1e-16)
+    assert abs(c["loss"] - 0.5 * a["loss"]) <= 1e-15
+
+
+def test_rejects_bad_ids():
+    H, W, idx, t = rand_problem(3, 4, 10, 3, 110)
+    bad = idx.copy()
+    bad[1, 2] = bad[1, 0]
+    with pytest.raises(ValueError):
+        oracle.kl_dense(H, W, bad, t, 1.0)
+    bad = idx.copy()
+    bad[0, 0] = 10
+    with pytest.raises(ValueError):
+        oracle.kl_fused(H, W, bad, t, 1.0, chunk=2, vtile=3)
+
+
+def test_topk_cache_matches_sort():
+    """The cache producer's oracle against a plain per-row sort, ties by lower id."""
+    g = np.random.default_rng(120)
+    x = np.round(g.standard_normal((6, 50)) * 2) / 2  # many ties
+    idx, vals = oracle.topk_cache(x, 7)
+    for n in range(6):
+        pairs = sorted(range(50), key=lambda v: (-x[n, v], v))[:7]
+        assert list(idx[n]) == pairs
+        np.testing.assert_array_equal(vals[n], x[n, pairs])
