@@ -1,0 +1,187 @@
+/*
+ * kdkl.h -- C ABI of libkdkl: the fused chunked top-K KL distillation loss over the LM head,
+ * forward and backward, on one AMD Instinct MI355X (gfx950).
+ *
+ * What it computes. The teacher side is an offline cache: for each sequence position, the
+ * K most probable teacher tokens and their logits, computed once and reused. Sources:
+ * "Making knowledge distillation cheap enough to run in production" (aiexpert.news),
+ * paragraph on the first fix (offline distillation); dailyai.com.br launch note, section
+ * "As duas inovacoes", item 1.
+ *
+ * The student side is the LM head applied to the student's last hidden states. The loss is
+ * the Kullback-Leibler divergence from the teacher's top-K distribution to the student's
+ * full-vocabulary distribution. Its fused chunked form projects one piece of the hidden
+ * states at a time, folds it into a running accumulator, discards it, and recomputes it in
+ * the backward pass. Source: same aiexpert.news article, paragraph on the second fix and
+ * its three equivalent formulations.
+ *
+ * It is a drop-in KL term: inputs are hidden states and the head weight, and nothing about
+ * the model changes. Source: same article, paragraph on the integration surface.
+ *
+ * With
+ *   H [N,d]    student hidden states, row-major (N = batch * sequence rows);
+ *   W [V,d]    LM-head weight, row-major (the layout of a torch nn.Linear(d, V) weight);
+ *   idx [N,K]  cached teacher token ids (int32, distinct within a row, in [0,V));
+ *   t [N,K]    cached teacher logits;
+ *   T          temperature;
+ *   z = H W^T  student logits, never stored whole;
+ *   u = z/T    tempered student logits;
+ *   lse_n = log sum_v exp(u_nv);
+ *   p_t = softmax(t/T) over the K cached entries (the tail beyond the top-K is dropped);
+ *   KL_n = sum_k p_t[n,k] * (log p_t[n,k] - u[n,idx[n,k]] + lse_n);
+ *   loss = T^2 / n_norm * sum_n KL_n;
+ *   with g = d(outer loss)/d(loss), the backward is
+ *     G = g * T / n_norm * (softmax(u) - P_t), P_t = p_t scattered at idx, zero elsewhere;
+ *     dH = G W;
+ *     dW = G^T H.
+ *
+ * Readings of points the pages leave open:
+ *   - KL direction is teacher -> student;
+ *   - temperature enters both sides and the loss carries T^2;
+ *   - the mean is over n_norm rows;
+ *   - the student is normalised over all V tokens.
+ *
+ * Conventions shared by every call:
+ *   - Memory: every pointer argument except `p` is device memory on the current HIP
+ *     device, allocated and owned by the caller. `p` is host memory. The library allocates,
+ *     frees and keeps nothing across calls. Calls that do not share output or workspace
+ *     buffers may run concurrently on different streams.
+ *   - Streams: work is enqueued on `stream`, an hipStream_t (NULL means the null stream).
+ *     Outputs are valid once the caller has synchronised that stream. No call synchronises,
+ *     except as noted for KD_VALIDATE_IDX.
+ *   - Errors: arguments are checked on the host before anything is enqueued, and a bad
+ *     argument returns its kd_status at once with nothing written. A launch failure returns
+ *     KD_ERR_HIP. A fault inside a kernel surfaces at the caller's next synchronisation of
+ *     the stream. No C++ exception crosses this interface.
+ *   - Preconditions the host cannot check without reading device memory: idx in [0,V) and
+ *     distinct within each row. Out-of-range ids are skipped, never dereferenced. Results
+ *     are undefined if the ids repeat. Set KD_VALIDATE_IDX to have them checked.
+ *   - Workspace: the caller passes ws (256-byte aligned) of at least the bytes returned by
+ *     the matching *_workspace_bytes query for the same problem. Its contents on entry do not
+ *     matter; on return they are unspecified.
+ */
+#ifndef KDKL_H
+#define KDKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDKL_ABI_VERSION 1
+
+/* Same type as hipStream_t; declared here so that this header does not need the HIP headers. */
+typedef struct ihipStream_t* kd_stream;
+
+typedef enum kd_status {
+    KD_OK = 0,
+    KD_ERR_NULL = 1,      /* a required pointer is NULL */
+    KD_ERR_SHAPE = 2,     /* N, d, V, K or chunk out of the supported range */
+    KD_ERR_DTYPE = 3,     /* unknown or unsupported dtype */
+    KD_ERR_VALUE = 4,     /* T not finite and > 0, or n_norm not finite, or unknown flag */
+    KD_ERR_WORKSPACE = 5, /* ws_bytes smaller than the query, or ws not 256-byte aligned */
+    KD_ERR_INDEX = 6,     /* KD_VALIDATE_IDX found an id out of range or repeated in a row */
+    KD_ERR_HIP = 7,       /* the HIP runtime reported an error while enqueueing */
+    KD_ERR_INTERNAL = 8
+} kd_status;
+
+typedef enum kd_dtype {
+    KD_FP32 = 0,
+    KD_BF16 = 1
+} kd_dtype;
+
+/* flags */
+#define KD_VALIDATE_IDX  0x1u /* check idx on the device first; this syncs the stream once */
+#define KD_ACCUMULATE_DW 0x2u /* kd_fused_kl_bwd / kd_dense_kl add into dW instead of overwriting */
+
+/*
+ * Problem descriptor (host memory).
+ *   N, d, V, K   sizes as above; limits: N >= 1, d >= 8 and d % 8 == 0, 1 <= V <= 4194304,
+ *                1 <= K <= min(V, 128), N * K < 2^31, N * d < 2^31, V * d < 2^31.
+ *   chunk        rows per backward chunk (>= 1; N need not be a multiple). It bounds the
+ *                backward's per-chunk gradient tile G_c [chunk, V] in the workspace. The
+ *                forward keeps each projected tile in registers only, so its memory does not
+ *                depend on chunk.
+ *   T            temperature, finite and > 0.
+ *   n_norm       denominator of the mean; <= 0 means N. Set it to the global row count when
+ *                one batch is split over several calls.
+ *   act          dtype of H, W and dH: KD_BF16 (fp32 accumulation) or KD_FP32 (fp32 products).
+ *   tlogit       dtype of the cached teacher logits t: KD_BF16 or KD_FP32.
+ *   flags        KD_VALIDATE_IDX | KD_ACCUMULATE_DW.
+ */
+typedef struct kd_problem {
+    int64_t N;
+    int64_t d;
+    int64_t V;
+    int64_t K;
+    int64_t chunk;
+    float T;
+    float n_norm;
+    int32_t act;
+    int32_t tlogit;
+    uint32_t flags;
+    uint32_t reserved; /* must be 0 */
+} kd_problem;
+
+/* ABI version of the loaded library (KDKL_ABI_VERSION it was built with). */
+int kd_abi_version(void);
+
+/* Static English text for a status code; never NULL. */
+const char* kd_status_str(kd_status s);
+
+/* Workspace bytes for kd_fused_kl_fwd and kd_fused_kl_bwd (one query serves both). Grows
+ * with N only through O(N*K) and O(N) terms; the rest is O(chunk * V + V). Returns 0 if p is
+ * NULL or invalid. */
+size_t kd_fused_workspace_bytes(const kd_problem* p);
+
+/*
+ * Fused forward.
+ *   H [N,d] act, W [V,d] act, idx [N,K] int32, tlog [N,K] tlogit       (inputs)
+ *   loss [1] fp32      T^2/n_norm * sum_n KL_n                          (output)
+ *   lse [N] fp32       logsumexp_v z_nv/T; the backward needs it        (output)
+ *   row_kl [N] fp32    KL_n, or NULL to skip                            (output)
+ *   zk [N,K] fp32      z at the cached ids, z[n, idx[n,k]], or NULL     (output)
+ * Source: aiexpert.news "Making knowledge distillation cheap enough...", paragraph on the
+ * three formulations (the fused chunked forward).
+ */
+kd_status kd_fused_kl_fwd(const kd_problem* p, const void* H, const void* W, const int32_t* idx,
+                          const void* tlog, float* loss, float* lse, float* row_kl, float* zk,
+                          void* ws, size_t ws_bytes, kd_stream stream);
+
+/*
+ * Fused backward: recomputes each chunk's logits instead of storing them.
+ *   H, W, idx, tlog        as in the forward
+ *   lse [N] fp32           from kd_fused_kl_fwd on the same inputs
+ *   grad_loss [1] fp32     upstream gradient g of the scalar loss (device), or NULL for 1
+ *   dH [N,d] act           written (overwritten)
+ *   dW [V,d] fp32          overwritten, or incremented under KD_ACCUMULATE_DW
+ * Source: same paragraph (the backward recomputes each chunk on the fly); dailyai.com.br
+ * launch note, section "As duas inovacoes", item 2.
+ */
+kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, const int32_t* idx,
+                          const void* tlog, const float* lse, const float* grad_loss, void* dH,
+                          float* dW, void* ws, size_t ws_bytes, kd_stream stream);
+
+/* Workspace bytes for kd_dense_kl: two fp32 [N, V] grids (rounded up to whole tiles) plus a
+ * small remainder. Returns 0 if p is NULL or invalid. */
+size_t kd_dense_workspace_bytes(const kd_problem* p);
+
+/*
+ * Dense formulation, forward and backward in one call, for memory and speed comparison.
+ * It expands the cached teacher into a full [N, V] probability grid and compares it with the
+ * full [N, V] student log-probability grid, so two vocabulary-by-sequence grids are resident
+ * at once. Source: aiexpert.news article, paragraph on the three formulations (dense KL).
+ *   Arguments as in the two fused calls; row_kl may be NULL. Same results up to rounding.
+ */
+kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const int32_t* idx,
+                      const void* tlog, const float* grad_loss, float* loss, float* lse,
+                      float* row_kl, void* dH, float* dW, void* ws, size_t ws_bytes,
+                      kd_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDKL_H */

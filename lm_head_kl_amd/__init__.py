@@ -1,0 +1,182 @@
+"""lm_head_kl_amd: the fused chunked top-K KL distillation loss over the LM head on MI355X.
+
+Python binding of libkdkl (include/kdkl.h). This layer only marshals arguments. PyTorch
+supplies device memory (outputs and workspace come from torch.empty on the inputs' device)
+and the current HIP stream. Every step of the computation runs in the library's HIP
+kernels; there is no CPU or PyTorch fallback.
+
+The loss is a drop-in KL term for a distillation loop: hidden states and the LM-head weight
+go in, the offline top-K teacher cache is the target. Source: "Making knowledge distillation
+cheap enough to run in production" (aiexpert.news), paragraphs on the two fixes and on the
+integration surface.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import KD_ACCUMULATE_DW, KD_BF16, KD_FP32, KD_VALIDATE_IDX, KdError, KdProblem
+
+__all__ = [
+    "FusedKL",
+    "fused_kl",
+    "fused_kl_fwd",
+    "fused_kl_bwd",
+    "dense_kl",
+    "fused_workspace_bytes",
+    "dense_workspace_bytes",
+    "make_problem",
+    "KdError",
+    "KD_VALIDATE_IDX",
+    "KD_ACCUMULATE_DW",
+]
+
+_DT = {torch.bfloat16: KD_BF16, torch.float32: KD_FP32}
+
+
+def make_problem(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, tlog: torch.Tensor, T: float,
+                 chunk: int, n_norm: float = 0.0, flags: int = 0) -> KdProblem:
+    if H.dtype not in _DT or W.dtype != H.dtype:
+        raise KdError(3, "make_problem", "H and W must both be bfloat16 or both float32")
+    if tlog.dtype not in _DT:
+        raise KdError(3, "make_problem", "teacher logits must be bfloat16 or float32")
+    if idx.dtype != torch.int32:
+        raise KdError(3, "make_problem", "idx must be int32")
+    N, d = H.shape
+    V, d2 = W.shape
+    if d2 != d or tuple(idx.shape) != tuple(tlog.shape) or idx.shape[0] != N:
+        raise KdError(2, "make_problem", f"shape mismatch H{tuple(H.shape)} W{tuple(W.shape)} "
+                                         f"idx{tuple(idx.shape)} t{tuple(tlog.shape)}")
+    return KdProblem(N=N, d=d, V=V, K=idx.shape[1], chunk=int(chunk), T=float(T), n_norm=float(n_norm),
+                     act=_DT[H.dtype], tlogit=_DT[tlog.dtype], flags=int(flags), reserved=0)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need_device(*ts):
+    dev = ts[0].device
+    for t in ts:
+        if t is None:
+            continue
+        if t.device.type != "cuda" or t.device != dev:
+            raise KdError(1, "lm_head_kl_amd", "all tensors must be on the same GPU")
+        if not t.is_contiguous():
+            raise KdError(2, "lm_head_kl_amd", "tensors must be contiguous (row-major)")
+    return dev
+
+
+def fused_workspace_bytes(p: KdProblem) -> int:
+    return int(_lib.lib().kd_fused_workspace_bytes(ctypes.byref(p)))
+
+
+def dense_workspace_bytes(p: KdProblem) -> int:
+    return int(_lib.lib().kd_dense_workspace_bytes(ctypes.byref(p)))
+
+
+def _workspace(nbytes: int, dev) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+
+@dataclass
+class FwdOut:
+    loss: torch.Tensor    # [] fp32
+    lse: torch.Tensor     # [N] fp32
+    row_kl: torch.Tensor  # [N] fp32 or None
+    zk: torch.Tensor      # [N,K] fp32 or None
+
+
+def fused_kl_fwd(H, W, idx, tlog, T: float = 1.0, chunk: int = 2048, n_norm: float = 0.0,
+                 flags: int = 0, want_row_kl: bool = True, want_zk: bool = False,
+                 workspace: torch.Tensor | None = None) -> FwdOut:
+    """kd_fused_kl_fwd. Returns loss (0-d), lse [N], and optionally row_kl [N] and zk [N,K]."""
+    dev = _need_device(H, W, idx, tlog)
+    p = make_problem(H, W, idx, tlog, T, chunk, n_norm, flags)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(p.N, dtype=torch.float32, device=dev)
+    row_kl = torch.empty(p.N, dtype=torch.float32, device=dev) if want_row_kl else None
+    zk = torch.empty((p.N, p.K), dtype=torch.float32, device=dev) if want_zk else None
+    nb = fused_workspace_bytes(p)
+    ws = workspace if workspace is not None and workspace.numel() >= nb else _workspace(nb, dev)
+    code = _lib.lib().kd_fused_kl_fwd(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlog), _ptr(loss),
+                                      _ptr(lse), _ptr(row_kl), _ptr(zk), _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check(code, "kd_fused_kl_fwd")
+    return FwdOut(loss, lse, row_kl, zk)
+
+
+def fused_kl_bwd(H, W, idx, tlog, lse, grad_loss=None, T: float = 1.0, chunk: int = 2048,
+                 n_norm: float = 0.0, flags: int = 0, dW: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None):
+    """kd_fused_kl_bwd. Returns (dH [N,d] in H's dtype, dW [V,d] fp32). grad_loss is a device
+    scalar tensor or None (= 1). With KD_ACCUMULATE_DW, pass dW to add into."""
+    dev = _need_device(H, W, idx, tlog, lse)
+    p = make_problem(H, W, idx, tlog, T, chunk, n_norm, flags)
+    dH = torch.empty_like(H)
+    if dW is None:
+        if flags & KD_ACCUMULATE_DW:
+            raise KdError(1, "fused_kl_bwd", "KD_ACCUMULATE_DW needs a dW tensor")
+        dW = torch.empty(W.shape, dtype=torch.float32, device=dev)
+    elif dW.dtype != torch.float32 or tuple(dW.shape) != tuple(W.shape):
+        raise KdError(3, "fused_kl_bwd", "dW must be float32 with W's shape")
+    g = None
+    if grad_loss is not None:
+        g = grad_loss.detach().to(device=dev, dtype=torch.float32).reshape(1).contiguous()
+    nb = fused_workspace_bytes(p)
+    ws = workspace if workspace is not None and workspace.numel() >= nb else _workspace(nb, dev)
+    code = _lib.lib().kd_fused_kl_bwd(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlog), _ptr(lse),
+                                      _ptr(g), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check(code, "kd_fused_kl_bwd")
+    return dH, dW
+
+
+def dense_kl(H, W, idx, tlog, T: float = 1.0, grad_loss=None, n_norm: float = 0.0, flags: int = 0,
+             want_row_kl: bool = True):
+    """kd_dense_kl: loss, lse, row_kl, dH, dW through two dense [N, V] grids."""
+    dev = _need_device(H, W, idx, tlog)
+    p = make_problem(H, W, idx, tlog, T, 1, n_norm, flags)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(p.N, dtype=torch.float32, device=dev)
+    row_kl = torch.empty(p.N, dtype=torch.float32, device=dev) if want_row_kl else None
+    dH = torch.empty_like(H)
+    dW = torch.empty(W.shape, dtype=torch.float32, device=dev)
+    g = None
+    if grad_loss is not None:
+        g = grad_loss.detach().to(device=dev, dtype=torch.float32).reshape(1).contiguous()
+    ws = _workspace(dense_workspace_bytes(p), dev)
+    code = _lib.lib().kd_dense_kl(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlog), _ptr(g), _ptr(loss),
+                                  _ptr(lse), _ptr(row_kl), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(),
+                                  _stream(dev))
+    _lib.check(code, "kd_dense_kl")
+    return loss, lse, row_kl, dH, dW
+
+
+class FusedKL(torch.autograd.Function):
+    """loss = FusedKL.apply(H, W, idx, tlog, T, chunk, n_norm): the KL term of a distillation
+    step. The forward saves only lse [N]; the backward recomputes the logits chunk by chunk."""
+
+    @staticmethod
+    def forward(ctx, H, W, idx, tlog, T=1.0, chunk=2048, n_norm=0.0):
+        out = fused_kl_fwd(H, W, idx, tlog, T=T, chunk=chunk, n_norm=n_norm, want_row_kl=False)
+        ctx.save_for_backward(H, W, idx, tlog, out.lse)
+        ctx.cfg = (T, chunk, n_norm)
+        return out.loss
+
+    @staticmethod
+    def backward(ctx, g):
+        H, W, idx, tlog, lse = ctx.saved_tensors
+        T, chunk, n_norm = ctx.cfg
+        dH, dW = fused_kl_bwd(H, W, idx, tlog, lse, grad_loss=g, T=T, chunk=chunk, n_norm=n_norm)
+        return dH, dW.to(W.dtype), None, None, None, None, None
+
+
+def fused_kl(H, W, idx, tlog, T: float = 1.0, chunk: int = 2048, n_norm: float = 0.0):
+    return FusedKL.apply(H, W, idx, tlog, T, chunk, n_norm)

@@ -1,0 +1,97 @@
+"""ctypes loader for libkdkl.so and the C structures of include/kdkl.h.
+
+Loading needs no GPU: the library links the HIP runtime, which is installed on every host
+of this image. Compute calls need a gfx950 device.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkdkl.so")
+
+KD_FP32, KD_BF16 = 0, 1
+KD_VALIDATE_IDX, KD_ACCUMULATE_DW = 0x1, 0x2
+
+STATUS = {
+    0: "KD_OK",
+    1: "KD_ERR_NULL",
+    2: "KD_ERR_SHAPE",
+    3: "KD_ERR_DTYPE",
+    4: "KD_ERR_VALUE",
+    5: "KD_ERR_WORKSPACE",
+    6: "KD_ERR_INDEX",
+    7: "KD_ERR_HIP",
+    8: "KD_ERR_INTERNAL",
+}
+
+# Every symbol include/kdkl.h declares.
+EXPORTS = (
+    "kd_abi_version",
+    "kd_status_str",
+    "kd_fused_workspace_bytes",
+    "kd_fused_kl_fwd",
+    "kd_fused_kl_bwd",
+    "kd_dense_workspace_bytes",
+    "kd_dense_kl",
+)
+
+
+class KdProblem(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int64),
+        ("d", ctypes.c_int64),
+        ("V", ctypes.c_int64),
+        ("K", ctypes.c_int64),
+        ("chunk", ctypes.c_int64),
+        ("T", ctypes.c_float),
+        ("n_norm", ctypes.c_float),
+        ("act", ctypes.c_int32),
+        ("tlogit", ctypes.c_int32),
+        ("flags", ctypes.c_uint32),
+        ("reserved", ctypes.c_uint32),
+    ]
+
+
+class KdError(RuntimeError):
+    def __init__(self, code: int, where: str, text: str):
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({text})")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library. Raises if it has not been built: there is no fallback path."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libkdkl.so not found at {LIB_PATH}; build it with "
+                          f"`python -m lm_head_kl_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, sz, P = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(KdProblem)
+    L.kd_abi_version.restype = ctypes.c_int
+    L.kd_abi_version.argtypes = []
+    L.kd_status_str.restype = ctypes.c_char_p
+    L.kd_status_str.argtypes = [ctypes.c_int]
+    L.kd_fused_workspace_bytes.restype = sz
+    L.kd_fused_workspace_bytes.argtypes = [P]
+    L.kd_dense_workspace_bytes.restype = sz
+    L.kd_dense_workspace_bytes.argtypes = [P]
+    L.kd_fused_kl_fwd.restype = ctypes.c_int
+    L.kd_fused_kl_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kd_fused_kl_bwd.restype = ctypes.c_int
+    L.kd_fused_kl_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kd_dense_kl.restype = ctypes.c_int
+    L.kd_dense_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    _lib = L
+    return L
+
+
+def check(code: int, where: str) -> None:
+    if code != 0:
+        raise KdError(code, where, lib().kd_status_str(code).decode())

@@ -1,0 +1,281 @@
+// C ABI of libkdkl (declared in include/kdkl.h): argument checks, workspace layout and the
+// order of kernel launches. All arithmetic lives in kdkl_kernels.hip.
+//
+// Orchestration follows the pages' fused chunked KL loss ("Making knowledge distillation
+// cheap enough to run in production", paragraph on the second fix):
+//   forward   one pass over all rows. Every 256 x 256 logit tile lives in registers only;
+//             it is folded into per-row running (max, sum) partials and the gather of the
+//             cached ids, then dropped.
+//   backward  one pass per chunk of rows. Recompute the chunk's logit tiles, form the
+//             gradient tile G_c [chunk, V] in the workspace, then dH = G_c W for those rows
+//             and dW += G_c^T H_c.
+// So peak memory depends on the sequence only through H, dH and the O(N*K) cache terms.
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "kdkl.h"
+#include "kdkl_internal.h"
+
+using namespace kdkl;
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+
+struct Carve {
+    uintptr_t base;
+    size_t used = 0;
+    explicit Carve(void* p) : base((uintptr_t)p) {}
+    void* take(size_t bytes) {
+        used = (size_t)round_up((int64_t)used, kAlign);
+        void* p = (void*)(base + used);
+        used += bytes;
+        return p;
+    }
+};
+
+int64_t n_vtiles(int64_t V) { return (V + kTileN - 1) / kTileN; }
+int64_t n_rblocks(int64_t rows) { return (rows + kTileM - 1) / kTileM; }
+size_t esize(int32_t dt) { return dt == KD_BF16 ? 2 : 4; }
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Host-side checks; nothing is enqueued before they pass.
+kd_status check_problem(const kd_problem* p) {
+    if (!p) return KD_ERR_NULL;
+    if (p->act != KD_FP32 && p->act != KD_BF16) return KD_ERR_DTYPE;
+    if (p->tlogit != KD_FP32 && p->tlogit != KD_BF16) return KD_ERR_DTYPE;
+    if (p->N < 1 || p->d < 8 || p->d % 8 != 0 || p->V < 1 || p->V > (int64_t)kTileN * kMaxVTiles) return KD_ERR_SHAPE;
+    if (p->K < 1 || p->K > kMaxK || p->K > p->V || p->chunk < 1) return KD_ERR_SHAPE;
+    const int64_t lim = (int64_t)1 << 31;
+    if ((p->N + kTileM) * p->K >= lim || p->N * p->d >= lim || p->V * p->d >= lim) return KD_ERR_SHAPE;
+    if (!std::isfinite(p->T) || !(p->T > 0.f)) return KD_ERR_VALUE;
+    if (!std::isfinite(p->n_norm)) return KD_ERR_VALUE;
+    if ((p->flags & ~(KD_VALIDATE_IDX | KD_ACCUMULATE_DW)) != 0 || p->reserved != 0) return KD_ERR_VALUE;
+    return KD_OK;
+}
+
+Shape make_shape(const kd_problem* p) {
+    Shape s;
+    s.N = p->N;
+    s.d = p->d;
+    s.V = p->V;
+    s.K = p->K;
+    s.T = p->T;
+    s.n_norm = p->n_norm > 0.f ? p->n_norm : (float)p->N;
+    s.act = p->act == KD_BF16 ? Dt::BF16 : Dt::F32;
+    s.tlog = p->tlogit == KD_BF16 ? Dt::BF16 : Dt::F32;
+    return s;
+}
+
+int64_t chunk_rows(const kd_problem* p) { return std::min(p->chunk, p->N); }
+
+// Workspace of the fused calls. The forward and backward parts are disjoint in time, so they
+// overlap in the workspace; the query returns the larger of the two.
+struct FusedWs {
+    int32_t* plan_off;
+    uint32_t* plan_ent;
+    float2* part;
+    float* zk;
+    double* blk_sum;
+    uint32_t* status;
+    // backward
+    int32_t* cplan_off;
+    uint32_t* cplan_ent;
+    float* pt;
+    void* Gc;
+    float* dh_part;
+    int64_t ldg;
+    int n_vsplit, n_split;
+    size_t fwd_bytes, bwd_bytes;
+};
+
+FusedWs layout_fused(const kd_problem* p, void* ws) {
+    FusedWs w{};
+    const int64_t N = p->N, K = p->K, V = p->V, d = p->d;
+    const int64_t n_vt = n_vtiles(V), Vp = n_vt * kTileN;
+    const int64_t C = chunk_rows(p);
+    w.n_vsplit = fwd_vsplits(N, V);
+    w.n_split = dh_splits(C, d, V);
+    w.ldg = Vp;
+    Carve f(ws);
+    w.status = (uint32_t*)f.take(kAlign);
+    w.plan_off = (int32_t*)f.take(sizeof(int32_t) * n_rblocks(N) * (n_vt + 1));
+    w.plan_ent = (uint32_t*)f.take(sizeof(uint32_t) * n_rblocks(N) * kTileM * K);
+    w.part = (float2*)f.take(sizeof(float2) * 2 * w.n_vsplit * N);
+    w.zk = (float*)f.take(sizeof(float) * N * K);
+    w.blk_sum = (double*)f.take(sizeof(double) * combine_blocks(N));
+    w.fwd_bytes = f.used;
+    Carve b(ws);
+    b.take(kAlign);  // status word shared with the forward layout
+    w.cplan_off = (int32_t*)b.take(sizeof(int32_t) * n_rblocks(C) * (n_vt + 1));
+    w.cplan_ent = (uint32_t*)b.take(sizeof(uint32_t) * n_rblocks(C) * kTileM * K);
+    w.pt = (float*)b.take(sizeof(float) * C * K);
+    w.Gc = b.take(esize(p->act) * C * Vp);
+    w.dh_part = w.n_split > 1 ? (float*)b.take(sizeof(float) * w.n_split * C * d) : nullptr;
+    w.bwd_bytes = b.used;
+    return w;
+}
+
+struct DenseWs {
+    float* Z;
+    float* P;
+    int64_t ldz;
+    double* row_sum;
+    double* blk_sum;
+    float* dh_part;
+    uint32_t* status;
+    int n_split;
+    size_t bytes;
+};
+
+DenseWs layout_dense(const kd_problem* p, void* ws) {
+    DenseWs w{};
+    const int64_t N = p->N, Vp = n_vtiles(p->V) * kTileN;
+    w.ldz = Vp;
+    w.n_split = dh_splits(N, p->d, p->V);
+    Carve c(ws);
+    w.status = (uint32_t*)c.take(kAlign);
+    w.Z = (float*)c.take(sizeof(float) * N * Vp);
+    w.P = (float*)c.take(sizeof(float) * N * Vp);
+    w.row_sum = (double*)c.take(sizeof(double) * N);
+    w.blk_sum = (double*)c.take(sizeof(double) * ((N + 1023) / 1024));
+    w.dh_part = w.n_split > 1 ? (float*)c.take(sizeof(float) * w.n_split * N * p->d) : nullptr;
+    w.bytes = c.used;
+    return w;
+}
+
+#define KD_TRY(x)                                  \
+    do {                                           \
+        if ((x) != hipSuccess) return KD_ERR_HIP;  \
+    } while (0)
+
+kd_status validate_ids(const kd_problem* p, const int32_t* idx, uint32_t* status, hipStream_t s) {
+    KD_TRY(launch_validate(idx, p->N, p->K, p->V, status, s));
+    uint32_t h = 0;
+    KD_TRY(hipMemcpyAsync(&h, status, sizeof(h), hipMemcpyDeviceToHost, s));
+    KD_TRY(hipStreamSynchronize(s));
+    return h ? KD_ERR_INDEX : KD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kd_abi_version(void) { return KDKL_ABI_VERSION; }
+
+const char* kd_status_str(kd_status s) {
+    switch (s) {
+        case KD_OK: return "ok";
+        case KD_ERR_NULL: return "a required pointer is NULL";
+        case KD_ERR_SHAPE: return "a size is out of the supported range";
+        case KD_ERR_DTYPE: return "unsupported dtype";
+        case KD_ERR_VALUE: return "invalid value (temperature, n_norm, flags, reserved or alignment)";
+        case KD_ERR_WORKSPACE: return "workspace too small or misaligned";
+        case KD_ERR_INDEX: return "a cached token id is out of range or repeated within a row";
+        case KD_ERR_HIP: return "the HIP runtime reported an error";
+        case KD_ERR_INTERNAL: return "internal error";
+    }
+    return "unknown status";
+}
+
+size_t kd_fused_workspace_bytes(const kd_problem* p) {
+    if (check_problem(p) != KD_OK) return 0;
+    const FusedWs w = layout_fused(p, nullptr);
+    return std::max(w.fwd_bytes, w.bwd_bytes);
+}
+
+size_t kd_dense_workspace_bytes(const kd_problem* p) {
+    if (check_problem(p) != KD_OK) return 0;
+    return layout_dense(p, nullptr).bytes;
+}
+
+kd_status kd_fused_kl_fwd(const kd_problem* p, const void* H, const void* W, const int32_t* idx, const void* tlog,
+                          float* loss, float* lse, float* row_kl, float* zk, void* ws, size_t ws_bytes,
+                          kd_stream stream) {
+    kd_status st = check_problem(p);
+    if (st != KD_OK) return st;
+    if (!H || !W || !idx || !tlog || !loss || !lse || !ws) return KD_ERR_NULL;
+    if (!aligned(H, 16) || !aligned(W, 16)) return KD_ERR_VALUE;
+    if (!aligned(ws, kAlign) || ws_bytes < kd_fused_workspace_bytes(p)) return KD_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();  // start from a clean error state
+    const Shape sh = make_shape(p);
+    const FusedWs w = layout_fused(p, ws);
+    if (p->flags & KD_VALIDATE_IDX) {
+        st = validate_ids(p, idx, w.status, s);
+        if (st != KD_OK) return st;
+    }
+    float* zk_out = zk ? zk : w.zk;
+    KD_TRY(launch_plan(idx, 0, p->N, p->K, p->V, w.plan_off, w.plan_ent, s));
+    KD_TRY(launch_fwd(sh, H, W, w.plan_off, w.plan_ent, w.n_vsplit, w.part, zk_out, s));
+    int n_blk = 0;
+    KD_TRY(launch_combine(sh, w.part, 2 * w.n_vsplit, zk_out, tlog, lse, row_kl, w.blk_sum, &n_blk, s));
+    KD_TRY(launch_loss_final(sh, w.blk_sum, n_blk, loss, s));
+    return KD_OK;
+}
+
+kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, const int32_t* idx, const void* tlog,
+                          const float* lse, const float* grad_loss, void* dH, float* dW, void* ws, size_t ws_bytes,
+                          kd_stream stream) {
+    kd_status st = check_problem(p);
+    if (st != KD_OK) return st;
+    if (!H || !W || !idx || !tlog || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16)) return KD_ERR_VALUE;
+    if (!aligned(ws, kAlign) || ws_bytes < kd_fused_workspace_bytes(p)) return KD_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    const Shape sh = make_shape(p);
+    const FusedWs w = layout_fused(p, ws);
+    if (p->flags & KD_VALIDATE_IDX) {
+        st = validate_ids(p, idx, w.status, s);
+        if (st != KD_OK) return st;
+    }
+    const int64_t C = chunk_rows(p);
+    const bool acc0 = (p->flags & KD_ACCUMULATE_DW) != 0;
+    for (int64_t c0 = 0; c0 < p->N; c0 += C) {
+        const int64_t cc = std::min(C, p->N - c0);
+        KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.cplan_off, w.cplan_ent, s));
+        KD_TRY(launch_teacher_prob(tlog, sh.tlog, c0, c0 + cc, p->K, p->T, w.pt, s));
+        KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt, grad_loss, c0, cc, w.cplan_off, w.cplan_ent, w.Gc, w.ldg, s));
+        KD_TRY(launch_dh(sh, w.Gc, w.ldg, W, c0, cc, w.n_split, w.dh_part, dH, s));
+        KD_TRY(launch_dw(sh, w.Gc, w.ldg, H, c0, cc, acc0 || c0 > 0, dW, s));
+    }
+    return KD_OK;
+}
+
+kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const int32_t* idx, const void* tlog,
+                      const float* grad_loss, float* loss, float* lse, float* row_kl, void* dH, float* dW, void* ws,
+                      size_t ws_bytes, kd_stream stream) {
+    kd_status st = check_problem(p);
+    if (st != KD_OK) return st;
+    if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16)) return KD_ERR_VALUE;
+    if (!aligned(ws, kAlign) || ws_bytes < kd_dense_workspace_bytes(p)) return KD_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    const Shape sh = make_shape(p);
+    const DenseWs w = layout_dense(p, ws);
+    if (p->flags & KD_VALIDATE_IDX) {
+        st = validate_ids(p, idx, w.status, s);
+        if (st != KD_OK) return st;
+    }
+    KD_TRY(launch_dense_logits(sh, H, W, w.Z, w.ldz, s));
+    KD_TRY(launch_dense_rows(sh, w.Z, w.P, w.ldz, idx, tlog, grad_loss, lse, row_kl, w.row_sum, nullptr, 0, s));
+    int n_blk = 0;
+    KD_TRY(launch_sum_rows(sh, w.row_sum, w.blk_sum, &n_blk, s));
+    KD_TRY(launch_loss_final(sh, w.blk_sum, n_blk, loss, s));
+    // G: bf16 over the logits grid (row stride 2*Vp elements), or fp32 in the teacher grid.
+    const void* G = sh.act == Dt::BF16 ? (const void*)w.Z : (const void*)w.P;
+    const int64_t ldg = sh.act == Dt::BF16 ? 2 * w.ldz : w.ldz;
+    KD_TRY(launch_dh(sh, G, ldg, W, 0, p->N, w.n_split, w.dh_part, dH, s));
+    KD_TRY(launch_dw(sh, G, ldg, H, 0, p->N, (p->flags & KD_ACCUMULATE_DW) != 0, dW, s));
+    return KD_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,88 @@
+// Internal interface between the C ABI (kdkl_api.cpp) and the HIP kernels (kdkl_kernels.hip).
+// Plain C++ types only; not installed, not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kdkl {
+
+// Workgroup tile of every MFMA kernel: 256 rows x 256 columns. The top-K entry plan buckets
+// cached ids by the same tile, so both constants are shared with the host code.
+constexpr int kTileM = 256;
+constexpr int kTileN = 256;
+constexpr int kMaxK = 128;
+constexpr int kMaxVTiles = 16384;  // plan kernel keeps one LDS counter per vocab tile
+
+enum class Dt : int { F32 = 0, BF16 = 1 };
+
+struct Shape {
+    int64_t N, d, V, K;
+    float T;
+    float n_norm;  // resolved: > 0
+    Dt act, tlog;
+};
+
+// Launchers return hipSuccess or the launch error.  All enqueue on `s`.
+
+// Bucket the cached ids of rows [row0, row1) by (row block of 256, vocab tile of 256).
+// off: [n_rb][n_vt + 1] int32 (absolute entry offsets), ent: [n_rb * 256 * K] uint32 packed
+// (row in block | col in tile << 8 | k << 16).
+hipError_t launch_plan(const int32_t* idx, int64_t row0, int64_t row1, int64_t K, int64_t V,
+                       int32_t* off, uint32_t* ent, hipStream_t s);
+
+// p_t[n,k] = softmax(t[n,:]/T)[k] for rows [row0, row1), written to pt[(n-row0)*K + k].
+hipError_t launch_teacher_prob(const void* tlog, Dt tdt, int64_t row0, int64_t row1, int64_t K,
+                               float T, float* pt, hipStream_t s);
+
+// Check ids: bit 0 = out of range, bit 1 = repeated in a row; ORed into *status (zeroed first).
+hipError_t launch_validate(const int32_t* idx, int64_t N, int64_t K, int64_t V, uint32_t* status,
+                           hipStream_t s);
+
+// Fused forward over all N rows: per (row block, vocab split) partial (max, sum) in the
+// log2 domain, and zk at every cached id.
+hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32_t* plan_off,
+                      const uint32_t* plan_ent, int n_vsplit, float2* part, float* zk,
+                      hipStream_t s);
+
+// Merge partials into lse, compute KL_n (row_kl) and per-block fp64 partial sums.
+hipError_t launch_combine(const Shape& sh, const float2* part, int n_part, const float* zk,
+                          const void* tlog, float* lse, float* row_kl, double* blk_sum,
+                          int* n_blk_out, hipStream_t s);
+int combine_blocks(int64_t N);
+
+// loss[0] = T^2/n_norm * sum(blk_sum[0..n_blk)) in a fixed order.
+hipError_t launch_loss_final(const Shape& sh, const double* blk_sum, int n_blk, float* loss,
+                             hipStream_t s);
+
+// Backward, one chunk of rows [c0, c0 + cc):
+//   G_c [cc, ldg] (act dtype, columns >= V are zero) = g*T/n_norm*(softmax(z/T) - P_t)
+hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const float* lse,
+                           const float* pt, const float* grad_loss, int64_t c0, int64_t cc,
+                           const int32_t* plan_off, const uint32_t* plan_ent, void* Gc,
+                           int64_t ldg, hipStream_t s);
+
+// dH rows [c0, c0+cc) = G_c W; split over the vocabulary into n_split fp32 partials when
+// n_split > 1 (part: [n_split][cc][d]), then reduced in a fixed order.
+hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, int64_t c0,
+                     int64_t cc, int n_split, float* part, void* dH, hipStream_t s);
+
+// dW (+)= G_c^T H[c0:c0+cc]
+hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H, int64_t c0,
+                     int64_t cc, bool accumulate, float* dW, hipStream_t s);
+
+// Dense path pieces.
+hipError_t launch_dense_logits(const Shape& sh, const void* H, const void* W, float* Z, int64_t ldz,
+                               hipStream_t s);
+hipError_t launch_dense_rows(const Shape& sh, float* Z, float* P, int64_t ldz, const int32_t* idx,
+                             const void* tlog, const float* grad_loss, float* lse, float* row_kl,
+                             double* row_sum, void* G, int64_t ldg, hipStream_t s);
+hipError_t launch_sum_rows(const Shape& sh, const double* row_sum, double* blk_sum, int* n_blk,
+                           hipStream_t s);
+
+int64_t round_up(int64_t x, int64_t m);
+int dh_splits(int64_t cc, int64_t d, int64_t V);
+int fwd_vsplits(int64_t N, int64_t V);
+
+}  // namespace kdkl

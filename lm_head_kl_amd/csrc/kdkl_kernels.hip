@@ -1,0 +1,1141 @@
+// HIP kernels of libkdkl for gfx950 (MI355X): the fused chunked top-K KL loss over the LM head.
+//
+// What is computed follows the pages' description of the fused chunked KL loss:
+// "Making knowledge distillation cheap enough to run in production" (aiexpert.news),
+// paragraph on the second fix. The hidden states are projected to logits one piece at a
+// time; each piece is folded into a running loss accumulator and then discarded; the
+// backward pass recomputes each piece. The teacher side is the top-K cache from the
+// paragraph on the first fix.
+//
+// Everything here is built on one MFMA tile engine. A workgroup of 256 threads (four
+// 64-wide waves in a 2x2 grid) computes a 256 x 256 fp32 tile of C = A B^T:
+//   - each wave owns 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16
+//     (v_mfma_f32_32x32x2_f32 for fp32 inputs);
+//   - both operands are staged through LDS, double-buffered over K, in 16-byte chunks;
+//   - the chunk position is XOR-swizzled by row so that fragment reads and tile writes are
+//     free of bank conflicts.
+// An operand stored with K contiguous is copied chunk by chunk. An operand stored with its
+// M/N index contiguous (W in dH = G W; G and H in dW = G^T H) is loaded as 8x8 (bf16) or
+// 4x4 (fp32) blocks and transposed in registers on the way to LDS. So every GEMM of the
+// path reads K-contiguous fragments, and no transposed copy of W, H or G is ever made.
+//
+// Epilogues:
+//   forward   online (max, sum) per row in the log2 domain, reduced across lanes with a
+//             reduce-scatter butterfly; gather of z at the cached ids through an LDS-staged
+//             copy of the tile;
+//   backward  G = g*T/n_norm*(softmax(z/T) - P_t), with P_t subtracted in the LDS-staged
+//             tile, then stored row-major in the activation dtype;
+//   dH        fp32 split-K partials or a direct store;
+//   dW        fp32 read-modify-write.
+//
+// MFMA lane layouts (checked on gfx950 hardware):
+//   32x32x16 bf16: lane l supplies A[m = l%32][k = 8*(l/32) + 0..7], B likewise with n.
+//   32x32x2 f32:   lane l supplies A[m = l%32][k = l/32].
+//   Accumulator element e of lane l: row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "kdkl_internal.h"
+
+namespace kdkl {
+
+typedef uint16_t bf16_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int NTHR = 256;
+constexpr int NCH = 8;                 // 16-byte chunks per tile row per K step
+constexpr int TILE_CHUNKS = kTileM * NCH;  // 2048 chunks = 32 KB per operand per stage
+constexpr int LDS_CHUNKS = 4 * TILE_CHUNKS;  // 2 stages x 2 operands = 128 KB
+constexpr int STG = kTileN + 4;        // staging row stride in floats (16-byte aligned)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLn2 = 0.69314718055994530942;
+
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> { static constexpr int VEC = 8; static constexpr int BK = 64; };
+template <> struct Elem<float> { static constexpr int VEC = 4; static constexpr int BK = 32; };
+
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint32_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+template <typename T> __device__ __forceinline__ float load_scalar(const T* p, int64_t i);
+template <> __device__ __forceinline__ float load_scalar<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ __forceinline__ float load_scalar<bf16_t>(const bf16_t* p, int64_t i) { return bf2f(p[i]); }
+
+__device__ __forceinline__ float load_t(const void* p, Dt dt, int64_t i) {
+    return dt == Dt::BF16 ? bf2f(((const bf16_t*)p)[i]) : ((const float*)p)[i];
+}
+
+template <typename T> __device__ __forceinline__ void mma(f32x16& c, const u32x4& a, const u32x4& b);
+template <> __device__ __forceinline__ void mma<bf16_t>(f32x16& c, const u32x4& a, const u32x4& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ void mma<float>(f32x16& c, const u32x4& a, const u32x4& b) {
+    // One 16-byte chunk holds 4 consecutive k; the two lane halves hold neighbouring chunks.
+    // Instruction i takes element i of each, so together they cover 8 distinct k, the same
+    // ones for A and B.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i]), __uint_as_float(b[i]), c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------------------------------
+// Operand loaders: global -> registers (8 x 16 bytes per thread) -> LDS tile [256 rows][8 chunks].
+
+// K contiguous: element (mn, k) at src[mn*ld + k]. Thread takes chunks q = tid + 256*t.
+template <typename T>
+__device__ __forceinline__ void load_kmaj(u32x4 (&r)[8], const T* src, int64_t ld, int64_t mn0,
+                                          int64_t mn_lim, int64_t k0, int64_t k_lim, int tid) {
+    constexpr int VEC = Elem<T>::VEC;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int q = tid + NTHR * t;
+        const int row = q >> 3, c = q & 7;
+        const int64_t mn = mn0 + row, k = k0 + c * VEC;
+        if (mn < mn_lim && k < k_lim)
+            r[t] = *(const u32x4*)(src + mn * ld + k);
+        else
+            r[t] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_kmaj(const u32x4 (&r)[8], u32x4* tile, int tid) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int q = tid + NTHR * t;
+        const int row = q >> 3, c = q & 7;
+        tile[row * NCH + swz(row, c)] = r[t];
+    }
+}
+
+// M/N contiguous: element (mn, k) at src[k*ld + mn].
+// bf16: one 8(k) x 8(mn) block per thread, mnb = tid%32 (8 mn each), kb = tid/32 (8 k each).
+// fp32: two 4(k) x 4(mn) blocks per thread, q = tid + 256*t, mnb = q%64, kb = q/64.
+template <typename T>
+__device__ __forceinline__ void load_mnmaj(u32x4 (&r)[8], const T* src, int64_t ld, int64_t mn0,
+                                           int64_t mn_lim, int64_t k0, int64_t k_lim, int tid);
+template <>
+__device__ __forceinline__ void load_mnmaj<bf16_t>(u32x4 (&r)[8], const bf16_t* src, int64_t ld, int64_t mn0,
+                                                   int64_t mn_lim, int64_t k0, int64_t k_lim, int tid) {
+    const int mnb = tid & 31, kb = tid >> 5;
+    const int64_t mn = mn0 + mnb * 8;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+        const int64_t k = k0 + kb * 8 + kk;
+        if (mn < mn_lim && k < k_lim)
+            r[kk] = *(const u32x4*)(src + k * ld + mn);
+        else
+            r[kk] = u32x4{0u, 0u, 0u, 0u};
+    }
+}
+template <>
+__device__ __forceinline__ void load_mnmaj<float>(u32x4 (&r)[8], const float* src, int64_t ld, int64_t mn0,
+                                                  int64_t mn_lim, int64_t k0, int64_t k_lim, int tid) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int q = tid + NTHR * t;
+        const int mnb = q & 63, kb = q >> 6;
+        const int64_t mn = mn0 + mnb * 4;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int64_t k = k0 + kb * 4 + kk;
+            if (mn < mn_lim && k < k_lim)
+                r[t * 4 + kk] = *(const u32x4*)(src + k * ld + mn);
+            else
+                r[t * 4 + kk] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_mnmaj(const u32x4 (&r)[8], u32x4* tile, int tid);
+template <>
+__device__ __forceinline__ void store_mnmaj<bf16_t>(const u32x4 (&r)[8], u32x4* tile, int tid) {
+    const int mnb = tid & 31, kb = tid >> 5;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        // Row i of the transposed block: element i of each of the 8 loaded k-rows.
+        const int wsel = i >> 1, sh = 16 * (i & 1);
+        u32x4 y;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const uint32_t lo = (r[2 * p][wsel] >> sh) & 0xffffu;
+            const uint32_t hi = (r[2 * p + 1][wsel] >> sh) & 0xffffu;
+            y[p] = lo | (hi << 16);
+        }
+        const int row = mnb * 8 + i;
+        tile[row * NCH + swz(row, kb)] = y;
+    }
+}
+template <>
+__device__ __forceinline__ void store_mnmaj<float>(const u32x4 (&r)[8], u32x4* tile, int tid) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const int q = tid + NTHR * t;
+        const int mnb = q & 63, kb = q >> 6;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 y{r[t * 4 + 0][i], r[t * 4 + 1][i], r[t * 4 + 2][i], r[t * 4 + 3][i]};
+            const int row = mnb * 4 + i;
+            tile[row * NCH + swz(row, kb)] = y;
+        }
+    }
+}
+
+template <typename T, bool KMAJ>
+__device__ __forceinline__ void load_op(u32x4 (&r)[8], const T* src, int64_t ld, int64_t mn0, int64_t mn_lim,
+                                        int64_t k0, int64_t k_lim, int tid) {
+    if constexpr (KMAJ)
+        load_kmaj<T>(r, src, ld, mn0, mn_lim, k0, k_lim, tid);
+    else
+        load_mnmaj<T>(r, src, ld, mn0, mn_lim, k0, k_lim, tid);
+}
+template <typename T, bool KMAJ>
+__device__ __forceinline__ void store_op(const u32x4 (&r)[8], u32x4* tile, int tid) {
+    if constexpr (KMAJ)
+        store_kmaj<T>(r, tile, tid);
+    else
+        store_mnmaj<T>(r, tile, tid);
+}
+
+// ------------------------------------------------------------------------------------------
+// The tile engine: acc (per wave 128 x 128 as 4 x 4 MFMA blocks) = A[m0:m0+256, kr] B[n0:n0+256, kr]^T.
+// ka_lim / kb_lim are the first k (exclusive) each operand may read; they must be multiples of
+// the 16-byte vector width. Rows at or beyond m_lim / n_lim read as zero.
+// Ends with a barrier, so the caller may reuse the LDS right away.
+
+struct WaveId {
+    int tid, lane, w, wm, wn, h, lr;
+    __device__ WaveId() {
+        tid = threadIdx.x;
+        lane = tid & 63;
+        w = tid >> 6;
+        wm = w >> 1;
+        wn = w & 1;
+        h = lane >> 5;
+        lr = lane & 31;
+    }
+};
+
+template <typename T>
+__device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const u32x4* tA, const u32x4* tB,
+                                              const WaveId& id) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        u32x4 a[4], b[4];
+        const int c = 2 * g + id.h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = id.wm * 128 + i * 32 + id.lr;
+            a[i] = tA[row * NCH + swz(row, c)];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = id.wn * 128 + j * 32 + id.lr;
+            b[j] = tB[row * NCH + swz(row, c)];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mma<T>(acc[i][j], a[i], b[j]);
+    }
+}
+
+template <typename T, bool AK, bool BKM>
+__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], u32x4* L, const WaveId& id,
+                                          const T* A, int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim,
+                                          const T* B, int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim,
+                                          int64_t k_begin, int64_t k_end) {
+    constexpr int BK = Elem<T>::BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    const int nk = (int)((k_end - k_begin + BK - 1) / BK);
+    if (nk <= 0) return;
+    u32x4 ra[8], rb[8];
+    load_op<T, AK>(ra, A, lda, m0, m_lim, k_begin, ka_lim, id.tid);
+    load_op<T, BKM>(rb, B, ldb, n0, n_lim, k_begin, kb_lim, id.tid);
+    store_op<T, AK>(ra, L, id.tid);
+    store_op<T, BKM>(rb, L + TILE_CHUNKS, id.tid);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            const int64_t k0 = k_begin + (int64_t)(kt + 1) * BK;
+            load_op<T, AK>(ra, A, lda, m0, m_lim, k0, ka_lim, id.tid);
+            load_op<T, BKM>(rb, B, ldb, n0, n_lim, k0, kb_lim, id.tid);
+        }
+        compute_stage<T>(acc, L + (2 * cur) * TILE_CHUNKS, L + (2 * cur + 1) * TILE_CHUNKS, id);
+        if (more) {
+            store_op<T, AK>(ra, L + (2 * (cur ^ 1)) * TILE_CHUNKS, id.tid);
+            store_op<T, BKM>(rb, L + (2 * (cur ^ 1) + 1) * TILE_CHUNKS, id.tid);
+        }
+        __syncthreads();
+    }
+}
+
+// Row of accumulator element (i, e) within the wave's 128 rows, and its row within the
+// 64-row staging slab of pass i.
+__device__ __forceinline__ int acc_row(int i, int e, int h) { return i * 32 + 8 * (e >> 2) + 4 * h + (e & 3); }
+
+// Merge (m2, s2) into (m, s): sums of 2^(y - m) over disjoint sets.
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) return;
+    s = s * exp2_fast(m - M) + s2 * exp2_fast(m2 - M);
+    m = M;
+}
+
+template <int HALF, int MASK, int NPOS>
+__device__ __forceinline__ void rs_step(float (&pm)[NPOS], float (&ps)[NPOS], int lane) {
+    const bool up = (lane & MASK) != 0;
+#pragma unroll
+    for (int q = 0; q < HALF; ++q) {
+        float km = up ? pm[q + HALF] : pm[q];
+        float ks = up ? ps[q + HALF] : ps[q];
+        const float sm = up ? pm[q] : pm[q + HALF];
+        const float ss = up ? ps[q] : ps[q + HALF];
+        const float rm = __shfl_xor(sm, MASK);
+        const float rsum = __shfl_xor(ss, MASK);
+        ms_merge(km, ks, rm, rsum);
+        pm[q] = km;
+        ps[q] = ks;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Plan: bucket cached ids by (row block of 256, vocab tile of 256).
+
+__global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ idx, int64_t row0, int64_t row1,
+                                              int K, int64_t V, int n_vt, int32_t* __restrict__ off,
+                                              uint32_t* __restrict__ ent) {
+    __shared__ int cnt[kMaxVTiles];
+    __shared__ int part[NTHR];
+    const int tid = threadIdx.x;
+    const int rb = blockIdx.x;
+    const int64_t r0 = row0 + (int64_t)rb * kTileM;
+    const int rows = (int)min<int64_t>(kTileM, row1 - r0);
+    const int64_t base = (int64_t)rb * kTileM * K;
+    for (int t = tid; t < n_vt; t += NTHR) cnt[t] = 0;
+    __syncthreads();
+    const int n_e = rows * K;
+    for (int i = tid; i < n_e; i += NTHR) {
+        const int v = idx[r0 * K + i];
+        if (v >= 0 && v < V) atomicAdd(&cnt[v >> 8], 1);
+    }
+    __syncthreads();
+    // exclusive scan of cnt[0..n_vt): each thread owns a contiguous segment
+    const int seg = (n_vt + NTHR - 1) / NTHR;
+    const int s0 = min(n_vt, tid * seg), s1 = min(n_vt, s0 + seg);
+    int sum = 0;
+    for (int t = s0; t < s1; ++t) sum += cnt[t];
+    part[tid] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int t = 0; t < NTHR; ++t) {
+            const int x = part[t];
+            part[t] = run;
+            run += x;
+        }
+    }
+    __syncthreads();
+    int run = part[tid];
+    int32_t* o = off + (int64_t)rb * (n_vt + 1);
+    for (int t = s0; t < s1; ++t) {
+        const int x = cnt[t];
+        cnt[t] = run;  // becomes the fill cursor
+        o[t] = (int32_t)(base + run);
+        run += x;
+    }
+    if (tid == NTHR - 1) o[n_vt] = (int32_t)(base + run);  // the last segment ends at the total
+    __syncthreads();
+    for (int i = tid; i < n_e; i += NTHR) {
+        const int v = idx[r0 * K + i];
+        if (v >= 0 && v < V) {
+            const int pos = atomicAdd(&cnt[v >> 8], 1);
+            const int r = i / K, k = i - r * K;
+            ent[base + pos] = (uint32_t)r | ((uint32_t)(v & 255) << 8) | ((uint32_t)k << 16);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Teacher probabilities: p_t = softmax(t/T) over the K cached entries (one wave per row).
+
+__device__ __forceinline__ double wave_max_d(double x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = fmax(x, __shfl_xor(x, m));
+    return x;
+}
+__device__ __forceinline__ double wave_sum_d(double x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+__global__ __launch_bounds__(256) void k_teacher_prob(const void* __restrict__ tlog, Dt tdt, int64_t row0,
+                                                      int64_t row1, int K, float T, float* __restrict__ pt) {
+    const int lane = threadIdx.x & 63;
+    const int64_t n = row0 + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (n >= row1) return;
+    double a0 = -INFINITY, a1 = -INFINITY;
+    if (lane < K) a0 = (double)load_t(tlog, tdt, n * K + lane) / T;
+    if (lane + 64 < K) a1 = (double)load_t(tlog, tdt, n * K + lane + 64) / T;
+    const double mx = wave_max_d(fmax(a0, a1));
+    double s = 0.0;
+    if (lane < K) s += exp(a0 - mx);
+    if (lane + 64 < K) s += exp(a1 - mx);
+    const double lz = mx + log(wave_sum_d(s));
+    float* o = pt + (n - row0) * K;
+    if (lane < K) o[lane] = (float)exp(a0 - lz);
+    if (lane + 64 < K) o[lane + 64] = (float)exp(a1 - lz);
+}
+
+// ------------------------------------------------------------------------------------------
+// Id validation: range and distinctness within each row (one wave per row).
+
+__global__ __launch_bounds__(256) void k_zero_u32(uint32_t* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(256) void k_validate(const int32_t* __restrict__ idx, int64_t N, int K, int64_t V,
+                                                  uint32_t* status) {
+    __shared__ int ids[4][kMaxK];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t n = (int64_t)blockIdx.x * 4 + w;
+    const bool live = n < N;
+    uint32_t bad = 0;
+    for (int k = lane; k < K; k += 64) {
+        const int v = live ? idx[n * K + k] : 0;
+        ids[w][k] = v;
+        if (live && (v < 0 || v >= V)) bad |= 1u;
+    }
+    __syncthreads();
+    if (live) {
+        for (int k = lane; k < K; k += 64) {
+            const int v = ids[w][k];
+            for (int j = 0; j < K; ++j)
+                if (j != k && ids[w][j] == v) bad |= 2u;
+        }
+    }
+    if (bad) atomicOr(status, bad);
+}
+
+// ------------------------------------------------------------------------------------------
+// Fused forward.
+
+struct FwdArgs {
+    const void* H;
+    const void* W;
+    int64_t N, d, V, K;
+    float c;  // log2(e)/T
+    const int32_t* off;
+    const uint32_t* ent;
+    int n_vt, tps;
+    float2* part;  // [2*n_vsplit][N]
+    float* zk;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
+    __shared__ u32x4 L[LDS_CHUNKS];
+    const WaveId id;
+    const int rb = blockIdx.x, vs = blockIdx.y;
+    const int64_t m0 = (int64_t)rb * kTileM;
+    const int t0 = vs * a.tps, t1 = min(a.n_vt, t0 + a.tps);
+    const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
+    float* stage = (float*)L;
+    float run_m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, run_s[4] = {0.f, 0.f, 0.f, 0.f};
+
+    for (int vt = t0; vt < t1; ++vt) {
+        const int64_t n0 = (int64_t)vt * kTileN;
+        f32x16 acc[4][4];
+        gemm_tile<T, true, true>(acc, L, id, (const T*)a.H, a.d, m0, a.N, a.d, (const T*)a.W, a.d, n0, a.V,
+                                 a.d, 0, a.d);
+
+        // Gather z at the cached ids of this (row block, vocab tile), one 64-row slab at a time.
+        const int e0 = off[vt], e1 = off[vt + 1];
+        if (e1 > e0) {
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int rl = id.wm * 32 + 8 * (e >> 2) + 4 * id.h + (e & 3);
+                        stage[rl * STG + id.wn * 128 + j * 32 + id.lr] = acc[p][j][e];
+                    }
+                __syncthreads();
+                for (int i = e0 + id.tid; i < e1; i += NTHR) {
+                    const uint32_t en = a.ent[i];
+                    const int r = en & 255;
+                    if (((r >> 5) & 3) != p) continue;
+                    const int c = (en >> 8) & 255, k = (int)(en >> 16);
+                    const int rl = (r >> 7) * 32 + (r & 31);
+                    a.zk[(m0 + r) * a.K + k] = stage[rl * STG + c];
+                }
+                __syncthreads();
+            }
+        }
+
+        // Online (max, sum) per row over this tile, in units of y = z*log2(e)/T, one 32-row
+        // MFMA block at a time. Each lane first folds its 4 columns; then a reduce-scatter over
+        // the 32 lanes of its half (masks 16, 8, 4, 2) leaves lane pair (2q, 2q+1) with row
+        // position e = q of the block, and a last exchange (mask 1) completes both copies.
+        bool colok[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) colok[j] = n0 + id.wn * 128 + j * 32 + id.lr < a.V;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float pm[16], ps[16];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                float y[4];
+                float m = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    y[j] = colok[j] ? acc[i][j][e] * a.c : -INFINITY;
+                    m = fmaxf(m, y[j]);
+                }
+                float s = 0.f;
+                if (m != -INFINITY) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) s += exp2_fast(y[j] - m);
+                }
+                pm[e] = m;
+                ps[e] = s;
+            }
+            rs_step<8, 16>(pm, ps, id.lane);
+            rs_step<4, 8>(pm, ps, id.lane);
+            rs_step<2, 4>(pm, ps, id.lane);
+            rs_step<1, 2>(pm, ps, id.lane);
+            const float m2 = __shfl_xor(pm[0], 1), s2 = __shfl_xor(ps[0], 1);
+            ms_merge(pm[0], ps[0], m2, s2);
+            ms_merge(run_m[i], run_s[i], pm[0], ps[0]);
+        }
+    }
+
+    // Lane pair (2q, 2q+1) of half h holds row position e = q of each block i; the even lane writes.
+    if ((id.lr & 1) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = id.lr >> 1;
+            const int row = id.wm * 128 + acc_row(i, e, id.h);
+            const int64_t g = m0 + row;
+            if (g < a.N) a.part[(int64_t)(vs * 2 + id.wn) * a.N + g] = make_float2(run_m[i], run_s[i]);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Combine: lse_n from the partials, KL_n from the cached teacher and zk, block sums in fp64.
+
+constexpr int kCombRows = 16;  // rows per workgroup (4 per wave)
+
+__global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ part, int n_part, int64_t N, int K,
+                                                 float T, const float* __restrict__ zk,
+                                                 const void* __restrict__ tlog, Dt tdt, float* __restrict__ lse,
+                                                 float* __restrict__ row_kl, double* __restrict__ blk_sum) {
+    __shared__ double wsum[4];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    double mine = 0.0;
+    for (int rr = 0; rr < kCombRows / 4; ++rr) {
+        const int64_t n = (int64_t)blockIdx.x * kCombRows + w * (kCombRows / 4) + rr;
+        if (n >= N) break;
+        float m = -INFINITY, s = 0.f;
+        for (int sl = lane; sl < n_part; sl += 64) {
+            const float2 v = part[(int64_t)sl * N + n];
+            if (v.y > 0.f) ms_merge(m, s, v.x, v.y);
+        }
+#pragma unroll
+        for (int mk = 32; mk >= 1; mk >>= 1) {
+            const float m2 = __shfl_xor(m, mk), s2 = __shfl_xor(s, mk);
+            ms_merge(m, s, m2, s2);
+        }
+        const double lse_d = ((double)m + log2((double)s)) * kLn2;
+        double a0 = -INFINITY, a1 = -INFINITY;
+        if (lane < K) a0 = (double)load_t(tlog, tdt, n * K + lane) / T;
+        if (lane + 64 < K) a1 = (double)load_t(tlog, tdt, n * K + lane + 64) / T;
+        const double mx = wave_max_d(fmax(a0, a1));
+        double se = 0.0;
+        if (lane < K) se += exp(a0 - mx);
+        if (lane + 64 < K) se += exp(a1 - mx);
+        const double lz = mx + log(wave_sum_d(se));
+        double term = 0.0;
+        if (lane < K) {
+            const double lp = a0 - lz;
+            term += exp(lp) * (lp - (double)zk[n * K + lane] / T + lse_d);
+        }
+        if (lane + 64 < K) {
+            const double lp = a1 - lz;
+            term += exp(lp) * (lp - (double)zk[n * K + lane + 64] / T + lse_d);
+        }
+        const double kl = wave_sum_d(term);
+        if (lane == 0) {
+            lse[n] = (float)lse_d;
+            if (row_kl) row_kl[n] = (float)kl;
+        }
+        mine += kl;
+    }
+    if (lane == 0) wsum[w] = mine;
+    __syncthreads();
+    if (threadIdx.x == 0) blk_sum[blockIdx.x] = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+__global__ __launch_bounds__(256) void k_loss_final(const double* __restrict__ blk_sum, int n_blk, double scale,
+                                                    float* __restrict__ loss) {
+    __shared__ double red[NTHR];
+    double s = 0.0;
+    for (int i = threadIdx.x; i < n_blk; i += NTHR) s += blk_sum[i];
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = NTHR / 2; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[0] = (float)(scale * red[0]);
+}
+
+// Per-row fp64 values summed into block partials in a fixed order (dense path).
+__global__ __launch_bounds__(256) void k_sum_rows(const double* __restrict__ v, int64_t N, double* __restrict__ blk) {
+    __shared__ double red[NTHR];
+    const int64_t i0 = (int64_t)blockIdx.x * 1024;
+    double s = 0.0;
+    for (int t = 0; t < 4; ++t) {
+        const int64_t i = i0 + t * NTHR + threadIdx.x;
+        if (i < N) s += v[i];
+    }
+    red[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = NTHR / 2; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) blk[blockIdx.x] = red[0];
+}
+
+// ------------------------------------------------------------------------------------------
+// Backward, per chunk: recompute the logit tile and form G = gs*(2^(y - lse2) - P_t).
+
+struct GradArgs {
+    const void* H;
+    const void* W;
+    int64_t d, V, K;
+    float c;      // log2(e)/T
+    float gsc;    // T/n_norm
+    const float* grad;  // device scalar or nullptr
+    const float* lse;
+    const float* pt;    // [cc][K], rows relative to c0
+    int64_t c0, cc;
+    const int32_t* off;
+    const uint32_t* ent;
+    int n_vt;
+    void* G;
+    int64_t ldg;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
+    __shared__ u32x4 L[LDS_CHUNKS];
+    __shared__ float lse2[kTileM];
+    const WaveId id;
+    const int vt = blockIdx.x, rb = blockIdx.y;
+    const int64_t r0 = (int64_t)rb * kTileM;  // row offset within the chunk
+    const int64_t n0 = (int64_t)vt * kTileN;
+    {
+        const int64_t r = r0 + id.tid;
+        lse2[id.tid] = r < a.cc ? a.lse[a.c0 + r] * kLog2e : 0.f;
+    }
+    const float gs = (a.grad ? a.grad[0] : 1.f) * a.gsc;
+    const T* Hc = (const T*)a.H + a.c0 * a.d;
+    f32x16 acc[4][4];
+    gemm_tile<T, true, true>(acc, L, id, Hc, a.d, r0, a.cc, a.d, (const T*)a.W, a.d, n0, a.V, a.d, 0, a.d);
+
+    float* stage = (float*)L;
+    const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
+    const int e0 = off[vt], e1 = off[vt + 1];
+    bool colok[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) colok[j] = n0 + id.wn * 128 + j * 32 + id.lr < a.V;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int rw = id.wm * 128 + acc_row(p, e, id.h);
+            const float l2 = lse2[rw];
+            const int rl = id.wm * 32 + 8 * (e >> 2) + 4 * id.h + (e & 3);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float v = colok[j] ? gs * exp2_fast(acc[p][j][e] * a.c - l2) : 0.f;
+                stage[rl * STG + id.wn * 128 + j * 32 + id.lr] = v;
+            }
+        }
+        __syncthreads();
+        for (int i = e0 + id.tid; i < e1; i += NTHR) {
+            const uint32_t en = a.ent[i];
+            const int r = en & 255;
+            if (((r >> 5) & 3) != p) continue;
+            const int c = (en >> 8) & 255, k = (int)(en >> 16);
+            const int rl = (r >> 7) * 32 + (r & 31);
+            stage[rl * STG + c] -= gs * a.pt[(r0 + r) * a.K + k];
+        }
+        __syncthreads();
+        // 64 rows x 32 groups of 8 columns; consecutive lanes take consecutive groups of a row.
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int it = id.tid + NTHR * t;
+            const int rl = it >> 5, cb = it & 31;
+            const int64_t row = r0 + (rl >> 5) * 128 + p * 32 + (rl & 31);
+            if (row < a.cc) {
+                const f32x4 v0 = *(const f32x4*)(stage + rl * STG + cb * 8);
+                const f32x4 v1 = *(const f32x4*)(stage + rl * STG + cb * 8 + 4);
+                if constexpr (sizeof(T) == 2) {
+                    u32x4 o;
+                    o[0] = f2bf(v0[0]) | (f2bf(v0[1]) << 16);
+                    o[1] = f2bf(v0[2]) | (f2bf(v0[3]) << 16);
+                    o[2] = f2bf(v1[0]) | (f2bf(v1[1]) << 16);
+                    o[3] = f2bf(v1[2]) | (f2bf(v1[3]) << 16);
+                    *(u32x4*)((bf16_t*)a.G + row * a.ldg + n0 + cb * 8) = o;
+                } else {
+                    float* gp = (float*)a.G + row * a.ldg + n0 + cb * 8;
+                    *(f32x4*)gp = v0;
+                    *(f32x4*)(gp + 4) = v1;
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// dH = G W (A = G_c with the vocabulary contiguous, B = W with d contiguous).
+
+struct DhArgs {
+    const void* G;
+    int64_t ldg, Vp;
+    const void* W;
+    int64_t d, V;
+    int64_t c0, cc;
+    int64_t kper;
+    int n_split;
+    float* part;
+    void* dH;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
+    __shared__ u32x4 L[LDS_CHUNKS];
+    const WaveId id;
+    const int nt = blockIdx.x, mt = blockIdx.y, ks = blockIdx.z;
+    const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
+    const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
+    f32x16 acc[4][4];
+    gemm_tile<T, true, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
+                              min(a.V, k_end), k_begin, k_end);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t row = m0 + id.wm * 128 + acc_row(i, e, id.h);
+            if (row >= a.cc) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = n0 + id.wn * 128 + j * 32 + id.lr;
+                if (col >= a.d) continue;
+                const float v = acc[i][j][e];
+                if (a.n_split > 1) {
+                    a.part[((int64_t)ks * a.cc + row) * a.d + col] = v;
+                } else if constexpr (sizeof(T) == 2) {
+                    ((bf16_t*)a.dH)[(a.c0 + row) * a.d + col] = (bf16_t)f2bf(v);
+                } else {
+                    ((float*)a.dH)[(a.c0 + row) * a.d + col] = v;
+                }
+            }
+        }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ part, int n_split, int64_t cc,
+                                                   int64_t d, int64_t c0, void* __restrict__ dH) {
+    const int64_t n4 = cc * d / 4;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        f32x4 s = ((const f32x4*)part)[i];
+        for (int k = 1; k < n_split; ++k) s += ((const f32x4*)(part + (int64_t)k * cc * d))[i];
+        const int64_t e = i * 4;
+        if constexpr (sizeof(T) == 2) {
+            uint2 o;
+            o.x = f2bf(s[0]) | (f2bf(s[1]) << 16);
+            o.y = f2bf(s[2]) | (f2bf(s[3]) << 16);
+            *(uint2*)((bf16_t*)dH + c0 * d + e) = o;
+        } else {
+            *(f32x4*)((float*)dH + c0 * d + e) = s;
+        }
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// dW (+)= G_c^T H_c (A = G_c^T: vocabulary contiguous; B = H_c: d contiguous).
+
+struct DwArgs {
+    const void* G;
+    int64_t ldg, Vp;
+    const void* H;
+    int64_t d, V;
+    int64_t c0, cc;
+    int accumulate;
+    float* dW;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
+    __shared__ u32x4 L[LDS_CHUNKS];
+    const WaveId id;
+    const int nt = blockIdx.x, mt = blockIdx.y;
+    const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
+    const T* Hc = (const T*)a.H + a.c0 * a.d;
+    f32x16 acc[4][4];
+    gemm_tile<T, false, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.cc, Hc, a.d, n0, a.d, a.cc, 0, a.cc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t row = m0 + id.wm * 128 + acc_row(i, e, id.h);
+            if (row >= a.V) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = n0 + id.wn * 128 + j * 32 + id.lr;
+                if (col >= a.d) continue;
+                float* p = a.dW + row * a.d + col;
+                *p = (a.accumulate ? *p : 0.f) + acc[i][j][e];
+            }
+        }
+}
+
+// ------------------------------------------------------------------------------------------
+// Dense path.
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void k_dense_logits(const void* H, const void* W, int64_t N, int64_t d,
+                                                         int64_t V, float* Z, int64_t ldz) {
+    __shared__ u32x4 L[LDS_CHUNKS];
+    const WaveId id;
+    const int vt = blockIdx.x, rb = blockIdx.y;
+    const int64_t m0 = (int64_t)rb * kTileM, n0 = (int64_t)vt * kTileN;
+    f32x16 acc[4][4];
+    gemm_tile<T, true, true>(acc, L, id, (const T*)H, d, m0, N, d, (const T*)W, d, n0, V, d, 0, d);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t row = m0 + id.wm * 128 + acc_row(i, e, id.h);
+            if (row >= N) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Z[row * ldz + n0 + id.wn * 128 + j * 32 + id.lr] = acc[i][j][e];
+        }
+}
+
+__device__ __forceinline__ double block_sum_d(double x, double* red) {
+    red[threadIdx.x] = x;
+    __syncthreads();
+    for (int w = NTHR / 2; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+        __syncthreads();
+    }
+    const double r = red[0];
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ double block_max_d(double x, double* red) {
+    red[threadIdx.x] = x;
+    __syncthreads();
+    for (int w = NTHR / 2; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) red[threadIdx.x] = fmax(red[threadIdx.x], red[threadIdx.x + w]);
+        __syncthreads();
+    }
+    const double r = red[0];
+    __syncthreads();
+    return r;
+}
+
+// One workgroup per row. Z row: logits (fp32); P row: the dense teacher grid, later G (fp32).
+// With a bf16 activation dtype, G is also written as bf16 over the start of the Z row.
+__global__ __launch_bounds__(256) void k_dense_rows(float* __restrict__ Z, float* __restrict__ P, int64_t ldz,
+                                                    int64_t V, int K, float T, float gsc,
+                                                    const int32_t* __restrict__ idx, const void* __restrict__ tlog,
+                                                    Dt tdt, const float* __restrict__ grad, float* __restrict__ lse,
+                                                    float* __restrict__ row_kl, double* __restrict__ row_sum,
+                                                    int g_bf16) {
+    __shared__ double red[NTHR];
+    const int64_t n = blockIdx.x;
+    const int tid = threadIdx.x;
+    float* z = Z + n * ldz;
+    float* pg = P + n * ldz;
+    const int64_t Vp = ldz;
+    // teacher distribution over the K cached entries
+    double a = -INFINITY;
+    if (tid < K) a = (double)load_t(tlog, tdt, n * K + tid) / T;
+    const double amax = block_max_d(a, red);
+    const double asum = block_sum_d(tid < K ? exp(a - amax) : 0.0, red);
+    const double alz = amax + log(asum);
+    // student log-normaliser over all V
+    const double cT = 1.0 / T;
+    double mx = -INFINITY;
+    for (int64_t v = tid; v < V; v += NTHR) mx = fmax(mx, (double)z[v] * cT);
+    mx = block_max_d(mx, red);
+    double se = 0.0;
+    for (int64_t v = tid; v < V; v += NTHR) se += exp((double)z[v] * cT - mx);
+    se = block_sum_d(se, red);
+    const double lsed = mx + log(se);
+    // expand the cached teacher into the dense grid
+    for (int64_t v = tid; v < Vp; v += NTHR) pg[v] = 0.f;
+    __syncthreads();
+    if (tid < K) {
+        const int v = idx[n * K + tid];
+        if (v >= 0 && v < V) pg[v] = (float)exp(a - alz);  // out-of-range ids are skipped
+    }
+    __syncthreads();
+    // KL over the whole vocabulary (terms with P = 0 contribute 0)
+    double kl = 0.0;
+    for (int64_t v = tid; v < V; v += NTHR) {
+        const float pv = pg[v];
+        if (pv > 0.f) kl += (double)pv * (log((double)pv) - ((double)z[v] * cT - lsed));
+    }
+    kl = block_sum_d(kl, red);
+    // gradient grid, in place of the teacher grid
+    const float gs = (grad ? grad[0] : 1.f) * gsc;
+    const float l2 = (float)(lsed * 1.4426950408889634);
+    const float c2 = (float)(cT * 1.4426950408889634);
+    for (int64_t v = tid; v < Vp; v += NTHR) pg[v] = v < V ? gs * (exp2_fast(z[v] * c2 - l2) - pg[v]) : 0.f;
+    if (g_bf16) {
+        __syncthreads();
+        bf16_t* gb = (bf16_t*)z;
+        for (int64_t v = tid; v < Vp; v += NTHR) gb[v] = (bf16_t)f2bf(pg[v]);
+    }
+    if (tid == 0) {
+        lse[n] = (float)lsed;
+        if (row_kl) row_kl[n] = (float)kl;
+        row_sum[n] = kl;
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Launchers.
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int fwd_vsplits(int64_t N, int64_t V) {
+    const int64_t n_rb = (N + kTileM - 1) / kTileM;
+    const int64_t n_vt = (V + kTileN - 1) / kTileN;
+    int64_t s = (256 + n_rb - 1) / n_rb;
+    if (s < 1) s = 1;
+    if (s > n_vt) s = n_vt;
+    return (int)s;
+}
+
+int dh_splits(int64_t cc, int64_t d, int64_t V) {
+    const int64_t tiles = ((cc + kTileM - 1) / kTileM) * ((d + kTileN - 1) / kTileN);
+    if (tiles >= 512) return 1;
+    int64_t s = (768 + tiles - 1) / tiles;
+    const int64_t ksteps = (V + 63) / 64;
+    if (s > ksteps / 4) s = ksteps / 4;
+    if (s > 32) s = 32;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+int combine_blocks(int64_t N) { return (int)((N + kCombRows - 1) / kCombRows); }
+
+hipError_t launch_plan(const int32_t* idx, int64_t row0, int64_t row1, int64_t K, int64_t V, int32_t* off,
+                       uint32_t* ent, hipStream_t s) {
+    const int n_rb = (int)((row1 - row0 + kTileM - 1) / kTileM);
+    const int n_vt = (int)((V + kTileN - 1) / kTileN);
+    hipLaunchKernelGGL(k_plan, dim3(n_rb), dim3(NTHR), 0, s, idx, row0, row1, (int)K, V, n_vt, off, ent);
+    return hipGetLastError();
+}
+
+hipError_t launch_teacher_prob(const void* tlog, Dt tdt, int64_t row0, int64_t row1, int64_t K, float T,
+                               float* pt, hipStream_t s) {
+    const int64_t rows = row1 - row0;
+    hipLaunchKernelGGL(k_teacher_prob, dim3((unsigned)((rows + 3) / 4)), dim3(NTHR), 0, s, tlog, tdt, row0, row1,
+                       (int)K, T, pt);
+    return hipGetLastError();
+}
+
+hipError_t launch_validate(const int32_t* idx, int64_t N, int64_t K, int64_t V, uint32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, status, 1);
+    hipLaunchKernelGGL(k_validate, dim3((unsigned)((N + 3) / 4)), dim3(NTHR), 0, s, idx, N, (int)K, V, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32_t* plan_off,
+                      const uint32_t* plan_ent, int n_vsplit, float2* part, float* zk, hipStream_t s) {
+    FwdArgs a;
+    a.H = H;
+    a.W = W;
+    a.N = sh.N;
+    a.d = sh.d;
+    a.V = sh.V;
+    a.K = sh.K;
+    a.c = kLog2e / sh.T;
+    a.off = plan_off;
+    a.ent = plan_ent;
+    a.n_vt = (int)((sh.V + kTileN - 1) / kTileN);
+    a.tps = (a.n_vt + n_vsplit - 1) / n_vsplit;
+    a.part = part;
+    a.zk = zk;
+    const dim3 grid((unsigned)((sh.N + kTileM - 1) / kTileM), (unsigned)n_vsplit);
+    if (sh.act == Dt::BF16)
+        hipLaunchKernelGGL(k_fwd<bf16_t>, grid, dim3(NTHR), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_fwd<float>, grid, dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const Shape& sh, const float2* part, int n_part, const float* zk, const void* tlog,
+                          float* lse, float* row_kl, double* blk_sum, int* n_blk_out, hipStream_t s) {
+    const int nb = combine_blocks(sh.N);
+    hipLaunchKernelGGL(k_combine, dim3(nb), dim3(NTHR), 0, s, part, n_part, sh.N, (int)sh.K, sh.T, zk, tlog, sh.tlog,
+                       lse, row_kl, blk_sum);
+    if (n_blk_out) *n_blk_out = nb;
+    return hipGetLastError();
+}
+
+hipError_t launch_loss_final(const Shape& sh, const double* blk_sum, int n_blk, float* loss, hipStream_t s) {
+    const double scale = (double)sh.T * (double)sh.T / (double)sh.n_norm;
+    hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(NTHR), 0, s, blk_sum, n_blk, scale, loss);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const float* lse, const float* pt,
+                           const float* grad_loss, int64_t c0, int64_t cc, const int32_t* plan_off,
+                           const uint32_t* plan_ent, void* Gc, int64_t ldg, hipStream_t s) {
+    GradArgs a;
+    a.H = H;
+    a.W = W;
+    a.d = sh.d;
+    a.V = sh.V;
+    a.K = sh.K;
+    a.c = kLog2e / sh.T;
+    a.gsc = sh.T / sh.n_norm;
+    a.grad = grad_loss;
+    a.lse = lse;
+    a.pt = pt;
+    a.c0 = c0;
+    a.cc = cc;
+    a.off = plan_off;
+    a.ent = plan_ent;
+    a.n_vt = (int)((sh.V + kTileN - 1) / kTileN);
+    a.G = Gc;
+    a.ldg = ldg;
+    const dim3 grid((unsigned)a.n_vt, (unsigned)((cc + kTileM - 1) / kTileM));
+    if (sh.act == Dt::BF16)
+        hipLaunchKernelGGL(k_bwd_grad<bf16_t>, grid, dim3(NTHR), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_bwd_grad<float>, grid, dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, int64_t c0, int64_t cc,
+                     int n_split, float* part, void* dH, hipStream_t s) {
+    DhArgs a;
+    a.G = Gc;
+    a.ldg = ldg;
+    a.Vp = round_up(sh.V, kTileN);
+    a.W = W;
+    a.d = sh.d;
+    a.V = sh.V;
+    a.c0 = c0;
+    a.cc = cc;
+    a.n_split = n_split;
+    a.kper = round_up((a.Vp + n_split - 1) / n_split, 64);
+    a.part = part;
+    a.dH = dH;
+    const dim3 grid((unsigned)((sh.d + kTileN - 1) / kTileN), (unsigned)((cc + kTileM - 1) / kTileM),
+                    (unsigned)n_split);
+    if (sh.act == Dt::BF16)
+        hipLaunchKernelGGL(k_dh<bf16_t>, grid, dim3(NTHR), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_dh<float>, grid, dim3(NTHR), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n_split <= 1) return e;
+    const int64_t n4 = cc * sh.d / 4;
+    const unsigned blocks = (unsigned)std::min<int64_t>((n4 + NTHR - 1) / NTHR, 4096);
+    if (sh.act == Dt::BF16)
+        hipLaunchKernelGGL(k_dh_reduce<bf16_t>, dim3(blocks), dim3(NTHR), 0, s, part, n_split, cc, sh.d, c0, dH);
+    else
+        hipLaunchKernelGGL(k_dh_reduce<float>, dim3(blocks), dim3(NTHR), 0, s, part, n_split, cc, sh.d, c0, dH);
+    return hipGetLastError();
+}
+
+hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H, int64_t c0, int64_t cc,
+                     bool accumulate, float* dW, hipStream_t s) {
+    DwArgs a;
+    a.G = Gc;
+    a.ldg = ldg;
+    a.Vp = round_up(sh.V, kTileN);
+    a.H = H;
+    a.d = sh.d;
+    a.V = sh.V;
+    a.c0 = c0;
+    a.cc = cc;
+    a.accumulate = accumulate ? 1 : 0;
+    a.dW = dW;
+    const dim3 grid((unsigned)((sh.d + kTileN - 1) / kTileN), (unsigned)(a.Vp / kTileM));
+    if (sh.act == Dt::BF16)
+        hipLaunchKernelGGL(k_dw<bf16_t>, grid, dim3(NTHR), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_dw<float>, grid, dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_logits(const Shape& sh, const void* H, const void* W, float* Z, int64_t ldz, hipStream_t s) {
+    const dim3 grid((unsigned)(ldz / kTileN), (unsigned)((sh.N + kTileM - 1) / kTileM));
+    if (sh.act == Dt::BF16)
+        hipLaunchKernelGGL(k_dense_logits<bf16_t>, grid, dim3(NTHR), 0, s, H, W, sh.N, sh.d, sh.V, Z, ldz);
+    else
+        hipLaunchKernelGGL(k_dense_logits<float>, grid, dim3(NTHR), 0, s, H, W, sh.N, sh.d, sh.V, Z, ldz);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_rows(const Shape& sh, float* Z, float* P, int64_t ldz, const int32_t* idx, const void* tlog,
+                             const float* grad_loss, float* lse, float* row_kl, double* row_sum, void* G,
+                             int64_t ldg, hipStream_t s) {
+    (void)G;
+    (void)ldg;
+    hipLaunchKernelGGL(k_dense_rows, dim3((unsigned)sh.N), dim3(NTHR), 0, s, Z, P, ldz, sh.V, (int)sh.K, sh.T,
+                       sh.T / sh.n_norm, idx, tlog, sh.tlog, grad_loss, lse, row_kl, row_sum,
+                       sh.act == Dt::BF16 ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_rows(const Shape& sh, const double* row_sum, double* blk_sum, int* n_blk, hipStream_t s) {
+    const int nb = (int)((sh.N + 1023) / 1024);
+    hipLaunchKernelGGL(k_sum_rows, dim3(nb), dim3(NTHR), 0, s, row_sum, sh.N, blk_sum);
+    if (n_blk) *n_blk = nb;
+    return hipGetLastError();
+}
+
+}  // namespace kdkl

@@ -1,0 +1,158 @@
+"""The C ABI of libkdkl without a GPU: symbols, status strings, workspace queries, and the
+host-side argument checks that must reject bad calls before anything is enqueued."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from lm_head_kl_amd import _lib
+from lm_head_kl_amd._lib import KD_BF16, KD_FP32, KdProblem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdkl.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libkdkl.so not built")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kd_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if l.strip()}
+    for fn in header_functions():
+        assert fn in exported, fn
+    L = _lib.lib()
+    for fn in header_functions():
+        assert hasattr(L, fn)
+
+
+def test_abi_version_matches_header():
+    v = int(re.search(r"#define KDKL_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert _lib.lib().kd_abi_version() == v
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for code in range(0, 9):
+        s = L.kd_status_str(code)
+        assert s and len(s) > 1
+    assert L.kd_status_str(99) == b"unknown status"
+
+
+def prob(**kw):
+    base = dict(N=4096, d=1024, V=32000, K=100, chunk=1024, T=1.0, n_norm=0.0, act=KD_BF16, tlogit=KD_BF16,
+                flags=0, reserved=0)
+    base.update(kw)
+    return KdProblem(**base)
+
+
+def ws_bytes(**kw):
+    return _lib.lib().kd_fused_workspace_bytes(ctypes.byref(prob(**kw)))
+
+
+def test_workspace_queries():
+    L = _lib.lib()
+    assert ws_bytes() > 0
+    assert L.kd_fused_workspace_bytes(None) == 0
+    assert ws_bytes(K=0) == 0 and ws_bytes(T=-1.0) == 0
+    # The gradient tile grows with chunk ...
+    sizes = [ws_bytes(chunk=c) for c in (256, 512, 1024, 2048, 4096)]
+    assert all(a < b for a, b in zip(sizes, sizes[1:]))
+    # ... and is at least chunk x V in the activation dtype.
+    assert ws_bytes(chunk=2048) >= 2048 * 32000 * 2
+    # N enters only through O(N*K) and O(N) terms: second differences vanish once N > chunk.
+    a, b, c = (ws_bytes(N=n, chunk=1024) for n in (8192, 16384, 24576))
+    assert abs((c - b) - (b - a)) <= 4096
+    per_row = (b - a) / 8192
+    assert per_row < 100 * 4 * 3 + 64  # a few words per cached entry, nothing per vocab entry
+    # Dense: two fp32 N x V grids.
+    dn = L.kd_dense_workspace_bytes(ctypes.byref(prob(N=512)))
+    assert dn >= 2 * 512 * 32000 * 4
+
+
+# ------------------------------------------------------------------ argument checks
+# These pass fake device addresses; the checks must reject the call before any launch.
+# They are skipped where a GPU is visible, so that a checking bug can never turn into a
+# kernel launch on made-up pointers.
+
+nogpu = pytest.mark.skipif(
+    __import__("torch").cuda.is_available(), reason="fake pointers are only passed when no GPU is visible")
+
+F = ctypes.c_void_p(0x10000)  # 16- and 256-byte aligned, never dereferenced
+
+
+def fwd(p, H=F, W=F, idx=F, t=F, loss=F, lse=F, ws=F, nbytes=None):
+    L = _lib.lib()
+    if nbytes is None:
+        nbytes = max(1, L.kd_fused_workspace_bytes(ctypes.byref(p)))
+    return L.kd_fused_kl_fwd(ctypes.byref(p), H, W, idx, t, loss, lse, None, None, ws, nbytes, None)
+
+
+def bwd(p, H=F, W=F, idx=F, t=F, lse=F, dH=F, dW=F, ws=F, nbytes=None):
+    L = _lib.lib()
+    if nbytes is None:
+        nbytes = max(1, L.kd_fused_workspace_bytes(ctypes.byref(p)))
+    return L.kd_fused_kl_bwd(ctypes.byref(p), H, W, idx, t, lse, None, dH, dW, ws, nbytes, None)
+
+
+def dense(p, H=F, dH=F, ws=F, nbytes=None):
+    L = _lib.lib()
+    if nbytes is None:
+        nbytes = max(1, L.kd_dense_workspace_bytes(ctypes.byref(p)))
+    return L.kd_dense_kl(ctypes.byref(p), H, F, F, F, None, F, F, None, dH, F, ws, nbytes, None)
+
+
+@nogpu
+@pytest.mark.parametrize("bad,code", [
+    (dict(N=0), 2), (dict(d=0), 2), (dict(d=12), 2), (dict(V=0), 2), (dict(K=0), 2), (dict(K=129), 2),
+    (dict(V=50, K=60), 2), (dict(chunk=0), 2), (dict(V=256 * 16384 + 1), 2), (dict(N=1 << 30, d=8), 2),
+    (dict(act=2), 3), (dict(tlogit=-1), 3),
+    (dict(T=0.0), 4), (dict(T=-1.0), 4), (dict(T=float("nan")), 4), (dict(T=float("inf")), 4),
+    (dict(n_norm=float("nan")), 4), (dict(flags=4), 4), (dict(reserved=1), 4),
+])
+def test_bad_problem_rejected(bad, code):
+    p = prob(**bad)
+    assert fwd(p) == code
+    assert bwd(p) == code
+    assert dense(p) == code
+
+
+@nogpu
+def test_null_pointers_rejected():
+    p = prob()
+    L = _lib.lib()
+    assert L.kd_fused_kl_fwd(None, F, F, F, F, F, F, None, None, F, 1 << 40, None) == 1
+    for kw in ("H", "W", "idx", "t", "loss", "lse", "ws"):
+        assert fwd(p, **{kw: None}) == 1, kw
+    for kw in ("H", "W", "idx", "t", "lse", "dH", "dW", "ws"):
+        assert bwd(p, **{kw: None}) == 1, kw
+    assert dense(p, H=None) == 1 and dense(p, dH=None) == 1
+
+
+@nogpu
+def test_workspace_and_alignment_rejected():
+    p = prob()
+    need = ws_bytes()
+    assert fwd(p, nbytes=need - 1) == 5
+    assert bwd(p, nbytes=need - 1) == 5
+    assert fwd(p, ws=ctypes.c_void_p(0x10000 + 128)) == 5  # not 256-byte aligned
+    assert fwd(p, H=ctypes.c_void_p(0x10008)) == 4          # vector loads need 16-byte alignment
+    assert bwd(p, dH=ctypes.c_void_p(0x10004)) == 4
+    dn = _lib.lib().kd_dense_workspace_bytes(ctypes.byref(p))
+    assert dense(p, nbytes=dn - 1) == 5
+
+
+def test_fp32_problem_is_valid():
+    assert ws_bytes(act=KD_FP32, tlogit=KD_FP32, d=128, V=2048, K=16, N=256, chunk=64) > 0

@@ -1,0 +1,209 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle, element by element.
+
+Small and tail-shaped problems are compared in full; the large configurations on 256 seeded
+rows (lse, zk, KL_n, rows of dH), with dW checked in full on a 256-row sub-batch at the
+same (V, d) and by properties that hold at any size."""
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import lm_head_kl_amd as kd
+from gpu_helpers import TOL, device_inputs, host, max_rel, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_fused(H, W, idx, t, T, chunk, n_norm=0.0, grad=None, flags=0):
+    f = kd.fused_kl_fwd(H, W, idx, t, T=T, chunk=chunk, n_norm=n_norm, flags=flags, want_zk=True)
+    g = None if grad is None else torch.tensor(grad, dtype=torch.float32, device=H.device)
+    dH, dW = kd.fused_kl_bwd(H, W, idx, t, f.lse, grad_loss=g, T=T, chunk=chunk, n_norm=n_norm, flags=flags)
+    torch.cuda.synchronize()
+    return f, dH, dW
+
+
+def compare_full(p, chunk, tol, grad=1.0, n_norm=None, label=""):
+    say("full parity", label or p.name, f"N={p.N} d={p.d} V={p.V} K={p.K} chunk={chunk} dtype={p.dtype}")
+    H, W, idx, t = device_inputs(p)
+    nn = 0.0 if n_norm is None else n_norm
+    f, dH, dW = run_fused(H, W, idx, t, p.T, chunk, n_norm=nn, grad=grad)
+    ref = oracle.kl_chunked(p.f64("H"), p.f64("W"), p.idx, p.f64("tlog"), p.T, chunk=max(chunk, 256),
+                            n_norm=n_norm, g=grad)
+    # The oracle's loss carries the upstream weight g; the library's forward loss does not.
+    loss = float(f.loss.item()) * grad
+    assert abs(loss - ref["loss"]) <= tol["loss"] * abs(ref["loss"]), (loss, ref["loss"])
+    assert max_rel(host(f.lse), ref["lse"]) <= tol["lse"]
+    assert np.max(np.abs(host(f.row_kl) - ref["row_kl"])) <= tol["loss"] * np.abs(ref["row_kl"]).max()
+    np.testing.assert_allclose(host(f.zk), ref["zk"], rtol=tol["lse"], atol=tol["lse"] * 4)
+    e_dh, e_dw = rel_l2(host(dH), ref["dH"]), rel_l2(host(dW), ref["dW"])
+    say(f"  loss rel {abs(loss - ref['loss']) / abs(ref['loss']):.2e}  dH relL2 {e_dh:.2e}  dW relL2 {e_dw:.2e}")
+    assert e_dh <= tol["grad"] and e_dw <= tol["grad"]
+    return f, dH, dW, ref
+
+
+def test_tiny_fp32_full():
+    p = datagen.make("tiny")
+    compare_full(p, p.chunk, TOL["fp32"])
+
+
+def test_tiny_fp32_dense_path():
+    p = datagen.make("tiny")
+    say("dense path tiny fp32")
+    H, W, idx, t = device_inputs(p)
+    loss, lse, row_kl, dH, dW = kd.dense_kl(H, W, idx, t, T=p.T)
+    torch.cuda.synchronize()
+    ref = oracle.kl_dense(p.f64("H"), p.f64("W"), p.idx, p.f64("tlog"), p.T)
+    tol = TOL["fp32"]
+    assert abs(loss.item() - ref["loss"]) <= tol["loss"] * ref["loss"]
+    assert max_rel(host(lse), ref["lse"]) <= tol["lse"]
+    assert rel_l2(host(dH), ref["dH"]) <= tol["grad"] and rel_l2(host(dW), ref["dW"]) <= tol["grad"]
+
+
+def test_small_bf16_full():
+    p = datagen.make("small")
+    compare_full(p, p.chunk, TOL["bf16"])
+
+
+def test_small_bf16_dense_path():
+    p = datagen.make("small", N=1024)
+    say("dense path small bf16, 1024 rows")
+    H, W, idx, t = device_inputs(p)
+    loss, lse, row_kl, dH, dW = kd.dense_kl(H, W, idx, t, T=p.T)
+    torch.cuda.synchronize()
+    ref = oracle.kl_chunked(p.f64("H"), p.f64("W"), p.idx, p.f64("tlog"), p.T, chunk=512)
+    tol = TOL["bf16"]
+    assert abs(loss.item() - ref["loss"]) <= tol["loss"] * ref["loss"]
+    assert max_rel(host(lse), ref["lse"]) <= tol["lse"]
+    assert rel_l2(host(dH), ref["dH"]) <= tol["grad"] and rel_l2(host(dW), ref["dW"]) <= tol["grad"]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("shape", [
+    dict(N=300, d=200, V=1000, K=7, chunk=128, T=1.3),     # every size ragged
+    dict(N=1, d=64, V=300, K=1, chunk=1, T=0.7),           # one row, K = 1
+    dict(N=257, d=136, V=513, K=128, chunk=256, T=2.0),     # K at its maximum, one row past a block
+    dict(N=64, d=32, V=40, K=40, chunk=64, T=1.0),          # K = V: every token cached
+])
+def test_ragged_and_edge_shapes(dtype, shape):
+    p = datagen.make("tiny", N=shape["N"], d=shape["d"], V=shape["V"], K=shape["K"], T=shape["T"],
+                     dtype=dtype, chunk=shape["chunk"])
+    compare_full(p, shape["chunk"], TOL[dtype], grad=0.75, label=f"edge {shape} {dtype}")
+
+
+def test_nnorm_and_grad_scaling():
+    p = datagen.make("tiny")
+    compare_full(p, 96, TOL["fp32"], grad=-1.7, n_norm=1000.0, label="n_norm=1000, g=-1.7, chunk=96")
+
+
+# --------------------------------------------------------------- gather bit-exactness
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_gather_bit_exact_on_exact_arithmetic(dtype):
+    """Small-integer H and W make every logit an exact fp32 integer whatever the summation
+    order, so the gathered zk must equal the oracle bit for bit."""
+    N, d, V, K = 512, 1024, 4096, 100
+    g = np.random.default_rng(7)
+    Hn = g.integers(-2, 3, size=(N, d)).astype(np.float32)
+    Wn = g.integers(-2, 3, size=(V, d)).astype(np.float32)
+    p = datagen.make("small", N=N, d=d, V=V, K=K, dtype=dtype)
+    if dtype == "bf16":
+        p.H, p.W = datagen.bf16_bits(Hn), datagen.bf16_bits(Wn)
+    else:
+        p.H, p.W = Hn, Wn
+    say("exact gather", dtype)
+    H, W, idx, t = device_inputs(p)
+    f = kd.fused_kl_fwd(H, W, idx, t, T=1.0, chunk=256, want_zk=True)
+    torch.cuda.synchronize()
+    z = Hn.astype(np.float64) @ Wn.astype(np.float64).T
+    want = np.take_along_axis(z, p.idx.astype(np.int64), axis=1).astype(np.float32)
+    got = f.zk.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_zero_kl_when_student_matches_teacher(dtype):
+    """V = d, W = I and H = teacher logits at the cached ids (-3e4 elsewhere): z = H exactly,
+    the student equals the teacher on the top-K and vanishes elsewhere, so KL_n = 0."""
+    N, V, K = 256, 512, 16
+    p = datagen.make("tiny", N=N, d=V, V=V, K=K, dtype=dtype)
+    tl = p.f32("tlog")
+    Hn = np.full((N, V), -3.0e4, np.float32)
+    np.put_along_axis(Hn, p.idx.astype(np.int64), tl, axis=1)
+    Wn = np.eye(V, dtype=np.float32)
+    if dtype == "bf16":
+        p.H, p.W = datagen.bf16_bits(Hn), datagen.bf16_bits(Wn)
+    else:
+        p.H, p.W = Hn, Wn
+    say("zero KL", dtype)
+    H, W, idx, t = device_inputs(p)
+    f = kd.fused_kl_fwd(H, W, idx, t, T=1.0, chunk=128)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(f.row_kl.cpu().numpy())) <= 1e-6
+    assert abs(f.loss.item()) <= 1e-6
+
+
+# --------------------------------------------------------------- large configs, sampled
+
+def sampled_check(name, chunk=None, n_rows=256):
+    p = datagen.make(name)
+    chunk = chunk or p.chunk
+    say("sampled parity", name, f"N={p.N} chunk={chunk}")
+    H, W, idx, t = device_inputs(p)
+    f, dH, dW = run_fused(H, W, idx, t, p.T, chunk)
+    rows = datagen.sample_rows(p.N, n_rows, p.extra["seed"])
+    ref = oracle.kl_rows(None, p.f64("W"), p.idx, p.f64("tlog"), p.T, rows, n_norm=p.N,
+                         H_rows=datagen.bf16_to_f32(p.H[rows]))
+    tol = TOL["bf16"]
+    lse = host(f.lse)[rows]
+    assert max_rel(lse, ref["lse"]) <= tol["lse"]
+    np.testing.assert_allclose(host(f.zk)[rows], ref["zk"], rtol=tol["lse"], atol=5e-3)
+    rk = host(f.row_kl)[rows]
+    assert np.max(np.abs(rk - ref["row_kl"])) <= tol["loss"] * np.abs(ref["row_kl"]).max() * 2
+    e = rel_l2(host(dH[torch.from_numpy(rows).to(dH.device)]), ref["dH"])
+    say(f"  sampled dH relL2 {e:.2e}")
+    assert e <= tol["grad"]
+    # the scalar loss is T^2/N times the sum of the per-row terms
+    s = float(np.sum(host(f.row_kl), dtype=np.float64)) * p.T * p.T / p.N
+    assert abs(f.loss.item() - s) <= 1e-5 * abs(s)
+    # every row of G sums to zero, so the columns of dW do too
+    colsum = dW.double().sum(0)
+    scale = dW.double().abs().sum(0)
+    assert float((colsum.abs() / scale.clamp_min(1e-30)).max()) < 1e-3
+    return p, f, dH, dW
+
+
+def subbatch_dw_check(name, n=256):
+    """The full dW at the config's (V, d) on a 256-row sub-batch, against the oracle."""
+    p = datagen.make(name, N=n)
+    say("sub-batch dW", name, f"rows={n}")
+    H, W, idx, t = device_inputs(p)
+    f, dH, dW = run_fused(H, W, idx, t, p.T, p.chunk)
+    ref = oracle.kl_chunked(p.f64("H"), p.f64("W"), p.idx, p.f64("tlog"), p.T, chunk=n)
+    e = rel_l2(host(dW), ref["dW"])
+    say(f"  dW relL2 {e:.2e}")
+    assert e <= TOL["bf16"]["grad"]
+    assert rel_l2(host(dH), ref["dH"]) <= TOL["bf16"]["grad"]
+    assert abs(f.loss.item() - ref["loss"]) <= TOL["bf16"]["loss"] * ref["loss"]
+
+
+@pytest.mark.parametrize("chunk", [512, 1024, 2048, 4096])
+def test_qwen_chunk_sweep(chunk):
+    sampled_check("qwen", chunk=chunk)
+
+
+def test_qwen_subbatch_dw():
+    subbatch_dw_check("qwen")
+
+
+def test_gptoss_sampled():
+    sampled_check("gptoss")
+
+
+def test_gptoss_subbatch_dw():
+    subbatch_dw_check("gptoss")
+
+
+def test_full_shape_sampled():
+    sampled_check("full")
