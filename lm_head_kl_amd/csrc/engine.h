@@ -1,0 +1,478 @@
+// MFMA tile engine for gfx950, shared by every GEMM-shaped kernel of libkdkl.
+//
+// A workgroup of 256 threads computes one 256 x 256 fp32 tile of C = A B^T over a K range.
+// The threads form four 64-wide waves in a 2 x 2 grid. Each wave owns 128 x 128 of the tile
+// as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, or of v_mfma_f32_32x32x2_f32 for fp32
+// inputs. The accumulators (256 per lane) live in AGPRs.
+//
+// Operands reach LDS in 16-byte chunks, double-buffered over K (two stages of 2 x 32 KB):
+//   - K contiguous (element (mn, k) at src[mn*ld + k]): buffer_load_dwordx4 with the LDS
+//     destination bit, straight from memory into LDS. No VGPRs and no ds_write are used.
+//     A wave instruction fills 64 consecutive LDS chunks, so each lane fetches the global
+//     chunk that belongs at its destination under the swizzle below.
+//   - M/N contiguous (element (mn, k) at src[k*ld + mn]): buffer loads of 8 x 8 (bf16) or
+//     4 x 4 (fp32) blocks into VGPRs, transposed in registers and written with ds_write_b128.
+// Rows and k beyond the operand's limits are read through an out-of-range offset of the
+// buffer descriptor. The hardware returns zeros for those, so the loop has no branches.
+//
+// LDS tile layout: [256 rows][8 chunks of 16 bytes]. Chunk c of row r sits at
+// c ^ ((r ^ (r >> 3)) & 7). This is conflict free for the MFMA fragment reads (32 rows, one
+// chunk column), for the DMA fill (8 rows x 8 chunks per 1 KB), and for the transposed
+// writes (rows 8 apart).
+//
+// MFMA lane layouts (checked on gfx950 hardware):
+//   32x32x16 bf16: lane l supplies A[m = l%32][k = 8*(l/32) + 0..7], and B likewise with n.
+//   32x32x2 f32:   lane l supplies A[m = l%32][k = l/32].
+//   Accumulator element e of lane l: row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+// The DMA fill places lane l's 16 bytes at M0 + 16*l; an out-of-range offset writes zeros
+// (also checked on hardware).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kdkl_internal.h"
+
+namespace kdkl {
+
+typedef uint16_t bf16_t;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int NTHR = 256;
+constexpr int NCH = 8;                       // 16-byte chunks per tile row per K step
+constexpr int TILE_CHUNKS = kTileM * NCH;    // 2048 chunks = 32 KB per operand per stage
+constexpr int LDS_CHUNKS = 4 * TILE_CHUNKS;  // 2 stages x 2 operands = 128 KB
+constexpr uint32_t kOOB = 0x7FFFFFF0u;       // descriptor range; offsets >= it read as zero
+
+template <typename T> struct Elem;
+template <> struct Elem<bf16_t> { static constexpr int VEC = 8; static constexpr int BK = 64; };
+template <> struct Elem<float> { static constexpr int VEC = 4; static constexpr int BK = 32; };
+
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
+
+// The base is the same in every lane; say so, so that the descriptor lives in SGPRs and the
+// loads need no waterfall loop.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(base)), (short)0, (int)kOOB,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+struct WaveId {
+    int tid, lane, w, wm, wn, h, lr;
+    __device__ WaveId() {
+        tid = threadIdx.x;
+        lane = tid & 63;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        wm = w >> 1;
+        wn = w & 1;
+        h = lane >> 5;
+        lr = lane & 31;
+    }
+};
+
+template <typename T> __device__ __forceinline__ void mma(f32x16& c, const u32x4& a, const u32x4& b);
+template <> __device__ __forceinline__ void mma<bf16_t>(f32x16& c, const u32x4& a, const u32x4& b) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ void mma<float>(f32x16& c, const u32x4& a, const u32x4& b) {
+    // A 16-byte chunk holds 4 consecutive k and the two lane halves hold neighbouring chunks.
+    // Instruction i takes element i of each, so the four together cover 8 distinct k, the
+    // same ones for A and B.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i]), __uint_as_float(b[i]), c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------------------------------
+// K-contiguous operand, filled by DMA. Wave w's instruction t fills LDS chunks
+// 256t + 64w + lane, i.e. row 32t + 8w + lane/8, physical chunk lane%8.
+template <typename T>
+struct KOperand {
+    static constexpr int VEC = Elem<T>::VEC;
+    const char* base;  // &src[mn0*ld] (uniform)
+    uint32_t off[8];   // byte offset of this lane's chunk for instruction t at k = 0, or kOOB
+    int chunk[2];      // logical chunk (k/VEC within the step) for even / odd t
+
+    __device__ __forceinline__ void init(const T* src, int64_t ld, int64_t mn0, int64_t mn_lim, const WaveId& id) {
+        base = (const char*)(src + mn0 * ld);
+        const int r8 = id.lane >> 3, p = id.lane & 7;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) chunk[t] = p ^ ((r8 ^ (4 * t + id.w)) & 7);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int row = 32 * t + 8 * id.w + r8;
+            off[t] = mn0 + row < mn_lim ? (uint32_t)((row * ld + chunk[t & 1] * VEC) * (int64_t)sizeof(T)) : kOOB;
+        }
+    }
+    // Enqueue the K step starting at k0 into the LDS tile (no wait).
+    __device__ __forceinline__ void issue(u32x4* tile, int64_t k0, int64_t k_lim, const WaveId& id) const {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + k0 * (int64_t)sizeof(T));
+        const int64_t kc = (k_lim - k0 + VEC - 1) / VEC;  // chunks of this step inside the K range
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const uint32_t o = chunk[t & 1] < kc ? off[t] : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + 256 * t + 64 * id.w), 16, (int)o, 0, 0, 0);
+        }
+    }
+    __device__ __forceinline__ void commit(u32x4*, const WaveId&) const {}
+};
+
+// M/N-contiguous operand, through VGPRs with an in-register transpose.
+template <typename T> struct MNOperand;
+
+template <>
+struct MNOperand<bf16_t> {
+    // thread: mnb = tid%32 (8 mn), kb = tid/32 (8 k); loads 8 rows of 16 bytes.
+    const char* base;  // &src[mn0] (uniform)
+    int64_t ldb;       // row stride in bytes
+    uint32_t off0;     // (kb*8)*ldb + mnb*16, or kOOB if the mn block is outside
+    int kb;
+    u32x4 r[8];
+
+    __device__ __forceinline__ void init(const bf16_t* src, int64_t ld, int64_t mn0, int64_t mn_lim,
+                                         const WaveId& id) {
+        base = (const char*)(src + mn0);
+        ldb = ld * 2;
+        const int mnb = id.tid & 31;
+        kb = id.tid >> 5;
+        off0 = mn0 + mnb * 8 < mn_lim ? (uint32_t)(kb * 8 * ldb + mnb * 16) : kOOB;
+    }
+    __device__ __forceinline__ void issue(u32x4*, int64_t k0, int64_t k_lim, const WaveId&) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * ldb);
+        const int64_t kr = k_lim - k0 - kb * 8;  // rows of this thread's block inside the K range
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const uint32_t o = (kk < kr && off0 != kOOB) ? off0 + (uint32_t)(kk * ldb) : kOOB;
+            r[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0));
+        }
+    }
+    __device__ __forceinline__ void commit(u32x4* tile, const WaveId& id) const {
+        const int mnb = id.tid & 31;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            // row i of the transposed block: element i of each of the 8 loaded k-rows
+            const int wsel = i >> 1, sh = 16 * (i & 1);
+            u32x4 y;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t lo = (r[2 * p][wsel] >> sh) & 0xffffu;
+                const uint32_t hi = (r[2 * p + 1][wsel] >> sh) & 0xffffu;
+                y[p] = lo | (hi << 16);
+            }
+            const int row = mnb * 8 + i;
+            tile[row * NCH + swz(row, kb)] = y;
+        }
+    }
+};
+
+template <>
+struct MNOperand<float> {
+    // two 4(k) x 4(mn) blocks per thread: q = tid + 256*t, mnb = q%64, kb = q/64.
+    const char* base;
+    int64_t ldb;
+    uint32_t off0[2];
+    u32x4 r[8];
+
+    __device__ __forceinline__ void init(const float* src, int64_t ld, int64_t mn0, int64_t mn_lim,
+                                         const WaveId& id) {
+        base = (const char*)(src + mn0);
+        ldb = ld * 4;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int q = id.tid + NTHR * t, mnb = q & 63, kb = q >> 6;
+            off0[t] = mn0 + mnb * 4 < mn_lim ? (uint32_t)(kb * 4 * ldb + mnb * 16) : kOOB;
+        }
+    }
+    __device__ __forceinline__ void issue(u32x4*, int64_t k0, int64_t k_lim, const WaveId& id) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * ldb);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int kb = (id.tid + NTHR * t) >> 6;
+            const int64_t kr = k_lim - k0 - kb * 4;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const uint32_t o = (kk < kr && off0[t] != kOOB) ? off0[t] + (uint32_t)(kk * ldb) : kOOB;
+                r[t * 4 + kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0));
+            }
+        }
+    }
+    __device__ __forceinline__ void commit(u32x4* tile, const WaveId& id) const {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int q = id.tid + NTHR * t, mnb = q & 63, kb = q >> 6;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const u32x4 y{r[t * 4 + 0][i], r[t * 4 + 1][i], r[t * 4 + 2][i], r[t * 4 + 3][i]};
+                const int row = mnb * 4 + i;
+                tile[row * NCH + swz(row, kb)] = y;
+            }
+        }
+    }
+};
+
+template <typename T, bool KMAJ> struct OperandSel { using type = KOperand<T>; };
+template <typename T> struct OperandSel<T, false> { using type = MNOperand<T>; };
+
+// One K step from LDS: for each of the 4 k-groups, 4 A and 4 B fragments and 16 MFMAs.
+// Fragments are double-buffered so the reads of group g+1 overlap the MFMAs of group g.
+template <typename T>
+__device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const u32x4* tA, const u32x4* tB,
+                                              const WaveId& id) {
+    u32x4 fa[2][4], fb[2][4];
+    auto read = [&](int g, u32x4(&a)[4], u32x4(&b)[4]) {
+        const int c = 2 * g + id.h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = id.wm * 128 + i * 32 + id.lr;
+            a[i] = tA[row * NCH + swz(row, c)];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = id.wn * 128 + j * 32 + id.lr;
+            b[j] = tB[row * NCH + swz(row, c)];
+        }
+    };
+    read(0, fa[0], fb[0]);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        if (g < 3) read(g + 1, fa[(g + 1) & 1], fb[(g + 1) & 1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mma<T>(acc[i][j], fa[g & 1][i], fb[g & 1][j]);
+    }
+}
+
+// acc = A[m0:m0+256, k_begin:k_end] B[n0:n0+256, k_begin:k_end]^T.
+// AK / BK: operand is K contiguous. ka_lim / kb_lim: first k each operand may not read
+// (multiples of the 16-byte vector width). Rows at or past m_lim / n_lim read as zero.
+// Ends with a barrier, so the LDS may be reused right away.
+template <typename T, bool AK, bool BKM>
+__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], u32x4* L, const WaveId& id,
+                                          const T* A, int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim,
+                                          const T* B, int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim,
+                                          int64_t k_begin, int64_t k_end) {
+    constexpr int BK = Elem<T>::BK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    const int nk = (int)((k_end - k_begin + BK - 1) / BK);
+    if (nk <= 0) return;
+    typename OperandSel<T, AK>::type opA;
+    typename OperandSel<T, BKM>::type opB;
+    opA.init(A, lda, m0, m_lim, id);
+    opB.init(B, ldb, n0, n_lim, id);
+    opA.issue(L, k_begin, ka_lim, id);
+    opB.issue(L + TILE_CHUNKS, k_begin, kb_lim, id);
+    wait_vmem();
+    opA.commit(L, id);
+    opB.commit(L + TILE_CHUNKS, id);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        const bool more = kt + 1 < nk;
+        u32x4* nA = L + (2 * (cur ^ 1)) * TILE_CHUNKS;
+        u32x4* nB = nA + TILE_CHUNKS;
+        if (more) {
+            const int64_t k0 = k_begin + (int64_t)(kt + 1) * BK;
+            opA.issue(nA, k0, ka_lim, id);
+            opB.issue(nB, k0, kb_lim, id);
+        }
+        compute_stage<T>(acc, L + (2 * cur) * TILE_CHUNKS, L + (2 * cur + 1) * TILE_CHUNKS, id);
+        if (more) {
+            wait_vmem();
+            opA.commit(nA, id);
+            opB.commit(nB, id);
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Deep-pipelined variant for two K-contiguous operands: four LDS stages of half the K step
+// (32 bf16 / 16 fp32), each tile [256 rows][4 chunks]. DMA loads run three stages ahead of
+// the MFMAs, which covers memory latency beyond one step. The chunk swizzle for 4-chunk rows
+// is c ^ (((r >> 2) ^ (r >> 1)) & 3). It is conflict free for fragment reads served 8 or 16
+// lanes at a time.
+constexpr int NCH4 = 4;
+constexpr int TILE4 = kTileM * NCH4;  // 1024 chunks = 16 KB per operand per stage
+__device__ __forceinline__ int swz4(int r, int c) { return c ^ (((r >> 2) ^ (r >> 1)) & 3); }
+
+template <typename T>
+struct KOperand4 {
+    static constexpr int VEC = Elem<T>::VEC;
+    __amdgpu_buffer_rsrc_t rsrc;  // tile origin &src[mn0*ld]; k0 goes in the scalar offset
+    uint32_t off[4];
+    int chunk;
+    // Wave w's instruction t fills chunks 256t + 64w + lane: row 64t + 16w + lane/4, slot lane%4.
+    __device__ __forceinline__ void init(const T* src, int64_t ld, int64_t mn0, int64_t mn_lim, const WaveId& id) {
+        rsrc = make_rsrc(src + mn0 * ld);
+        chunk = (id.lane & 3) ^ (((id.lane >> 4) ^ (id.lane >> 3)) & 3);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int row = 64 * t + 16 * id.w + (id.lane >> 2);
+            off[t] = mn0 + row < mn_lim ? (uint32_t)((row * ld + chunk * VEC) * (int64_t)sizeof(T)) : kOOB;
+        }
+    }
+    // Load instruction t of the K step at k0 into the stage tile. Chunks at or past k_lim, and
+    // every chunk when `live` is false, read as zero (no memory access). `full` (uniform) says
+    // the whole step is inside the K range.
+    __device__ __forceinline__ void issue_one(u32x4* tile, int t, int64_t k0, int64_t k_lim, bool full, bool live,
+                                              const WaveId& id) const {
+        const bool in = live && (full || (int64_t)chunk * VEC < k_lim - k0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + 256 * t + 64 * id.w), 16,
+                                                 (int)(in ? off[t] : kOOB), (int)(k0 * (int64_t)sizeof(T)), 0, 0);
+    }
+    __device__ __forceinline__ void issue(u32x4* tile, int64_t k0, int64_t k_lim, bool live, const WaveId& id) const {
+        const bool full = k0 + Elem<T>::BK / 2 <= k_lim;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) issue_one(tile, t, k0, k_lim, full, live, id);
+    }
+};
+
+// Fragments of one k-group (g = 0, 1) of a 4-chunk stage: 4 A and 4 B chunks.
+template <typename T>
+__device__ __forceinline__ void read_frags4(u32x4 (&fa)[4], u32x4 (&fb)[4], const u32x4* tA, const u32x4* tB,
+                                            int g, const WaveId& id) {
+    const int c = 2 * g + id.h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = id.wm * 128 + i * 32 + id.lr;
+        fa[i] = tA[row * NCH4 + swz4(row, c)];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = id.wn * 128 + j * 32 + id.lr;
+        fb[j] = tB[row * NCH4 + swz4(row, c)];
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void mma_block(f32x16 (&acc)[4][4], const u32x4 (&fa)[4], const u32x4 (&fb)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mma<T>(acc[i][j], fa[i], fb[j]);
+}
+
+template <int N> __device__ __forceinline__ void wait_vmem_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+#define KD_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
+// sched_group_barrier masks
+#define KD_SG_MFMA 0x008
+#define KD_SG_VMEM_RD 0x020
+#define KD_SG_DS_RD 0x100
+
+// Same contract as gemm_tile with both operands K contiguous.
+// Four LDS stages of half a K step. Schedule of stage kt (k-groups g0, g1; fragment sets F0, F1):
+//   [MFMA(F0) interleaved with reads F1 <- (kt, g1)]
+//   wait for stage kt+1, barrier
+//   [MFMA(F1) interleaved with DMA of stage kt+4 into stage kt's buffer and reads F0 <- (kt+1, g0)]
+// Stage kt's buffer is free after that barrier (its last fragments were read before it), so
+// the DMA runs four stages ahead. Every LDS read is issued one MFMA block ahead of its use.
+template <typename T>
+__device__ __forceinline__ void gemm_tile_kk(f32x16 (&acc)[4][4], u32x4* L, const WaveId& id,
+                                             const T* A, int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim,
+                                             const T* B, int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim,
+                                             int64_t k_begin, int64_t k_end) {
+    constexpr int BKH = Elem<T>::BK / 2;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    const int nk = (int)((k_end - k_begin + BKH - 1) / BKH);
+    if (nk <= 0) return;
+    KOperand4<T> opA, opB;
+    opA.init(A, lda, m0, m_lim, id);
+    opB.init(B, ldb, n0, n_lim, id);
+    auto stageA = [&](int s) { return L + (2 * (s & 3)) * TILE4; };
+    auto stageB = [&](int s) { return L + (2 * (s & 3) + 1) * TILE4; };
+    auto kof = [&](int s) { return k_begin + (int64_t)s * BKH; };
+    // Every stage slot issues its 8 loads, live or not, so the wait counts are constant:
+    // stage s is complete once at most the 3 (prologue) or 2 (loop) later stages are in flight.
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        opA.issue(stageA(s), kof(s), ka_lim, s < nk, id);
+        opB.issue(stageB(s), kof(s), kb_lim, s < nk, id);
+    }
+    wait_vmem_le<24>();
+    __syncthreads();
+    u32x4 f0a[4], f0b[4], f1a[4], f1b[4];
+    read_frags4<T>(f0a, f0b, stageA(0), stageB(0), 0, id);
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+        KD_SCHED_FENCE();
+        read_frags4<T>(f1a, f1b, stageA(kt), stageB(kt), 1, id);
+        mma_block<T>(acc, f0a, f0b);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 8, 0);
+        KD_SCHED_FENCE();
+        wait_vmem_le<16>();  // stage kt+1 complete; kt+2 and kt+3 may be in flight
+        __syncthreads();
+        KD_SCHED_FENCE();
+        {
+            const int s = kt + 4;
+            const bool live = s < nk;
+            const bool fa = kof(s) + BKH <= ka_lim, fb = kof(s) + BKH <= kb_lim;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                opA.issue_one(stageA(s), t, kof(s), ka_lim, fa, live, id);
+                opB.issue_one(stageB(s), t, kof(s), kb_lim, fb, live, id);
+            }
+        }
+        read_frags4<T>(f0a, f0b, stageA(kt + 1), stageB(kt + 1), 0, id);
+        mma_block<T>(acc, f1a, f1b);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM_RD, 1, 1);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 1);
+        }
+        KD_SCHED_FENCE();
+    }
+    // last stage
+    KD_SCHED_FENCE();
+    read_frags4<T>(f1a, f1b, stageA(nk - 1), stageB(nk - 1), 1, id);
+    KD_SCHED_FENCE();
+    mma_block<T>(acc, f0a, f0b);
+    KD_SCHED_FENCE();
+    mma_block<T>(acc, f1a, f1b);
+    KD_SCHED_FENCE();
+    wait_vmem_le<0>();  // no zero-fill may land after the caller reuses the LDS
+    __syncthreads();
+}
+
+// Workgroups go to the 8 XCDs round robin (id % 8). Give XCD x the contiguous range
+// [x*per, (x+1)*per) of logical tiles, in dispatch order, so tiles that share operands run
+// on the same L2 at about the same time. Returns n (no work) for the padding ids.
+__device__ __forceinline__ int64_t xcd_tile(int64_t id, int64_t n) {
+    const int64_t per = (n + 7) / 8;
+    const int64_t t = (id % 8) * per + id / 8;
+    return t < n ? t : n;
+}
+
+__device__ __forceinline__ int acc_row(int i, int e, int h) { return i * 32 + 8 * (e >> 2) + 4 * h + (e & 3); }
+
+}  // namespace kdkl

@@ -40,29 +40,14 @@
 
 #include <algorithm>
 
+#include "engine.h"
 #include "kdkl_internal.h"
 
 namespace kdkl {
 
-typedef uint16_t bf16_t;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-constexpr int NTHR = 256;
-constexpr int NCH = 8;                 // 16-byte chunks per tile row per K step
-constexpr int TILE_CHUNKS = kTileM * NCH;  // 2048 chunks = 32 KB per operand per stage
-constexpr int LDS_CHUNKS = 4 * TILE_CHUNKS;  // 2 stages x 2 operands = 128 KB
-constexpr int STG = kTileN + 4;        // staging row stride in floats (16-byte aligned)
+constexpr int STG = kTileN + 4;  // staging row stride in floats (16-byte aligned)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kLn2 = 0.69314718055994530942;
-
-template <typename T> struct Elem;
-template <> struct Elem<bf16_t> { static constexpr int VEC = 8; static constexpr int BK = 64; };
-template <> struct Elem<float> { static constexpr int VEC = 4; static constexpr int BK = 32; };
-
-__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r ^ (r >> 3)) & 7); }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -75,229 +60,9 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 }
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
-template <typename T> __device__ __forceinline__ float load_scalar(const T* p, int64_t i);
-template <> __device__ __forceinline__ float load_scalar<float>(const float* p, int64_t i) { return p[i]; }
-template <> __device__ __forceinline__ float load_scalar<bf16_t>(const bf16_t* p, int64_t i) { return bf2f(p[i]); }
-
 __device__ __forceinline__ float load_t(const void* p, Dt dt, int64_t i) {
     return dt == Dt::BF16 ? bf2f(((const bf16_t*)p)[i]) : ((const float*)p)[i];
 }
-
-template <typename T> __device__ __forceinline__ void mma(f32x16& c, const u32x4& a, const u32x4& b);
-template <> __device__ __forceinline__ void mma<bf16_t>(f32x16& c, const u32x4& a, const u32x4& b) {
-    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                c, 0, 0, 0);
-}
-template <> __device__ __forceinline__ void mma<float>(f32x16& c, const u32x4& a, const u32x4& b) {
-    // One 16-byte chunk holds 4 consecutive k; the two lane halves hold neighbouring chunks.
-    // Instruction i takes element i of each, so together they cover 8 distinct k, the same
-    // ones for A and B.
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        c = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[i]), __uint_as_float(b[i]), c, 0, 0, 0);
-}
-
-// ------------------------------------------------------------------------------------------
-// Operand loaders: global -> registers (8 x 16 bytes per thread) -> LDS tile [256 rows][8 chunks].
-
-// K contiguous: element (mn, k) at src[mn*ld + k]. Thread takes chunks q = tid + 256*t.
-template <typename T>
-__device__ __forceinline__ void load_kmaj(u32x4 (&r)[8], const T* src, int64_t ld, int64_t mn0,
-                                          int64_t mn_lim, int64_t k0, int64_t k_lim, int tid) {
-    constexpr int VEC = Elem<T>::VEC;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int q = tid + NTHR * t;
-        const int row = q >> 3, c = q & 7;
-        const int64_t mn = mn0 + row, k = k0 + c * VEC;
-        if (mn < mn_lim && k < k_lim)
-            r[t] = *(const u32x4*)(src + mn * ld + k);
-        else
-            r[t] = u32x4{0u, 0u, 0u, 0u};
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ void store_kmaj(const u32x4 (&r)[8], u32x4* tile, int tid) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int q = tid + NTHR * t;
-        const int row = q >> 3, c = q & 7;
-        tile[row * NCH + swz(row, c)] = r[t];
-    }
-}
-
-// M/N contiguous: element (mn, k) at src[k*ld + mn].
-// bf16: one 8(k) x 8(mn) block per thread, mnb = tid%32 (8 mn each), kb = tid/32 (8 k each).
-// fp32: two 4(k) x 4(mn) blocks per thread, q = tid + 256*t, mnb = q%64, kb = q/64.
-template <typename T>
-__device__ __forceinline__ void load_mnmaj(u32x4 (&r)[8], const T* src, int64_t ld, int64_t mn0,
-                                           int64_t mn_lim, int64_t k0, int64_t k_lim, int tid);
-template <>
-__device__ __forceinline__ void load_mnmaj<bf16_t>(u32x4 (&r)[8], const bf16_t* src, int64_t ld, int64_t mn0,
-                                                   int64_t mn_lim, int64_t k0, int64_t k_lim, int tid) {
-    const int mnb = tid & 31, kb = tid >> 5;
-    const int64_t mn = mn0 + mnb * 8;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-        const int64_t k = k0 + kb * 8 + kk;
-        if (mn < mn_lim && k < k_lim)
-            r[kk] = *(const u32x4*)(src + k * ld + mn);
-        else
-            r[kk] = u32x4{0u, 0u, 0u, 0u};
-    }
-}
-template <>
-__device__ __forceinline__ void load_mnmaj<float>(u32x4 (&r)[8], const float* src, int64_t ld, int64_t mn0,
-                                                  int64_t mn_lim, int64_t k0, int64_t k_lim, int tid) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int q = tid + NTHR * t;
-        const int mnb = q & 63, kb = q >> 6;
-        const int64_t mn = mn0 + mnb * 4;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int64_t k = k0 + kb * 4 + kk;
-            if (mn < mn_lim && k < k_lim)
-                r[t * 4 + kk] = *(const u32x4*)(src + k * ld + mn);
-            else
-                r[t * 4 + kk] = u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ void store_mnmaj(const u32x4 (&r)[8], u32x4* tile, int tid);
-template <>
-__device__ __forceinline__ void store_mnmaj<bf16_t>(const u32x4 (&r)[8], u32x4* tile, int tid) {
-    const int mnb = tid & 31, kb = tid >> 5;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        // Row i of the transposed block: element i of each of the 8 loaded k-rows.
-        const int wsel = i >> 1, sh = 16 * (i & 1);
-        u32x4 y;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t lo = (r[2 * p][wsel] >> sh) & 0xffffu;
-            const uint32_t hi = (r[2 * p + 1][wsel] >> sh) & 0xffffu;
-            y[p] = lo | (hi << 16);
-        }
-        const int row = mnb * 8 + i;
-        tile[row * NCH + swz(row, kb)] = y;
-    }
-}
-template <>
-__device__ __forceinline__ void store_mnmaj<float>(const u32x4 (&r)[8], u32x4* tile, int tid) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int q = tid + NTHR * t;
-        const int mnb = q & 63, kb = q >> 6;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 y{r[t * 4 + 0][i], r[t * 4 + 1][i], r[t * 4 + 2][i], r[t * 4 + 3][i]};
-            const int row = mnb * 4 + i;
-            tile[row * NCH + swz(row, kb)] = y;
-        }
-    }
-}
-
-template <typename T, bool KMAJ>
-__device__ __forceinline__ void load_op(u32x4 (&r)[8], const T* src, int64_t ld, int64_t mn0, int64_t mn_lim,
-                                        int64_t k0, int64_t k_lim, int tid) {
-    if constexpr (KMAJ)
-        load_kmaj<T>(r, src, ld, mn0, mn_lim, k0, k_lim, tid);
-    else
-        load_mnmaj<T>(r, src, ld, mn0, mn_lim, k0, k_lim, tid);
-}
-template <typename T, bool KMAJ>
-__device__ __forceinline__ void store_op(const u32x4 (&r)[8], u32x4* tile, int tid) {
-    if constexpr (KMAJ)
-        store_kmaj<T>(r, tile, tid);
-    else
-        store_mnmaj<T>(r, tile, tid);
-}
-
-// ------------------------------------------------------------------------------------------
-// The tile engine: acc (per wave 128 x 128 as 4 x 4 MFMA blocks) = A[m0:m0+256, kr] B[n0:n0+256, kr]^T.
-// ka_lim / kb_lim are the first k (exclusive) each operand may read; they must be multiples of
-// the 16-byte vector width. Rows at or beyond m_lim / n_lim read as zero.
-// Ends with a barrier, so the caller may reuse the LDS right away.
-
-struct WaveId {
-    int tid, lane, w, wm, wn, h, lr;
-    __device__ WaveId() {
-        tid = threadIdx.x;
-        lane = tid & 63;
-        w = tid >> 6;
-        wm = w >> 1;
-        wn = w & 1;
-        h = lane >> 5;
-        lr = lane & 31;
-    }
-};
-
-template <typename T>
-__device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const u32x4* tA, const u32x4* tB,
-                                              const WaveId& id) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        u32x4 a[4], b[4];
-        const int c = 2 * g + id.h;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = id.wm * 128 + i * 32 + id.lr;
-            a[i] = tA[row * NCH + swz(row, c)];
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = id.wn * 128 + j * 32 + id.lr;
-            b[j] = tB[row * NCH + swz(row, c)];
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) mma<T>(acc[i][j], a[i], b[j]);
-    }
-}
-
-template <typename T, bool AK, bool BKM>
-__device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], u32x4* L, const WaveId& id,
-                                          const T* A, int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim,
-                                          const T* B, int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim,
-                                          int64_t k_begin, int64_t k_end) {
-    constexpr int BK = Elem<T>::BK;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-    const int nk = (int)((k_end - k_begin + BK - 1) / BK);
-    if (nk <= 0) return;
-    u32x4 ra[8], rb[8];
-    load_op<T, AK>(ra, A, lda, m0, m_lim, k_begin, ka_lim, id.tid);
-    load_op<T, BKM>(rb, B, ldb, n0, n_lim, k_begin, kb_lim, id.tid);
-    store_op<T, AK>(ra, L, id.tid);
-    store_op<T, BKM>(rb, L + TILE_CHUNKS, id.tid);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            const int64_t k0 = k_begin + (int64_t)(kt + 1) * BK;
-            load_op<T, AK>(ra, A, lda, m0, m_lim, k0, ka_lim, id.tid);
-            load_op<T, BKM>(rb, B, ldb, n0, n_lim, k0, kb_lim, id.tid);
-        }
-        compute_stage<T>(acc, L + (2 * cur) * TILE_CHUNKS, L + (2 * cur + 1) * TILE_CHUNKS, id);
-        if (more) {
-            store_op<T, AK>(ra, L + (2 * (cur ^ 1)) * TILE_CHUNKS, id.tid);
-            store_op<T, BKM>(rb, L + (2 * (cur ^ 1) + 1) * TILE_CHUNKS, id.tid);
-        }
-        __syncthreads();
-    }
-}
-
-// Row of accumulator element (i, e) within the wave's 128 rows, and its row within the
-// 64-row staging slab of pass i.
-__device__ __forceinline__ int acc_row(int i, int e, int h) { return i * 32 + 8 * (e >> 2) + 4 * h + (e & 3); }
 
 // Merge (m2, s2) into (m, s): sums of 2^(y - m) over disjoint sets.
 __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2) {
@@ -454,98 +219,109 @@ struct FwdArgs {
     float c;  // log2(e)/T
     const int32_t* off;
     const uint32_t* ent;
-    int n_vt, tps;
-    float2* part;  // [2*n_vsplit][N]
+    int n_vt;
+    int Q;          // vocab lanes: unit (rb, q) takes vocab tiles q, q + Q, q + 2Q, ...
+    int64_t n_unit; // row blocks * Q
+    float2* part;   // [2Q][N]: per (lane, wave column) partial (max, sum) of each row
     float* zk;
 };
 
+// Persistent forward. Units (row block, vocab lane) are ordered row-block major. XCD x
+// takes the contiguous band [x*band, (x+1)*band), so its 32 workgroups work on a few row
+// blocks times Q vocab lanes at once. Those share both the H rows and the W tiles in the
+// XCD's L2.
 template <typename T>
 __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
     const WaveId id;
-    const int rb = blockIdx.x, vs = blockIdx.y;
-    const int64_t m0 = (int64_t)rb * kTileM;
-    const int t0 = vs * a.tps, t1 = min(a.n_vt, t0 + a.tps);
-    const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
+    const int64_t P = gridDim.x;
+    const int64_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd = P / 8;
+    const int64_t band = (a.n_unit + 7) / 8;
+    const int64_t u_end = min(a.n_unit, (xcd + 1) * band);
     float* stage = (float*)L;
-    float run_m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, run_s[4] = {0.f, 0.f, 0.f, 0.f};
 
-    for (int vt = t0; vt < t1; ++vt) {
-        const int64_t n0 = (int64_t)vt * kTileN;
-        f32x16 acc[4][4];
-        gemm_tile<T, true, true>(acc, L, id, (const T*)a.H, a.d, m0, a.N, a.d, (const T*)a.W, a.d, n0, a.V,
-                                 a.d, 0, a.d);
+    for (int64_t u = xcd * band + slot; u < u_end; u += per_xcd) {
+        const int rb = (int)(u / a.Q), q = (int)(u % a.Q);
+        const int64_t m0 = (int64_t)rb * kTileM;
+        const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
+        float run_m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, run_s[4] = {0.f, 0.f, 0.f, 0.f};
 
-        // Gather z at the cached ids of this (row block, vocab tile), one 64-row slab at a time.
-        const int e0 = off[vt], e1 = off[vt + 1];
-        if (e1 > e0) {
+        for (int vt = q; vt < a.n_vt; vt += a.Q) {
+            const int64_t n0 = (int64_t)vt * kTileN;
+            f32x16 acc[4][4];
+            gemm_tile_kk<T>(acc, L, id, (const T*)a.H, a.d, m0, a.N, a.d, (const T*)a.W, a.d, n0,
+                                     a.V, a.d, 0, a.d);
+
+            // Gather z at the cached ids of this (row block, vocab tile), one 64-row slab at a time.
+            const int e0 = off[vt], e1 = off[vt + 1];
+            if (e1 > e0) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
+                for (int p = 0; p < 4; ++p) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                    for (int j = 0; j < 4; ++j)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const int rl = id.wm * 32 + 8 * (e >> 2) + 4 * id.h + (e & 3);
-                        stage[rl * STG + id.wn * 128 + j * 32 + id.lr] = acc[p][j][e];
+                        for (int e = 0; e < 16; ++e) {
+                            const int rl = id.wm * 32 + 8 * (e >> 2) + 4 * id.h + (e & 3);
+                            stage[rl * STG + id.wn * 128 + j * 32 + id.lr] = acc[p][j][e];
+                        }
+                    __syncthreads();
+                    for (int i = e0 + id.tid; i < e1; i += NTHR) {
+                        const uint32_t en = a.ent[i];
+                        const int r = en & 255;
+                        if (((r >> 5) & 3) != p) continue;
+                        const int c = (en >> 8) & 255, k = (int)(en >> 16);
+                        const int rl = (r >> 7) * 32 + (r & 31);
+                        a.zk[(m0 + r) * a.K + k] = stage[rl * STG + c];
                     }
-                __syncthreads();
-                for (int i = e0 + id.tid; i < e1; i += NTHR) {
-                    const uint32_t en = a.ent[i];
-                    const int r = en & 255;
-                    if (((r >> 5) & 3) != p) continue;
-                    const int c = (en >> 8) & 255, k = (int)(en >> 16);
-                    const int rl = (r >> 7) * 32 + (r & 31);
-                    a.zk[(m0 + r) * a.K + k] = stage[rl * STG + c];
+                    __syncthreads();
                 }
-                __syncthreads();
+            }
+
+            // Online (max, sum) per row, in units of y = z*log2(e)/T, one 32-row MFMA block
+            // at a time. Each lane first folds its 4 columns. A reduce-scatter over the 32 lanes
+            // of its half (masks 16, 8, 4, 2) then leaves lane pair (2q', 2q'+1) with row
+            // position e = q' of the block, and a last exchange (mask 1) completes both copies.
+            bool colok[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) colok[j] = n0 + id.wn * 128 + j * 32 + id.lr < a.V;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float pm[16], ps[16];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    float y[4];
+                    float m = -INFINITY;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        y[j] = colok[j] ? acc[i][j][e] * a.c : -INFINITY;
+                        m = fmaxf(m, y[j]);
+                    }
+                    float sum = 0.f;
+                    if (m != -INFINITY) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) sum += exp2_fast(y[j] - m);
+                    }
+                    pm[e] = m;
+                    ps[e] = sum;
+                }
+                rs_step<8, 16>(pm, ps, id.lane);
+                rs_step<4, 8>(pm, ps, id.lane);
+                rs_step<2, 4>(pm, ps, id.lane);
+                rs_step<1, 2>(pm, ps, id.lane);
+                const float m2 = __shfl_xor(pm[0], 1), s2 = __shfl_xor(ps[0], 1);
+                ms_merge(pm[0], ps[0], m2, s2);
+                ms_merge(run_m[i], run_s[i], pm[0], ps[0]);
             }
         }
 
-        // Online (max, sum) per row over this tile, in units of y = z*log2(e)/T, one 32-row
-        // MFMA block at a time. Each lane first folds its 4 columns; then a reduce-scatter over
-        // the 32 lanes of its half (masks 16, 8, 4, 2) leaves lane pair (2q, 2q+1) with row
-        // position e = q of the block, and a last exchange (mask 1) completes both copies.
-        bool colok[4];
+        // Lane pair (2q', 2q'+1) of half h holds row position e = q' of each block i; the even lane writes.
+        if ((id.lr & 1) == 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) colok[j] = n0 + id.wn * 128 + j * 32 + id.lr < a.V;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float pm[16], ps[16];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                float y[4];
-                float m = -INFINITY;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    y[j] = colok[j] ? acc[i][j][e] * a.c : -INFINITY;
-                    m = fmaxf(m, y[j]);
-                }
-                float s = 0.f;
-                if (m != -INFINITY) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) s += exp2_fast(y[j] - m);
-                }
-                pm[e] = m;
-                ps[e] = s;
+            for (int i = 0; i < 4; ++i) {
+                const int row = id.wm * 128 + acc_row(i, id.lr >> 1, id.h);
+                const int64_t g = m0 + row;
+                if (g < a.N) a.part[(int64_t)(q * 2 + id.wn) * a.N + g] = make_float2(run_m[i], run_s[i]);
             }
-            rs_step<8, 16>(pm, ps, id.lane);
-            rs_step<4, 8>(pm, ps, id.lane);
-            rs_step<2, 4>(pm, ps, id.lane);
-            rs_step<1, 2>(pm, ps, id.lane);
-            const float m2 = __shfl_xor(pm[0], 1), s2 = __shfl_xor(ps[0], 1);
-            ms_merge(pm[0], ps[0], m2, s2);
-            ms_merge(run_m[i], run_s[i], pm[0], ps[0]);
-        }
-    }
-
-    // Lane pair (2q, 2q+1) of half h holds row position e = q of each block i; the even lane writes.
-    if ((id.lr & 1) == 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = id.lr >> 1;
-            const int row = id.wm * 128 + acc_row(i, e, id.h);
-            const int64_t g = m0 + row;
-            if (g < a.N) a.part[(int64_t)(vs * 2 + id.wn) * a.N + g] = make_float2(run_m[i], run_s[i]);
         }
     }
 }
@@ -652,7 +428,7 @@ struct GradArgs {
     int64_t c0, cc;
     const int32_t* off;
     const uint32_t* ent;
-    int n_vt;
+    int n_vt, n_rbc;
     void* G;
     int64_t ldg;
 };
@@ -662,7 +438,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
     __shared__ float lse2[kTileM];
     const WaveId id;
-    const int vt = blockIdx.x, rb = blockIdx.y;
+    // Logical tiles are vocab-tile major, so an XCD's band covers a few W tiles times every
+    // row block of the chunk.
+    const int64_t n_tiles = (int64_t)a.n_vt * a.n_rbc;
+    const int64_t t = xcd_tile(blockIdx.x, n_tiles);
+    if (t >= n_tiles) return;
+    const int vt = (int)(t / a.n_rbc), rb = (int)(t % a.n_rbc);
     const int64_t r0 = (int64_t)rb * kTileM;  // row offset within the chunk
     const int64_t n0 = (int64_t)vt * kTileN;
     {
@@ -672,7 +453,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
     const float gs = (a.grad ? a.grad[0] : 1.f) * a.gsc;
     const T* Hc = (const T*)a.H + a.c0 * a.d;
     f32x16 acc[4][4];
-    gemm_tile<T, true, true>(acc, L, id, Hc, a.d, r0, a.cc, a.d, (const T*)a.W, a.d, n0, a.V, a.d, 0, a.d);
+    gemm_tile_kk<T>(acc, L, id, Hc, a.d, r0, a.cc, a.d, (const T*)a.W, a.d, n0, a.V, a.d, 0, a.d);
 
     float* stage = (float*)L;
     const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
@@ -740,7 +521,7 @@ struct DhArgs {
     int64_t d, V;
     int64_t c0, cc;
     int64_t kper;
-    int n_split;
+    int n_split, n_nt, n_mt;
     float* part;
     void* dH;
 };
@@ -749,7 +530,14 @@ template <typename T>
 __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
     const WaveId id;
-    const int nt = blockIdx.x, mt = blockIdx.y, ks = blockIdx.z;
+    // Logical tiles are split major, then column tile, then row tile: an XCD's band shares one
+    // vocabulary slice of G_c and W.
+    const int64_t n_tiles = (int64_t)a.n_split * a.n_nt * a.n_mt;
+    const int64_t t = xcd_tile(blockIdx.x, n_tiles);
+    if (t >= n_tiles) return;
+    const int ks = (int)(t / ((int64_t)a.n_nt * a.n_mt));
+    const int rem = (int)(t % ((int64_t)a.n_nt * a.n_mt));
+    const int nt = rem / a.n_mt, mt = rem % a.n_mt;
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
     const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
     f32x16 acc[4][4];
@@ -806,6 +594,7 @@ struct DwArgs {
     int64_t d, V;
     int64_t c0, cc;
     int accumulate;
+    int n_mt, n_nt;
     float* dW;
 };
 
@@ -813,13 +602,31 @@ template <typename T>
 __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
     const WaveId id;
-    const int nt = blockIdx.x, mt = blockIdx.y;
+    // Logical tiles are vocab-row major: an XCD's band shares a few G_c column slabs and H_c.
+    const int64_t n_tiles = (int64_t)a.n_mt * a.n_nt;
+    const int64_t t = xcd_tile(blockIdx.x, n_tiles);
+    if (t >= n_tiles) return;
+    const int mt = (int)(t / a.n_nt), nt = (int)(t % a.n_nt);
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
     const T* Hc = (const T*)a.H + a.c0 * a.d;
     f32x16 acc[4][4];
     gemm_tile<T, false, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.cc, Hc, a.d, n0, a.d, a.cc, 0, a.cc);
+    bool colok[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) colok[j] = n0 + id.wn * 128 + j * 32 + id.lr < a.d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // read the 64 old values of this lane's rows in block i first, then add and store
+        float old[4][16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t row = m0 + id.wm * 128 + acc_row(i, e, id.h);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = n0 + id.wn * 128 + j * 32 + id.lr;
+                old[j][e] = (a.accumulate && row < a.V && colok[j]) ? a.dW[row * a.d + col] : 0.f;
+            }
+        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int64_t row = m0 + id.wm * 128 + acc_row(i, e, id.h);
@@ -827,11 +634,10 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int64_t col = n0 + id.wn * 128 + j * 32 + id.lr;
-                if (col >= a.d) continue;
-                float* p = a.dW + row * a.d + col;
-                *p = (a.accumulate ? *p : 0.f) + acc[i][j][e];
+                if (colok[j]) a.dW[row * a.d + col] = old[j][e] + acc[i][j][e];
             }
         }
+    }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -842,10 +648,13 @@ __global__ __launch_bounds__(256, 1) void k_dense_logits(const void* H, const vo
                                                          int64_t V, float* Z, int64_t ldz) {
     __shared__ u32x4 L[LDS_CHUNKS];
     const WaveId id;
-    const int vt = blockIdx.x, rb = blockIdx.y;
-    const int64_t m0 = (int64_t)rb * kTileM, n0 = (int64_t)vt * kTileN;
+    const int64_t n_rb = (N + kTileM - 1) / kTileM, n_vt = ldz / kTileN;
+    const int64_t t = xcd_tile(blockIdx.x, n_rb * n_vt);
+    if (t >= n_rb * n_vt) return;
+    const int64_t vt = t / n_rb, rb = t % n_rb;
+    const int64_t m0 = rb * kTileM, n0 = vt * kTileN;
     f32x16 acc[4][4];
-    gemm_tile<T, true, true>(acc, L, id, (const T*)H, d, m0, N, d, (const T*)W, d, n0, V, d, 0, d);
+    gemm_tile_kk<T>(acc, L, id, (const T*)H, d, m0, N, d, (const T*)W, d, n0, V, d, 0, d);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -946,14 +755,29 @@ __global__ __launch_bounds__(256) void k_dense_rows(float* __restrict__ Z, float
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// Vocab lanes of the forward: at least 8, and enough units to give every CU one.
 int fwd_vsplits(int64_t N, int64_t V) {
     const int64_t n_rb = (N + kTileM - 1) / kTileM;
     const int64_t n_vt = (V + kTileN - 1) / kTileN;
-    int64_t s = (256 + n_rb - 1) / n_rb;
-    if (s < 1) s = 1;
-    if (s > n_vt) s = n_vt;
-    return (int)s;
+    int64_t q = std::max<int64_t>(8, (256 + n_rb - 1) / n_rb);
+    if (q > n_vt) q = n_vt;
+    return (int)q;
 }
+
+// Compute units of the current device (cached per device id).
+static int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+static unsigned grid_xcd(int64_t n_tiles) { return (unsigned)(8 * ((n_tiles + 7) / 8)); }
 
 int dh_splits(int64_t cc, int64_t d, int64_t V) {
     const int64_t tiles = ((cc + kTileM - 1) / kTileM) * ((d + kTileN - 1) / kTileN);
@@ -1003,14 +827,17 @@ hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32
     a.off = plan_off;
     a.ent = plan_ent;
     a.n_vt = (int)((sh.V + kTileN - 1) / kTileN);
-    a.tps = (a.n_vt + n_vsplit - 1) / n_vsplit;
+    a.Q = n_vsplit;
+    a.n_unit = ((sh.N + kTileM - 1) / kTileM) * (int64_t)n_vsplit;
     a.part = part;
     a.zk = zk;
-    const dim3 grid((unsigned)((sh.N + kTileM - 1) / kTileM), (unsigned)n_vsplit);
+    // One workgroup per CU (the LDS use allows no more), a multiple of 8 for the XCD bands.
+    const int64_t cus = std::max(8, device_cus() / 8 * 8);
+    const unsigned grid = (unsigned)std::min<int64_t>(cus, 8 * ((a.n_unit + 7) / 8));
     if (sh.act == Dt::BF16)
-        hipLaunchKernelGGL(k_fwd<bf16_t>, grid, dim3(NTHR), 0, s, a);
+        hipLaunchKernelGGL(k_fwd<bf16_t>, dim3(grid), dim3(NTHR), 0, s, a);
     else
-        hipLaunchKernelGGL(k_fwd<float>, grid, dim3(NTHR), 0, s, a);
+        hipLaunchKernelGGL(k_fwd<float>, dim3(grid), dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1048,9 +875,10 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
     a.off = plan_off;
     a.ent = plan_ent;
     a.n_vt = (int)((sh.V + kTileN - 1) / kTileN);
+    a.n_rbc = (int)((cc + kTileM - 1) / kTileM);
     a.G = Gc;
     a.ldg = ldg;
-    const dim3 grid((unsigned)a.n_vt, (unsigned)((cc + kTileM - 1) / kTileM));
+    const dim3 grid(grid_xcd((int64_t)a.n_vt * a.n_rbc));
     if (sh.act == Dt::BF16)
         hipLaunchKernelGGL(k_bwd_grad<bf16_t>, grid, dim3(NTHR), 0, s, a);
     else
@@ -1073,8 +901,9 @@ hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W
     a.kper = round_up((a.Vp + n_split - 1) / n_split, 64);
     a.part = part;
     a.dH = dH;
-    const dim3 grid((unsigned)((sh.d + kTileN - 1) / kTileN), (unsigned)((cc + kTileM - 1) / kTileM),
-                    (unsigned)n_split);
+    a.n_nt = (int)((sh.d + kTileN - 1) / kTileN);
+    a.n_mt = (int)((cc + kTileM - 1) / kTileM);
+    const dim3 grid(grid_xcd((int64_t)n_split * a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16)
         hipLaunchKernelGGL(k_dh<bf16_t>, grid, dim3(NTHR), 0, s, a);
     else
@@ -1103,7 +932,9 @@ hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H
     a.cc = cc;
     a.accumulate = accumulate ? 1 : 0;
     a.dW = dW;
-    const dim3 grid((unsigned)((sh.d + kTileN - 1) / kTileN), (unsigned)(a.Vp / kTileM));
+    a.n_nt = (int)((sh.d + kTileN - 1) / kTileN);
+    a.n_mt = (int)(a.Vp / kTileM);
+    const dim3 grid(grid_xcd((int64_t)a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16)
         hipLaunchKernelGGL(k_dw<bf16_t>, grid, dim3(NTHR), 0, s, a);
     else
@@ -1112,7 +943,7 @@ hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H
 }
 
 hipError_t launch_dense_logits(const Shape& sh, const void* H, const void* W, float* Z, int64_t ldz, hipStream_t s) {
-    const dim3 grid((unsigned)(ldz / kTileN), (unsigned)((sh.N + kTileM - 1) / kTileM));
+    const dim3 grid(grid_xcd((ldz / kTileN) * ((sh.N + kTileM - 1) / kTileM)));
     if (sh.act == Dt::BF16)
         hipLaunchKernelGGL(k_dense_logits<bf16_t>, grid, dim3(NTHR), 0, s, H, W, sh.N, sh.d, sh.V, Z, ldz);
     else
