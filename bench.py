@@ -106,6 +106,9 @@ def main():
           f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
     prob = kd.make_problem(H, W, idx, t, p.T, chunk)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    inputs_mem = torch.cuda.memory_allocated(dev)
     ws = torch.empty(kd.fused_workspace_bytes(prob), dtype=torch.uint8, device=dev)
     dW = torch.empty(W.shape, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -126,16 +129,18 @@ def main():
         torch.cuda.synchronize()
         print(f"[bench] warmup {i + 1}/{args.warmup} done", file=sys.stderr, flush=True)
 
-    torch.cuda.reset_peak_memory_stats(dev)
-    base_mem = torch.cuda.memory_allocated(dev)
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    kd.timing_reset()
+    kd.timing_enable(True)  # the library brackets each of its launches with HIP events
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    peak_fused = torch.cuda.max_memory_allocated(dev)
+    kd.timing_enable(False)
+    kernels = kd.timing_read()
+    peak_fused = torch.cuda.max_memory_allocated(dev) - inputs_mem
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
     bwd_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
     ms_step = wall * 1e3 / args.steps
@@ -145,8 +150,18 @@ def main():
     N, d, V = p.N, p.d, p.V
     flops_step = 8.0 * N * d * V
     tokens_s = N / (ms_step / 1e3)
-    fwd_flops = 2.0 * N * d * V  # one launch of the forward tile kernel covers all N rows
-    achieved = fwd_flops / (fwd_ms / 1e3) / 1e12
+    # Each GEMM-shaped kernel does 2*N*d*V counted FLOPs per step: the forward in one launch,
+    # the recompute (bwd_grad), dH and dW in one launch per chunk.
+    gemm_kinds = ("fwd", "bwd_grad", "dh", "dw")
+    per_kernel = {}
+    for name, (n, ms) in kernels.items():
+        e = {"launches": n, "avg_ms": ms / n, "ms_per_step": ms / args.steps}
+        if name in gemm_kinds:
+            e["tflops"] = 2.0 * N * d * V * args.steps / (ms / 1e3) / 1e12
+        per_kernel[name] = e
+    dom = max((k for k in per_kernel if k in gemm_kinds), key=lambda k: per_kernel[k]["ms_per_step"])
+    dom_flops_launch = 2.0 * N * d * V * args.steps / per_kernel[dom]["launches"]
+    achieved = dom_flops_launch / (per_kernel[dom]["avg_ms"] / 1e3) / 1e12
 
     out = {
         "metric": METRIC,
@@ -170,9 +185,11 @@ def main():
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
         "counted_flops_per_step": flops_step,
-        "peak_hbm_fused_gb": (peak_fused - base_mem) / 1e9,
+        "peak_hbm_fused_gb": peak_fused / 1e9,
+        "kernels": per_kernel,
         "roofline": {
-            "kernel": "k_fwd (fused forward tile kernel; the forward call is this kernel plus <1% of small ones)",
+            "kernel": f"{dom} (largest share of the step; {per_kernel[dom]['launches'] // args.steps} "
+                      f"launch(es) per step, {dom_flops_launch:.4g} counted FLOP per launch)",
             "bound": "mfma",
             "achieved": achieved,
             "peak": PEAK_BF16_TFLOPS,
@@ -183,8 +200,9 @@ def main():
     }
 
     if not args.no_dense:
-        del ws
+        del ws, dW
         torch.cuda.empty_cache()
+        torch.cuda.synchronize()
         torch.cuda.reset_peak_memory_stats(dev)
         base = torch.cuda.memory_allocated(dev)
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]

@@ -180,6 +180,23 @@ kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const i
                       float* row_kl, void* dH, float* dW, void* ws, size_t ws_bytes,
                       kd_stream stream);
 
+/*
+ * Per-kernel timing (profiling; off by default). While enabled, every kernel the library
+ * launches, from any thread, is bracketed by two HIP events recorded on the launch's own
+ * stream. kd_timing_read waits for the recorded events. It then returns, for one kernel kind,
+ * the number of launches and their total duration in milliseconds accumulated since the last
+ * kd_timing_reset.
+ *   kd_timing_enable(on) returns the previous setting; kd_timing_kinds() is the number of
+ *   kinds; kd_timing_name(kind) is a static name ("fwd", "bwd_grad", "dh", "dw", ...).
+ * The events are owned and reused by the library; enabling timing adds two event records per
+ * launch and nothing else.
+ */
+int kd_timing_enable(int on);
+int kd_timing_kinds(void);
+const char* kd_timing_name(int kind);
+kd_status kd_timing_read(int kind, int64_t* launches, double* total_ms);
+void kd_timing_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,6 +30,9 @@ __all__ = [
     "fused_workspace_bytes",
     "dense_workspace_bytes",
     "make_problem",
+    "timing_enable",
+    "timing_read",
+    "timing_reset",
     "KdError",
     "KD_VALIDATE_IDX",
     "KD_ACCUMULATE_DW",
@@ -180,3 +183,25 @@ class FusedKL(torch.autograd.Function):
 
 def fused_kl(H, W, idx, tlog, T: float = 1.0, chunk: int = 2048, n_norm: float = 0.0):
     return FusedKL.apply(H, W, idx, tlog, T, chunk, n_norm)
+
+
+def timing_enable(on: bool = True) -> bool:
+    """Turn per-kernel HIP-event timing inside the library on or off; returns the old setting."""
+    return bool(_lib.lib().kd_timing_enable(1 if on else 0))
+
+
+def timing_reset() -> None:
+    _lib.lib().kd_timing_reset()
+
+
+def timing_read() -> dict:
+    """{kernel kind: (launches, total milliseconds)} accumulated since the last reset (waits for
+    the recorded events)."""
+    L = _lib.lib()
+    out = {}
+    for k in range(L.kd_timing_kinds()):
+        n, ms = ctypes.c_int64(0), ctypes.c_double(0.0)
+        _lib.check(L.kd_timing_read(k, ctypes.byref(n), ctypes.byref(ms)), "kd_timing_read")
+        if n.value:
+            out[L.kd_timing_name(k).decode()] = (int(n.value), float(ms.value))
+    return out

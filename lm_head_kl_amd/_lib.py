@@ -36,6 +36,11 @@ EXPORTS = (
     "kd_fused_kl_bwd",
     "kd_dense_workspace_bytes",
     "kd_dense_kl",
+    "kd_timing_enable",
+    "kd_timing_kinds",
+    "kd_timing_name",
+    "kd_timing_read",
+    "kd_timing_reset",
 )
 
 
@@ -88,6 +93,16 @@ def lib() -> ctypes.CDLL:
     L.kd_fused_kl_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kd_dense_kl.restype = ctypes.c_int
     L.kd_dense_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kd_timing_enable.restype = ctypes.c_int
+    L.kd_timing_enable.argtypes = [ctypes.c_int]
+    L.kd_timing_kinds.restype = ctypes.c_int
+    L.kd_timing_kinds.argtypes = []
+    L.kd_timing_name.restype = ctypes.c_char_p
+    L.kd_timing_name.argtypes = [ctypes.c_int]
+    L.kd_timing_read.restype = ctypes.c_int
+    L.kd_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double)]
+    L.kd_timing_reset.restype = None
+    L.kd_timing_reset.argtypes = []
     _lib = L
     return L
 

@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkdkl.so")
-SOURCES = ["kdkl_kernels.hip", "kdkl_api.cpp"]
+SOURCES = ["kdkl_kernels.hip", "kdkl_api.cpp", "kdkl_timing.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950",

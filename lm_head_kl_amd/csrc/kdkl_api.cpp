@@ -88,9 +88,12 @@ struct FusedWs {
     int32_t* cplan_off;
     uint32_t* cplan_ent;
     float* pt;
-    void* Gc;
+    void* Gc;   // [C][ldg]
+    void* GT;   // [Vp][ldgt]: G_c transposed
+    void* WT;   // [d][Vp]: W transposed, columns >= V zero
+    void* HT;   // [d][ldgt]: H_c transposed
     float* dh_part;
-    int64_t ldg;
+    int64_t ldg, ldgt;
     int n_vsplit, n_split;
     size_t fwd_bytes, bwd_bytes;
 };
@@ -116,7 +119,11 @@ FusedWs layout_fused(const kd_problem* p, void* ws) {
     w.cplan_off = (int32_t*)b.take(sizeof(int32_t) * n_rblocks(C) * (n_vt + 1));
     w.cplan_ent = (uint32_t*)b.take(sizeof(uint32_t) * n_rblocks(C) * kTileM * K);
     w.pt = (float*)b.take(sizeof(float) * C * K);
+    w.ldgt = round_up(C, 8);
     w.Gc = b.take(esize(p->act) * C * Vp);
+    w.GT = b.take(esize(p->act) * Vp * w.ldgt);
+    w.WT = b.take(esize(p->act) * d * Vp);
+    w.HT = b.take(esize(p->act) * d * w.ldgt);
     w.dh_part = w.n_split > 1 ? (float*)b.take(sizeof(float) * w.n_split * C * d) : nullptr;
     w.bwd_bytes = b.used;
     return w;
@@ -237,14 +244,22 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
         if (st != KD_OK) return st;
     }
     const int64_t C = chunk_rows(p);
+    const int64_t Vp = n_vtiles(p->V) * kTileN;
     const bool acc0 = (p->flags & KD_ACCUMULATE_DW) != 0;
+    // W^T once per call: dH = G_c W then reads both operands with the vocabulary contiguous.
+    KD_TRY(launch_transpose(sh.act, W, p->d, p->V, p->d, w.WT, Vp, Vp, s));
     for (int64_t c0 = 0; c0 < p->N; c0 += C) {
         const int64_t cc = std::min(C, p->N - c0);
+        const size_t es = esize(p->act);
         KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.cplan_off, w.cplan_ent, s));
         KD_TRY(launch_teacher_prob(tlog, sh.tlog, c0, c0 + cc, p->K, p->T, w.pt, s));
-        KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt, grad_loss, c0, cc, w.cplan_off, w.cplan_ent, w.Gc, w.ldg, s));
-        KD_TRY(launch_dh(sh, w.Gc, w.ldg, W, c0, cc, w.n_split, w.dh_part, dH, s));
-        KD_TRY(launch_dw(sh, w.Gc, w.ldg, H, c0, cc, acc0 || c0 > 0, dW, s));
+        // H_c^T, so that dW = G_c^T H_c reads both operands with the chunk rows contiguous
+        KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d, w.HT, w.ldgt,
+                                round_up(cc, 8), s));
+        KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt, grad_loss, c0, cc, w.cplan_off, w.cplan_ent, w.Gc, w.ldg,
+                               w.GT, w.ldgt, s));
+        KD_TRY(launch_dh(sh, w.Gc, w.ldg, W, w.WT, Vp, c0, cc, w.n_split, w.dh_part, dH, s));
+        KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, cc, acc0 || c0 > 0, dW, s));
     }
     return KD_OK;
 }
@@ -273,7 +288,7 @@ kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const i
     // G: bf16 over the logits grid (row stride 2*Vp elements), or fp32 in the teacher grid.
     const void* G = sh.act == Dt::BF16 ? (const void*)w.Z : (const void*)w.P;
     const int64_t ldg = sh.act == Dt::BF16 ? 2 * w.ldz : w.ldz;
-    KD_TRY(launch_dh(sh, G, ldg, W, 0, p->N, w.n_split, w.dh_part, dH, s));
+    KD_TRY(launch_dh(sh, G, ldg, W, nullptr, 0, 0, p->N, w.n_split, w.dh_part, dH, s));
     KD_TRY(launch_dw(sh, G, ldg, H, 0, p->N, (p->flags & KD_ACCUMULATE_DW) != 0, dW, s));
     return KD_OK;
 }

@@ -17,6 +17,28 @@ constexpr int kMaxVTiles = 16384;  // plan kernel keeps one LDS counter per voca
 
 enum class Dt : int { F32 = 0, BF16 = 1 };
 
+// Kernel kinds for the optional per-launch timing (kd_timing_* in kdkl.h).
+enum Kind : int {
+    kKindPlan = 0,
+    kKindTeacherProb,
+    kKindValidate,
+    kKindFwd,
+    kKindCombine,
+    kKindLossFinal,
+    kKindBwdGrad,
+    kKindTranspose,
+    kKindDh,
+    kKindDhReduce,
+    kKindDw,
+    kKindDenseLogits,
+    kKindDenseRows,
+    kKindSumRows,
+    kNumKinds
+};
+// Bracket one launch on stream s with timing events (no-ops unless timing is enabled).
+void timing_begin(int kind, hipStream_t s);
+void timing_end(int kind, hipStream_t s);
+
 struct Shape {
     int64_t N, d, V, K;
     float T;
@@ -57,20 +79,30 @@ hipError_t launch_loss_final(const Shape& sh, const double* blk_sum, int n_blk, 
                              hipStream_t s);
 
 // Backward, one chunk of rows [c0, c0 + cc):
-//   G_c [cc, ldg] (act dtype, columns >= V are zero) = g*T/n_norm*(softmax(z/T) - P_t)
+//   G_c [cc, ldg] (act dtype, columns >= V zero) = g*T/n_norm*(softmax(z/T) - P_t), and, if GT
+//   is not null, its transpose G_c^T [Vp, ldgt] with columns [cc, round_up(cc, 8)) zero.
 hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const float* lse,
                            const float* pt, const float* grad_loss, int64_t c0, int64_t cc,
                            const int32_t* plan_off, const uint32_t* plan_ent, void* Gc,
-                           int64_t ldg, hipStream_t s);
+                           int64_t ldg, void* GT, int64_t ldgt, hipStream_t s);
 
-// dH rows [c0, c0+cc) = G_c W; split over the vocabulary into n_split fp32 partials when
-// n_split > 1 (part: [n_split][cc][d]), then reduced in a fixed order.
-hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, int64_t c0,
-                     int64_t cc, int n_split, float* part, void* dH, hipStream_t s);
+// dst[c][r] = src[r][c] (r < rows), zero for rows <= r < rows_pad; cols, rows_pad multiples of 8.
+hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst,
+                            int64_t ldd, int64_t rows_pad, hipStream_t s);
 
-// dW (+)= G_c^T H[c0:c0+cc]
+// dH rows [c0, c0+cc) = G_c W; B is W^T [d, ldwt] (K contiguous) when WT is not null, else W.
+// Split over the vocabulary into n_split fp32 partials when n_split > 1 (part: [n_split][cc][d]),
+// then reduced in a fixed order.
+hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, const void* WT,
+                     int64_t ldwt, int64_t c0, int64_t cc, int n_split, float* part, void* dH,
+                     hipStream_t s);
+
+// dW (+)= G_c^T H[c0:c0+cc] from G_c [cc][ldg] and H (both M/N contiguous).
 hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H, int64_t c0,
                      int64_t cc, bool accumulate, float* dW, hipStream_t s);
+// dW (+)= G_c^T H_c from G_c^T [Vp][ldgt] and H_c^T [d][ldht] (both K contiguous).
+hipError_t launch_dw_t(const Shape& sh, const void* GT, int64_t ldgt, const void* HT, int64_t ldht,
+                       int64_t cc, bool accumulate, float* dW, hipStream_t s);
 
 // Dense path pieces.
 hipError_t launch_dense_logits(const Shape& sh, const void* H, const void* W, float* Z, int64_t ldz,

@@ -45,6 +45,13 @@
 
 namespace kdkl {
 
+#define KD_LAUNCH(kind, stream, ...)         \
+    do {                                     \
+        timing_begin(kind, stream);          \
+        hipLaunchKernelGGL(__VA_ARGS__);     \
+        timing_end(kind, stream);            \
+    } while (0)
+
 constexpr int STG = kTileN + 4;  // staging row stride in floats (16-byte aligned)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kLn2 = 0.69314718055994530942;
@@ -429,8 +436,10 @@ struct GradArgs {
     const int32_t* off;
     const uint32_t* ent;
     int n_vt, n_rbc;
-    void* G;
+    void* G;     // [cc][ldg] row-major
     int64_t ldg;
+    void* GT;    // [Vp][ldgt]: G transposed, columns [cc, ccp) zero; nullptr to skip
+    int64_t ldgt, ccp;
 };
 
 template <typename T>
@@ -468,9 +477,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
             const int rw = id.wm * 128 + acc_row(p, e, id.h);
             const float l2 = lse2[rw];
             const int rl = id.wm * 32 + 8 * (e >> 2) + 4 * id.h + (e & 3);
+            const bool rowok = r0 + rw < a.cc;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float v = colok[j] ? gs * exp2_fast(acc[p][j][e] * a.c - l2) : 0.f;
+                const float v = (colok[j] && rowok) ? gs * exp2_fast(acc[p][j][e] * a.c - l2) : 0.f;
                 stage[rl * STG + id.wn * 128 + j * 32 + id.lr] = v;
             }
         }
@@ -507,7 +517,58 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
                 }
             }
         }
+        if (a.GT) {
+            // Transposed copy: 256 vocabulary rows x 8 groups of 8 chunk rows. Consecutive lanes
+            // take consecutive vocabulary entries, so the staging reads are conflict free.
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int it = id.tid + NTHR * t;
+                const int v = it & 255, rg = it >> 8;
+                const int rl0 = (rg >> 2) * 32 + (rg & 3) * 8;
+                const int64_t row = r0 + (rg >> 2) * 128 + p * 32 + (rg & 3) * 8;
+                if (row < a.ccp) {
+                    float x[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) x[u] = stage[(rl0 + u) * STG + v];
+                    if constexpr (sizeof(T) == 2) {
+                        u32x4 o;
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) o[u] = f2bf(x[2 * u]) | (f2bf(x[2 * u + 1]) << 16);
+                        *(u32x4*)((bf16_t*)a.GT + (n0 + v) * a.ldgt + row) = o;
+                    } else {
+                        float* gp = (float*)a.GT + (n0 + v) * a.ldgt + row;
+                        *(f32x4*)gp = f32x4{x[0], x[1], x[2], x[3]};
+                        *(f32x4*)(gp + 4) = f32x4{x[4], x[5], x[6], x[7]};
+                    }
+                }
+            }
+        }
         __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------------------------------
+// Transpose: dst[c*ldd + r] = src[r*lds + c] for r < rows, zero for rows <= r < rows_pad,
+// c < cols. 64 x 64 tiles through LDS. cols and rows_pad are multiples of 8.
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, int64_t lds, int64_t rows,
+                                                   int64_t cols, T* __restrict__ dst, int64_t ldd, int64_t rows_pad) {
+    __shared__ T tile[64][65];
+    const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = ty + 4 * i;
+        const int64_t gr = r0 + r, gc = c0 + tx;
+        tile[r][tx] = (gr < rows && gc < cols) ? src[gr * lds + gc] : (T)0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int c = ty + 4 * i;
+        const int64_t gc = c0 + c, gr = r0 + tx;
+        if (gc < cols && gr < rows_pad) dst[gc * ldd + gr] = tile[tx][c];
     }
 }
 
@@ -517,7 +578,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
 struct DhArgs {
     const void* G;
     int64_t ldg, Vp;
-    const void* W;
+    const void* W;   // W [V][d], or W^T [d][ldwt] zero-padded to Vp columns
+    int64_t ldwt;
     int64_t d, V;
     int64_t c0, cc;
     int64_t kper;
@@ -526,7 +588,7 @@ struct DhArgs {
     void* dH;
 };
 
-template <typename T>
+template <typename T, bool WT>
 __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
     const WaveId id;
@@ -541,8 +603,12 @@ __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
     const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
     f32x16 acc[4][4];
-    gemm_tile<T, true, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
-                              min(a.V, k_end), k_begin, k_end);
+    if constexpr (WT)
+        gemm_tile_kk<T>(acc, L, id, (const T*)a.G, a.ldg, m0, a.cc, k_end, (const T*)a.W, a.ldwt, n0, a.d, k_end,
+                        k_begin, k_end);
+    else
+        gemm_tile<T, true, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
+                                  min(a.V, k_end), k_begin, k_end);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -588,17 +654,18 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
 // dW (+)= G_c^T H_c (A = G_c^T: vocabulary contiguous; B = H_c: d contiguous).
 
 struct DwArgs {
-    const void* G;
+    const void* G;   // G_c [cc][ldg], or G_c^T [Vp][ldg] (K contiguous)
     int64_t ldg, Vp;
-    const void* H;
+    const void* H;   // H (rows from c0), or H_c^T [d][ldh] (K contiguous)
+    int64_t ldh;
     int64_t d, V;
-    int64_t c0, cc;
+    int64_t c0, cc, ccp;
     int accumulate;
     int n_mt, n_nt;
     float* dW;
 };
 
-template <typename T>
+template <typename T, bool KK>
 __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
     const WaveId id;
@@ -608,9 +675,13 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
     if (t >= n_tiles) return;
     const int mt = (int)(t / a.n_nt), nt = (int)(t % a.n_nt);
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
-    const T* Hc = (const T*)a.H + a.c0 * a.d;
     f32x16 acc[4][4];
-    gemm_tile<T, false, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.cc, Hc, a.d, n0, a.d, a.cc, 0, a.cc);
+    if constexpr (KK)
+        gemm_tile_kk<T>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.ccp, (const T*)a.H, a.ldh, n0, a.d, a.ccp, 0,
+                        a.ccp);
+    else
+        gemm_tile<T, false, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.cc, (const T*)a.H + a.c0 * a.d,
+                                   a.d, n0, a.d, a.cc, 0, a.cc);
     bool colok[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) colok[j] = n0 + id.wn * 128 + j * 32 + id.lr < a.d;
@@ -796,21 +867,21 @@ hipError_t launch_plan(const int32_t* idx, int64_t row0, int64_t row1, int64_t K
                        uint32_t* ent, hipStream_t s) {
     const int n_rb = (int)((row1 - row0 + kTileM - 1) / kTileM);
     const int n_vt = (int)((V + kTileN - 1) / kTileN);
-    hipLaunchKernelGGL(k_plan, dim3(n_rb), dim3(NTHR), 0, s, idx, row0, row1, (int)K, V, n_vt, off, ent);
+    KD_LAUNCH(kKindPlan, s, k_plan, dim3(n_rb), dim3(NTHR), 0, s, idx, row0, row1, (int)K, V, n_vt, off, ent);
     return hipGetLastError();
 }
 
 hipError_t launch_teacher_prob(const void* tlog, Dt tdt, int64_t row0, int64_t row1, int64_t K, float T,
                                float* pt, hipStream_t s) {
     const int64_t rows = row1 - row0;
-    hipLaunchKernelGGL(k_teacher_prob, dim3((unsigned)((rows + 3) / 4)), dim3(NTHR), 0, s, tlog, tdt, row0, row1,
+    KD_LAUNCH(kKindTeacherProb, s, k_teacher_prob, dim3((unsigned)((rows + 3) / 4)), dim3(NTHR), 0, s, tlog, tdt, row0, row1,
                        (int)K, T, pt);
     return hipGetLastError();
 }
 
 hipError_t launch_validate(const int32_t* idx, int64_t N, int64_t K, int64_t V, uint32_t* status, hipStream_t s) {
-    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(64), 0, s, status, 1);
-    hipLaunchKernelGGL(k_validate, dim3((unsigned)((N + 3) / 4)), dim3(NTHR), 0, s, idx, N, (int)K, V, status);
+    KD_LAUNCH(kKindValidate, s, k_zero_u32, dim3(1), dim3(64), 0, s, status, 1);
+    KD_LAUNCH(kKindValidate, s, k_validate, dim3((unsigned)((N + 3) / 4)), dim3(NTHR), 0, s, idx, N, (int)K, V, status);
     return hipGetLastError();
 }
 
@@ -835,16 +906,16 @@ hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32
     const int64_t cus = std::max(8, device_cus() / 8 * 8);
     const unsigned grid = (unsigned)std::min<int64_t>(cus, 8 * ((a.n_unit + 7) / 8));
     if (sh.act == Dt::BF16)
-        hipLaunchKernelGGL(k_fwd<bf16_t>, dim3(grid), dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindFwd, s, k_fwd<bf16_t>, dim3(grid), dim3(NTHR), 0, s, a);
     else
-        hipLaunchKernelGGL(k_fwd<float>, dim3(grid), dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindFwd, s, k_fwd<float>, dim3(grid), dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_combine(const Shape& sh, const float2* part, int n_part, const float* zk, const void* tlog,
                           float* lse, float* row_kl, double* blk_sum, int* n_blk_out, hipStream_t s) {
     const int nb = combine_blocks(sh.N);
-    hipLaunchKernelGGL(k_combine, dim3(nb), dim3(NTHR), 0, s, part, n_part, sh.N, (int)sh.K, sh.T, zk, tlog, sh.tlog,
+    KD_LAUNCH(kKindCombine, s, k_combine, dim3(nb), dim3(NTHR), 0, s, part, n_part, sh.N, (int)sh.K, sh.T, zk, tlog, sh.tlog,
                        lse, row_kl, blk_sum);
     if (n_blk_out) *n_blk_out = nb;
     return hipGetLastError();
@@ -852,13 +923,13 @@ hipError_t launch_combine(const Shape& sh, const float2* part, int n_part, const
 
 hipError_t launch_loss_final(const Shape& sh, const double* blk_sum, int n_blk, float* loss, hipStream_t s) {
     const double scale = (double)sh.T * (double)sh.T / (double)sh.n_norm;
-    hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(NTHR), 0, s, blk_sum, n_blk, scale, loss);
+    KD_LAUNCH(kKindLossFinal, s, k_loss_final, dim3(1), dim3(NTHR), 0, s, blk_sum, n_blk, scale, loss);
     return hipGetLastError();
 }
 
 hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const float* lse, const float* pt,
                            const float* grad_loss, int64_t c0, int64_t cc, const int32_t* plan_off,
-                           const uint32_t* plan_ent, void* Gc, int64_t ldg, hipStream_t s) {
+                           const uint32_t* plan_ent, void* Gc, int64_t ldg, void* GT, int64_t ldgt, hipStream_t s) {
     GradArgs a;
     a.H = H;
     a.W = W;
@@ -878,21 +949,37 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
     a.n_rbc = (int)((cc + kTileM - 1) / kTileM);
     a.G = Gc;
     a.ldg = ldg;
+    a.GT = GT;
+    a.ldgt = ldgt;
+    a.ccp = round_up(cc, 8);
     const dim3 grid(grid_xcd((int64_t)a.n_vt * a.n_rbc));
     if (sh.act == Dt::BF16)
-        hipLaunchKernelGGL(k_bwd_grad<bf16_t>, grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindBwdGrad, s, k_bwd_grad<bf16_t>, grid, dim3(NTHR), 0, s, a);
     else
-        hipLaunchKernelGGL(k_bwd_grad<float>, grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindBwdGrad, s, k_bwd_grad<float>, grid, dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
-hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, int64_t c0, int64_t cc,
-                     int n_split, float* part, void* dH, hipStream_t s) {
+hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst, int64_t ldd,
+                            int64_t rows_pad, hipStream_t s) {
+    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows_pad + 63) / 64));
+    if (dt == Dt::BF16)
+        KD_LAUNCH(kKindTranspose, s, k_transpose<bf16_t>, grid, dim3(NTHR), 0, s, (const bf16_t*)src, lds, rows, cols,
+                           (bf16_t*)dst, ldd, rows_pad);
+    else
+        KD_LAUNCH(kKindTranspose, s, k_transpose<float>, grid, dim3(NTHR), 0, s, (const float*)src, lds, rows, cols,
+                           (float*)dst, ldd, rows_pad);
+    return hipGetLastError();
+}
+
+hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, const void* WT, int64_t ldwt,
+                     int64_t c0, int64_t cc, int n_split, float* part, void* dH, hipStream_t s) {
     DhArgs a;
     a.G = Gc;
     a.ldg = ldg;
     a.Vp = round_up(sh.V, kTileN);
-    a.W = W;
+    a.W = WT ? WT : W;
+    a.ldwt = ldwt;
     a.d = sh.d;
     a.V = sh.V;
     a.c0 = c0;
@@ -904,18 +991,25 @@ hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W
     a.n_nt = (int)((sh.d + kTileN - 1) / kTileN);
     a.n_mt = (int)((cc + kTileM - 1) / kTileM);
     const dim3 grid(grid_xcd((int64_t)n_split * a.n_nt * a.n_mt));
-    if (sh.act == Dt::BF16)
-        hipLaunchKernelGGL(k_dh<bf16_t>, grid, dim3(NTHR), 0, s, a);
-    else
-        hipLaunchKernelGGL(k_dh<float>, grid, dim3(NTHR), 0, s, a);
+    if (sh.act == Dt::BF16) {
+        if (WT)
+            KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, true>), grid, dim3(NTHR), 0, s, a);
+        else
+            KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, false>), grid, dim3(NTHR), 0, s, a);
+    } else {
+        if (WT)
+            KD_LAUNCH(kKindDh, s, (k_dh<float, true>), grid, dim3(NTHR), 0, s, a);
+        else
+            KD_LAUNCH(kKindDh, s, (k_dh<float, false>), grid, dim3(NTHR), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split <= 1) return e;
     const int64_t n4 = cc * sh.d / 4;
     const unsigned blocks = (unsigned)std::min<int64_t>((n4 + NTHR - 1) / NTHR, 4096);
     if (sh.act == Dt::BF16)
-        hipLaunchKernelGGL(k_dh_reduce<bf16_t>, dim3(blocks), dim3(NTHR), 0, s, part, n_split, cc, sh.d, c0, dH);
+        KD_LAUNCH(kKindDhReduce, s, k_dh_reduce<bf16_t>, dim3(blocks), dim3(NTHR), 0, s, part, n_split, cc, sh.d, c0, dH);
     else
-        hipLaunchKernelGGL(k_dh_reduce<float>, dim3(blocks), dim3(NTHR), 0, s, part, n_split, cc, sh.d, c0, dH);
+        KD_LAUNCH(kKindDhReduce, s, k_dh_reduce<float>, dim3(blocks), dim3(NTHR), 0, s, part, n_split, cc, sh.d, c0, dH);
     return hipGetLastError();
 }
 
@@ -926,28 +1020,55 @@ hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H
     a.ldg = ldg;
     a.Vp = round_up(sh.V, kTileN);
     a.H = H;
+    a.ldh = sh.d;
     a.d = sh.d;
     a.V = sh.V;
     a.c0 = c0;
     a.cc = cc;
+    a.ccp = cc;
     a.accumulate = accumulate ? 1 : 0;
     a.dW = dW;
     a.n_nt = (int)((sh.d + kTileN - 1) / kTileN);
     a.n_mt = (int)(a.Vp / kTileM);
     const dim3 grid(grid_xcd((int64_t)a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16)
-        hipLaunchKernelGGL(k_dw<bf16_t>, grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindDw, s, (k_dw<bf16_t, false>), grid, dim3(NTHR), 0, s, a);
     else
-        hipLaunchKernelGGL(k_dw<float>, grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindDw, s, (k_dw<float, false>), grid, dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dw_t(const Shape& sh, const void* GT, int64_t ldgt, const void* HT, int64_t ldht, int64_t cc,
+                       bool accumulate, float* dW, hipStream_t s) {
+    DwArgs a;
+    a.G = GT;
+    a.ldg = ldgt;
+    a.Vp = round_up(sh.V, kTileN);
+    a.H = HT;
+    a.ldh = ldht;
+    a.d = sh.d;
+    a.V = sh.V;
+    a.c0 = 0;
+    a.cc = cc;
+    a.ccp = round_up(cc, 8);
+    a.accumulate = accumulate ? 1 : 0;
+    a.dW = dW;
+    a.n_nt = (int)((sh.d + kTileN - 1) / kTileN);
+    a.n_mt = (int)(a.Vp / kTileM);
+    const dim3 grid(grid_xcd((int64_t)a.n_nt * a.n_mt));
+    if (sh.act == Dt::BF16)
+        KD_LAUNCH(kKindDw, s, (k_dw<bf16_t, true>), grid, dim3(NTHR), 0, s, a);
+    else
+        KD_LAUNCH(kKindDw, s, (k_dw<float, true>), grid, dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_dense_logits(const Shape& sh, const void* H, const void* W, float* Z, int64_t ldz, hipStream_t s) {
     const dim3 grid(grid_xcd((ldz / kTileN) * ((sh.N + kTileM - 1) / kTileM)));
     if (sh.act == Dt::BF16)
-        hipLaunchKernelGGL(k_dense_logits<bf16_t>, grid, dim3(NTHR), 0, s, H, W, sh.N, sh.d, sh.V, Z, ldz);
+        KD_LAUNCH(kKindDenseLogits, s, k_dense_logits<bf16_t>, grid, dim3(NTHR), 0, s, H, W, sh.N, sh.d, sh.V, Z, ldz);
     else
-        hipLaunchKernelGGL(k_dense_logits<float>, grid, dim3(NTHR), 0, s, H, W, sh.N, sh.d, sh.V, Z, ldz);
+        KD_LAUNCH(kKindDenseLogits, s, k_dense_logits<float>, grid, dim3(NTHR), 0, s, H, W, sh.N, sh.d, sh.V, Z, ldz);
     return hipGetLastError();
 }
 
@@ -956,7 +1077,7 @@ hipError_t launch_dense_rows(const Shape& sh, float* Z, float* P, int64_t ldz, c
                              int64_t ldg, hipStream_t s) {
     (void)G;
     (void)ldg;
-    hipLaunchKernelGGL(k_dense_rows, dim3((unsigned)sh.N), dim3(NTHR), 0, s, Z, P, ldz, sh.V, (int)sh.K, sh.T,
+    KD_LAUNCH(kKindDenseRows, s, k_dense_rows, dim3((unsigned)sh.N), dim3(NTHR), 0, s, Z, P, ldz, sh.V, (int)sh.K, sh.T,
                        sh.T / sh.n_norm, idx, tlog, sh.tlog, grad_loss, lse, row_kl, row_sum,
                        sh.act == Dt::BF16 ? 1 : 0);
     return hipGetLastError();
@@ -964,7 +1085,7 @@ hipError_t launch_dense_rows(const Shape& sh, float* Z, float* P, int64_t ldz, c
 
 hipError_t launch_sum_rows(const Shape& sh, const double* row_sum, double* blk_sum, int* n_blk, hipStream_t s) {
     const int nb = (int)((sh.N + 1023) / 1024);
-    hipLaunchKernelGGL(k_sum_rows, dim3(nb), dim3(NTHR), 0, s, row_sum, sh.N, blk_sum);
+    KD_LAUNCH(kKindSumRows, s, k_sum_rows, dim3(nb), dim3(NTHR), 0, s, row_sum, sh.N, blk_sum);
     if (n_blk) *n_blk = nb;
     return hipGetLastError();
 }
