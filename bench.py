@@ -8,7 +8,8 @@ V = 201,088, K = 100 cached teacher entries per row, chunk 2048, T = 1. Inputs a
 synthetic bf16, resident in HBM before timing starts.
 
 Prints one JSON line. Along with the throughput it carries:
-  - roofline: for the fused forward kernel, measured with HIP events on the library's stream;
+  - roofline: for the kernel with the largest share of the step, measured with the library's
+    per-launch HIP events on its stream, and its HBM bytes from the committed counter summary;
   - cpu_baseline: the fp64 oracle timed on the host on a bounded slice of rows;
   - peak device memory: fused, and the dense path's at the same shape.
 
@@ -41,7 +42,36 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 1 GiB device-to-device once (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+def kernel_sources_sha() -> str:
+    """Hash of the kernel sources; a traffic figure measured on other sources is stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lm_head_kl_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary for this workload,
+    or None when there is none or it was taken on other kernel sources. Lines look like
+    'traffic <kernel> fetch_bytes <F> write_bytes <W> sources <sha>'."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{config}.txt")
+    if not os.path.exists(path):
+        return None
+    sha = kernel_sources_sha()
+    for line in open(path):
+        f = line.split()
+        if len(f) == 8 and f[0] == "traffic" and f[1] == kernel and f[7] == sha:
+            return float(f[3]) + float(f[5])
+    return None
 
 
 def cpu_baseline(p, n_rows):
@@ -89,6 +119,14 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_probe:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 1 << 30}))
+        return
     t_gen = time.perf_counter()
     p = datagen.make(args.config, N=args.rows or None)
     chunk = args.chunk or p.chunk
@@ -195,7 +233,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(args.config, dom),
         },
     }
 
