@@ -26,6 +26,7 @@ using namespace kdkl;
 namespace {
 
 constexpr int64_t kAlign = 256;
+constexpr int64_t kDwGroup = 2;  // chunks per dW pass
 
 struct Carve {
     uintptr_t base;
@@ -119,7 +120,9 @@ FusedWs layout_fused(const kd_problem* p, void* ws) {
     w.cplan_off = (int32_t*)b.take(sizeof(int32_t) * n_rblocks(C) * (n_vt + 1));
     w.cplan_ent = (uint32_t*)b.take(sizeof(uint32_t) * n_rblocks(C) * kTileM * K);
     w.pt = (float*)b.take(sizeof(float) * C * K);
-    w.ldgt = round_up(C, 8);
+    // G_c^T and H_c^T hold kDwGroup chunks side by side (slot s at columns s*round_up(C, 8)), so
+    // one dW pass reduces over kDwGroup chunks and dW is read and written once per group.
+    w.ldgt = kDwGroup * round_up(C, 8);
     w.Gc = b.take(esize(p->act) * C * Vp);
     w.GT = b.take(esize(p->act) * Vp * w.ldgt);
     w.WT = b.take(esize(p->act) * d * Vp);
@@ -248,18 +251,26 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
     const bool acc0 = (p->flags & KD_ACCUMULATE_DW) != 0;
     // W^T once per call: dH = G_c W then reads both operands with the vocabulary contiguous.
     KD_TRY(launch_transpose(sh.act, W, p->d, p->V, p->d, w.WT, Vp, Vp, s));
-    for (int64_t c0 = 0; c0 < p->N; c0 += C) {
+    const int64_t C8 = round_up(C, 8);
+    const size_t es = esize(p->act);
+    int64_t ci = 0;
+    bool dw_written = false;
+    for (int64_t c0 = 0; c0 < p->N; c0 += C, ++ci) {
         const int64_t cc = std::min(C, p->N - c0);
-        const size_t es = esize(p->act);
+        const int64_t slot = ci % kDwGroup;
         KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.cplan_off, w.cplan_ent, s));
         KD_TRY(launch_teacher_prob(tlog, sh.tlog, c0, c0 + cc, p->K, p->T, w.pt, s));
-        // H_c^T, so that dW = G_c^T H_c reads both operands with the chunk rows contiguous
-        KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d, w.HT, w.ldgt,
-                                round_up(cc, 8), s));
+        // H_c^T into its slot, so that dW = G^T H reads both operands with the rows contiguous
+        KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
+                                (char*)w.HT + slot * C8 * es, w.ldgt, round_up(cc, 8), s));
         KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt, grad_loss, c0, cc, w.cplan_off, w.cplan_ent, w.Gc, w.ldg,
-                               w.GT, w.ldgt, s));
+                               (char*)w.GT + slot * C8 * es, w.ldgt, s));
         KD_TRY(launch_dh(sh, w.Gc, w.ldg, W, w.WT, Vp, c0, cc, w.n_split, w.dh_part, dH, s));
-        KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, cc, acc0 || c0 > 0, dW, s));
+        // One dW pass per group of chunks (K = the group's rows; the slots are zero-padded to 8)
+        if (slot == kDwGroup - 1 || c0 + cc >= p->N) {
+            KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * C8 + cc, acc0 || dw_written, dW, s));
+            dw_written = true;
+        }
     }
     return KD_OK;
 }

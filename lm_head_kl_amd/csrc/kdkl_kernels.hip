@@ -255,12 +255,15 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
 
         for (int vt = q; vt < a.n_vt; vt += a.Q) {
             const int64_t n0 = (int64_t)vt * kTileN;
+            // The tile's first 256 cached-id entries go to registers (one per thread) before the
+            // mainloop, so their load latency hides behind it.
+            const int e0 = off[vt], e1 = off[vt + 1];
+            const uint32_t my_en = e0 + id.tid < e1 ? a.ent[e0 + id.tid] : 0xffffffffu;
             f32x16 acc[4][4];
             gemm_tile_kk<T>(acc, L, id, (const T*)a.H, a.d, m0, a.N, a.d, (const T*)a.W, a.d, n0,
                                      a.V, a.d, 0, a.d);
 
             // Gather z at the cached ids of this (row block, vocab tile), one 64-row slab at a time.
-            const int e0 = off[vt], e1 = off[vt + 1];
             if (e1 > e0) {
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
@@ -272,7 +275,11 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
                             stage[rl * STG + id.wn * 128 + j * 32 + id.lr] = acc[p][j][e];
                         }
                     __syncthreads();
-                    for (int i = e0 + id.tid; i < e1; i += NTHR) {
+                    if (my_en != 0xffffffffu && ((my_en >> 5) & 3) == (uint32_t)p) {
+                        const int r = my_en & 255, c = (my_en >> 8) & 255, k = (int)(my_en >> 16);
+                        a.zk[(m0 + r) * a.K + k] = stage[((r >> 7) * 32 + (r & 31)) * STG + c];
+                    }
+                    for (int i = e0 + NTHR + id.tid; i < e1; i += NTHR) {
                         const uint32_t en = a.ent[i];
                         const int r = en & 255;
                         if (((r >> 5) & 3) != p) continue;
@@ -460,13 +467,21 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
         lse2[id.tid] = r < a.cc ? a.lse[a.c0 + r] * kLog2e : 0.f;
     }
     const float gs = (a.grad ? a.grad[0] : 1.f) * a.gsc;
+    // This tile's cached-id entries: the first 256 are loaded into registers (one per thread)
+    // before the mainloop, so their latency hides behind it; more only occur on Zipf-hot tiles.
+    const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
+    const int e0 = off[vt], e1 = off[vt + 1];
+    uint32_t my_en = 0xffffffffu;
+    float my_pt = 0.f;
+    if (e0 + id.tid < e1) {
+        my_en = a.ent[e0 + id.tid];
+        my_pt = a.pt[(r0 + (my_en & 255)) * a.K + (my_en >> 16)];
+    }
     const T* Hc = (const T*)a.H + a.c0 * a.d;
     f32x16 acc[4][4];
     gemm_tile_kk<T>(acc, L, id, Hc, a.d, r0, a.cc, a.d, (const T*)a.W, a.d, n0, a.V, a.d, 0, a.d);
 
     float* stage = (float*)L;
-    const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
-    const int e0 = off[vt], e1 = off[vt + 1];
     bool colok[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) colok[j] = n0 + id.wn * 128 + j * 32 + id.lr < a.V;
@@ -485,7 +500,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
             }
         }
         __syncthreads();
-        for (int i = e0 + id.tid; i < e1; i += NTHR) {
+        if (my_en != 0xffffffffu && ((my_en >> 5) & 3) == (uint32_t)p) {
+            const int r = my_en & 255, c = (my_en >> 8) & 255;
+            stage[((r >> 7) * 32 + (r & 31)) * STG + c] -= gs * my_pt;
+        }
+        for (int i = e0 + NTHR + id.tid; i < e1; i += NTHR) {
             const uint32_t en = a.ent[i];
             const int r = en & 255;
             if (((r >> 5) & 3) != p) continue;
