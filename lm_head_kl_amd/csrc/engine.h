@@ -81,6 +81,17 @@ struct WaveId {
         h = lane >> 5;
         lr = lane & 31;
     }
+    // A copy whose per-lane fields the compiler must recompute where it is taken. Epilogues
+    // inside persistent tile loops take one, so their many LDS addresses are not hoisted out
+    // of the loop and kept live (spilled) across the mainloop.
+    __device__ __forceinline__ WaveId fresh() const {
+        WaveId c = *this;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(c.tid) : "v"(tid));
+        c.lane = c.tid & 63;
+        c.h = c.lane >> 5;
+        c.lr = c.lane & 31;
+        return c;
+    }
 };
 
 template <typename T> __device__ __forceinline__ void mma(f32x16& c, const u32x4& a, const u32x4& b);

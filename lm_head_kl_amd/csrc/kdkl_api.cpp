@@ -26,7 +26,7 @@ using namespace kdkl;
 namespace {
 
 constexpr int64_t kAlign = 256;
-constexpr int64_t kDwGroup = 2;  // chunks per dW pass
+constexpr int64_t kDwGroup = 4;  // chunks per dW pass
 
 struct Carve {
     uintptr_t base;
@@ -75,6 +75,7 @@ Shape make_shape(const kd_problem* p) {
 }
 
 int64_t chunk_rows(const kd_problem* p) { return std::min(p->chunk, p->N); }
+bool whole_plan(const kd_problem* p) { return chunk_rows(p) % kTileM == 0; }
 
 // Workspace of the fused calls. The forward and backward parts are disjoint in time, so they
 // overlap in the workspace; the query returns the larger of the two.
@@ -117,9 +118,12 @@ FusedWs layout_fused(const kd_problem* p, void* ws) {
     w.fwd_bytes = f.used;
     Carve b(ws);
     b.take(kAlign);  // status word shared with the forward layout
-    w.cplan_off = (int32_t*)b.take(sizeof(int32_t) * n_rblocks(C) * (n_vt + 1));
-    w.cplan_ent = (uint32_t*)b.take(sizeof(uint32_t) * n_rblocks(C) * kTileM * K);
-    w.pt = (float*)b.take(sizeof(float) * C * K);
+    // When chunks start on row-block boundaries one plan over all N rows serves every chunk;
+    // otherwise each chunk builds its own.
+    const int64_t plan_rows = whole_plan(p) ? N : C;
+    w.cplan_off = (int32_t*)b.take(sizeof(int32_t) * n_rblocks(plan_rows) * (n_vt + 1));
+    w.cplan_ent = (uint32_t*)b.take(sizeof(uint32_t) * n_rblocks(plan_rows) * kTileM * K);
+    w.pt = (float*)b.take(sizeof(float) * N * K);
     // G_c^T and H_c^T hold kDwGroup chunks side by side (slot s at columns s*round_up(C, 8)), so
     // one dW pass reduces over kDwGroup chunks and dW is read and written once per group.
     w.ldgt = kDwGroup * round_up(C, 8);
@@ -253,17 +257,22 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
     KD_TRY(launch_transpose(sh.act, W, p->d, p->V, p->d, w.WT, Vp, Vp, s));
     const int64_t C8 = round_up(C, 8);
     const size_t es = esize(p->act);
+    const bool one_plan = whole_plan(p);
+    const int64_t plan_stride = n_vtiles(p->V) + 1;
+    if (one_plan) KD_TRY(launch_plan(idx, 0, p->N, p->K, p->V, w.cplan_off, w.cplan_ent, s));
+    KD_TRY(launch_teacher_prob(tlog, sh.tlog, 0, p->N, p->K, p->T, w.pt, s));
     int64_t ci = 0;
     bool dw_written = false;
     for (int64_t c0 = 0; c0 < p->N; c0 += C, ++ci) {
         const int64_t cc = std::min(C, p->N - c0);
         const int64_t slot = ci % kDwGroup;
-        KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.cplan_off, w.cplan_ent, s));
-        KD_TRY(launch_teacher_prob(tlog, sh.tlog, c0, c0 + cc, p->K, p->T, w.pt, s));
+        if (!one_plan) KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.cplan_off, w.cplan_ent, s));
+        // The chunk's row blocks in the plan; entry offsets in it are absolute.
+        const int32_t* c_off = w.cplan_off + (one_plan ? (c0 / kTileM) * plan_stride : 0);
         // H_c^T into its slot, so that dW = G^T H reads both operands with the rows contiguous
         KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
                                 (char*)w.HT + slot * C8 * es, w.ldgt, round_up(cc, 8), s));
-        KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt, grad_loss, c0, cc, w.cplan_off, w.cplan_ent, w.Gc, w.ldg,
+        KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.cplan_ent, w.Gc, w.ldg,
                                (char*)w.GT + slot * C8 * es, w.ldgt, s));
         KD_TRY(launch_dh(sh, w.Gc, w.ldg, W, w.WT, Vp, c0, cc, w.n_split, w.dh_part, dH, s));
         // One dW pass per group of chunks (K = the group's rows; the slots are zero-padded to 8)

@@ -52,7 +52,6 @@ namespace kdkl {
         timing_end(kind, stream);            \
     } while (0)
 
-constexpr int STG = kTileN + 4;  // staging row stride in floats (16-byte aligned)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr double kLn2 = 0.69314718055994530942;
 
@@ -95,6 +94,28 @@ __device__ __forceinline__ void rs_step(float (&pm)[NPOS], float (&ps)[NPOS], in
         ps[q] = ks;
     }
 }
+
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2{lo, hi}), bf16x2));
+}
+
+// Row of accumulator element e of lane half h inside its 32 x 32 MFMA block.
+__device__ __forceinline__ int blk_row(int e, int h) { return 8 * (e >> 2) + 4 * h + (e & 3); }
+
+// Staging of half a transposed tile in LDS: 128 rows (vocabulary entries) x 256 columns
+// (tokens) of fp32. Stage row sr holds tile row (sr/64)*128 + pass*64 + sr%64. Column t of row
+// r sits at t ^ st_swz(r); the XOR touches bits 2..5 only, so runs of 4 columns stay
+// contiguous and 16-byte aligned. With 64 four-byte banks it is conflict free for the
+// accumulator writes (rows r and r+4 of a wave land in opposite bank halves) and for column
+// reads of 16 rows 8 apart by 4 tokens.
+constexpr int SST = kTileN;
+__device__ __forceinline__ int st_swz(int r) { return (((r >> 3) ^ (((r >> 2) & 1) << 3)) & 15) << 2; }
+__device__ __forceinline__ int st_idx(int r, int t) { return r * SST + (t ^ st_swz(r)); }
+// Stage row of tile row c in the pass that holds it (pass (c >> 6) & 1).
+__device__ __forceinline__ int st_row(int c) { return (c >> 7) * 64 + (c & 63); }
 
 // ------------------------------------------------------------------------------------------
 // Plan: bucket cached ids by (row block of 256, vocab tile of 256).
@@ -237,6 +258,11 @@ struct FwdArgs {
 // takes the contiguous band [x*band, (x+1)*band), so its 32 workgroups work on a few row
 // blocks times Q vocab lanes at once. Those share both the H rows and the W tiles in the
 // XCD's L2.
+//
+// The tile is computed transposed, z^T = W_tile H_block^T: accumulator rows are vocabulary
+// entries and columns are tokens. Each lane then holds 64 vocabulary entries of each of its
+// 4 token columns, so the per-token (max, sum) over the vocabulary is folded inside the lane,
+// and lanes only meet once per unit.
 template <typename T>
 __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
@@ -249,8 +275,10 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
 
     for (int64_t u = xcd * band + slot; u < u_end; u += per_xcd) {
         const int rb = (int)(u / a.Q), q = (int)(u % a.Q);
-        const int64_t m0 = (int64_t)rb * kTileM;
+        const int64_t m0 = (int64_t)rb * kTileM;  // first token of the row block
         const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
+        // Running (max, sum) in units of y = z*log2(e)/T for this lane's token columns j, over
+        // the vocabulary rows the lane holds.
         float run_m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, run_s[4] = {0.f, 0.f, 0.f, 0.f};
 
         for (int vt = q; vt < a.n_vt; vt += a.Q) {
@@ -260,81 +288,83 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
             const int e0 = off[vt], e1 = off[vt + 1];
             const uint32_t my_en = e0 + id.tid < e1 ? a.ent[e0 + id.tid] : 0xffffffffu;
             f32x16 acc[4][4];
-            gemm_tile_kk<T>(acc, L, id, (const T*)a.H, a.d, m0, a.N, a.d, (const T*)a.W, a.d, n0,
-                                     a.V, a.d, 0, a.d);
+            gemm_tile_kk<T>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, (const T*)a.H, a.d, m0, a.N, a.d, 0,
+                            a.d);
+            const WaveId ie = id.fresh();
 
-            // Gather z at the cached ids of this (row block, vocab tile), one 64-row slab at a time.
+            // Gather z at the cached ids of this (row block, vocab tile): two passes of 128
+            // vocabulary rows staged in LDS.
             if (e1 > e0) {
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
+                for (int pq = 0; pq < 2; ++pq) {
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
+                    for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
-                            const int rl = id.wm * 32 + 8 * (e >> 2) + 4 * id.h + (e & 3);
-                            stage[rl * STG + id.wn * 128 + j * 32 + id.lr] = acc[p][j][e];
+                            const int sr = ie.wm * 64 + ii * 32 + blk_row(e, ie.h);
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                stage[st_idx(sr, ie.wn * 128 + j * 32 + ie.lr)] = acc[2 * pq + ii][j][e];
                         }
                     __syncthreads();
-                    if (my_en != 0xffffffffu && ((my_en >> 5) & 3) == (uint32_t)p) {
+                    if (my_en != 0xffffffffu && ((my_en >> 14) & 1) == (uint32_t)pq) {
                         const int r = my_en & 255, c = (my_en >> 8) & 255, k = (int)(my_en >> 16);
-                        a.zk[(m0 + r) * a.K + k] = stage[((r >> 7) * 32 + (r & 31)) * STG + c];
+                        a.zk[(m0 + r) * a.K + k] = stage[st_idx(st_row(c), r)];
                     }
-                    for (int i = e0 + NTHR + id.tid; i < e1; i += NTHR) {
+                    for (int i = e0 + NTHR + ie.tid; i < e1; i += NTHR) {
                         const uint32_t en = a.ent[i];
-                        const int r = en & 255;
-                        if (((r >> 5) & 3) != p) continue;
-                        const int c = (en >> 8) & 255, k = (int)(en >> 16);
-                        const int rl = (r >> 7) * 32 + (r & 31);
-                        a.zk[(m0 + r) * a.K + k] = stage[rl * STG + c];
+                        const int c = (en >> 8) & 255;
+                        if (((c >> 6) & 1) != pq) continue;
+                        const int r = en & 255, k = (int)(en >> 16);
+                        a.zk[(m0 + r) * a.K + k] = stage[st_idx(st_row(c), r)];
                     }
                     __syncthreads();
                 }
             }
 
-            // Online (max, sum) per row, in units of y = z*log2(e)/T, one 32-row MFMA block
-            // at a time. Each lane first folds its 4 columns. A reduce-scatter over the 32 lanes
-            // of its half (masks 16, 8, 4, 2) then leaves lane pair (2q', 2q'+1) with row
-            // position e = q' of the block, and a last exchange (mask 1) completes both copies.
-            bool colok[4];
+            // Tile (max, sum) per token column, folded over the lane's 64 vocabulary rows, then
+            // merged into the running pair. Rows past V (last tile only) count as -inf.
+            const bool vfull = n0 + kTileN <= a.V;
+            const int rows_left = (int)min<int64_t>(kTileN, a.V - n0) - ie.wm * 128 - 4 * ie.h;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) colok[j] = n0 + id.wn * 128 + j * 32 + id.lr < a.V;
+            for (int j = 0; j < 4; ++j) {
+                float mx = -INFINITY;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float pm[16], ps[16];
+                for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    float y[4];
-                    float m = -INFINITY;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        y[j] = colok[j] ? acc[i][j][e] * a.c : -INFINITY;
-                        m = fmaxf(m, y[j]);
+                    for (int e = 0; e < 16; ++e) {
+                        const bool ok = vfull || i * 32 + 8 * (e >> 2) + (e & 3) < rows_left;
+                        mx = fmaxf(mx, ok ? acc[i][j][e] : -INFINITY);
                     }
-                    float sum = 0.f;
-                    if (m != -INFINITY) {
+                // Re-read the accumulators for the sum instead of keeping 64 copies live.
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) sum += exp2_fast(y[j] - m);
-                    }
-                    pm[e] = m;
-                    ps[e] = sum;
+                for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[i][j]));
+                const float mt = mx * a.c;
+                float s = 0.f;
+                if (mx != -INFINITY) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            const bool ok = vfull || i * 32 + 8 * (e >> 2) + (e & 3) < rows_left;
+                            s += ok ? exp2_fast(fmaf(acc[i][j][e], a.c, -mt)) : 0.f;
+                        }
                 }
-                rs_step<8, 16>(pm, ps, id.lane);
-                rs_step<4, 8>(pm, ps, id.lane);
-                rs_step<2, 4>(pm, ps, id.lane);
-                rs_step<1, 2>(pm, ps, id.lane);
-                const float m2 = __shfl_xor(pm[0], 1), s2 = __shfl_xor(ps[0], 1);
-                ms_merge(pm[0], ps[0], m2, s2);
-                ms_merge(run_m[i], run_s[i], pm[0], ps[0]);
+                ms_merge(run_m[j], run_s[j], mt, s);
             }
         }
 
-        // Lane pair (2q', 2q'+1) of half h holds row position e = q' of each block i; the even lane writes.
-        if ((id.lr & 1) == 0) {
+        // Lanes l and l^32 hold the same token columns over different vocabulary rows.
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int row = id.wm * 128 + acc_row(i, id.lr >> 1, id.h);
-                const int64_t g = m0 + row;
-                if (g < a.N) a.part[(int64_t)(q * 2 + id.wn) * a.N + g] = make_float2(run_m[i], run_s[i]);
+        for (int j = 0; j < 4; ++j) {
+            const float m2 = __shfl_xor(run_m[j], 32), s2 = __shfl_xor(run_s[j], 32);
+            ms_merge(run_m[j], run_s[j], m2, s2);
+        }
+        if (id.h == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int64_t g = m0 + id.wn * 128 + j * 32 + id.lr;
+                if (g < a.N) a.part[(int64_t)(q * 2 + id.wm) * a.N + g] = make_float2(run_m[j], run_s[j]);
             }
         }
     }
@@ -429,6 +459,12 @@ __global__ __launch_bounds__(256) void k_sum_rows(const double* __restrict__ v, 
 
 // ------------------------------------------------------------------------------------------
 // Backward, per chunk: recompute the logit tile and form G = gs*(2^(y - lse2) - P_t).
+//
+// Like the forward, the tile is computed transposed (rows: vocabulary entries, columns:
+// tokens), so each lane needs the lse of only its 4 token columns, kept in registers. The
+// tile leaves through LDS in two passes of 128 vocabulary rows, which lets both copies be
+// written in whole 128-byte lines: G row-major (a token's 64 consecutive entries per group)
+// and G^T (a vocabulary entry's 256 consecutive tokens).
 
 struct GradArgs {
     const void* H;
@@ -450,119 +486,122 @@ struct GradArgs {
 };
 
 template <typename T>
+__device__ __forceinline__ void store8(T* dst, const float (&x)[8]) {
+    if constexpr (sizeof(T) == 2) {
+        u32x4 o;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[u] = pack_bf16x2(x[2 * u], x[2 * u + 1]);
+        *(u32x4*)dst = o;
+    } else {
+        *(f32x4*)dst = f32x4{x[0], x[1], x[2], x[3]};
+        *(f32x4*)(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
+    }
+}
+
+template <typename T>
 __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
-    __shared__ float lse2[kTileM];
     const WaveId id;
-    // Logical tiles are vocab-tile major, so an XCD's band covers a few W tiles times every
-    // row block of the chunk.
+    // Persistent when launched with fewer workgroups than tiles. Logical tiles are vocab-tile
+    // major; XCD x owns the contiguous band [x*band, (x+1)*band) and walks it with stride
+    // per_xcd, so the tiles in flight on one XCD are a few W tiles times every row block of
+    // the chunk, which share operand lines in the XCD's L2.
     const int64_t n_tiles = (int64_t)a.n_vt * a.n_rbc;
-    const int64_t t = xcd_tile(blockIdx.x, n_tiles);
-    if (t >= n_tiles) return;
-    const int vt = (int)(t / a.n_rbc), rb = (int)(t % a.n_rbc);
-    const int64_t r0 = (int64_t)rb * kTileM;  // row offset within the chunk
-    const int64_t n0 = (int64_t)vt * kTileN;
-    {
-        const int64_t r = r0 + id.tid;
-        lse2[id.tid] = r < a.cc ? a.lse[a.c0 + r] * kLog2e : 0.f;
-    }
-    const float gs = (a.grad ? a.grad[0] : 1.f) * a.gsc;
-    // This tile's cached-id entries: the first 256 are loaded into registers (one per thread)
-    // before the mainloop, so their latency hides behind it; more only occur on Zipf-hot tiles.
-    const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
-    const int e0 = off[vt], e1 = off[vt + 1];
-    uint32_t my_en = 0xffffffffu;
-    float my_pt = 0.f;
-    if (e0 + id.tid < e1) {
-        my_en = a.ent[e0 + id.tid];
-        my_pt = a.pt[(r0 + (my_en & 255)) * a.K + (my_en >> 16)];
-    }
-    const T* Hc = (const T*)a.H + a.c0 * a.d;
-    f32x16 acc[4][4];
-    gemm_tile_kk<T>(acc, L, id, Hc, a.d, r0, a.cc, a.d, (const T*)a.W, a.d, n0, a.V, a.d, 0, a.d);
-
+    const int64_t band = (n_tiles + 7) / 8, per_xcd = gridDim.x / 8;
+    const int64_t t_beg = (blockIdx.x % 8) * band, t_end = min(n_tiles, t_beg + band);
     float* stage = (float*)L;
-    bool colok[4];
+    const T* Hc = (const T*)a.H + a.c0 * a.d;
+    for (int64_t t = t_beg + blockIdx.x / 8; t < t_end; t += per_xcd) {
+        const int vt = (int)(t / a.n_rbc), rb = (int)(t % a.n_rbc);
+        const int64_t r0 = (int64_t)rb * kTileM;  // token offset within the chunk
+        const int64_t n0 = (int64_t)vt * kTileN;
+        const float gs = (a.grad ? a.grad[0] : 1.f) * a.gsc;
+        float l2[4];
+        bool tok_ok[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) colok[j] = n0 + id.wn * 128 + j * 32 + id.lr < a.V;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int rw = id.wm * 128 + acc_row(p, e, id.h);
-            const float l2 = lse2[rw];
-            const int rl = id.wm * 32 + 8 * (e >> 2) + 4 * id.h + (e & 3);
-            const bool rowok = r0 + rw < a.cc;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float v = (colok[j] && rowok) ? gs * exp2_fast(acc[p][j][e] * a.c - l2) : 0.f;
-                stage[rl * STG + id.wn * 128 + j * 32 + id.lr] = v;
-            }
+        for (int j = 0; j < 4; ++j) {
+            const int64_t tr = r0 + id.wn * 128 + j * 32 + id.lr;
+            tok_ok[j] = tr < a.cc;
+            l2[j] = tok_ok[j] ? a.lse[a.c0 + tr] * kLog2e : 0.f;
         }
-        __syncthreads();
-        if (my_en != 0xffffffffu && ((my_en >> 5) & 3) == (uint32_t)p) {
-            const int r = my_en & 255, c = (my_en >> 8) & 255;
-            stage[((r >> 7) * 32 + (r & 31)) * STG + c] -= gs * my_pt;
+        // This tile's cached-id entries: the first 256 are loaded into registers (one per
+        // thread) before the mainloop; more only occur on Zipf-hot tiles.
+        const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
+        const int e0 = off[vt], e1 = off[vt + 1];
+        uint32_t my_en = 0xffffffffu;
+        float my_pt = 0.f;
+        if (e0 + id.tid < e1) {
+            my_en = a.ent[e0 + id.tid];
+            my_pt = a.pt[(r0 + (my_en & 255)) * a.K + (my_en >> 16)];
         }
-        for (int i = e0 + NTHR + id.tid; i < e1; i += NTHR) {
-            const uint32_t en = a.ent[i];
-            const int r = en & 255;
-            if (((r >> 5) & 3) != p) continue;
-            const int c = (en >> 8) & 255, k = (int)(en >> 16);
-            const int rl = (r >> 7) * 32 + (r & 31);
-            stage[rl * STG + c] -= gs * a.pt[(r0 + r) * a.K + k];
-        }
-        __syncthreads();
-        // 64 rows x 32 groups of 8 columns; consecutive lanes take consecutive groups of a row.
+        f32x16 acc[4][4];
+        gemm_tile_kk<T>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, Hc, a.d, r0, a.cc, a.d, 0, a.d);
+        const WaveId ie = id.fresh();
+
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int it = id.tid + NTHR * t;
-            const int rl = it >> 5, cb = it & 31;
-            const int64_t row = r0 + (rl >> 5) * 128 + p * 32 + (rl & 31);
-            if (row < a.cc) {
-                const f32x4 v0 = *(const f32x4*)(stage + rl * STG + cb * 8);
-                const f32x4 v1 = *(const f32x4*)(stage + rl * STG + cb * 8 + 4);
-                if constexpr (sizeof(T) == 2) {
-                    u32x4 o;
-                    o[0] = f2bf(v0[0]) | (f2bf(v0[1]) << 16);
-                    o[1] = f2bf(v0[2]) | (f2bf(v0[3]) << 16);
-                    o[2] = f2bf(v1[0]) | (f2bf(v1[1]) << 16);
-                    o[3] = f2bf(v1[2]) | (f2bf(v1[3]) << 16);
-                    *(u32x4*)((bf16_t*)a.G + row * a.ldg + n0 + cb * 8) = o;
-                } else {
-                    float* gp = (float*)a.G + row * a.ldg + n0 + cb * 8;
-                    *(f32x4*)gp = v0;
-                    *(f32x4*)(gp + 4) = v1;
-                }
-            }
-        }
-        if (a.GT) {
-            // Transposed copy: 256 vocabulary rows x 8 groups of 8 chunk rows. Consecutive lanes
-            // take consecutive vocabulary entries, so the staging reads are conflict free.
+        for (int pq = 0; pq < 2; ++pq) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int it = id.tid + NTHR * t;
-                const int v = it & 255, rg = it >> 8;
-                const int rl0 = (rg >> 2) * 32 + (rg & 3) * 8;
-                const int64_t row = r0 + (rg >> 2) * 128 + p * 32 + (rg & 3) * 8;
-                if (row < a.ccp) {
-                    float x[8];
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * pq + ii;
 #pragma unroll
-                    for (int u = 0; u < 8; ++u) x[u] = stage[(rl0 + u) * STG + v];
-                    if constexpr (sizeof(T) == 2) {
-                        u32x4 o;
+                for (int e = 0; e < 16; ++e) {
+                    const bool vok = n0 + ie.wm * 128 + i * 32 + blk_row(e, ie.h) < a.V;
+                    const int sr = ie.wm * 64 + ii * 32 + blk_row(e, ie.h);
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) o[u] = f2bf(x[2 * u]) | (f2bf(x[2 * u + 1]) << 16);
-                        *(u32x4*)((bf16_t*)a.GT + (n0 + v) * a.ldgt + row) = o;
-                    } else {
-                        float* gp = (float*)a.GT + (n0 + v) * a.ldgt + row;
-                        *(f32x4*)gp = f32x4{x[0], x[1], x[2], x[3]};
-                        *(f32x4*)(gp + 4) = f32x4{x[4], x[5], x[6], x[7]};
+                    for (int j = 0; j < 4; ++j) {
+                        const float v = (vok && tok_ok[j]) ? gs * exp2_fast(fmaf(acc[i][j][e], a.c, -l2[j])) : 0.f;
+                        stage[st_idx(sr, ie.wn * 128 + j * 32 + ie.lr)] = v;
                     }
                 }
             }
+            __syncthreads();
+            if (my_en != 0xffffffffu && ((my_en >> 14) & 1) == (uint32_t)pq) {
+                const int r = my_en & 255, c = (my_en >> 8) & 255;
+                stage[st_idx(st_row(c), r)] -= gs * my_pt;
+            }
+            for (int i = e0 + NTHR + ie.tid; i < e1; i += NTHR) {
+                const uint32_t en = a.ent[i];
+                const int c = (en >> 8) & 255;
+                if (((c >> 6) & 1) != pq) continue;
+                const int r = en & 255, k = (int)(en >> 16);
+                stage[st_idx(st_row(c), r)] -= gs * a.pt[(r0 + r) * a.K + k];
+            }
+            __syncthreads();
+            // G rows: token tl, group g of 8 vocabulary entries (stage rows 8g .. 8g+7). Eight
+            // consecutive lanes cover one token's 64 entries of a half: a whole 128-byte line.
+#pragma unroll 4
+            for (int it8 = 0; it8 < 16; ++it8) {
+                const int it = ie.tid + NTHR * it8;
+                const int g = it & 15, tl = it >> 4;
+                const int64_t tr = r0 + tl;
+                if (tr < a.cc) {
+                    float x[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) x[u] = stage[st_idx(8 * g + u, tl)];
+                    const int vb = (g >> 3) * 128 + pq * 64 + (g & 7) * 8;
+                    store8<T>((T*)a.G + tr * a.ldg + n0 + vb, x);
+                }
+            }
+            // G^T rows: vocabulary entry of stage row sr, group cb of 8 tokens; 32 lanes write a
+            // row's 256 tokens.
+            if (a.GT) {
+#pragma unroll 4
+                for (int it8 = 0; it8 < 16; ++it8) {
+                    const int it = ie.tid + NTHR * it8;
+                    const int sr = it >> 5, cb = it & 31;
+                    const int64_t tr = r0 + cb * 8;
+                    if (tr < a.ccp) {
+                        const float* row = stage + sr * SST;
+                        const f32x4 v0 = *(const f32x4*)(row + ((cb * 8) ^ st_swz(sr)));
+                        const f32x4 v1 = *(const f32x4*)(row + ((cb * 8 + 4) ^ st_swz(sr)));
+                        const float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                        const int vr = (sr >> 6) * 128 + pq * 64 + (sr & 63);
+                        store8<T>((T*)a.GT + (n0 + vr) * a.ldgt + tr, x);
+                    }
+                }
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
@@ -971,6 +1010,8 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
     a.GT = GT;
     a.ldgt = ldgt;
     a.ccp = round_up(cc, 8);
+    // One tile per workgroup: measured a little faster than the persistent launch, whose
+    // workgroups stay in lockstep and so issue their tile stores all at once.
     const dim3 grid(grid_xcd((int64_t)a.n_vt * a.n_rbc));
     if (sh.act == Dt::BF16)
         KD_LAUNCH(kKindBwdGrad, s, k_bwd_grad<bf16_t>, grid, dim3(NTHR), 0, s, a);
