@@ -324,30 +324,53 @@ constexpr int NCH4 = 4;
 constexpr int TILE4 = kTileM * NCH4;  // 1024 chunks = 16 KB per operand per stage
 __device__ __forceinline__ int swz4(int r, int c) { return c ^ (((r >> 2) ^ (r >> 1)) & 3); }
 
-template <typename T>
+// Two operand layouts:
+//   row-major   element (mn, k) at src[mn*ld + k];
+//   K-blocked   the K axis cut into blocks of 256, each block a row-major [R][256] slab:
+//               element (mn, k) at src[((k >> 8)*R + mn)*256 + (k & 255)], with ld = R.
+// The K-blocked layout keeps the 256 rows of a tile within 128 KB (bf16) however long K is.
+// A row-major operand with a long K (the vocabulary) puts each of a tile's rows on its own
+// memory page, and its loads run about 15 % slower.
+template <typename T, bool BLK = false>
 struct KOperand4 {
     static constexpr int VEC = Elem<T>::VEC;
-    __amdgpu_buffer_rsrc_t rsrc;  // tile origin &src[mn0*ld]; k0 goes in the scalar offset
+    __amdgpu_buffer_rsrc_t rsrc;  // tile origin &src[mn0*ld] (row-major); k0 goes in the scalar offset
+    const char* base;             // K-blocked: &src[mn0*256] in block 0
+    int64_t blk_bytes;            // K-blocked: bytes per block
     uint32_t off[4];
     int chunk;
     // Wave w's instruction t fills chunks 256t + 64w + lane: row 64t + 16w + lane/4, slot lane%4.
     __device__ __forceinline__ void init(const T* src, int64_t ld, int64_t mn0, int64_t mn_lim, const WaveId& id) {
-        rsrc = make_rsrc(src + mn0 * ld);
+        const int64_t row_ld = BLK ? 256 : ld;
+        if constexpr (BLK) {
+            base = (const char*)uniform_ptr(src + mn0 * 256);
+            blk_bytes = ld * 256 * (int64_t)sizeof(T);
+        } else {
+            rsrc = make_rsrc(src + mn0 * ld);
+        }
         chunk = (id.lane & 3) ^ (((id.lane >> 4) ^ (id.lane >> 3)) & 3);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int row = 64 * t + 16 * id.w + (id.lane >> 2);
-            off[t] = mn0 + row < mn_lim ? (uint32_t)((row * ld + chunk * VEC) * (int64_t)sizeof(T)) : kOOB;
+            off[t] = mn0 + row < mn_lim ? (uint32_t)((row * row_ld + chunk * VEC) * (int64_t)sizeof(T)) : kOOB;
         }
     }
     // Load instruction t of the K step at k0 into the stage tile. Chunks at or past k_lim, and
     // every chunk when `live` is false, read as zero (no memory access). `full` (uniform) says
-    // the whole step is inside the K range.
+    // the whole step is inside the K range. A step never straddles a K block (k0 is a multiple
+    // of the step and the step divides 256).
     __device__ __forceinline__ void issue_one(u32x4* tile, int t, int64_t k0, int64_t k_lim, bool full, bool live,
                                               const WaveId& id) const {
         const bool in = live && (full || (int64_t)chunk * VEC < k_lim - k0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + 256 * t + 64 * id.w), 16,
-                                                 (int)(in ? off[t] : kOOB), (int)(k0 * (int64_t)sizeof(T)), 0, 0);
+        if constexpr (BLK) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (k0 >> 8) * blk_bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + 256 * t + 64 * id.w), 16,
+                                                     (int)(in ? off[t] : kOOB), (int)((k0 & 255) * (int64_t)sizeof(T)),
+                                                     0, 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + 256 * t + 64 * id.w), 16,
+                                                     (int)(in ? off[t] : kOOB), (int)(k0 * (int64_t)sizeof(T)), 0, 0);
+        }
     }
     __device__ __forceinline__ void issue(u32x4* tile, int64_t k0, int64_t k_lim, bool live, const WaveId& id) const {
         const bool full = k0 + Elem<T>::BK / 2 <= k_lim;
@@ -396,7 +419,8 @@ template <int N> __device__ __forceinline__ void wait_vmem_le() { asm volatile("
 //   [MFMA(F1) interleaved with DMA of stage kt+4 into stage kt's buffer and reads F0 <- (kt+1, g0)]
 // Stage kt's buffer is free after that barrier (its last fragments were read before it), so
 // the DMA runs four stages ahead. Every LDS read is issued one MFMA block ahead of its use.
-template <typename T>
+// BA / BB select the K-blocked layout for A / B (then lda / ldb is the operand's row count).
+template <typename T, bool BA = false, bool BB = false>
 __device__ __forceinline__ void gemm_tile_kk(f32x16 (&acc)[4][4], u32x4* L, const WaveId& id,
                                              const T* A, int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim,
                                              const T* B, int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim,
@@ -408,7 +432,8 @@ __device__ __forceinline__ void gemm_tile_kk(f32x16 (&acc)[4][4], u32x4* L, cons
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
     const int nk = (int)((k_end - k_begin + BKH - 1) / BKH);
     if (nk <= 0) return;
-    KOperand4<T> opA, opB;
+    KOperand4<T, BA> opA;
+    KOperand4<T, BB> opB;
     opA.init(A, lda, m0, m_lim, id);
     opB.init(B, ldb, n0, n_lim, id);
     auto stageA = [&](int s) { return L + (2 * (s & 3)) * TILE4; };

@@ -90,12 +90,12 @@ struct FusedWs {
     int32_t* cplan_off;
     uint32_t* cplan_ent;
     float* pt;
-    void* Gc;   // [C][ldg]
+    void* Gc;   // K-blocked [Vp/256][cc][256]
     void* GT;   // [Vp][ldgt]: G_c transposed
-    void* WT;   // [d][Vp]: W transposed, columns >= V zero
+    void* WT;   // K-blocked W^T [Vp/256][d][256], entries past V zero
     void* HT;   // [d][ldgt]: H_c transposed
     float* dh_part;
-    int64_t ldg, ldgt;
+    int64_t ldgt;
     int n_vsplit, n_split;
     size_t fwd_bytes, bwd_bytes;
 };
@@ -107,7 +107,6 @@ FusedWs layout_fused(const kd_problem* p, void* ws) {
     const int64_t C = chunk_rows(p);
     w.n_vsplit = fwd_vsplits(N, V);
     w.n_split = dh_splits(C, d, V);
-    w.ldg = Vp;
     Carve f(ws);
     w.status = (uint32_t*)f.take(kAlign);
     w.plan_off = (int32_t*)f.take(sizeof(int32_t) * n_rblocks(N) * (n_vt + 1));
@@ -254,7 +253,7 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
     const int64_t Vp = n_vtiles(p->V) * kTileN;
     const bool acc0 = (p->flags & KD_ACCUMULATE_DW) != 0;
     // W^T once per call: dH = G_c W then reads both operands with the vocabulary contiguous.
-    KD_TRY(launch_transpose(sh.act, W, p->d, p->V, p->d, w.WT, Vp, Vp, s));
+    KD_TRY(launch_transpose_blocked(sh.act, W, p->d, p->V, p->d, w.WT, Vp, s));
     const int64_t C8 = round_up(C, 8);
     const size_t es = esize(p->act);
     const bool one_plan = whole_plan(p);
@@ -272,9 +271,9 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
         // H_c^T into its slot, so that dW = G^T H reads both operands with the rows contiguous
         KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
                                 (char*)w.HT + slot * C8 * es, w.ldgt, round_up(cc, 8), s));
-        KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.cplan_ent, w.Gc, w.ldg,
+        KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.cplan_ent, w.Gc,
                                (char*)w.GT + slot * C8 * es, w.ldgt, s));
-        KD_TRY(launch_dh(sh, w.Gc, w.ldg, W, w.WT, Vp, c0, cc, w.n_split, w.dh_part, dH, s));
+        KD_TRY(launch_dh(sh, w.Gc, 0, W, w.WT, c0, cc, w.n_split, w.dh_part, dH, s));
         // One dW pass per group of chunks (K = the group's rows; the slots are zero-padded to 8)
         if (slot == kDwGroup - 1 || c0 + cc >= p->N) {
             KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * C8 + cc, acc0 || dw_written, dW, s));
@@ -308,7 +307,7 @@ kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const i
     // G: bf16 over the logits grid (row stride 2*Vp elements), or fp32 in the teacher grid.
     const void* G = sh.act == Dt::BF16 ? (const void*)w.Z : (const void*)w.P;
     const int64_t ldg = sh.act == Dt::BF16 ? 2 * w.ldz : w.ldz;
-    KD_TRY(launch_dh(sh, G, ldg, W, nullptr, 0, 0, p->N, w.n_split, w.dh_part, dH, s));
+    KD_TRY(launch_dh(sh, G, ldg, W, nullptr, 0, p->N, w.n_split, w.dh_part, dH, s));
     KD_TRY(launch_dw(sh, G, ldg, H, 0, p->N, (p->flags & KD_ACCUMULATE_DW) != 0, dW, s));
     return KD_OK;
 }

@@ -79,23 +79,27 @@ hipError_t launch_loss_final(const Shape& sh, const double* blk_sum, int n_blk, 
                              hipStream_t s);
 
 // Backward, one chunk of rows [c0, c0 + cc):
-//   G_c [cc, ldg] (act dtype, columns >= V zero) = g*T/n_norm*(softmax(z/T) - P_t), and, if GT
-//   is not null, its transpose G_c^T [Vp, ldgt] with columns [cc, round_up(cc, 8)) zero.
+//   G_c = g*T/n_norm*(softmax(z/T) - P_t) in the act dtype, K-blocked [Vp/256][cc][256] (entry
+//   (t, v) at ((v/256)*cc + t)*256 + v%256; entries v >= V zero), and, if GT is not null, its
+//   transpose G_c^T [Vp, ldgt] with columns [cc, round_up(cc, 8)) zero.
 hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const float* lse,
                            const float* pt, const float* grad_loss, int64_t c0, int64_t cc,
                            const int32_t* plan_off, const uint32_t* plan_ent, void* Gc,
-                           int64_t ldg, void* GT, int64_t ldgt, hipStream_t s);
+                           void* GT, int64_t ldgt, hipStream_t s);
 
 // dst[c][r] = src[r][c] (r < rows), zero for rows <= r < rows_pad; cols, rows_pad multiples of 8.
 hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst,
                             int64_t ldd, int64_t rows_pad, hipStream_t s);
+// The same transpose into the K-blocked layout [rows_pad/256][cols][256] (rows_pad % 256 == 0).
+hipError_t launch_transpose_blocked(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols,
+                                    void* dst, int64_t rows_pad, hipStream_t s);
 
-// dH rows [c0, c0+cc) = G_c W; B is W^T [d, ldwt] (K contiguous) when WT is not null, else W.
-// Split over the vocabulary into n_split fp32 partials when n_split > 1 (part: [n_split][cc][d]),
-// then reduced in a fixed order.
+// dH rows [c0, c0+cc) = G_c W. With WT not null, G_c is the K-blocked tile written by
+// launch_bwd_grad and WT is W^T K-blocked [Vp/256][d][256]; with WT null, G_c is [cc][ldg]
+// row-major and W is read as stored. Split over the vocabulary into n_split fp32 partials when
+// n_split > 1 (part: [n_split][cc][d]), then reduced in a fixed order.
 hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, const void* WT,
-                     int64_t ldwt, int64_t c0, int64_t cc, int n_split, float* part, void* dH,
-                     hipStream_t s);
+                     int64_t c0, int64_t cc, int n_split, float* part, void* dH, hipStream_t s);
 
 // dW (+)= G_c^T H[c0:c0+cc] from G_c [cc][ldg] and H (both M/N contiguous).
 hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H, int64_t c0,

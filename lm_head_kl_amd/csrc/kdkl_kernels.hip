@@ -479,8 +479,7 @@ struct GradArgs {
     const int32_t* off;
     const uint32_t* ent;
     int n_vt, n_rbc;
-    void* G;     // [cc][ldg] row-major
-    int64_t ldg;
+    void* G;     // K-blocked [Vp/256][cc][256]: entry (t, v) at ((v/256)*cc + t)*256 + v%256
     void* GT;    // [Vp][ldgt]: G transposed, columns [cc, ccp) zero; nullptr to skip
     int64_t ldgt, ccp;
 };
@@ -579,7 +578,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
 #pragma unroll
                     for (int u = 0; u < 8; ++u) x[u] = stage[st_idx(8 * g + u, tl)];
                     const int vb = (g >> 3) * 128 + pq * 64 + (g & 7) * 8;
-                    store8<T>((T*)a.G + tr * a.ldg + n0 + vb, x);
+                    store8<T>((T*)a.G + ((int64_t)vt * a.cc + tr) * kTileN + vb, x);
                 }
             }
             // G^T rows: vocabulary entry of stage row sr, group cb of 8 tokens; 32 lanes write a
@@ -609,7 +608,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
 // Transpose: dst[c*ldd + r] = src[r*lds + c] for r < rows, zero for rows <= r < rows_pad,
 // c < cols. 64 x 64 tiles through LDS. cols and rows_pad are multiples of 8.
 
-template <typename T>
+template <typename T, bool BLK>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, int64_t lds, int64_t rows,
                                                    int64_t cols, T* __restrict__ dst, int64_t ldd, int64_t rows_pad) {
     __shared__ T tile[64][65];
@@ -626,7 +625,12 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, in
     for (int i = 0; i < 16; ++i) {
         const int c = ty + 4 * i;
         const int64_t gc = c0 + c, gr = r0 + tx;
-        if (gc < cols && gr < rows_pad) dst[gc * ldd + gr] = tile[tx][c];
+        if (gc < cols && gr < rows_pad) {
+            if constexpr (BLK)
+                dst[((gr >> 8) * cols + gc) * 256 + (gr & 255)] = tile[tx][c];
+            else
+                dst[gc * ldd + gr] = tile[tx][c];
+        }
     }
 }
 
@@ -634,10 +638,9 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, in
 // dH = G W (A = G_c with the vocabulary contiguous, B = W with d contiguous).
 
 struct DhArgs {
-    const void* G;
+    const void* G;   // G_c [cc][ldg] row-major, or K-blocked [Vp/256][cc][256] (with W^T)
     int64_t ldg, Vp;
-    const void* W;   // W [V][d], or W^T [d][ldwt] zero-padded to Vp columns
-    int64_t ldwt;
+    const void* W;   // W [V][d], or W^T K-blocked [Vp/256][d][256], zero past V
     int64_t d, V;
     int64_t c0, cc;
     int64_t kper;
@@ -662,8 +665,8 @@ __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
     const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
     f32x16 acc[4][4];
     if constexpr (WT)
-        gemm_tile_kk<T>(acc, L, id, (const T*)a.G, a.ldg, m0, a.cc, k_end, (const T*)a.W, a.ldwt, n0, a.d, k_end,
-                        k_begin, k_end);
+        gemm_tile_kk<T, true, true>(acc, L, id, (const T*)a.G, a.cc, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
+                                    k_end, k_begin, k_end);
     else
         gemm_tile<T, true, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
                                   min(a.V, k_end), k_begin, k_end);
@@ -740,32 +743,55 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
     else
         gemm_tile<T, false, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.cc, (const T*)a.H + a.c0 * a.d,
                                    a.d, n0, a.d, a.cc, 0, a.cc);
-    bool colok[4];
+    // Read-modify-write through LDS, in two passes of 128 rows. Every dW access is a 16-byte
+    // vector and a wave covers 1 KB of one row. The old values of a pass's first half are
+    // requested before its staging writes and those of the second half before the first half
+    // is added, so the load latency hides behind LDS work.
+    const WaveId ie = id.fresh();
+    float* stage = (float*)L;
+    auto item = [&](int pq, int bt, int k, int& sr, int64_t& row, int64_t& col) {
+        const int it = ie.tid + NTHR * (16 * bt + k);
+        sr = it >> 6;
+        row = m0 + (sr >> 6) * 128 + pq * 64 + (sr & 63);
+        col = n0 + (it & 63) * 4;
+    };
+    auto load_old = [&](int pq, int bt, f32x4 (&old)[16]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) colok[j] = n0 + id.wn * 128 + j * 32 + id.lr < a.d;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // read the 64 old values of this lane's rows in block i first, then add and store
-        float old[4][16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t row = m0 + id.wm * 128 + acc_row(i, e, id.h);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t col = n0 + id.wn * 128 + j * 32 + id.lr;
-                old[j][e] = (a.accumulate && row < a.V && colok[j]) ? a.dW[row * a.d + col] : 0.f;
-            }
+        for (int k = 0; k < 16; ++k) {
+            int sr;
+            int64_t row, col;
+            item(pq, bt, k, sr, row, col);
+            old[k] = (a.accumulate && row < a.V && col < a.d) ? *(const f32x4*)(a.dW + row * a.d + col)
+                                                              : f32x4{0.f, 0.f, 0.f, 0.f};
         }
+    };
+    auto add_store = [&](int pq, int bt, const f32x4 (&old)[16]) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t row = m0 + id.wm * 128 + acc_row(i, e, id.h);
-            if (row >= a.V) continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t col = n0 + id.wn * 128 + j * 32 + id.lr;
-                if (colok[j]) a.dW[row * a.d + col] = old[j][e] + acc[i][j][e];
-            }
+        for (int k = 0; k < 16; ++k) {
+            int sr;
+            int64_t row, col;
+            item(pq, bt, k, sr, row, col);
+            if (row < a.V && col < a.d)
+                *(f32x4*)(a.dW + row * a.d + col) = old[k] + *(const f32x4*)(stage + st_idx(sr, (int)(col - n0)));
         }
+    };
+#pragma unroll
+    for (int pq = 0; pq < 2; ++pq) {
+        f32x4 old0[16], old1[16];
+        load_old(pq, 0, old0);
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int sr = ie.wm * 64 + ii * 32 + blk_row(e, ie.h);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) stage[st_idx(sr, ie.wn * 128 + j * 32 + ie.lr)] = acc[2 * pq + ii][j][e];
+            }
+        __syncthreads();
+        load_old(pq, 1, old1);
+        add_store(pq, 0, old0);
+        add_store(pq, 1, old1);
+        __syncthreads();
     }
 }
 
@@ -987,7 +1013,7 @@ hipError_t launch_loss_final(const Shape& sh, const double* blk_sum, int n_blk, 
 
 hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const float* lse, const float* pt,
                            const float* grad_loss, int64_t c0, int64_t cc, const int32_t* plan_off,
-                           const uint32_t* plan_ent, void* Gc, int64_t ldg, void* GT, int64_t ldgt, hipStream_t s) {
+                           const uint32_t* plan_ent, void* Gc, void* GT, int64_t ldgt, hipStream_t s) {
     GradArgs a;
     a.H = H;
     a.W = W;
@@ -1006,7 +1032,6 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
     a.n_vt = (int)((sh.V + kTileN - 1) / kTileN);
     a.n_rbc = (int)((cc + kTileM - 1) / kTileM);
     a.G = Gc;
-    a.ldg = ldg;
     a.GT = GT;
     a.ldgt = ldgt;
     a.ccp = round_up(cc, 8);
@@ -1024,22 +1049,34 @@ hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, i
                             int64_t rows_pad, hipStream_t s) {
     const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows_pad + 63) / 64));
     if (dt == Dt::BF16)
-        KD_LAUNCH(kKindTranspose, s, k_transpose<bf16_t>, grid, dim3(NTHR), 0, s, (const bf16_t*)src, lds, rows, cols,
-                           (bf16_t*)dst, ldd, rows_pad);
+        KD_LAUNCH(kKindTranspose, s, (k_transpose<bf16_t, false>), grid, dim3(NTHR), 0, s, (const bf16_t*)src, lds, rows,
+                  cols, (bf16_t*)dst, ldd, rows_pad);
     else
-        KD_LAUNCH(kKindTranspose, s, k_transpose<float>, grid, dim3(NTHR), 0, s, (const float*)src, lds, rows, cols,
-                           (float*)dst, ldd, rows_pad);
+        KD_LAUNCH(kKindTranspose, s, (k_transpose<float, false>), grid, dim3(NTHR), 0, s, (const float*)src, lds, rows,
+                  cols, (float*)dst, ldd, rows_pad);
     return hipGetLastError();
 }
 
-hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, const void* WT, int64_t ldwt,
-                     int64_t c0, int64_t cc, int n_split, float* part, void* dH, hipStream_t s) {
+hipError_t launch_transpose_blocked(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst,
+                                    int64_t rows_pad, hipStream_t s) {
+    if (rows_pad % 256 != 0) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows_pad + 63) / 64));
+    if (dt == Dt::BF16)
+        KD_LAUNCH(kKindTranspose, s, (k_transpose<bf16_t, true>), grid, dim3(NTHR), 0, s, (const bf16_t*)src, lds, rows,
+                  cols, (bf16_t*)dst, (int64_t)0, rows_pad);
+    else
+        KD_LAUNCH(kKindTranspose, s, (k_transpose<float, true>), grid, dim3(NTHR), 0, s, (const float*)src, lds, rows,
+                  cols, (float*)dst, (int64_t)0, rows_pad);
+    return hipGetLastError();
+}
+
+hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, const void* WT, int64_t c0,
+                     int64_t cc, int n_split, float* part, void* dH, hipStream_t s) {
     DhArgs a;
     a.G = Gc;
     a.ldg = ldg;
     a.Vp = round_up(sh.V, kTileN);
     a.W = WT ? WT : W;
-    a.ldwt = ldwt;
     a.d = sh.d;
     a.V = sh.V;
     a.c0 = c0;
