@@ -11,10 +11,11 @@ Prints one JSON line. Along with the throughput it carries:
   - roofline: for the kernel with the largest share of the step, measured with the library's
     per-launch HIP events on its stream, and its HBM bytes from the committed counter summary;
   - cpu_baseline: the fp64 oracle timed on the host on a bounded slice of rows;
-  - peak device memory: fused, and the dense path's at the same shape.
+  - formulations: time and peak device memory of the same step through the other three
+    formulations (single pass, forward-chunked, dense) on the same inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gptoss] [--chunk C]
-       [--no-cpu-baseline] [--no-dense]
+       [--no-cpu-baseline] [--no-dense] [--no-formulations]
 """
 
 import argparse
@@ -41,6 +42,8 @@ def parse():
     ap.add_argument("--rows", type=int, default=0, help="override N (default: the config's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-formulations", action="store_true",
+                    help="skip timing the single-pass and forward-chunked formulations")
     ap.add_argument("--cpu-rows", type=int, default=512)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device-to-device once (reference for the HBM byte counters)")
@@ -237,25 +240,47 @@ def main():
         },
     }
 
+    # The other formulations on the same inputs: one call each does forward and backward.
+    # Each is warmed up once and timed over a few calls; peak memory is measured from the
+    # inputs up, like the fused path's.
+    del ws, dW
+    forms = {"fused_recompute": {"ms": ms_step, "peak_hbm_gb": peak_fused / 1e9, "counted_flops": flops_step}}
+    others = [("single_pass", lambda: kd.fused_kl_fwdbwd(H, W, idx, t, T=p.T, chunk=chunk), 6.0),
+              ("forward_chunked", lambda: kd.chunked_kl(H, W, idx, t, T=p.T, chunk=chunk), 6.0)]
     if not args.no_dense:
-        del ws, dW
+        others.append(("dense", lambda: kd.dense_kl(H, W, idx, t, T=p.T), 8.0))
+    for name, call, fl in others:
+        if args.no_formulations and name != "dense":
+            continue
         torch.cuda.empty_cache()
         torch.cuda.synchronize()
         torch.cuda.reset_peak_memory_stats(dev)
         base = torch.cuda.memory_allocated(dev)
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         try:
-            kd.dense_kl(H, W, idx, t, T=p.T)
+            call()
             torch.cuda.synchronize()
+            peak = (torch.cuda.max_memory_allocated(dev) - base) / 1e9
+            reps = 1 if name == "dense" else 3
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
             e[0].record(stream)
-            kd.dense_kl(H, W, idx, t, T=p.T)
+            for _ in range(reps):
+                call()
             e[1].record(stream)
             torch.cuda.synchronize()
-            out["dense_ms"] = e[0].elapsed_time(e[1])
-            out["peak_hbm_dense_gb"] = (torch.cuda.max_memory_allocated(dev) - base) / 1e9
+            forms[name] = {"ms": e[0].elapsed_time(e[1]) / reps, "peak_hbm_gb": peak,
+                           "counted_flops": fl * N * d * V}
         except (RuntimeError, torch.OutOfMemoryError) as ex:
-            out["dense_error"] = str(ex)[:200]
-        print("[bench] dense path done", file=sys.stderr, flush=True)
+            forms[name] = {"error": str(ex)[:200]}
+        torch.cuda.empty_cache()
+        print(f"[bench] {name} path done", file=sys.stderr, flush=True)
+    for f in forms.values():
+        if "ms" in f:
+            f["tokens_per_s"] = N / (f["ms"] / 1e3)
+            f["pct_bf16_peak_of_counted"] = 100.0 * f["counted_flops"] / (f["ms"] / 1e3) / (PEAK_BF16_TFLOPS * 1e12)
+    out["formulations"] = forms
+    if "dense" in forms and "ms" in forms["dense"]:
+        out["dense_ms"] = forms["dense"]["ms"]
+        out["peak_hbm_dense_gb"] = forms["dense"]["peak_hbm_gb"]
 
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline on {args.cpu_rows} rows", file=sys.stderr, flush=True)

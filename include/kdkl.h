@@ -181,13 +181,47 @@ kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const i
                       kd_stream stream);
 
 /*
+ * Forward-chunked formulation, forward and backward in one call. The teacher stays sparse and
+ * the loss is computed one slice of rows at a time, but every student logit is kept (as z^T,
+ * fp32, in the workspace) for the backward, which reads them instead of recomputing. Memory
+ * therefore grows with N (4 * N * V bytes of logits) while the work drops to 6*N*d*V FLOPs.
+ * Source: aiexpert.news "Making knowledge distillation cheap enough to run in production",
+ * paragraph on the three formulations (forward-chunked KL: fastest, logits materialised for
+ * the backward, memory still scaling with sequence length).
+ *   Arguments as in kd_dense_kl; grad_loss (device scalar or NULL for 1) is applied to dH and
+ *   dW; KD_ACCUMULATE_DW adds into dW. Same results as the fused calls up to rounding.
+ */
+size_t kd_chunked_workspace_bytes(const kd_problem* p);
+kd_status kd_chunked_kl(const kd_problem* p, const void* H, const void* W, const int32_t* idx,
+                        const void* tlog, const float* grad_loss, float* loss, float* lse,
+                        float* row_kl, void* dH, float* dW, void* ws, size_t ws_bytes,
+                        kd_stream stream);
+
+/*
+ * Single-pass fused formulation: each chunk of rows is taken end to end (logits, its loss
+ * terms, G_c, dH_c and its share of dW) and discarded before the next, so the logits are
+ * computed once (6*N*d*V FLOPs instead of 8) and memory stays bounded by the chunk (the
+ * chunk's fp32 logits, 4 * chunk * V bytes, on top of the fused backward's buffers). The
+ * upstream gradient must be known at call time: grad_loss (device scalar or NULL for 1) is
+ * applied to dH and dW. Source: aiexpert.news ticker "Multiverse Computing publishes efficient
+ * KD technique cutting distillation VRAM", second change (sequence chunks processed end to
+ * end and discarded after the backward pass).
+ *   Arguments as in kd_dense_kl; KD_ACCUMULATE_DW adds into dW.
+ */
+size_t kd_fused_fwdbwd_workspace_bytes(const kd_problem* p);
+kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, const int32_t* idx,
+                             const void* tlog, const float* grad_loss, float* loss, float* lse,
+                             float* row_kl, void* dH, float* dW, void* ws, size_t ws_bytes,
+                             kd_stream stream);
+
+/*
  * Per-kernel timing (profiling; off by default). While enabled, every kernel the library
  * launches, from any thread, is bracketed by two HIP events recorded on the launch's own
  * stream. kd_timing_read waits for the recorded events. It then returns, for one kernel kind,
  * the number of launches and their total duration in milliseconds accumulated since the last
  * kd_timing_reset.
  *   kd_timing_enable(on) returns the previous setting; kd_timing_kinds() is the number of
- *   kinds; kd_timing_name(kind) is a static name ("fwd", "bwd_grad", "dh", "dw", ...).
+ *   kinds; kd_timing_name(kind) is a static name ("fwd", "bwd_grad", "dh", "dw", "grad_z", ...).
  * The events are owned and reused by the library; enabling timing adds two event records per
  * launch and nothing else.
  */

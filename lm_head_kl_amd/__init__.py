@@ -27,8 +27,12 @@ __all__ = [
     "fused_kl_fwd",
     "fused_kl_bwd",
     "dense_kl",
+    "chunked_kl",
+    "fused_kl_fwdbwd",
     "fused_workspace_bytes",
     "dense_workspace_bytes",
+    "chunked_workspace_bytes",
+    "fused_fwdbwd_workspace_bytes",
     "make_problem",
     "timing_enable",
     "timing_read",
@@ -160,6 +164,56 @@ def dense_kl(H, W, idx, tlog, T: float = 1.0, grad_loss=None, n_norm: float = 0.
                                   _stream(dev))
     _lib.check(code, "kd_dense_kl")
     return loss, lse, row_kl, dH, dW
+
+
+def _one_call(fn_name: str, ws_name: str, H, W, idx, tlog, T, chunk, grad_loss, n_norm, flags, want_row_kl, dW,
+              workspace):
+    dev = _need_device(H, W, idx, tlog)
+    p = make_problem(H, W, idx, tlog, T, chunk, n_norm, flags)
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(p.N, dtype=torch.float32, device=dev)
+    row_kl = torch.empty(p.N, dtype=torch.float32, device=dev) if want_row_kl else None
+    dH = torch.empty_like(H)
+    if dW is None:
+        if flags & KD_ACCUMULATE_DW:
+            raise KdError(1, fn_name, "KD_ACCUMULATE_DW needs a dW tensor")
+        dW = torch.empty(W.shape, dtype=torch.float32, device=dev)
+    elif dW.dtype != torch.float32 or tuple(dW.shape) != tuple(W.shape):
+        raise KdError(3, fn_name, "dW must be float32 with W's shape")
+    g = None
+    if grad_loss is not None:
+        g = grad_loss.detach().to(device=dev, dtype=torch.float32).reshape(1).contiguous()
+    L = _lib.lib()
+    nb = int(getattr(L, ws_name)(ctypes.byref(p)))
+    ws = workspace if workspace is not None and workspace.numel() >= nb else _workspace(nb, dev)
+    code = getattr(L, fn_name)(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlog), _ptr(g), _ptr(loss),
+                               _ptr(lse), _ptr(row_kl), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream(dev))
+    _lib.check(code, fn_name)
+    return loss, lse, row_kl, dH, dW
+
+
+def chunked_workspace_bytes(p: KdProblem) -> int:
+    return int(_lib.lib().kd_chunked_workspace_bytes(ctypes.byref(p)))
+
+
+def fused_fwdbwd_workspace_bytes(p: KdProblem) -> int:
+    return int(_lib.lib().kd_fused_fwdbwd_workspace_bytes(ctypes.byref(p)))
+
+
+def chunked_kl(H, W, idx, tlog, T: float = 1.0, chunk: int = 2048, grad_loss=None, n_norm: float = 0.0,
+               flags: int = 0, want_row_kl: bool = True, dW=None, workspace=None):
+    """kd_chunked_kl (forward-chunked formulation: every logit kept for the backward).
+    Returns (loss, lse, row_kl, dH, dW)."""
+    return _one_call("kd_chunked_kl", "kd_chunked_workspace_bytes", H, W, idx, tlog, T, chunk, grad_loss, n_norm,
+                     flags, want_row_kl, dW, workspace)
+
+
+def fused_kl_fwdbwd(H, W, idx, tlog, T: float = 1.0, chunk: int = 2048, grad_loss=None, n_norm: float = 0.0,
+                    flags: int = 0, want_row_kl: bool = True, dW=None, workspace=None):
+    """kd_fused_kl_fwdbwd (single pass per chunk, no recompute; grad_loss applied now).
+    Returns (loss, lse, row_kl, dH, dW)."""
+    return _one_call("kd_fused_kl_fwdbwd", "kd_fused_fwdbwd_workspace_bytes", H, W, idx, tlog, T, chunk, grad_loss,
+                     n_norm, flags, want_row_kl, dW, workspace)
 
 
 class FusedKL(torch.autograd.Function):

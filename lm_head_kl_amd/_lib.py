@@ -36,6 +36,10 @@ EXPORTS = (
     "kd_fused_kl_bwd",
     "kd_dense_workspace_bytes",
     "kd_dense_kl",
+    "kd_chunked_workspace_bytes",
+    "kd_chunked_kl",
+    "kd_fused_fwdbwd_workspace_bytes",
+    "kd_fused_kl_fwdbwd",
     "kd_timing_enable",
     "kd_timing_kinds",
     "kd_timing_name",
@@ -93,6 +97,12 @@ def lib() -> ctypes.CDLL:
     L.kd_fused_kl_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kd_dense_kl.restype = ctypes.c_int
     L.kd_dense_kl.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for name in ("kd_chunked_workspace_bytes", "kd_fused_fwdbwd_workspace_bytes"):
+        getattr(L, name).restype = sz
+        getattr(L, name).argtypes = [P]
+    for name in ("kd_chunked_kl", "kd_fused_kl_fwdbwd"):
+        getattr(L, name).restype = ctypes.c_int
+        getattr(L, name).argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kd_timing_enable.restype = ctypes.c_int
     L.kd_timing_enable.argtypes = [ctypes.c_int]
     L.kd_timing_kinds.restype = ctypes.c_int

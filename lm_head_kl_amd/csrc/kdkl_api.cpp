@@ -135,6 +135,63 @@ FusedWs layout_fused(const kd_problem* p, void* ws) {
     return w;
 }
 
+// Workspace of the two paths that keep the logits (z^T, fp32) instead of recomputing them:
+//   all_rows = true   forward-chunked: z^T of all N rows, [Vp][round_up(N, 4)];
+//   all_rows = false  single pass: z^T of one chunk, [Vp][round_up(C, 4)].
+// The backward buffers (G_c, G_c^T, W^T, H_c^T, dH partials) are those of the fused path.
+struct StoredWs {
+    uint32_t* status;
+    int32_t* plan_off;
+    uint32_t* plan_ent;
+    float* pt;
+    float* zk;
+    float2* part;
+    double* blk_sum;
+    float* zt;
+    int64_t ldzt;
+    void* Gc;
+    void* GT;
+    void* WT;
+    void* HT;
+    float* dh_part;
+    int64_t ldgt;
+    int n_vsplit, n_split;
+    size_t bytes;
+};
+
+StoredWs layout_stored(const kd_problem* p, void* ws, bool all_rows) {
+    StoredWs w{};
+    const int64_t N = p->N, K = p->K, V = p->V, d = p->d;
+    const int64_t n_vt = n_vtiles(V), Vp = n_vt * kTileN;
+    const int64_t C = chunk_rows(p);
+    const int64_t fwd_rows = all_rows ? N : C;
+    w.n_vsplit = fwd_vsplits(fwd_rows, V);
+    w.n_split = dh_splits(C, d, V);
+    w.ldzt = round_up(fwd_rows, 4);
+    w.ldgt = kDwGroup * round_up(C, 8);
+    const int64_t n_chunks = (N + C - 1) / C;
+    Carve c(ws);
+    w.status = (uint32_t*)c.take(kAlign);
+    w.plan_off = (int32_t*)c.take(sizeof(int32_t) * n_rblocks(N) * (n_vt + 1));
+    w.plan_ent = (uint32_t*)c.take(sizeof(uint32_t) * n_rblocks(N) * kTileM * K);
+    w.pt = (float*)c.take(sizeof(float) * N * K);
+    w.zk = (float*)c.take(sizeof(float) * N * K);
+    // Per-row partials of one forward launch; the last chunk may use more vocab lanes.
+    const int64_t last = N - (n_chunks - 1) * C;
+    const int64_t n_part_rows =
+        all_rows ? w.n_vsplit * N : std::max(w.n_vsplit * C, (int64_t)fwd_vsplits(last, V) * last);
+    w.part = (float2*)c.take(sizeof(float2) * 2 * n_part_rows);
+    w.blk_sum = (double*)c.take(sizeof(double) * (all_rows ? combine_blocks(N) : n_chunks * combine_blocks(C)));
+    w.zt = (float*)c.take(sizeof(float) * Vp * w.ldzt);
+    w.Gc = c.take(esize(p->act) * C * Vp);
+    w.GT = c.take(esize(p->act) * Vp * w.ldgt);
+    w.WT = c.take(esize(p->act) * d * Vp);
+    w.HT = c.take(esize(p->act) * d * w.ldgt);
+    w.dh_part = w.n_split > 1 ? (float*)c.take(sizeof(float) * w.n_split * C * d) : nullptr;
+    w.bytes = c.used;
+    return w;
+}
+
 struct DenseWs {
     float* Z;
     float* P;
@@ -174,6 +231,36 @@ kd_status validate_ids(const kd_problem* p, const int32_t* idx, uint32_t* status
     KD_TRY(hipMemcpyAsync(&h, status, sizeof(h), hipMemcpyDeviceToHost, s));
     KD_TRY(hipStreamSynchronize(s));
     return h ? KD_ERR_INDEX : KD_OK;
+}
+
+// Backward over chunks from stored logits (forward-chunked path): G_c from z^T, then dH_c and
+// the grouped dW passes, as in kd_fused_kl_bwd.
+kd_status stored_backward(const kd_problem* p, const Shape& sh, const StoredWs& w, const void* H, const int32_t* idx,
+                          const float* lse, const float* grad_loss, void* dH, float* dW, hipStream_t s) {
+    const int64_t C = chunk_rows(p);
+    const bool one_plan = whole_plan(p);
+    const int64_t plan_stride = n_vtiles(p->V) + 1;
+    const int64_t C8 = round_up(C, 8);
+    const size_t es = esize(p->act);
+    const bool acc0 = (p->flags & KD_ACCUMULATE_DW) != 0;
+    int64_t ci = 0;
+    bool dw_written = false;
+    for (int64_t c0 = 0; c0 < p->N; c0 += C, ++ci) {
+        const int64_t cc = std::min(C, p->N - c0);
+        const int64_t slot = ci % kDwGroup;
+        if (!one_plan) KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.plan_off, w.plan_ent, s));
+        const int32_t* c_off = w.plan_off + (one_plan ? (c0 / kTileM) * plan_stride : 0);
+        KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
+                                (char*)w.HT + slot * C8 * es, w.ldgt, round_up(cc, 8), s));
+        KD_TRY(launch_grad_z(sh, w.zt, w.ldzt, c0, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.plan_ent, w.Gc,
+                             (char*)w.GT + slot * C8 * es, w.ldgt, s));
+        KD_TRY(launch_dh(sh, w.Gc, 0, nullptr, w.WT, c0, cc, w.n_split, w.dh_part, dH, s));
+        if (slot == kDwGroup - 1 || c0 + cc >= p->N) {
+            KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * C8 + cc, acc0 || dw_written, dW, s));
+            dw_written = true;
+        }
+    }
+    return KD_OK;
 }
 
 }  // namespace
@@ -226,7 +313,7 @@ kd_status kd_fused_kl_fwd(const kd_problem* p, const void* H, const void* W, con
     }
     float* zk_out = zk ? zk : w.zk;
     KD_TRY(launch_plan(idx, 0, p->N, p->K, p->V, w.plan_off, w.plan_ent, s));
-    KD_TRY(launch_fwd(sh, H, W, w.plan_off, w.plan_ent, w.n_vsplit, w.part, zk_out, s));
+    KD_TRY(launch_fwd(sh, H, W, w.plan_off, w.plan_ent, w.n_vsplit, w.part, zk_out, nullptr, 0, s));
     int n_blk = 0;
     KD_TRY(launch_combine(sh, w.part, 2 * w.n_vsplit, zk_out, tlog, lse, row_kl, w.blk_sum, &n_blk, s));
     KD_TRY(launch_loss_final(sh, w.blk_sum, n_blk, loss, s));
@@ -309,6 +396,100 @@ kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const i
     const int64_t ldg = sh.act == Dt::BF16 ? 2 * w.ldz : w.ldz;
     KD_TRY(launch_dh(sh, G, ldg, W, nullptr, 0, p->N, w.n_split, w.dh_part, dH, s));
     KD_TRY(launch_dw(sh, G, ldg, H, 0, p->N, (p->flags & KD_ACCUMULATE_DW) != 0, dW, s));
+    return KD_OK;
+}
+
+size_t kd_chunked_workspace_bytes(const kd_problem* p) {
+    if (check_problem(p) != KD_OK) return 0;
+    return layout_stored(p, nullptr, true).bytes;
+}
+
+size_t kd_fused_fwdbwd_workspace_bytes(const kd_problem* p) {
+    if (check_problem(p) != KD_OK) return 0;
+    return layout_stored(p, nullptr, false).bytes;
+}
+
+kd_status kd_chunked_kl(const kd_problem* p, const void* H, const void* W, const int32_t* idx, const void* tlog,
+                        const float* grad_loss, float* loss, float* lse, float* row_kl, void* dH, float* dW, void* ws,
+                        size_t ws_bytes, kd_stream stream) {
+    kd_status st = check_problem(p);
+    if (st != KD_OK) return st;
+    if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16)) return KD_ERR_VALUE;
+    if (!aligned(ws, kAlign) || ws_bytes < kd_chunked_workspace_bytes(p)) return KD_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    const Shape sh = make_shape(p);
+    const StoredWs w = layout_stored(p, ws, true);
+    if (p->flags & KD_VALIDATE_IDX) {
+        st = validate_ids(p, idx, w.status, s);
+        if (st != KD_OK) return st;
+    }
+    // Forward over all rows, keeping every logit (z^T) for the backward.
+    KD_TRY(launch_plan(idx, 0, p->N, p->K, p->V, w.plan_off, w.plan_ent, s));
+    KD_TRY(launch_teacher_prob(tlog, sh.tlog, 0, p->N, p->K, p->T, w.pt, s));
+    KD_TRY(launch_fwd(sh, H, W, w.plan_off, w.plan_ent, w.n_vsplit, w.part, w.zk, w.zt, w.ldzt, s));
+    int n_blk = 0;
+    KD_TRY(launch_combine(sh, w.part, 2 * w.n_vsplit, w.zk, tlog, lse, row_kl, w.blk_sum, &n_blk, s));
+    KD_TRY(launch_loss_final(sh, w.blk_sum, n_blk, loss, s));
+    KD_TRY(launch_transpose_blocked(sh.act, W, p->d, p->V, p->d, w.WT, n_vtiles(p->V) * kTileN, s));
+    return stored_backward(p, sh, w, H, idx, lse, grad_loss, dH, dW, s);
+}
+
+kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, const int32_t* idx, const void* tlog,
+                             const float* grad_loss, float* loss, float* lse, float* row_kl, void* dH, float* dW,
+                             void* ws, size_t ws_bytes, kd_stream stream) {
+    kd_status st = check_problem(p);
+    if (st != KD_OK) return st;
+    if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16)) return KD_ERR_VALUE;
+    if (!aligned(ws, kAlign) || ws_bytes < kd_fused_fwdbwd_workspace_bytes(p)) return KD_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    const Shape sh = make_shape(p);
+    const StoredWs w = layout_stored(p, ws, false);
+    if (p->flags & KD_VALIDATE_IDX) {
+        st = validate_ids(p, idx, w.status, s);
+        if (st != KD_OK) return st;
+    }
+    const int64_t C = chunk_rows(p);
+    const bool one_plan = whole_plan(p);
+    const int64_t plan_stride = n_vtiles(p->V) + 1;
+    const int64_t C8 = round_up(C, 8);
+    const size_t es = esize(p->act), ets = esize(p->tlogit);
+    const bool acc0 = (p->flags & KD_ACCUMULATE_DW) != 0;
+    if (one_plan) KD_TRY(launch_plan(idx, 0, p->N, p->K, p->V, w.plan_off, w.plan_ent, s));
+    KD_TRY(launch_teacher_prob(tlog, sh.tlog, 0, p->N, p->K, p->T, w.pt, s));
+    KD_TRY(launch_transpose_blocked(sh.act, W, p->d, p->V, p->d, w.WT, n_vtiles(p->V) * kTileN, s));
+    int64_t ci = 0;
+    int n_blk = 0;
+    bool dw_written = false;
+    for (int64_t c0 = 0; c0 < p->N; c0 += C, ++ci) {
+        const int64_t cc = std::min(C, p->N - c0);
+        const int64_t slot = ci % kDwGroup;
+        if (!one_plan) KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.plan_off, w.plan_ent, s));
+        const int32_t* c_off = w.plan_off + (one_plan ? (c0 / kTileM) * plan_stride : 0);
+        // The chunk's logits, once: loss terms and z^T, which the gradient tile then reads.
+        Shape shc = sh;
+        shc.N = cc;
+        const int nvs = fwd_vsplits(cc, p->V);
+        KD_TRY(launch_fwd(shc, (const char*)H + c0 * p->d * es, W, c_off, w.plan_ent, nvs, w.part, w.zk + c0 * p->K,
+                          w.zt, w.ldzt, s));
+        int nb = 0;
+        KD_TRY(launch_combine(shc, w.part, 2 * nvs, w.zk + c0 * p->K, (const char*)tlog + c0 * p->K * ets, lse + c0,
+                              row_kl ? row_kl + c0 : nullptr, w.blk_sum + n_blk, &nb, s));
+        n_blk += nb;
+        KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
+                                (char*)w.HT + slot * C8 * es, w.ldgt, round_up(cc, 8), s));
+        KD_TRY(launch_grad_z(sh, w.zt, w.ldzt, 0, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.plan_ent, w.Gc,
+                             (char*)w.GT + slot * C8 * es, w.ldgt, s));
+        KD_TRY(launch_dh(sh, w.Gc, 0, nullptr, w.WT, c0, cc, w.n_split, w.dh_part, dH, s));
+        if (slot == kDwGroup - 1 || c0 + cc >= p->N) {
+            KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * C8 + cc, acc0 || dw_written, dW, s));
+            dw_written = true;
+        }
+    }
+    KD_TRY(launch_loss_final(sh, w.blk_sum, n_blk, loss, s));
     return KD_OK;
 }
 

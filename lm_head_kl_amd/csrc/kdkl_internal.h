@@ -33,6 +33,7 @@ enum Kind : int {
     kKindDenseLogits,
     kKindDenseRows,
     kKindSumRows,
+    kKindGradZ,
     kNumKinds
 };
 // Bracket one launch on stream s with timing events (no-ops unless timing is enabled).
@@ -62,11 +63,12 @@ hipError_t launch_teacher_prob(const void* tlog, Dt tdt, int64_t row0, int64_t r
 hipError_t launch_validate(const int32_t* idx, int64_t N, int64_t K, int64_t V, uint32_t* status,
                            hipStream_t s);
 
-// Fused forward over all N rows: per (row block, vocab split) partial (max, sum) in the
-// log2 domain, and zk at every cached id.
+// Fused forward over the sh.N rows of H: per (row block, vocab split) partial (max, sum) in
+// the log2 domain, and zk at every cached id. With zt not null the logits are also stored
+// transposed, z^T [Vp][ldzt] (columns: rows of H), for the paths that keep them.
 hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32_t* plan_off,
                       const uint32_t* plan_ent, int n_vsplit, float2* part, float* zk,
-                      hipStream_t s);
+                      float* zt, int64_t ldzt, hipStream_t s);
 
 // Merge partials into lse, compute KL_n (row_kl) and per-block fp64 partial sums.
 hipError_t launch_combine(const Shape& sh, const float2* part, int n_part, const float* zk,
@@ -86,6 +88,13 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
                            const float* pt, const float* grad_loss, int64_t c0, int64_t cc,
                            const int32_t* plan_off, const uint32_t* plan_ent, void* Gc,
                            void* GT, int64_t ldgt, hipStream_t s);
+
+// The same G_c and G_c^T as launch_bwd_grad, from stored logits z^T [Vp][ldzt] (chunk row r
+// in column zt_col0 + r) instead of recomputing them.
+hipError_t launch_grad_z(const Shape& sh, const float* zt, int64_t ldzt, int64_t zt_col0,
+                         const float* lse, const float* pt, const float* grad_loss, int64_t c0,
+                         int64_t cc, const int32_t* plan_off, const uint32_t* plan_ent, void* Gc,
+                         void* GT, int64_t ldgt, hipStream_t s);
 
 // dst[c][r] = src[r][c] (r < rows), zero for rows <= r < rows_pad; cols, rows_pad multiples of 8.
 hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst,

@@ -250,8 +250,10 @@ struct FwdArgs {
     int n_vt;
     int Q;          // vocab lanes: unit (rb, q) takes vocab tiles q, q + Q, q + 2Q, ...
     int64_t n_unit; // row blocks * Q
-    float2* part;   // [2Q][N]: per (lane, wave column) partial (max, sum) of each row
+    float2* part;   // [2Q][N]: per (lane, wave row) partial (max, sum) of each row
     float* zk;
+    float* zt;      // if not null, the logits are also stored transposed: z^T [Vp][ldzt]
+    int64_t ldzt;
 };
 
 // Persistent forward. Units (row block, vocab lane) are ordered row-block major. XCD x
@@ -263,7 +265,7 @@ struct FwdArgs {
 // entries and columns are tokens. Each lane then holds 64 vocabulary entries of each of its
 // 4 token columns, so the per-token (max, sum) over the vocabulary is folded inside the lane,
 // and lanes only meet once per unit.
-template <typename T>
+template <typename T, bool ZT>
 __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
     const WaveId id;
@@ -293,8 +295,9 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
             const WaveId ie = id.fresh();
 
             // Gather z at the cached ids of this (row block, vocab tile): two passes of 128
-            // vocabulary rows staged in LDS.
-            if (e1 > e0) {
+            // vocabulary rows staged in LDS. The paths that keep the logits also store the
+            // staged rows as z^T, a wave writing 1 KB of one row per step.
+            if (ZT || e1 > e0) {
 #pragma unroll
                 for (int pq = 0; pq < 2; ++pq) {
 #pragma unroll
@@ -317,6 +320,16 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
                         if (((c >> 6) & 1) != pq) continue;
                         const int r = en & 255, k = (int)(en >> 16);
                         a.zk[(m0 + r) * a.K + k] = stage[st_idx(st_row(c), r)];
+                    }
+                    if constexpr (ZT) {
+#pragma unroll 8
+                        for (int k = 0; k < 32; ++k) {
+                            const int it = ie.tid + NTHR * k;
+                            const int sr = it >> 6, tok = (it & 63) * 4;
+                            const int64_t v = n0 + (sr >> 6) * 128 + pq * 64 + (sr & 63);
+                            if (v < a.V && m0 + tok < a.N)
+                                *(f32x4*)(a.zt + v * a.ldzt + m0 + tok) = *(const f32x4*)(stage + st_idx(sr, tok));
+                        }
                     }
                     __syncthreads();
                 }
@@ -482,6 +495,8 @@ struct GradArgs {
     void* G;     // K-blocked [Vp/256][cc][256]: entry (t, v) at ((v/256)*cc + t)*256 + v%256
     void* GT;    // [Vp][ldgt]: G transposed, columns [cc, ccp) zero; nullptr to skip
     int64_t ldgt, ccp;
+    const float* zt;  // stored logits z^T [Vp][ldzt] (k_grad_z), chunk columns from zt_col0
+    int64_t ldzt, zt_col0;
 };
 
 template <typename T>
@@ -495,6 +510,61 @@ __device__ __forceinline__ void store8(T* dst, const float (&x)[8]) {
         *(f32x4*)dst = f32x4{x[0], x[1], x[2], x[3]};
         *(f32x4*)(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
     }
+}
+
+// Second half of a gradient pass, once the pass's 128 vocabulary rows of gs*softmax are staged:
+// subtract gs*p_t at the cached ids that fall in the pass, then write the rows of G (K-blocked)
+// and of G^T. Ends with a barrier, so the stage may be refilled.
+template <typename T>
+__device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, int pq, const WaveId& ie, int vt,
+                                              int64_t r0, int64_t n0, int e0, int e1, uint32_t my_en, float my_pt,
+                                              float gs) {
+    if (my_en != 0xffffffffu && ((my_en >> 14) & 1) == (uint32_t)pq) {
+        const int r = my_en & 255, c = (my_en >> 8) & 255;
+        stage[st_idx(st_row(c), r)] -= gs * my_pt;
+    }
+    for (int i = e0 + NTHR + ie.tid; i < e1; i += NTHR) {
+        const uint32_t en = a.ent[i];
+        const int c = (en >> 8) & 255;
+        if (((c >> 6) & 1) != pq) continue;
+        const int r = en & 255, k = (int)(en >> 16);
+        stage[st_idx(st_row(c), r)] -= gs * a.pt[(r0 + r) * a.K + k];
+    }
+    __syncthreads();
+    // G rows: token tl, group g of 8 vocabulary entries (stage rows 8g .. 8g+7). Eight
+    // consecutive lanes cover one token's 64 entries of a half: a whole 128-byte line.
+#pragma unroll 4
+    for (int it8 = 0; it8 < 16; ++it8) {
+        const int it = ie.tid + NTHR * it8;
+        const int g = it & 15, tl = it >> 4;
+        const int64_t tr = r0 + tl;
+        if (tr < a.cc) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = stage[st_idx(8 * g + u, tl)];
+            const int vb = (g >> 3) * 128 + pq * 64 + (g & 7) * 8;
+            store8<T>((T*)a.G + ((int64_t)vt * a.cc + tr) * kTileN + vb, x);
+        }
+    }
+    // G^T rows: vocabulary entry of stage row sr, group cb of 8 tokens; 32 lanes write a row's
+    // 256 tokens.
+    if (a.GT) {
+#pragma unroll 4
+        for (int it8 = 0; it8 < 16; ++it8) {
+            const int it = ie.tid + NTHR * it8;
+            const int sr = it >> 5, cb = it & 31;
+            const int64_t tr = r0 + cb * 8;
+            if (tr < a.ccp) {
+                const float* row = stage + sr * SST;
+                const f32x4 v0 = *(const f32x4*)(row + ((cb * 8) ^ st_swz(sr)));
+                const f32x4 v1 = *(const f32x4*)(row + ((cb * 8 + 4) ^ st_swz(sr)));
+                const float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                const int vr = (sr >> 6) * 128 + pq * 64 + (sr & 63);
+                store8<T>((T*)a.GT + (n0 + vr) * a.ldgt + tr, x);
+            }
+        }
+    }
+    __syncthreads();
 }
 
 template <typename T>
@@ -554,53 +624,78 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
                 }
             }
             __syncthreads();
-            if (my_en != 0xffffffffu && ((my_en >> 14) & 1) == (uint32_t)pq) {
-                const int r = my_en & 255, c = (my_en >> 8) & 255;
-                stage[st_idx(st_row(c), r)] -= gs * my_pt;
-            }
-            for (int i = e0 + NTHR + ie.tid; i < e1; i += NTHR) {
-                const uint32_t en = a.ent[i];
-                const int c = (en >> 8) & 255;
-                if (((c >> 6) & 1) != pq) continue;
-                const int r = en & 255, k = (int)(en >> 16);
-                stage[st_idx(st_row(c), r)] -= gs * a.pt[(r0 + r) * a.K + k];
-            }
-            __syncthreads();
-            // G rows: token tl, group g of 8 vocabulary entries (stage rows 8g .. 8g+7). Eight
-            // consecutive lanes cover one token's 64 entries of a half: a whole 128-byte line.
-#pragma unroll 4
-            for (int it8 = 0; it8 < 16; ++it8) {
-                const int it = ie.tid + NTHR * it8;
-                const int g = it & 15, tl = it >> 4;
-                const int64_t tr = r0 + tl;
-                if (tr < a.cc) {
-                    float x[8];
-#pragma unroll
-                    for (int u = 0; u < 8; ++u) x[u] = stage[st_idx(8 * g + u, tl)];
-                    const int vb = (g >> 3) * 128 + pq * 64 + (g & 7) * 8;
-                    store8<T>((T*)a.G + ((int64_t)vt * a.cc + tr) * kTileN + vb, x);
-                }
-            }
-            // G^T rows: vocabulary entry of stage row sr, group cb of 8 tokens; 32 lanes write a
-            // row's 256 tokens.
-            if (a.GT) {
-#pragma unroll 4
-                for (int it8 = 0; it8 < 16; ++it8) {
-                    const int it = ie.tid + NTHR * it8;
-                    const int sr = it >> 5, cb = it & 31;
-                    const int64_t tr = r0 + cb * 8;
-                    if (tr < a.ccp) {
-                        const float* row = stage + sr * SST;
-                        const f32x4 v0 = *(const f32x4*)(row + ((cb * 8) ^ st_swz(sr)));
-                        const f32x4 v1 = *(const f32x4*)(row + ((cb * 8 + 4) ^ st_swz(sr)));
-                        const float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                        const int vr = (sr >> 6) * 128 + pq * 64 + (sr & 63);
-                        store8<T>((T*)a.GT + (n0 + vr) * a.ldgt + tr, x);
-                    }
-                }
-            }
-            __syncthreads();
+            grad_pass_out<T>(a, stage, pq, ie, vt, r0, n0, e0, e1, my_en, my_pt, gs);
         }
+    }
+}
+
+// Gradient tile from stored logits z^T (forward-chunked and single-pass paths): the same G and
+// G^T as k_bwd_grad, with the tile read from memory instead of recomputed. HBM-bound: it reads
+// 4 bytes and writes 2 x 2 bytes per entry.
+template <typename T>
+__global__ __launch_bounds__(256) void k_grad_z(GradArgs a) {
+    __shared__ u32x4 L[LDS_CHUNKS + kTileM / 4];
+    float* stage = (float*)L;
+    float* lse2 = (float*)(L + LDS_CHUNKS);
+    const WaveId id;
+    const int64_t n_tiles = (int64_t)a.n_vt * a.n_rbc;
+    const int64_t t = xcd_tile(blockIdx.x, n_tiles);
+    if (t >= n_tiles) return;
+    const int vt = (int)(t / a.n_rbc), rb = (int)(t % a.n_rbc);
+    const int64_t r0 = (int64_t)rb * kTileM;
+    const int64_t n0 = (int64_t)vt * kTileN;
+    {
+        const int64_t r = r0 + id.tid;
+        lse2[id.tid] = r < a.cc ? a.lse[a.c0 + r] * kLog2e : 0.f;
+    }
+    const float gs = (a.grad ? a.grad[0] : 1.f) * a.gsc;
+    const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
+    const int e0 = off[vt], e1 = off[vt + 1];
+    uint32_t my_en = 0xffffffffu;
+    float my_pt = 0.f;
+    if (e0 + id.tid < e1) {
+        my_en = a.ent[e0 + id.tid];
+        my_pt = a.pt[(r0 + (my_en & 255)) * a.K + (my_en >> 16)];
+    }
+    __syncthreads();
+    // Vector loads when every chunk column offset is 16-byte aligned (uniform).
+    const bool vec = ((a.ldzt | (a.zt_col0 + r0)) & 3) == 0;
+    for (int pq = 0; pq < 2; ++pq) {
+        // 128 vocabulary rows x 256 tokens; a wave reads 1 KB of one z^T row per step. All
+        // of a pass's loads are issued before the first is used.
+        f32x4 z[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            const int it = id.tid + NTHR * k;
+            const int sr = it >> 6, tok = (it & 63) * 4;
+            const int64_t v = n0 + (sr >> 6) * 128 + pq * 64 + (sr & 63);
+            z[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (v < a.V && r0 + tok < a.cc) {
+                const float* zr = a.zt + v * a.ldzt + a.zt_col0 + r0 + tok;
+                if (vec) {
+                    z[k] = *(const f32x4*)zr;
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (r0 + tok + u < a.cc) z[k][u] = zr[u];
+                }
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            const int it = id.tid + NTHR * k;
+            const int sr = it >> 6, tok = (it & 63) * 4;
+            const int64_t v = n0 + (sr >> 6) * 128 + pq * 64 + (sr & 63);
+            f32x4 g = {0.f, 0.f, 0.f, 0.f};
+            if (v < a.V) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (r0 + tok + u < a.cc) g[u] = gs * exp2_fast(fmaf(z[k][u], a.c, -lse2[tok + u]));
+            }
+            *(f32x4*)(stage + st_idx(sr, tok)) = g;
+        }
+        __syncthreads();
+        grad_pass_out<T>(a, stage, pq, id, vt, r0, n0, e0, e1, my_en, my_pt, gs);
     }
 }
 
@@ -970,7 +1065,8 @@ hipError_t launch_validate(const int32_t* idx, int64_t N, int64_t K, int64_t V, 
 }
 
 hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32_t* plan_off,
-                      const uint32_t* plan_ent, int n_vsplit, float2* part, float* zk, hipStream_t s) {
+                      const uint32_t* plan_ent, int n_vsplit, float2* part, float* zk, float* zt, int64_t ldzt,
+                      hipStream_t s) {
     FwdArgs a;
     a.H = H;
     a.W = W;
@@ -986,13 +1082,22 @@ hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32
     a.n_unit = ((sh.N + kTileM - 1) / kTileM) * (int64_t)n_vsplit;
     a.part = part;
     a.zk = zk;
+    a.zt = zt;
+    a.ldzt = ldzt;
     // One workgroup per CU (the LDS use allows no more), a multiple of 8 for the XCD bands.
     const int64_t cus = std::max(8, device_cus() / 8 * 8);
     const unsigned grid = (unsigned)std::min<int64_t>(cus, 8 * ((a.n_unit + 7) / 8));
-    if (sh.act == Dt::BF16)
-        KD_LAUNCH(kKindFwd, s, k_fwd<bf16_t>, dim3(grid), dim3(NTHR), 0, s, a);
-    else
-        KD_LAUNCH(kKindFwd, s, k_fwd<float>, dim3(grid), dim3(NTHR), 0, s, a);
+    if (sh.act == Dt::BF16) {
+        if (zt)
+            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, true>), dim3(grid), dim3(NTHR), 0, s, a);
+        else
+            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, false>), dim3(grid), dim3(NTHR), 0, s, a);
+    } else {
+        if (zt)
+            KD_LAUNCH(kKindFwd, s, (k_fwd<float, true>), dim3(grid), dim3(NTHR), 0, s, a);
+        else
+            KD_LAUNCH(kKindFwd, s, (k_fwd<float, false>), dim3(grid), dim3(NTHR), 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -1017,6 +1122,8 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
     GradArgs a;
     a.H = H;
     a.W = W;
+    a.zt = nullptr;
+    a.ldzt = a.zt_col0 = 0;
     a.d = sh.d;
     a.V = sh.V;
     a.K = sh.K;
@@ -1042,6 +1149,41 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
         KD_LAUNCH(kKindBwdGrad, s, k_bwd_grad<bf16_t>, grid, dim3(NTHR), 0, s, a);
     else
         KD_LAUNCH(kKindBwdGrad, s, k_bwd_grad<float>, grid, dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_grad_z(const Shape& sh, const float* zt, int64_t ldzt, int64_t zt_col0, const float* lse,
+                         const float* pt, const float* grad_loss, int64_t c0, int64_t cc, const int32_t* plan_off,
+                         const uint32_t* plan_ent, void* Gc, void* GT, int64_t ldgt, hipStream_t s) {
+    GradArgs a;
+    a.H = nullptr;
+    a.W = nullptr;
+    a.zt = zt;
+    a.ldzt = ldzt;
+    a.zt_col0 = zt_col0;
+    a.d = sh.d;
+    a.V = sh.V;
+    a.K = sh.K;
+    a.c = kLog2e / sh.T;
+    a.gsc = sh.T / sh.n_norm;
+    a.grad = grad_loss;
+    a.lse = lse;
+    a.pt = pt;
+    a.c0 = c0;
+    a.cc = cc;
+    a.off = plan_off;
+    a.ent = plan_ent;
+    a.n_vt = (int)((sh.V + kTileN - 1) / kTileN);
+    a.n_rbc = (int)((cc + kTileM - 1) / kTileM);
+    a.G = Gc;
+    a.GT = GT;
+    a.ldgt = ldgt;
+    a.ccp = round_up(cc, 8);
+    const dim3 grid(grid_xcd((int64_t)a.n_vt * a.n_rbc));
+    if (sh.act == Dt::BF16)
+        KD_LAUNCH(kKindGradZ, s, k_grad_z<bf16_t>, grid, dim3(NTHR), 0, s, a);
+    else
+        KD_LAUNCH(kKindGradZ, s, k_grad_z<float>, grid, dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 

@@ -82,6 +82,27 @@ def test_workspace_queries():
     assert dn >= 2 * 512 * 32000 * 4
 
 
+def test_stored_logit_workspaces():
+    """The forward-chunked path keeps every logit, so its workspace grows by at least 4 V bytes
+    per row; the single-pass path keeps one chunk's logits, so N enters only through O(N*K)."""
+    L = _lib.lib()
+
+    def ch(**kw):
+        return L.kd_chunked_workspace_bytes(ctypes.byref(prob(**kw)))
+
+    def sp(**kw):
+        return L.kd_fused_fwdbwd_workspace_bytes(ctypes.byref(prob(**kw)))
+
+    assert L.kd_chunked_workspace_bytes(None) == 0 and L.kd_fused_fwdbwd_workspace_bytes(None) == 0
+    assert ch(K=0) == 0 and sp(T=0.0) == 0
+    a, b = ch(N=8192), ch(N=16384)
+    assert b - a >= 8192 * 32000 * 4
+    a, b, c = (sp(N=n, chunk=1024) for n in (8192, 16384, 24576))
+    assert abs((c - b) - (b - a)) <= 4096 and (b - a) / 8192 < 100 * 4 * 4 + 64
+    # one chunk of fp32 logits on top of the fused backward's buffers
+    assert sp(chunk=1024) >= ws_bytes(chunk=1024) + 1024 * 32000 * 4 - 8192 * 100 * 8
+
+
 # ------------------------------------------------------------------ argument checks
 # These pass fake device addresses; the checks must reject the call before any launch.
 # They are skipped where a GPU is visible, so that a checking bug can never turn into a
