@@ -215,6 +215,23 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
                              kd_stream stream);
 
 /*
+ * Offline top-K cache producer: the step before the loss, run once over the teacher's logits.
+ * For each of N rows of logits (row n at logits + n*ld, V entries, dtype KD_FP32 or KD_BF16),
+ * writes the K largest values and their token ids, largest first; equal values are ordered by
+ * the lower token id, and -0 counts as equal to +0. Source: aiexpert.news "Making knowledge
+ * distillation cheap enough to run in production", paragraph on the first fix (run the
+ * teacher once, cache the 100 most probable tokens per position, reuse the cache); the
+ * dailyai.com.br launch note, section "As duas inovacoes", item 1.
+ *   logits [N][ld]   device, dtype (a NaN ranks below every number)
+ *   idx [N][K]       device int32, written
+ *   values [N][K]    device, same dtype as logits, written (copies of the selected entries)
+ *   limits: 1 <= K <= min(V, 1024), V <= 4194304, ld >= V. Needs no workspace.
+ * The output can be passed as (idx, tlog) to the loss calls, with tlogit = dtype.
+ */
+kd_status kd_topk_cache(const void* logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, int64_t K,
+                        int32_t* idx, void* values, kd_stream stream);
+
+/*
  * Per-kernel timing (profiling; off by default). While enabled, every kernel the library
  * launches, from any thread, is bracketed by two HIP events recorded on the launch's own
  * stream. kd_timing_read waits for the recorded events. It then returns, for one kernel kind,

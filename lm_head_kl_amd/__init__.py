@@ -29,6 +29,7 @@ __all__ = [
     "dense_kl",
     "chunked_kl",
     "fused_kl_fwdbwd",
+    "topk_cache",
     "fused_workspace_bytes",
     "dense_workspace_bytes",
     "chunked_workspace_bytes",
@@ -214,6 +215,26 @@ def fused_kl_fwdbwd(H, W, idx, tlog, T: float = 1.0, chunk: int = 2048, grad_los
     Returns (loss, lse, row_kl, dH, dW)."""
     return _one_call("kd_fused_kl_fwdbwd", "kd_fused_fwdbwd_workspace_bytes", H, W, idx, tlog, T, chunk, grad_loss,
                      n_norm, flags, want_row_kl, dW, workspace)
+
+
+def topk_cache(logits: torch.Tensor, K: int):
+    """kd_topk_cache: the offline teacher cache. logits [N, V] (bf16 or fp32, rows may be
+    strided) -> (idx [N, K] int32, values [N, K] in the logits' dtype), largest first, ties by
+    the lower token id."""
+    if logits.dtype not in _DT:
+        raise KdError(3, "topk_cache", "logits must be bfloat16 or float32")
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise KdError(2, "topk_cache", "logits must be [N, V] with contiguous rows")
+    if logits.device.type != "cuda":
+        raise KdError(1, "topk_cache", "logits must be on a GPU")
+    dev = logits.device
+    N, V = logits.shape
+    idx = torch.empty((N, K), dtype=torch.int32, device=dev)
+    vals = torch.empty((N, K), dtype=logits.dtype, device=dev)
+    code = _lib.lib().kd_topk_cache(_ptr(logits), _DT[logits.dtype], N, V, logits.stride(0), int(K), _ptr(idx),
+                                    _ptr(vals), _stream(dev))
+    _lib.check(code, "kd_topk_cache")
+    return idx, vals
 
 
 class FusedKL(torch.autograd.Function):

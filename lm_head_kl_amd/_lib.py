@@ -40,6 +40,7 @@ EXPORTS = (
     "kd_chunked_kl",
     "kd_fused_fwdbwd_workspace_bytes",
     "kd_fused_kl_fwdbwd",
+    "kd_topk_cache",
     "kd_timing_enable",
     "kd_timing_kinds",
     "kd_timing_name",
@@ -103,6 +104,9 @@ def lib() -> ctypes.CDLL:
     for name in ("kd_chunked_kl", "kd_fused_kl_fwdbwd"):
         getattr(L, name).restype = ctypes.c_int
         getattr(L, name).argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    i64 = ctypes.c_int64
+    L.kd_topk_cache.restype = ctypes.c_int
+    L.kd_topk_cache.argtypes = [vp, ctypes.c_int32, i64, i64, i64, i64, vp, vp, vp]
     L.kd_timing_enable.restype = ctypes.c_int
     L.kd_timing_enable.argtypes = [ctypes.c_int]
     L.kd_timing_kinds.restype = ctypes.c_int

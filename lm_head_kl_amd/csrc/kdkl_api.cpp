@@ -399,6 +399,19 @@ kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const i
     return KD_OK;
 }
 
+kd_status kd_topk_cache(const void* logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, int64_t K,
+                        int32_t* idx, void* values, kd_stream stream) {
+    if (!logits || !idx || !values) return KD_ERR_NULL;
+    if (dtype != KD_FP32 && dtype != KD_BF16) return KD_ERR_DTYPE;
+    if (N < 1 || N > 0x7FFFFFFF || V < 1 || V > kMaxTopV || K < 1 || K > V || K > kMaxTopK || ld < V)
+        return KD_ERR_SHAPE;
+    const size_t es = esize(dtype);
+    if (!aligned(logits, es) || !aligned(values, es) || !aligned(idx, 4)) return KD_ERR_VALUE;
+    (void)hipGetLastError();
+    KD_TRY(launch_topk(dtype == KD_BF16 ? Dt::BF16 : Dt::F32, logits, ld, N, V, K, idx, values, (hipStream_t)stream));
+    return KD_OK;
+}
+
 size_t kd_chunked_workspace_bytes(const kd_problem* p) {
     if (check_problem(p) != KD_OK) return 0;
     return layout_stored(p, nullptr, true).bytes;

@@ -13,6 +13,8 @@ namespace kdkl {
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
 constexpr int kMaxK = 128;
+constexpr int kMaxTopK = 1024;  // largest K of the offline top-K producer
+constexpr int64_t kMaxTopV = 1 << 22;  // token ids fit in the producer's 22-bit key field
 constexpr int kMaxVTiles = 16384;  // plan kernel keeps one LDS counter per vocab tile
 
 enum class Dt : int { F32 = 0, BF16 = 1 };
@@ -34,6 +36,7 @@ enum Kind : int {
     kKindDenseRows,
     kKindSumRows,
     kKindGradZ,
+    kKindTopk,
     kNumKinds
 };
 // Bracket one launch on stream s with timing events (no-ops unless timing is enabled).
@@ -95,6 +98,11 @@ hipError_t launch_grad_z(const Shape& sh, const float* zt, int64_t ldzt, int64_t
                          const float* lse, const float* pt, const float* grad_loss, int64_t c0,
                          int64_t cc, const int32_t* plan_off, const uint32_t* plan_ent, void* Gc,
                          void* GT, int64_t ldgt, hipStream_t s);
+
+// Offline cache: per row of X [N][ld] (V entries), the K largest values and their ids, largest
+// first, ties in lower-id order.
+hipError_t launch_topk(Dt dt, const void* X, int64_t ld, int64_t N, int64_t V, int64_t K, int32_t* idx,
+                       void* val, hipStream_t s);
 
 // dst[c][r] = src[r][c] (r < rows), zero for rows <= r < rows_pad; cols, rows_pad multiples of 8.
 hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst,

@@ -1001,6 +1001,266 @@ __global__ __launch_bounds__(256) void k_dense_rows(float* __restrict__ Z, float
 }
 
 // ------------------------------------------------------------------------------------------
+// Offline top-K cache: per row of teacher logits, the K largest values and their token ids,
+// largest first, equal values in lower-id order. Source: "Making knowledge distillation cheap
+// enough to run in production" (aiexpert.news), paragraph on the first fix (run the teacher
+// once and keep the top-100 tokens per position).
+//
+// One workgroup per row. Every entry gets a 54-bit key that orders (value desc, id asc):
+//   key32 = order-preserving image of the fp32 value (-0 folded onto +0, NaN lowest), and
+//   ck = key32 << 22 | (2^22 - 1 - id), unique per entry, larger is better;
+// the answer is the K entries with the largest ck. Fast path, two reads of the row:
+//   1. each thread keeps the largest value of m interleaved groups of its entries (G = 256 m
+//      >= 4K groups in all); the K-th largest group maximum L is a lower bound of the K-th
+//      largest value, since the K groups at or above it each hold an entry >= L;
+//   2. every entry >= L is collected in LDS (little more than K for logit rows), sorted by ck
+//      (bitonic) and the first K written out.
+// If more than kTopkSort entries pass the bound (rows full of equal values), a radix select
+// takes over: levels of 11 bits histogram the entries matching the prefix fixed so far until
+// the bin holding the K-th largest has at most kTopkCap entries, then one more read collects
+// everything at or above that bin.
+
+constexpr int kTopkBits = 11, kTopkBins = 1 << kTopkBits;
+constexpr int kTopkCap = 2048;   // candidates kept from the threshold bin (radix path)
+constexpr int kTopkSort = 4096;  // sort buffer: a power of two >= kTopkCap + kMaxTopK
+static_assert(kTopkSort >= kTopkCap + kMaxTopK && (kTopkSort & (kTopkSort - 1)) == 0, "sort buffer");
+constexpr int kTopkMaxGroups = 8;  // group maxima per thread (G = 256 m groups, m <= 8)
+
+__device__ __forceinline__ uint32_t order_key(uint32_t bits) {
+    if (bits == 0x80000000u) bits = 0u;                     // -0 ranks with +0
+    if ((bits & 0x7FFFFFFFu) > 0x7F800000u) return 0u;      // NaN ranks last
+    return (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+}
+
+template <typename T>
+__device__ __forceinline__ uint32_t fp32_bits(T x);
+template <> __device__ __forceinline__ uint32_t fp32_bits<bf16_t>(bf16_t x) { return (uint32_t)x << 16; }
+template <> __device__ __forceinline__ uint32_t fp32_bits<float>(float x) { return __float_as_uint(x); }
+
+// Calls f(v, bits) for every entry of row x[0..V) handled by this thread, with 16-byte loads
+// for the aligned body; j counts this thread's loads (for the group choice).
+template <typename T, typename F>
+__device__ __forceinline__ void topk_scan(const T* x, int V, F&& f) {
+    constexpr int VEC = 16 / sizeof(T);
+    const int tid = threadIdx.x;
+    const int head = (int)(((16 - ((uintptr_t)x & 15)) & 15) / sizeof(T));
+    const int h = head < V ? head : V;
+    if (tid < h) f(tid, fp32_bits<T>(x[tid]), 0);
+    const int nvec = (V - h) / VEC;
+    const u32x4* xv = (const u32x4*)(x + h);
+    int j = 0;
+    for (int q = tid; q < nvec; q += NTHR, ++j) {
+        const u32x4 c = xv[q];
+        const int v0 = h + q * VEC;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                f(v0 + 2 * u, c[u] << 16, j);
+                f(v0 + 2 * u + 1, c[u] & 0xFFFF0000u, j);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) f(v0 + u, c[u], j);
+        }
+    }
+    for (int v = h + nvec * VEC + tid; v < V; v += NTHR) f(v, fp32_bits<T>(x[v]), 0);
+}
+
+// Largest value of each of m interleaved groups of this thread's entries (load j of the thread
+// goes to group j % m), four 16-byte loads in flight per lane.
+template <typename T>
+__device__ __forceinline__ void topk_scan_max(const T* x, int V, int m, float (&gmax)[kTopkMaxGroups]) {
+    constexpr int VEC = 16 / sizeof(T);
+    const int tid = threadIdx.x;
+    const int head = (int)(((16 - ((uintptr_t)x & 15)) & 15) / sizeof(T));
+    const int h = head < V ? head : V;
+    if (tid < h) gmax[0] = fmaxf(gmax[0], __uint_as_float(fp32_bits<T>(x[tid])));
+    const int nvec = (V - h) / VEC;
+    const u32x4* xv = (const u32x4*)(x + h);
+    auto vmax = [](const u32x4& c) {
+        float r;
+        if constexpr (sizeof(T) == 2) {
+            float a = fmaxf(__uint_as_float(c[0] << 16), __uint_as_float(c[0] & 0xFFFF0000u));
+            float b = fmaxf(__uint_as_float(c[1] << 16), __uint_as_float(c[1] & 0xFFFF0000u));
+            float e = fmaxf(__uint_as_float(c[2] << 16), __uint_as_float(c[2] & 0xFFFF0000u));
+            float f = fmaxf(__uint_as_float(c[3] << 16), __uint_as_float(c[3] & 0xFFFF0000u));
+            r = fmaxf(fmaxf(a, b), fmaxf(e, f));
+        } else {
+            r = fmaxf(fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1])),
+                      fmaxf(__uint_as_float(c[2]), __uint_as_float(c[3])));
+        }
+        return r;
+    };
+    int j = 0;
+    int q = tid;
+    for (; q + 3 * NTHR < nvec; q += 4 * NTHR) {
+        const u32x4 c0 = xv[q], c1 = xv[q + NTHR], c2 = xv[q + 2 * NTHR], c3 = xv[q + 3 * NTHR];
+        const float r[4] = {vmax(c0), vmax(c1), vmax(c2), vmax(c3)};
+#pragma unroll
+        for (int u = 0; u < 4; ++u, ++j) {
+            const int g = j % m;
+#pragma unroll
+            for (int t = 0; t < kTopkMaxGroups; ++t)
+                if (t == g) gmax[t] = fmaxf(gmax[t], r[u]);
+        }
+    }
+    for (; q < nvec; q += NTHR, ++j) {
+        const float r = vmax(xv[q]);
+        const int g = j % m;
+#pragma unroll
+        for (int t = 0; t < kTopkMaxGroups; ++t)
+            if (t == g) gmax[t] = fmaxf(gmax[t], r);
+    }
+    for (int v = h + nvec * VEC + tid; v < V; v += NTHR) gmax[0] = fmaxf(gmax[0], __uint_as_float(fp32_bits<T>(x[v])));
+}
+
+__device__ __forceinline__ uint64_t topk_ck(int v, uint32_t bits) {
+    return ((uint64_t)order_key(bits) << 22) | (uint64_t)(0x3FFFFF - v);
+}
+
+// Bitonic sort of a[0..P) descending (P a power of two), by all threads of the block.
+__device__ __forceinline__ void bitonic_desc(uint64_t* a, int P) {
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = threadIdx.x; i < P / 2; i += NTHR) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t a0 = a[lo], a1 = a[hi];
+                if ((a0 < a1) == desc) {
+                    a[lo] = a1;
+                    a[hi] = a0;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_topk(const T* __restrict__ X, int64_t ld, int64_t N, int V, int K,
+                                              int32_t* __restrict__ idx_out, T* __restrict__ val_out) {
+    __shared__ uint32_t hist[4][kTopkBins];
+    __shared__ uint64_t cand[kTopkSort];
+    __shared__ uint32_t wsum[NTHR];
+    __shared__ int s_bin, s_above, s_cnt, s_ncoll;
+    const int tid = threadIdx.x, w = tid >> 6;
+    const int64_t n = blockIdx.x;
+    const T* x = X + n * ld;
+    int nc = 0;
+    bool done = false;
+
+    // ---- fast path: lower bound from group maxima, then one collecting read. Both reads
+    // work on fp32 values (max and compare treat -0 as +0, as the key does); only the
+    // collected entries get their 54-bit keys.
+    {
+        const int m = min(kTopkMaxGroups, max(1, (4 * K + NTHR - 1) / NTHR));
+        float gmax[kTopkMaxGroups];
+#pragma unroll
+        for (int g = 0; g < kTopkMaxGroups; ++g) gmax[g] = -INFINITY;
+        topk_scan_max<T>(x, V, m, gmax);
+        const int G = NTHR * m;  // <= 2048 <= kTopkSort
+        int P = 1;
+        while (P < G) P <<= 1;
+#pragma unroll
+        for (int q = 0; q < kTopkMaxGroups; ++q)
+            if (q < m) cand[q * NTHR + tid] = (uint64_t)order_key(__float_as_uint(gmax[q]));
+        for (int i = G + tid; i < P; i += NTHR) cand[i] = 0ull;
+        __syncthreads();
+        bitonic_desc(cand, P);
+        const uint32_t Lk = (uint32_t)cand[K - 1];
+        // back to the value: keys >= 2^31 are non-negative floats
+        const float L = __uint_as_float(Lk & 0x80000000u ? (Lk & 0x7FFFFFFFu) : ~Lk);
+        if (tid == 0) s_ncoll = 0;
+        __syncthreads();
+        topk_scan<T>(x, V, [&](int v, uint32_t bits, int) {
+            if (__uint_as_float(bits) >= L) {
+                const int pos = atomicAdd(&s_ncoll, 1);
+                if (pos < kTopkSort) cand[pos] = topk_ck(v, bits);
+            }
+        });
+        __syncthreads();
+        nc = s_ncoll;
+        done = nc >= K && nc <= kTopkSort;  // fewer than K only if NaNs were skipped
+        __syncthreads();
+    }
+
+    // ---- radix select when too many entries passed the bound
+    if (!done) {
+        uint64_t prefix = 0;
+        int shift = 54, need = K;
+        while (true) {
+            const int wd = shift < kTopkBits ? shift : kTopkBits;
+            const int s = shift - wd;
+            for (int i = tid; i < 4 * kTopkBins; i += NTHR) (&hist[0][0])[i] = 0u;
+            __syncthreads();
+            topk_scan<T>(x, V, [&](int v, uint32_t bits, int) {
+                const uint64_t ck = topk_ck(v, bits);
+                if ((ck >> shift) == prefix) atomicAdd(&hist[w][(uint32_t)(ck >> s) & ((1u << wd) - 1u)], 1u);
+            });
+            __syncthreads();
+            // Bins of this level, highest first: thread t owns bins [8t, 8t+8) counted from the top.
+            constexpr int PER = kTopkBins / NTHR;
+            uint32_t mine[PER], tot = 0;
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                const int b = kTopkBins - 1 - (tid * PER + q);
+                mine[q] = hist[0][b] + hist[1][b] + hist[2][b] + hist[3][b];
+                tot += mine[q];
+            }
+            wsum[tid] = tot;
+            __syncthreads();
+            if (tid == 0) {  // exclusive scan of the 256 thread totals, from the top
+                uint32_t run = 0;
+                for (int t = 0; t < NTHR; ++t) {
+                    const uint32_t c = wsum[t];
+                    wsum[t] = run;
+                    run += c;
+                }
+            }
+            __syncthreads();
+            uint32_t above = wsum[tid];
+#pragma unroll
+            for (int q = 0; q < PER; ++q) {
+                if (above < (uint32_t)need && above + mine[q] >= (uint32_t)need) {
+                    s_bin = kTopkBins - 1 - (tid * PER + q);
+                    s_above = (int)above;
+                    s_cnt = (int)mine[q];
+                }
+                above += mine[q];
+            }
+            __syncthreads();
+            prefix = (prefix << wd) | (uint64_t)s_bin;
+            need -= s_above;
+            shift = s;
+            const int cnt = s_cnt;
+            __syncthreads();
+            if (cnt <= kTopkCap || shift == 0) break;
+        }
+        // Every entry at or above the threshold bin: K - need above it, the bin's own after.
+        if (tid == 0) s_ncoll = 0;
+        __syncthreads();
+        topk_scan<T>(x, V, [&](int v, uint32_t bits, int) {
+            const uint64_t ck = topk_ck(v, bits);
+            if ((ck >> shift) >= prefix) cand[atomicAdd(&s_ncoll, 1)] = ck;
+        });
+        __syncthreads();
+        nc = s_ncoll;
+    }
+
+    int P = 1;
+    while (P < nc) P <<= 1;
+    for (int i = nc + tid; i < P; i += NTHR) cand[i] = 0ull;  // below every real key
+    __syncthreads();
+    bitonic_desc(cand, P);
+    for (int k = tid; k < K; k += NTHR) {
+        const int v = 0x3FFFFF - (int)(cand[k] & 0x3FFFFFull);
+        idx_out[n * K + k] = v;
+        val_out[n * K + k] = x[v];
+    }
+}
+
+// ------------------------------------------------------------------------------------------
 // Launchers.
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -1184,6 +1444,18 @@ hipError_t launch_grad_z(const Shape& sh, const float* zt, int64_t ldzt, int64_t
         KD_LAUNCH(kKindGradZ, s, k_grad_z<bf16_t>, grid, dim3(NTHR), 0, s, a);
     else
         KD_LAUNCH(kKindGradZ, s, k_grad_z<float>, grid, dim3(NTHR), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(Dt dt, const void* X, int64_t ld, int64_t N, int64_t V, int64_t K, int32_t* idx, void* val,
+                       hipStream_t s) {
+    if (N > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (dt == Dt::BF16)
+        KD_LAUNCH(kKindTopk, s, k_topk<bf16_t>, dim3((unsigned)N), dim3(NTHR), 0, s, (const bf16_t*)X, ld, N, (int)V,
+                  (int)K, idx, (bf16_t*)val);
+    else
+        KD_LAUNCH(kKindTopk, s, k_topk<float>, dim3((unsigned)N), dim3(NTHR), 0, s, (const float*)X, ld, N, (int)V,
+                  (int)K, idx, (float*)val);
     return hipGetLastError();
 }
 

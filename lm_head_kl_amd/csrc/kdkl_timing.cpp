@@ -19,7 +19,7 @@ namespace {
 
 const char* const kNames[kNumKinds] = {
     "plan", "teacher_prob", "validate", "fwd", "combine", "loss_final", "bwd_grad", "transpose",
-    "dh", "dh_reduce", "dw", "dense_logits", "dense_rows", "sum_rows", "grad_z",
+    "dh", "dh_reduce", "dw", "dense_logits", "dense_rows", "sum_rows", "grad_z", "topk",
 };
 
 struct Rec {

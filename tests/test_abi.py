@@ -177,3 +177,18 @@ def test_workspace_and_alignment_rejected():
 
 def test_fp32_problem_is_valid():
     assert ws_bytes(act=KD_FP32, tlogit=KD_FP32, d=128, V=2048, K=16, N=256, chunk=64) > 0
+
+
+@nogpu
+@pytest.mark.parametrize("args,code", [
+    (dict(logits=None), 1), (dict(idx=None), 1), (dict(values=None), 1),
+    (dict(dtype=2), 3),
+    (dict(N=0), 2), (dict(V=0), 2), (dict(K=0), 2), (dict(K=1025, V=2000), 2), (dict(K=11, V=10), 2),
+    (dict(V=(1 << 22) + 1), 2), (dict(ld=99), 2),
+])
+def test_topk_bad_arguments(args, code):
+    a = dict(logits=F, dtype=KD_BF16, N=4, V=100, ld=100, K=10, idx=F, values=F)
+    a.update(args)
+    L = _lib.lib()
+    assert L.kd_topk_cache(a["logits"], a["dtype"], a["N"], a["V"], a["ld"], a["K"], a["idx"], a["values"],
+                           None) == code

@@ -1,0 +1,101 @@
+"""The offline top-K cache producer (kd_topk_cache) against the oracle's sort, bit for bit:
+ids and values, on random rows, rows full of ties, signed zeros and infinities, K at its limits,
+padded rows, and rows at the gpt-oss vocabulary size."""
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import lm_head_kl_amd as kd
+from gpu_helpers import say, to_torch
+
+pytestmark = pytest.mark.gpu
+
+
+def check(x: np.ndarray, K: int, dtype: str, label: str, ld: int = 0):
+    """x: fp32 values (exactly representable in dtype). Compares ids and values bitwise."""
+    say("topk", label, f"N={x.shape[0]} V={x.shape[1]} K={K} {dtype}")
+    N, V = x.shape
+    if dtype == "bf16":
+        store = datagen.bf16_bits(x)
+        assert np.array_equal(datagen.bf16_to_f32(store), x)
+    else:
+        store = x.astype(np.float32)
+    if ld > V:
+        pad = np.zeros((N, ld), store.dtype)
+        pad[:, :V] = store
+        dev = to_torch(pad)[:, :V]
+    else:
+        dev = to_torch(store)
+    idx, vals = kd.topk_cache(dev, K)
+    torch.cuda.synchronize()
+    want_idx, want_val = oracle.topk_cache(x, K)
+    got_idx = idx.cpu().numpy()
+    assert np.array_equal(got_idx, want_idx), label
+    got_val = vals.float().cpu().numpy()
+    # values are copies of the selected entries
+    assert np.array_equal(got_val.view(np.uint32), np.take_along_axis(x, want_idx.astype(np.int64), 1).view(np.uint32))
+
+
+def bf16_values(a):
+    return datagen.bf16_to_f32(datagen.bf16_bits(a.astype(np.float32)))
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_random_rows(dtype):
+    g = np.random.default_rng(11)
+    x = g.standard_normal((64, 2048)).astype(np.float32) * 3
+    if dtype == "bf16":
+        x = bf16_values(x)
+    check(x, 16, dtype, "random")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_ties_and_special_values(dtype):
+    g = np.random.default_rng(12)
+    rows = [
+        g.integers(-2, 3, 1000).astype(np.float32),                      # five distinct values
+        np.full(1000, 0.75, np.float32),                                  # every entry equal
+        np.where(g.random(1000) < 0.5, np.float32(-0.0), np.float32(0.0)),  # signed zeros only
+        np.concatenate([[np.inf, -np.inf, np.inf], g.standard_normal(997).astype(np.float32)]),
+    ]
+    x = np.stack(rows).astype(np.float32)
+    x[2, 500] = 1.0
+    if dtype == "bf16":
+        x = bf16_values(x)
+    for K in (1, 7, 100, 1000):
+        check(x, K, dtype, f"ties/special K={K}")
+
+
+def test_k_limits_and_padded_rows():
+    g = np.random.default_rng(13)
+    x = bf16_values(g.standard_normal((8, 3000)))
+    check(x, 1024, "bf16", "K=1024")
+    check(x[:, :777], 777, "bf16", "K=V")
+    check(x, 100, "bf16", "padded rows", ld=3072 + 8)
+
+
+@pytest.mark.parametrize("K", [100, 500])
+def test_gptoss_vocabulary(K):
+    """Rows at V = 201,088: Gaussian teacher logits in bf16 (many exact ties near the K-th) and
+    peaked rows whose top token is far above the rest."""
+    g = np.random.default_rng(14)
+    x = g.standard_normal((32, 201088)).astype(np.float32) * 2.0
+    x[::2, g.integers(0, 201088, 16)] += 12.0
+    check(bf16_values(x), K, "bf16", "gpt-oss vocabulary")
+
+
+def test_cache_feeds_the_loss():
+    """The produced cache used as the teacher of the fused loss gives the oracle's loss."""
+    p = datagen.make("tiny")
+    g = np.random.default_rng(15)
+    teacher = g.standard_normal((p.N, p.V)).astype(np.float32) * 2
+    idx, vals = kd.topk_cache(to_torch(teacher), p.K)
+    H, W = to_torch(p.H), to_torch(p.W)
+    f = kd.fused_kl_fwd(H, W, idx, vals, T=p.T, chunk=p.chunk)
+    torch.cuda.synchronize()
+    ci, cv = oracle.topk_cache(teacher, p.K)
+    ref = oracle.kl_dense(p.f64("H"), p.f64("W"), ci, cv, p.T)
+    assert abs(f.loss.item() - ref["loss"]) <= 1e-6 * abs(ref["loss"])
