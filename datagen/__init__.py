@@ -182,6 +182,28 @@ def flat_logits(n: int, K: int, var: float, rng: np.random.Generator) -> np.ndar
     return -np.sort(-(np.sqrt(var) * rng.standard_normal((n, K))), axis=1)
 
 
+def full_teacher_logits(kind: str, n: int, V: int, seed: int) -> np.ndarray:
+    """Full-vocabulary teacher logits (float32) for the top-K truncation study.
+    peaked: 6*N(0,1) logits with the largest raised so that it carries probability 0.6 (T = 1);
+            the next hundred tokens then hold almost all of the remaining mass;
+    flat:   0.5*N(0,1) logits, spread almost evenly over the vocabulary."""
+    g = np.random.default_rng([seed, 11, 0 if kind == "peaked" else 1])
+    x = g.standard_normal((n, V))
+    if kind == "peaked":
+        x *= 6.0
+        top = np.argmax(x, axis=1)
+        rows = np.arange(n)
+        rest = x.copy()
+        rest[rows, top] = -np.inf
+        mx = rest.max(axis=1)
+        x[rows, top] = mx + np.log(1.5 * np.exp(rest - mx[:, None]).sum(axis=1))
+    elif kind == "flat":
+        x *= 0.5
+    else:
+        raise ValueError(kind)
+    return x.astype(np.float32)
+
+
 @dataclass
 class Problem:
     """One synthetic workload. Arrays are in their storage dtype:

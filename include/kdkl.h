@@ -99,7 +99,7 @@ typedef enum kd_dtype {
 /*
  * Problem descriptor (host memory).
  *   N, d, V, K   sizes as above; limits: N >= 1, d >= 8 and d % 8 == 0, 1 <= V <= 4194304,
- *                1 <= K <= min(V, 128), N * K < 2^31, N * d < 2^31, V * d < 2^31.
+ *                1 <= K <= min(V, 1024), N * K < 2^31, N * d < 2^31, V * d < 2^31.
  *   chunk        rows per backward chunk (>= 1; N need not be a multiple). It bounds the
  *                backward's per-chunk gradient tile G_c [chunk, V] in the workspace. The
  *                forward keeps each projected tile in registers only, so its memory does not

@@ -12,7 +12,7 @@ namespace kdkl {
 // cached ids by the same tile, so both constants are shared with the host code.
 constexpr int kTileM = 256;
 constexpr int kTileN = 256;
-constexpr int kMaxK = 128;
+constexpr int kMaxK = 1024;  // cached entries per row
 constexpr int kMaxTopK = 1024;  // largest K of the offline top-K producer
 constexpr int64_t kMaxTopV = 1 << 22;  // token ids fit in the producer's 22-bit key field
 constexpr int kMaxVTiles = 16384;  // plan kernel keeps one LDS counter per vocab tile

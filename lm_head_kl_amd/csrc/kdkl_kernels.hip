@@ -193,17 +193,14 @@ __global__ __launch_bounds__(256) void k_teacher_prob(const void* __restrict__ t
     const int lane = threadIdx.x & 63;
     const int64_t n = row0 + (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (n >= row1) return;
-    double a0 = -INFINITY, a1 = -INFINITY;
-    if (lane < K) a0 = (double)load_t(tlog, tdt, n * K + lane) / T;
-    if (lane + 64 < K) a1 = (double)load_t(tlog, tdt, n * K + lane + 64) / T;
-    const double mx = wave_max_d(fmax(a0, a1));
+    double mx = -INFINITY;
+    for (int k = lane; k < K; k += 64) mx = fmax(mx, (double)load_t(tlog, tdt, n * K + k) / T);
+    mx = wave_max_d(mx);
     double s = 0.0;
-    if (lane < K) s += exp(a0 - mx);
-    if (lane + 64 < K) s += exp(a1 - mx);
+    for (int k = lane; k < K; k += 64) s += exp((double)load_t(tlog, tdt, n * K + k) / T - mx);
     const double lz = mx + log(wave_sum_d(s));
     float* o = pt + (n - row0) * K;
-    if (lane < K) o[lane] = (float)exp(a0 - lz);
-    if (lane + 64 < K) o[lane + 64] = (float)exp(a1 - lz);
+    for (int k = lane; k < K; k += 64) o[k] = (float)exp((double)load_t(tlog, tdt, n * K + k) / T - lz);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -409,22 +406,17 @@ __global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ part
             ms_merge(m, s, m2, s2);
         }
         const double lse_d = ((double)m + log2((double)s)) * kLn2;
-        double a0 = -INFINITY, a1 = -INFINITY;
-        if (lane < K) a0 = (double)load_t(tlog, tdt, n * K + lane) / T;
-        if (lane + 64 < K) a1 = (double)load_t(tlog, tdt, n * K + lane + 64) / T;
-        const double mx = wave_max_d(fmax(a0, a1));
+        const void* tl = tlog;
+        double mx = -INFINITY;
+        for (int k = lane; k < K; k += 64) mx = fmax(mx, (double)load_t(tl, tdt, n * K + k) / T);
+        mx = wave_max_d(mx);
         double se = 0.0;
-        if (lane < K) se += exp(a0 - mx);
-        if (lane + 64 < K) se += exp(a1 - mx);
+        for (int k = lane; k < K; k += 64) se += exp((double)load_t(tl, tdt, n * K + k) / T - mx);
         const double lz = mx + log(wave_sum_d(se));
         double term = 0.0;
-        if (lane < K) {
-            const double lp = a0 - lz;
-            term += exp(lp) * (lp - (double)zk[n * K + lane] / T + lse_d);
-        }
-        if (lane + 64 < K) {
-            const double lp = a1 - lz;
-            term += exp(lp) * (lp - (double)zk[n * K + lane + 64] / T + lse_d);
+        for (int k = lane; k < K; k += 64) {
+            const double lp = (double)load_t(tl, tdt, n * K + k) / T - lz;
+            term += exp(lp) * (lp - (double)zk[n * K + k] / T + lse_d);
         }
         const double kl = wave_sum_d(term);
         if (lane == 0) {
@@ -955,9 +947,11 @@ __global__ __launch_bounds__(256) void k_dense_rows(float* __restrict__ Z, float
     const int64_t Vp = ldz;
     // teacher distribution over the K cached entries
     double a = -INFINITY;
-    if (tid < K) a = (double)load_t(tlog, tdt, n * K + tid) / T;
+    for (int k = tid; k < K; k += NTHR) a = fmax(a, (double)load_t(tlog, tdt, n * K + k) / T);
     const double amax = block_max_d(a, red);
-    const double asum = block_sum_d(tid < K ? exp(a - amax) : 0.0, red);
+    double ae = 0.0;
+    for (int k = tid; k < K; k += NTHR) ae += exp((double)load_t(tlog, tdt, n * K + k) / T - amax);
+    const double asum = block_sum_d(ae, red);
     const double alz = amax + log(asum);
     // student log-normaliser over all V
     const double cT = 1.0 / T;
@@ -971,9 +965,9 @@ __global__ __launch_bounds__(256) void k_dense_rows(float* __restrict__ Z, float
     // expand the cached teacher into the dense grid
     for (int64_t v = tid; v < Vp; v += NTHR) pg[v] = 0.f;
     __syncthreads();
-    if (tid < K) {
-        const int v = idx[n * K + tid];
-        if (v >= 0 && v < V) pg[v] = (float)exp(a - alz);  // out-of-range ids are skipped
+    for (int k = tid; k < K; k += NTHR) {
+        const int v = idx[n * K + k];
+        if (v >= 0 && v < V) pg[v] = (float)exp((double)load_t(tlog, tdt, n * K + k) / T - alz);  // out-of-range ids are skipped
     }
     __syncthreads();
     // KL over the whole vocabulary (terms with P = 0 contribute 0)

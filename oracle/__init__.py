@@ -259,3 +259,40 @@ def topk_cache(logits, K: int):
     N, V = x.shape
     order = np.lexsort((np.broadcast_to(np.arange(V), x.shape), -x), axis=1)[:, :K]
     return order.astype(np.int32), np.take_along_axis(x, order, axis=1)
+
+
+def truncation_terms(H, W, teacher, K: int, T: float = 1.0) -> dict:
+    """What caching only the top K of a full-vocabulary teacher changes, per row.
+
+    The pages name the top-K cache as the method's remaining restriction: it drops the tail
+    of the teacher's distribution, which matters little for peaked positions and is lossy
+    where the teacher spreads its mass over hundreds of candidates. Source: "Making knowledge
+    distillation cheap enough to run in production", paragraph on the remaining restriction.
+
+    With p_t = softmax(teacher/T) over all V, S its top-K ids (``topk_cache``), m = sum_S p_t,
+    p_K = p_t/m on S and 0 elsewhere, p_s = softmax(H W^T / T):
+      mass      m
+      kl_full   KL(p_t || p_s), the loss against the whole teacher
+      kl_topk   KL(p_K || p_s), the loss against the cached teacher (what the method computes)
+      grad_rel  ||p_K - p_t|| / ||p_s - p_t|| (2-norms over V): the error of the cached
+                teacher's logit gradient (p_s - p_K) relative to the full teacher's (p_s - p_t).
+    """
+    Hd, Wd, Td = _f64(H), _f64(W), _f64(teacher)
+    N, V = Td.shape
+    u = (Hd @ Wd.T) / T
+    log_ps = u - logsumexp_rows(u)[:, None]
+    a = Td / T
+    log_pt = a - logsumexp_rows(a)[:, None]
+    pt = np.exp(log_pt)
+    ps = np.exp(log_ps)
+    idx, _ = topk_cache(Td, K)
+    rows = np.arange(N)[:, None]
+    in_top = np.zeros((N, V), dtype=bool)
+    in_top[rows, idx.astype(np.int64)] = True
+    mass = np.where(in_top, pt, 0.0).sum(axis=1)
+    kl_full = np.where(pt > 0, pt * (log_pt - log_ps), 0.0).sum(axis=1)
+    log_pk = np.where(in_top, log_pt - np.log(mass)[:, None], -np.inf)
+    pk = np.where(in_top, np.exp(log_pk), 0.0)
+    kl_topk = np.where(in_top, pk * (np.where(in_top, log_pk, 0.0) - log_ps), 0.0).sum(axis=1)
+    grad_rel = np.linalg.norm(pk - pt, axis=1) / np.linalg.norm(ps - pt, axis=1)
+    return dict(mass=mass, kl_full=kl_full, kl_topk=kl_topk, grad_rel=grad_rel, idx=idx)

@@ -137,7 +137,7 @@ def dense(p, H=F, dH=F, ws=F, nbytes=None):
 
 @nogpu
 @pytest.mark.parametrize("bad,code", [
-    (dict(N=0), 2), (dict(d=0), 2), (dict(d=12), 2), (dict(V=0), 2), (dict(K=0), 2), (dict(K=129), 2),
+    (dict(N=0), 2), (dict(d=0), 2), (dict(d=12), 2), (dict(V=0), 2), (dict(K=0), 2), (dict(K=1025, V=4000), 2),
     (dict(V=50, K=60), 2), (dict(chunk=0), 2), (dict(V=256 * 16384 + 1), 2), (dict(N=1 << 30, d=8), 2),
     (dict(act=2), 3), (dict(tlogit=-1), 3),
     (dict(T=0.0), 4), (dict(T=-1.0), 4), (dict(T=float("nan")), 4), (dict(T=float("inf")), 4),

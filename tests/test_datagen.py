@@ -110,3 +110,20 @@ def test_pages_workload_shape():
     assert abs(dense_bytes / 1e9 - gold["dense_teacher_gb_bf16"]) / gold["dense_teacher_gb_bf16"] < 0.1
     g2 = datagen.CONFIGS["gptoss"]
     assert g2["V"] == gold["vocab"] and g2["S"] == gold["seq_len"]
+
+
+
+def test_truncation_study_fixture():
+    """The committed study shows the restriction the pages describe: for peaked teachers the
+    top-100 cache keeps nearly all of the mass and moves the loss and gradient by a few percent;
+    for flat teachers it keeps a fraction of a percent and the gradient is dominated by the
+    truncation. More cached entries always help."""
+    import json
+    st = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "topk_truncation_study.json")))
+    pk, fl = st["kinds"]["peaked"], st["kinds"]["flat"]
+    assert pk["100"]["mass_mean"] > 0.95 and pk["100"]["grad_rel_mean"] < 0.05
+    assert fl["100"]["mass_mean"] < 0.01 and fl["100"]["grad_rel_mean"] > 1.0
+    for kind in (pk, fl):
+        g = [kind[str(k)]["grad_rel_mean"] for k in st["K"]]
+        m = [kind[str(k)]["mass_mean"] for k in st["K"]]
+        assert all(a > b for a, b in zip(g, g[1:])) and all(a < b for a, b in zip(m, m[1:]))

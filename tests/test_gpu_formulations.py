@@ -56,7 +56,7 @@ def test_small_bf16(path):
 @pytest.mark.parametrize("shape", [
     dict(N=300, d=200, V=1000, K=7, chunk=128, T=1.3),     # every size ragged
     dict(N=1, d=64, V=300, K=1, chunk=1, T=0.7),           # one row, K = 1
-    dict(N=257, d=136, V=513, K=128, chunk=256, T=2.0),     # K at its maximum, one row past a block
+    dict(N=257, d=136, V=513, K=128, chunk=256, T=2.0),     # two lanes' worth of K, one row past a block
     dict(N=301, d=64, V=700, K=9, chunk=3, T=1.0),          # chunks not a multiple of 4 or of a block
 ])
 def test_ragged_and_edge_shapes(path, dtype, shape):

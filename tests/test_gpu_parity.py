@@ -83,8 +83,9 @@ def test_small_bf16_dense_path():
 @pytest.mark.parametrize("shape", [
     dict(N=300, d=200, V=1000, K=7, chunk=128, T=1.3),     # every size ragged
     dict(N=1, d=64, V=300, K=1, chunk=1, T=0.7),           # one row, K = 1
-    dict(N=257, d=136, V=513, K=128, chunk=256, T=2.0),     # K at its maximum, one row past a block
+    dict(N=257, d=136, V=513, K=128, chunk=256, T=2.0),     # two lanes' worth of K, one row past a block
     dict(N=64, d=32, V=40, K=40, chunk=64, T=1.0),          # K = V: every token cached
+    dict(N=300, d=64, V=3000, K=1024, chunk=256, T=1.0),    # K at its maximum
 ])
 def test_ragged_and_edge_shapes(dtype, shape):
     p = datagen.make("tiny", N=shape["N"], d=shape["d"], V=shape["V"], K=shape["K"], T=shape["T"],

@@ -279,3 +279,66 @@ def test_topk_cache_matches_sort():
         pairs = sorted(range(50), key=lambda v: (-x[n, v], v))[:7]
         assert list(idx[n]) == pairs
         np.testing.assert_array_equal(vals[n], x[n, pairs])
+
+
+
+# --------------------------------------------------------------- top-K truncation study
+
+def _brute_truncation(H, W, teacher, K, T):
+    """Loops and math.fsum over one tiny row at a time, from the definitions."""
+    out = []
+    N, V = teacher.shape
+    for n in range(N):
+        z = [math.fsum(H[n, j] * W[v, j] for j in range(H.shape[1])) / T for v in range(V)]
+        a = [teacher[n, v] / T for v in range(V)]
+        zs, za = math.fsum(math.exp(x) for x in z), math.fsum(math.exp(x) for x in a)
+        ps = [math.exp(x) / zs for x in z]
+        pt = [math.exp(x) / za for x in a]
+        top = sorted(range(V), key=lambda v: (-teacher[n, v], v))[:K]
+        m = math.fsum(pt[v] for v in top)
+        pk = [pt[v] / m if v in top else 0.0 for v in range(V)]
+        kl_full = math.fsum(pt[v] * math.log(pt[v] / ps[v]) for v in range(V))
+        kl_topk = math.fsum(pk[v] * math.log(pk[v] / ps[v]) for v in top)
+        num = math.sqrt(math.fsum((pk[v] - pt[v]) ** 2 for v in range(V)))
+        den = math.sqrt(math.fsum((ps[v] - pt[v]) ** 2 for v in range(V)))
+        out.append((m, kl_full, kl_topk, num / den))
+    return np.array(out)
+
+
+def test_truncation_terms_brute_force():
+    g = np.random.default_rng(21)
+    H, W = g.standard_normal((3, 4)), g.standard_normal((9, 4))
+    t = g.standard_normal((3, 9)) * 2
+    t[1, :4] = 0.5  # ties across the K boundary: lower ids first
+    for K, T in ((1, 1.0), (3, 0.7), (5, 2.0)):
+        r = oracle.truncation_terms(H, W, t, K, T)
+        b = _brute_truncation(H, W, t, K, T)
+        for col, name in enumerate(("mass", "kl_full", "kl_topk", "grad_rel")):
+            np.testing.assert_allclose(r[name], b[:, col], rtol=1e-12, atol=1e-14, err_msg=name)
+
+
+def test_truncation_terms_identities():
+    g = np.random.default_rng(22)
+    H, W = g.standard_normal((6, 8)), g.standard_normal((50, 8)) / 3
+    t = g.standard_normal((6, 50)) * 1.5
+    # K = V keeps the whole teacher: nothing changes
+    r = oracle.truncation_terms(H, W, t, 50)
+    np.testing.assert_allclose(r["mass"], 1.0, rtol=1e-14)
+    np.testing.assert_allclose(r["kl_topk"], r["kl_full"], rtol=1e-12)
+    np.testing.assert_allclose(r["grad_rel"], 0.0, atol=1e-14)
+    # the cached part of KL_full: m*(KL_topk + log m) = sum over the top K of p_t log(p_t/p_s)
+    K = 7
+    r = oracle.truncation_terms(H, W, t, K)
+    u = H @ W.T
+    log_ps = u - np.log(np.exp(u).sum(1, keepdims=True))
+    log_pt = t - np.log(np.exp(t).sum(1, keepdims=True))
+    top = np.argsort(-t, axis=1, kind="stable")[:, :K]
+    rows = np.arange(6)[:, None]
+    head = (np.exp(log_pt[rows, top]) * (log_pt[rows, top] - log_ps[rows, top])).sum(1)
+    np.testing.assert_allclose(r["mass"] * (r["kl_topk"] + np.log(r["mass"])), head, rtol=1e-11)
+    # KL_topk is the method's loss with the top-K cache as the teacher
+    idx, vals = oracle.topk_cache(t, K)
+    np.testing.assert_allclose(r["kl_topk"], oracle.kl_dense(H, W, idx, vals, 1.0)["row_kl"], rtol=1e-11)
+    # more cached entries never lose mass
+    m = [oracle.truncation_terms(H, W, t, k)["mass"] for k in (1, 5, 20, 50)]
+    assert all(np.all(a <= b + 1e-15) for a, b in zip(m, m[1:]))
