@@ -70,22 +70,28 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-struct WaveId {
+// Position of a thread in the workgroup's wave grid over the 256 x 256 tile. NW = 4 waves
+// form a 2 x 2 grid (128 x 128 per wave, 4 x 4 MFMA blocks); NW = 8 waves a 2 x 4 grid
+// (128 x 64 per wave, 4 x 2 blocks, two waves per SIMD).
+template <int NW>
+struct WaveIdN {
+    static constexpr int JN = 16 / NW;       // MFMA blocks per wave along N
+    static constexpr int NSPAN = 32 * JN;    // tile columns per wave
     int tid, lane, w, wm, wn, h, lr;
-    __device__ WaveId() {
+    __device__ WaveIdN() {
         tid = threadIdx.x;
         lane = tid & 63;
         w = __builtin_amdgcn_readfirstlane(tid >> 6);
-        wm = w >> 1;
-        wn = w & 1;
+        wm = w / (NW / 2);
+        wn = w % (NW / 2);
         h = lane >> 5;
         lr = lane & 31;
     }
     // A copy whose per-lane fields the compiler must recompute where it is taken. Epilogues
     // inside persistent tile loops take one, so their many LDS addresses are not hoisted out
     // of the loop and kept live (spilled) across the mainloop.
-    __device__ __forceinline__ WaveId fresh() const {
-        WaveId c = *this;
+    __device__ __forceinline__ WaveIdN fresh() const {
+        WaveIdN c = *this;
         asm volatile("v_mov_b32 %0, %1" : "=v"(c.tid) : "v"(tid));
         c.lane = c.tid & 63;
         c.h = c.lane >> 5;
@@ -93,6 +99,7 @@ struct WaveId {
         return c;
     }
 };
+using WaveId = WaveIdN<4>;
 
 template <typename T> __device__ __forceinline__ void mma(f32x16& c, const u32x4& a, const u32x4& b);
 template <> __device__ __forceinline__ void mma<bf16_t>(f32x16& c, const u32x4& a, const u32x4& b) {
@@ -331,16 +338,18 @@ __device__ __forceinline__ int swz4(int r, int c) { return c ^ (((r >> 2) ^ (r >
 // The K-blocked layout keeps the 256 rows of a tile within 128 KB (bf16) however long K is.
 // A row-major operand with a long K (the vocabulary) puts each of a tile's rows on its own
 // memory page, and its loads run about 15 % slower.
-template <typename T, bool BLK = false>
+template <typename T, bool BLK = false, int NW = 4>
 struct KOperand4 {
+    static constexpr int TPI = 16 / NW;  // DMA instructions per wave per stage
     static constexpr int VEC = Elem<T>::VEC;
     __amdgpu_buffer_rsrc_t rsrc;  // tile origin &src[mn0*ld] (row-major); k0 goes in the scalar offset
     const char* base;             // K-blocked: &src[mn0*256] in block 0
     int64_t blk_bytes;            // K-blocked: bytes per block
-    uint32_t off[4];
+    uint32_t off[TPI];
     int chunk;
-    // Wave w's instruction t fills chunks 256t + 64w + lane: row 64t + 16w + lane/4, slot lane%4.
-    __device__ __forceinline__ void init(const T* src, int64_t ld, int64_t mn0, int64_t mn_lim, const WaveId& id) {
+    // Wave w's instruction t fills chunks 64 NW t + 64w + lane: row 16 NW t + 16w + lane/4, slot lane%4.
+    __device__ __forceinline__ void init(const T* src, int64_t ld, int64_t mn0, int64_t mn_lim,
+                                         const WaveIdN<NW>& id) {
         const int64_t row_ld = BLK ? 256 : ld;
         if constexpr (BLK) {
             base = (const char*)uniform_ptr(src + mn0 * 256);
@@ -350,8 +359,8 @@ struct KOperand4 {
         }
         chunk = (id.lane & 3) ^ (((id.lane >> 4) ^ (id.lane >> 3)) & 3);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int row = 64 * t + 16 * id.w + (id.lane >> 2);
+        for (int t = 0; t < TPI; ++t) {
+            const int row = 16 * NW * t + 16 * id.w + (id.lane >> 2);
             off[t] = mn0 + row < mn_lim ? (uint32_t)((row * row_ld + chunk * VEC) * (int64_t)sizeof(T)) : kOOB;
         }
     }
@@ -360,29 +369,30 @@ struct KOperand4 {
     // the whole step is inside the K range. A step never straddles a K block (k0 is a multiple
     // of the step and the step divides 256).
     __device__ __forceinline__ void issue_one(u32x4* tile, int t, int64_t k0, int64_t k_lim, bool full, bool live,
-                                              const WaveId& id) const {
+                                              const WaveIdN<NW>& id) const {
         const bool in = live && (full || (int64_t)chunk * VEC < k_lim - k0);
         if constexpr (BLK) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (k0 >> 8) * blk_bytes);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + 256 * t + 64 * id.w), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + 64 * NW * t + 64 * id.w), 16,
                                                      (int)(in ? off[t] : kOOB), (int)((k0 & 255) * (int64_t)sizeof(T)),
                                                      0, 0);
         } else {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + 256 * t + 64 * id.w), 16,
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + 64 * NW * t + 64 * id.w), 16,
                                                      (int)(in ? off[t] : kOOB), (int)(k0 * (int64_t)sizeof(T)), 0, 0);
         }
     }
-    __device__ __forceinline__ void issue(u32x4* tile, int64_t k0, int64_t k_lim, bool live, const WaveId& id) const {
+    __device__ __forceinline__ void issue(u32x4* tile, int64_t k0, int64_t k_lim, bool live,
+                                          const WaveIdN<NW>& id) const {
         const bool full = k0 + Elem<T>::BK / 2 <= k_lim;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) issue_one(tile, t, k0, k_lim, full, live, id);
+        for (int t = 0; t < TPI; ++t) issue_one(tile, t, k0, k_lim, full, live, id);
     }
 };
 
 // Fragments of one k-group (g = 0, 1) of a 4-chunk stage: 4 A and 4 B chunks.
-template <typename T>
-__device__ __forceinline__ void read_frags4(u32x4 (&fa)[4], u32x4 (&fb)[4], const u32x4* tA, const u32x4* tB,
-                                            int g, const WaveId& id) {
+template <typename T, int NW>
+__device__ __forceinline__ void read_frags4(u32x4 (&fa)[4], u32x4 (&fb)[16 / NW], const u32x4* tA, const u32x4* tB,
+                                            int g, const WaveIdN<NW>& id) {
     const int c = 2 * g + id.h;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -390,18 +400,18 @@ __device__ __forceinline__ void read_frags4(u32x4 (&fa)[4], u32x4 (&fb)[4], cons
         fa[i] = tA[row * NCH4 + swz4(row, c)];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = id.wn * 128 + j * 32 + id.lr;
+    for (int j = 0; j < 16 / NW; ++j) {
+        const int row = id.wn * (512 / NW) + j * 32 + id.lr;
         fb[j] = tB[row * NCH4 + swz4(row, c)];
     }
 }
 
-template <typename T>
-__device__ __forceinline__ void mma_block(f32x16 (&acc)[4][4], const u32x4 (&fa)[4], const u32x4 (&fb)[4]) {
+template <typename T, int JN>
+__device__ __forceinline__ void mma_block(f32x16 (&acc)[4][JN], const u32x4 (&fa)[4], const u32x4 (&fb)[JN]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mma<T>(acc[i][j], fa[i], fb[j]);
+        for (int j = 0; j < JN; ++j) mma<T>(acc[i][j], fa[i], fb[j]);
 }
 
 template <int N> __device__ __forceinline__ void wait_vmem_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
@@ -420,48 +430,53 @@ template <int N> __device__ __forceinline__ void wait_vmem_le() { asm volatile("
 // Stage kt's buffer is free after that barrier (its last fragments were read before it), so
 // the DMA runs four stages ahead. Every LDS read is issued one MFMA block ahead of its use.
 // BA / BB select the K-blocked layout for A / B (then lda / ldb is the operand's row count).
-template <typename T, bool BA = false, bool BB = false>
-__device__ __forceinline__ void gemm_tile_kk(f32x16 (&acc)[4][4], u32x4* L, const WaveId& id,
+// NW is the wave count of the workgroup (4 or 8, see WaveIdN); acc is [4][16/NW].
+template <typename T, bool BA = false, bool BB = false, int NW = 4>
+__device__ __forceinline__ void gemm_tile_kk(f32x16 (&acc)[4][16 / NW], u32x4* L, const WaveIdN<NW>& id,
                                              const T* A, int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim,
                                              const T* B, int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim,
                                              int64_t k_begin, int64_t k_end) {
     constexpr int BKH = Elem<T>::BK / 2;
+    constexpr int JN = 16 / NW;   // B fragments (and MFMA columns) per wave
+    constexpr int TPI = 16 / NW;  // DMA instructions per operand per wave per stage
+    constexpr int NFR = 4 + JN;   // fragment reads per k-group
+    constexpr int NMM = 4 * JN;   // MFMAs per k-group
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < JN; ++j) acc[i][j] = f32x16{};
     const int nk = (int)((k_end - k_begin + BKH - 1) / BKH);
     if (nk <= 0) return;
-    KOperand4<T, BA> opA;
-    KOperand4<T, BB> opB;
+    KOperand4<T, BA, NW> opA;
+    KOperand4<T, BB, NW> opB;
     opA.init(A, lda, m0, m_lim, id);
     opB.init(B, ldb, n0, n_lim, id);
     auto stageA = [&](int s) { return L + (2 * (s & 3)) * TILE4; };
     auto stageB = [&](int s) { return L + (2 * (s & 3) + 1) * TILE4; };
     auto kof = [&](int s) { return k_begin + (int64_t)s * BKH; };
-    // Every stage slot issues its 8 loads, live or not, so the wait counts are constant:
+    // Every stage slot issues its 2 TPI loads, live or not, so the wait counts are constant:
     // stage s is complete once at most the 3 (prologue) or 2 (loop) later stages are in flight.
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
         opA.issue(stageA(s), kof(s), ka_lim, s < nk, id);
         opB.issue(stageB(s), kof(s), kb_lim, s < nk, id);
     }
-    wait_vmem_le<24>();
+    wait_vmem_le<6 * TPI>();
     __syncthreads();
-    u32x4 f0a[4], f0b[4], f1a[4], f1b[4];
-    read_frags4<T>(f0a, f0b, stageA(0), stageB(0), 0, id);
+    u32x4 f0a[4], f0b[JN], f1a[4], f1b[JN];
+    read_frags4<T, NW>(f0a, f0b, stageA(0), stageB(0), 0, id);
     for (int kt = 0; kt + 1 < nk; ++kt) {
         KD_SCHED_FENCE();
-        read_frags4<T>(f1a, f1b, stageA(kt), stageB(kt), 1, id);
-        mma_block<T>(acc, f0a, f0b);
+        read_frags4<T, NW>(f1a, f1b, stageA(kt), stageB(kt), 1, id);
+        mma_block<T, JN>(acc, f0a, f0b);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+        for (int q = 0; q < NFR; ++q) {
             __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 0);
             __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, NMM - NFR, 0);
         KD_SCHED_FENCE();
-        wait_vmem_le<16>();  // stage kt+1 complete; kt+2 and kt+3 may be in flight
+        wait_vmem_le<4 * TPI>();  // stage kt+1 complete; kt+2 and kt+3 may be in flight
         __syncthreads();
         KD_SCHED_FENCE();
         {
@@ -469,32 +484,47 @@ __device__ __forceinline__ void gemm_tile_kk(f32x16 (&acc)[4][4], u32x4* L, cons
             const bool live = s < nk;
             const bool fa = kof(s) + BKH <= ka_lim, fb = kof(s) + BKH <= kb_lim;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
+            for (int t = 0; t < TPI; ++t) {
                 opA.issue_one(stageA(s), t, kof(s), ka_lim, fa, live, id);
                 opB.issue_one(stageB(s), t, kof(s), kb_lim, fb, live, id);
             }
         }
-        read_frags4<T>(f0a, f0b, stageA(kt + 1), stageB(kt + 1), 0, id);
-        mma_block<T>(acc, f1a, f1b);
+        read_frags4<T, NW>(f0a, f0b, stageA(kt + 1), stageB(kt + 1), 0, id);
+        mma_block<T, JN>(acc, f1a, f1b);
+        if constexpr (NW == 4) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM_RD, 1, 1);
-        }
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM_RD, 1, 1);
+            }
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 1);
+            }
+        } else {
+            // 8 MFMAs carry 4 DMA issues and 6 fragment reads
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM_RD, 1, 1);
+            }
+#pragma unroll
+            for (int q = 0; q < 3; ++q) {
+                __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 2, 1);
+            }
             __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 1);
         }
         KD_SCHED_FENCE();
     }
     // last stage
     KD_SCHED_FENCE();
-    read_frags4<T>(f1a, f1b, stageA(nk - 1), stageB(nk - 1), 1, id);
+    read_frags4<T, NW>(f1a, f1b, stageA(nk - 1), stageB(nk - 1), 1, id);
     KD_SCHED_FENCE();
-    mma_block<T>(acc, f0a, f0b);
+    mma_block<T, JN>(acc, f0a, f0b);
     KD_SCHED_FENCE();
-    mma_block<T>(acc, f1a, f1b);
+    mma_block<T, JN>(acc, f1a, f1b);
     KD_SCHED_FENCE();
     wait_vmem_le<0>();  // no zero-fill may land after the caller reuses the LDS
     __syncthreads();

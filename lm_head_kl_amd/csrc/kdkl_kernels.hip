@@ -736,10 +736,12 @@ struct DhArgs {
     void* dH;
 };
 
-template <typename T, bool WT>
-__global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
+template <typename T, bool WT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_dh(DhArgs a) {
+    static_assert(WT || NW == 4, "the M/N-contiguous path runs on four waves");
+    constexpr int JN = 16 / NW;
     __shared__ u32x4 L[LDS_CHUNKS];
-    const WaveId id;
+    const WaveIdN<NW> id;
     // Logical tiles are split major, then column tile, then row tile: an XCD's band shares one
     // vocabulary slice of G_c and W.
     const int64_t n_tiles = (int64_t)a.n_split * a.n_nt * a.n_mt;
@@ -750,10 +752,10 @@ __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
     const int nt = rem / a.n_mt, mt = rem % a.n_mt;
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
     const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
-    f32x16 acc[4][4];
+    f32x16 acc[4][JN];
     if constexpr (WT)
-        gemm_tile_kk<T, true, true>(acc, L, id, (const T*)a.G, a.cc, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
-                                    k_end, k_begin, k_end);
+        gemm_tile_kk<T, true, true, NW>(acc, L, id, (const T*)a.G, a.cc, m0, a.cc, k_end, (const T*)a.W, a.d, n0,
+                                        a.d, k_end, k_begin, k_end);
     else
         gemm_tile<T, true, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
                                   min(a.V, k_end), k_begin, k_end);
@@ -764,8 +766,8 @@ __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
             const int64_t row = m0 + id.wm * 128 + acc_row(i, e, id.h);
             if (row >= a.cc) continue;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t col = n0 + id.wn * 128 + j * 32 + id.lr;
+            for (int j = 0; j < JN; ++j) {
+                const int64_t col = n0 + id.wn * WaveIdN<NW>::NSPAN + j * 32 + id.lr;
                 if (col >= a.d) continue;
                 const float v = acc[i][j][e];
                 if (a.n_split > 1) {
@@ -813,20 +815,23 @@ struct DwArgs {
     float* dW;
 };
 
-template <typename T, bool KK>
-__global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
+template <typename T, bool KK, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_dw(DwArgs a) {
+    static_assert(KK || NW == 4, "the M/N-contiguous path runs on four waves");
+    constexpr int NT = 64 * NW, JN = 16 / NW;
+    constexpr int IB = 8192 / NT / 2;  // 16-byte items per thread per batch (two batches per pass)
     __shared__ u32x4 L[LDS_CHUNKS];
-    const WaveId id;
+    const WaveIdN<NW> id;
     // Logical tiles are vocab-row major: an XCD's band shares a few G_c column slabs and H_c.
     const int64_t n_tiles = (int64_t)a.n_mt * a.n_nt;
     const int64_t t = xcd_tile(blockIdx.x, n_tiles);
     if (t >= n_tiles) return;
     const int mt = (int)(t / a.n_nt), nt = (int)(t % a.n_nt);
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
-    f32x16 acc[4][4];
+    f32x16 acc[4][JN];
     if constexpr (KK)
-        gemm_tile_kk<T>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.ccp, (const T*)a.H, a.ldh, n0, a.d, a.ccp, 0,
-                        a.ccp);
+        gemm_tile_kk<T, false, false, NW>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.ccp, (const T*)a.H, a.ldh,
+                                          n0, a.d, a.ccp, 0, a.ccp);
     else
         gemm_tile<T, false, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.cc, (const T*)a.H + a.c0 * a.d,
                                    a.d, n0, a.d, a.cc, 0, a.cc);
@@ -834,17 +839,17 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
     // vector and a wave covers 1 KB of one row. The old values of a pass's first half are
     // requested before its staging writes and those of the second half before the first half
     // is added, so the load latency hides behind LDS work.
-    const WaveId ie = id.fresh();
+    const WaveIdN<NW> ie = id.fresh();
     float* stage = (float*)L;
     auto item = [&](int pq, int bt, int k, int& sr, int64_t& row, int64_t& col) {
-        const int it = ie.tid + NTHR * (16 * bt + k);
+        const int it = ie.tid + NT * (IB * bt + k);
         sr = it >> 6;
         row = m0 + (sr >> 6) * 128 + pq * 64 + (sr & 63);
         col = n0 + (it & 63) * 4;
     };
-    auto load_old = [&](int pq, int bt, f32x4 (&old)[16]) {
+    auto load_old = [&](int pq, int bt, f32x4 (&old)[IB]) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < IB; ++k) {
             int sr;
             int64_t row, col;
             item(pq, bt, k, sr, row, col);
@@ -852,9 +857,9 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
                                                               : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     };
-    auto add_store = [&](int pq, int bt, const f32x4 (&old)[16]) {
+    auto add_store = [&](int pq, int bt, const f32x4 (&old)[IB]) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < IB; ++k) {
             int sr;
             int64_t row, col;
             item(pq, bt, k, sr, row, col);
@@ -864,7 +869,7 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
     };
 #pragma unroll
     for (int pq = 0; pq < 2; ++pq) {
-        f32x4 old0[16], old1[16];
+        f32x4 old0[IB], old1[IB];
         load_old(pq, 0, old0);
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii)
@@ -872,7 +877,8 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
             for (int e = 0; e < 16; ++e) {
                 const int sr = ie.wm * 64 + ii * 32 + blk_row(e, ie.h);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) stage[st_idx(sr, ie.wn * 128 + j * 32 + ie.lr)] = acc[2 * pq + ii][j][e];
+                for (int j = 0; j < JN; ++j)
+                    stage[st_idx(sr, ie.wn * WaveIdN<NW>::NSPAN + j * 32 + ie.lr)] = acc[2 * pq + ii][j][e];
             }
         __syncthreads();
         load_old(pq, 1, old1);
@@ -1259,6 +1265,10 @@ __global__ __launch_bounds__(256) void k_topk(const T* __restrict__ X, int64_t l
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// Waves per workgroup of the dW and dH GEMMs: eight (two per SIMD) hide more of the operand
+// latency than four.
+constexpr int kDwWaves = 8, kDhWaves = 8;
+
 // Vocab lanes of the forward: at least 8, and enough units to give every CU one.
 int fwd_vsplits(int64_t N, int64_t V) {
     const int64_t n_rb = (N + kTileM - 1) / kTileM;
@@ -1498,14 +1508,14 @@ hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W
     const dim3 grid(grid_xcd((int64_t)n_split * a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16) {
         if (WT)
-            KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, true>), grid, dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, true, kDhWaves>), grid, dim3(64 * kDhWaves), 0, s, a);
         else
-            KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, false>), grid, dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, false, 4>), grid, dim3(NTHR), 0, s, a);
     } else {
         if (WT)
-            KD_LAUNCH(kKindDh, s, (k_dh<float, true>), grid, dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindDh, s, (k_dh<float, true, kDhWaves>), grid, dim3(64 * kDhWaves), 0, s, a);
         else
-            KD_LAUNCH(kKindDh, s, (k_dh<float, false>), grid, dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindDh, s, (k_dh<float, false, 4>), grid, dim3(NTHR), 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split <= 1) return e;
@@ -1537,9 +1547,9 @@ hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H
     a.n_mt = (int)(a.Vp / kTileM);
     const dim3 grid(grid_xcd((int64_t)a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16)
-        KD_LAUNCH(kKindDw, s, (k_dw<bf16_t, false>), grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindDw, s, (k_dw<bf16_t, false, 4>), grid, dim3(NTHR), 0, s, a);
     else
-        KD_LAUNCH(kKindDw, s, (k_dw<float, false>), grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindDw, s, (k_dw<float, false, 4>), grid, dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1562,9 +1572,9 @@ hipError_t launch_dw_t(const Shape& sh, const void* GT, int64_t ldgt, const void
     a.n_mt = (int)(a.Vp / kTileM);
     const dim3 grid(grid_xcd((int64_t)a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16)
-        KD_LAUNCH(kKindDw, s, (k_dw<bf16_t, true>), grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindDw, s, (k_dw<bf16_t, true, kDwWaves>), grid, dim3(64 * kDwWaves), 0, s, a);
     else
-        KD_LAUNCH(kKindDw, s, (k_dw<float, true>), grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindDw, s, (k_dw<float, true, kDwWaves>), grid, dim3(64 * kDwWaves), 0, s, a);
     return hipGetLastError();
 }
 
