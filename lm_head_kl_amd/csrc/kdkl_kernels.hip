@@ -262,10 +262,11 @@ struct FwdArgs {
 // entries and columns are tokens. Each lane then holds 64 vocabulary entries of each of its
 // 4 token columns, so the per-token (max, sum) over the vocabulary is folded inside the lane,
 // and lanes only meet once per unit.
-template <typename T, bool ZT>
-__global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
+template <typename T, bool ZT, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_fwd(FwdArgs a) {
+    constexpr int NT = 64 * NW, JN = 16 / NW, NSPAN = WaveIdN<NW>::NSPAN;
     __shared__ u32x4 L[LDS_CHUNKS];
-    const WaveId id;
+    const WaveIdN<NW> id;
     const int64_t P = gridDim.x;
     const int64_t xcd = blockIdx.x % 8, slot = blockIdx.x / 8, per_xcd = P / 8;
     const int64_t band = (a.n_unit + 7) / 8;
@@ -278,18 +279,23 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
         const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
         // Running (max, sum) in units of y = z*log2(e)/T for this lane's token columns j, over
         // the vocabulary rows the lane holds.
-        float run_m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, run_s[4] = {0.f, 0.f, 0.f, 0.f};
+        float run_m[JN], run_s[JN];
+#pragma unroll
+        for (int j = 0; j < JN; ++j) {
+            run_m[j] = -INFINITY;
+            run_s[j] = 0.f;
+        }
 
         for (int vt = q; vt < a.n_vt; vt += a.Q) {
             const int64_t n0 = (int64_t)vt * kTileN;
-            // The tile's first 256 cached-id entries go to registers (one per thread) before the
+            // The tile's first NT cached-id entries go to registers (one per thread) before the
             // mainloop, so their load latency hides behind it.
             const int e0 = off[vt], e1 = off[vt + 1];
             const uint32_t my_en = e0 + id.tid < e1 ? a.ent[e0 + id.tid] : 0xffffffffu;
-            f32x16 acc[4][4];
-            gemm_tile_kk<T>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, (const T*)a.H, a.d, m0, a.N, a.d, 0,
-                            a.d);
-            const WaveId ie = id.fresh();
+            f32x16 acc[4][JN];
+            gemm_tile_kk<T, false, false, NW>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, (const T*)a.H, a.d, m0,
+                                              a.N, a.d, 0, a.d);
+            const WaveIdN<NW> ie = id.fresh();
 
             // Gather z at the cached ids of this (row block, vocab tile): two passes of 128
             // vocabulary rows staged in LDS. The paths that keep the logits also store the
@@ -303,15 +309,15 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
                         for (int e = 0; e < 16; ++e) {
                             const int sr = ie.wm * 64 + ii * 32 + blk_row(e, ie.h);
 #pragma unroll
-                            for (int j = 0; j < 4; ++j)
-                                stage[st_idx(sr, ie.wn * 128 + j * 32 + ie.lr)] = acc[2 * pq + ii][j][e];
+                            for (int j = 0; j < JN; ++j)
+                                stage[st_idx(sr, ie.wn * NSPAN + j * 32 + ie.lr)] = acc[2 * pq + ii][j][e];
                         }
                     __syncthreads();
                     if (my_en != 0xffffffffu && ((my_en >> 14) & 1) == (uint32_t)pq) {
                         const int r = my_en & 255, c = (my_en >> 8) & 255, k = (int)(my_en >> 16);
                         a.zk[(m0 + r) * a.K + k] = stage[st_idx(st_row(c), r)];
                     }
-                    for (int i = e0 + NTHR + ie.tid; i < e1; i += NTHR) {
+                    for (int i = e0 + NT + ie.tid; i < e1; i += NT) {
                         const uint32_t en = a.ent[i];
                         const int c = (en >> 8) & 255;
                         if (((c >> 6) & 1) != pq) continue;
@@ -320,8 +326,8 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
                     }
                     if constexpr (ZT) {
 #pragma unroll 8
-                        for (int k = 0; k < 32; ++k) {
-                            const int it = ie.tid + NTHR * k;
+                        for (int k = 0; k < 8192 / NT; ++k) {
+                            const int it = ie.tid + NT * k;
                             const int sr = it >> 6, tok = (it & 63) * 4;
                             const int64_t v = n0 + (sr >> 6) * 128 + pq * 64 + (sr & 63);
                             if (v < a.V && m0 + tok < a.N)
@@ -337,7 +343,7 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
             const bool vfull = n0 + kTileN <= a.V;
             const int rows_left = (int)min<int64_t>(kTileN, a.V - n0) - ie.wm * 128 - 4 * ie.h;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < JN; ++j) {
                 float mx = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -346,9 +352,12 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
                         const bool ok = vfull || i * 32 + 8 * (e >> 2) + (e & 3) < rows_left;
                         mx = fmaxf(mx, ok ? acc[i][j][e] : -INFINITY);
                     }
-                // Re-read the accumulators for the sum instead of keeping 64 copies live.
+                // With the accumulators in AGPRs (four waves), re-read them for the sum instead of
+                // keeping 64 VGPR copies live.
+                if constexpr (NW == 4) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[i][j]));
+                    for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[i][j]));
+                }
                 const float mt = mx * a.c;
                 float s = 0.f;
                 if (mx != -INFINITY) {
@@ -366,14 +375,14 @@ __global__ __launch_bounds__(256, 1) void k_fwd(FwdArgs a) {
 
         // Lanes l and l^32 hold the same token columns over different vocabulary rows.
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < JN; ++j) {
             const float m2 = __shfl_xor(run_m[j], 32), s2 = __shfl_xor(run_s[j], 32);
             ms_merge(run_m[j], run_s[j], m2, s2);
         }
         if (id.h == 0) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int64_t g = m0 + id.wn * 128 + j * 32 + id.lr;
+            for (int j = 0; j < JN; ++j) {
+                const int64_t g = m0 + id.wn * NSPAN + j * 32 + id.lr;
                 if (g < a.N) a.part[(int64_t)(q * 2 + id.wm) * a.N + g] = make_float2(run_m[j], run_s[j]);
             }
         }
@@ -507,15 +516,16 @@ __device__ __forceinline__ void store8(T* dst, const float (&x)[8]) {
 // Second half of a gradient pass, once the pass's 128 vocabulary rows of gs*softmax are staged:
 // subtract gs*p_t at the cached ids that fall in the pass, then write the rows of G (K-blocked)
 // and of G^T. Ends with a barrier, so the stage may be refilled.
-template <typename T>
-__device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, int pq, const WaveId& ie, int vt,
+template <typename T, int NW>
+__device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, int pq, const WaveIdN<NW>& ie, int vt,
                                               int64_t r0, int64_t n0, int e0, int e1, uint32_t my_en, float my_pt,
                                               float gs) {
+    constexpr int NT = 64 * NW, IT = 4096 / NT;  // items per thread of each output layout
     if (my_en != 0xffffffffu && ((my_en >> 14) & 1) == (uint32_t)pq) {
         const int r = my_en & 255, c = (my_en >> 8) & 255;
         stage[st_idx(st_row(c), r)] -= gs * my_pt;
     }
-    for (int i = e0 + NTHR + ie.tid; i < e1; i += NTHR) {
+    for (int i = e0 + NT + ie.tid; i < e1; i += NT) {
         const uint32_t en = a.ent[i];
         const int c = (en >> 8) & 255;
         if (((c >> 6) & 1) != pq) continue;
@@ -526,8 +536,8 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
     // G rows: token tl, group g of 8 vocabulary entries (stage rows 8g .. 8g+7). Eight
     // consecutive lanes cover one token's 64 entries of a half: a whole 128-byte line.
 #pragma unroll 4
-    for (int it8 = 0; it8 < 16; ++it8) {
-        const int it = ie.tid + NTHR * it8;
+    for (int it8 = 0; it8 < IT; ++it8) {
+        const int it = ie.tid + NT * it8;
         const int g = it & 15, tl = it >> 4;
         const int64_t tr = r0 + tl;
         if (tr < a.cc) {
@@ -542,8 +552,8 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
     // 256 tokens.
     if (a.GT) {
 #pragma unroll 4
-        for (int it8 = 0; it8 < 16; ++it8) {
-            const int it = ie.tid + NTHR * it8;
+        for (int it8 = 0; it8 < IT; ++it8) {
+            const int it = ie.tid + NT * it8;
             const int sr = it >> 5, cb = it & 31;
             const int64_t tr = r0 + cb * 8;
             if (tr < a.ccp) {
@@ -559,10 +569,11 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
     __syncthreads();
 }
 
-template <typename T>
-__global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
+template <typename T, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
+    constexpr int NT = 64 * NW, JN = 16 / NW, NSPAN = WaveIdN<NW>::NSPAN;
     __shared__ u32x4 L[LDS_CHUNKS];
-    const WaveId id;
+    const WaveIdN<NW> id;
     // Persistent when launched with fewer workgroups than tiles. Logical tiles are vocab-tile
     // major; XCD x owns the contiguous band [x*band, (x+1)*band) and walks it with stride
     // per_xcd, so the tiles in flight on one XCD are a few W tiles times every row block of
@@ -577,15 +588,15 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
         const int64_t r0 = (int64_t)rb * kTileM;  // token offset within the chunk
         const int64_t n0 = (int64_t)vt * kTileN;
         const float gs = (a.grad ? a.grad[0] : 1.f) * a.gsc;
-        float l2[4];
-        bool tok_ok[4];
+        float l2[JN];
+        bool tok_ok[JN];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int64_t tr = r0 + id.wn * 128 + j * 32 + id.lr;
+        for (int j = 0; j < JN; ++j) {
+            const int64_t tr = r0 + id.wn * NSPAN + j * 32 + id.lr;
             tok_ok[j] = tr < a.cc;
             l2[j] = tok_ok[j] ? a.lse[a.c0 + tr] * kLog2e : 0.f;
         }
-        // This tile's cached-id entries: the first 256 are loaded into registers (one per
+        // This tile's cached-id entries: the first NT are loaded into registers (one per
         // thread) before the mainloop; more only occur on Zipf-hot tiles.
         const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
         const int e0 = off[vt], e1 = off[vt + 1];
@@ -595,9 +606,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
             my_en = a.ent[e0 + id.tid];
             my_pt = a.pt[(r0 + (my_en & 255)) * a.K + (my_en >> 16)];
         }
-        f32x16 acc[4][4];
-        gemm_tile_kk<T>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, Hc, a.d, r0, a.cc, a.d, 0, a.d);
-        const WaveId ie = id.fresh();
+        f32x16 acc[4][JN];
+        gemm_tile_kk<T, false, false, NW>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, Hc, a.d, r0, a.cc, a.d, 0,
+                                          a.d);
+        const WaveIdN<NW> ie = id.fresh();
 
 #pragma unroll
         for (int pq = 0; pq < 2; ++pq) {
@@ -609,14 +621,14 @@ __global__ __launch_bounds__(256, 1) void k_bwd_grad(GradArgs a) {
                     const bool vok = n0 + ie.wm * 128 + i * 32 + blk_row(e, ie.h) < a.V;
                     const int sr = ie.wm * 64 + ii * 32 + blk_row(e, ie.h);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
+                    for (int j = 0; j < JN; ++j) {
                         const float v = (vok && tok_ok[j]) ? gs * exp2_fast(fmaf(acc[i][j][e], a.c, -l2[j])) : 0.f;
-                        stage[st_idx(sr, ie.wn * 128 + j * 32 + ie.lr)] = v;
+                        stage[st_idx(sr, ie.wn * NSPAN + j * 32 + ie.lr)] = v;
                     }
                 }
             }
             __syncthreads();
-            grad_pass_out<T>(a, stage, pq, ie, vt, r0, n0, e0, e1, my_en, my_pt, gs);
+            grad_pass_out<T, NW>(a, stage, pq, ie, vt, r0, n0, e0, e1, my_en, my_pt, gs);
         }
     }
 }
@@ -687,7 +699,7 @@ __global__ __launch_bounds__(256) void k_grad_z(GradArgs a) {
             *(f32x4*)(stage + st_idx(sr, tok)) = g;
         }
         __syncthreads();
-        grad_pass_out<T>(a, stage, pq, id, vt, r0, n0, e0, e1, my_en, my_pt, gs);
+        grad_pass_out<T, 4>(a, stage, pq, id, vt, r0, n0, e0, e1, my_en, my_pt, gs);
     }
 }
 
@@ -1267,7 +1279,7 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Waves per workgroup of the dW and dH GEMMs: eight (two per SIMD) hide more of the operand
 // latency than four.
-constexpr int kDwWaves = 8, kDhWaves = 8;
+constexpr int kDwWaves = 8, kDhWaves = 8, kGradWaves = 8, kFwdWaves = 8;
 
 // Vocab lanes of the forward: at least 8, and enough units to give every CU one.
 int fwd_vsplits(int64_t N, int64_t V) {
@@ -1351,16 +1363,17 @@ hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32
     // One workgroup per CU (the LDS use allows no more), a multiple of 8 for the XCD bands.
     const int64_t cus = std::max(8, device_cus() / 8 * 8);
     const unsigned grid = (unsigned)std::min<int64_t>(cus, 8 * ((a.n_unit + 7) / 8));
+    const dim3 blk(64 * kFwdWaves);
     if (sh.act == Dt::BF16) {
         if (zt)
-            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, true>), dim3(grid), dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, true, kFwdWaves>), dim3(grid), blk, 0, s, a);
         else
-            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, false>), dim3(grid), dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, false, kFwdWaves>), dim3(grid), blk, 0, s, a);
     } else {
         if (zt)
-            KD_LAUNCH(kKindFwd, s, (k_fwd<float, true>), dim3(grid), dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindFwd, s, (k_fwd<float, true, kFwdWaves>), dim3(grid), blk, 0, s, a);
         else
-            KD_LAUNCH(kKindFwd, s, (k_fwd<float, false>), dim3(grid), dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindFwd, s, (k_fwd<float, false, kFwdWaves>), dim3(grid), blk, 0, s, a);
     }
     return hipGetLastError();
 }
@@ -1410,9 +1423,9 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
     // workgroups stay in lockstep and so issue their tile stores all at once.
     const dim3 grid(grid_xcd((int64_t)a.n_vt * a.n_rbc));
     if (sh.act == Dt::BF16)
-        KD_LAUNCH(kKindBwdGrad, s, k_bwd_grad<bf16_t>, grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<bf16_t, kGradWaves>), grid, dim3(64 * kGradWaves), 0, s, a);
     else
-        KD_LAUNCH(kKindBwdGrad, s, k_bwd_grad<float>, grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<float, kGradWaves>), grid, dim3(64 * kGradWaves), 0, s, a);
     return hipGetLastError();
 }
 
