@@ -56,6 +56,7 @@
  *   - Preconditions the host cannot check without reading device memory: idx in [0,V) and
  *     distinct within each row. Out-of-range ids are skipped, never dereferenced. Results
  *     are undefined if the ids repeat. Set KD_VALIDATE_IDX to have them checked.
+ *   - Alignment: H, W, dH and dW must be 16-byte aligned (KD_ERR_VALUE otherwise).
  *   - Workspace: the caller passes ws (256-byte aligned) of at least the bytes returned by
  *     the matching *_workspace_bytes query for the same problem. Its contents on entry do not
  *     matter; on return they are unspecified.
@@ -80,7 +81,8 @@ typedef enum kd_status {
     KD_ERR_NULL = 1,      /* a required pointer is NULL */
     KD_ERR_SHAPE = 2,     /* N, d, V, K or chunk out of the supported range */
     KD_ERR_DTYPE = 3,     /* unknown or unsupported dtype */
-    KD_ERR_VALUE = 4,     /* T not finite and > 0, or n_norm not finite, or unknown flag */
+    KD_ERR_VALUE = 4,     /* T not finite and > 0, n_norm not finite, unknown flag, or a
+                             H, W, dH or dW pointer not 16-byte aligned */
     KD_ERR_WORKSPACE = 5, /* ws_bytes smaller than the query, or ws not 256-byte aligned */
     KD_ERR_INDEX = 6,     /* KD_VALIDATE_IDX found an id out of range or repeated in a row */
     KD_ERR_HIP = 7,       /* the HIP runtime reported an error while enqueueing */
@@ -98,7 +100,7 @@ typedef enum kd_dtype {
 
 /*
  * Problem descriptor (host memory).
- *   N, d, V, K   sizes as above; limits: N >= 1, d >= 8 and d % 8 == 0, 1 <= V <= 4194304,
+ *   N, d, V, K   sizes as above; limits: N >= 1, 8 <= d <= 1048576 and d % 8 == 0, 1 <= V <= 4194304,
  *                1 <= K <= min(V, 1024), N * K < 2^31, N * d < 2^31, V * d < 2^31.
  *   chunk        rows per backward chunk (>= 1; N need not be a multiple). It bounds the
  *                backward's per-chunk gradient tile G_c [chunk, V] in the workspace. The

@@ -530,6 +530,189 @@ __device__ __forceinline__ void gemm_tile_kk(f32x16 (&acc)[4][16 / NW], u32x4* L
     __syncthreads();
 }
 
+// ------------------------------------------------------------------------------------------
+// Wide tile: 256 x 320 (M x N), for products whose N is the hidden size d. d = 2880 is 9 x 320
+// but 11.25 x 256, so 256-wide column tiles waste a quarter of their last tile; a 320-wide tile
+// also moves about 10 % fewer operand bytes per FLOP. Eight waves in a 4 x 2 grid, 64 x 160 per
+// wave (2 x 5 MFMA blocks, two waves per SIMD). The stage layout, swizzle, pipeline and schedule
+// are those of gemm_tile_kk: four stages of half a K step, A [256][4 chunks] + B [320][4 chunks]
+// = 36 KB each. B takes 20 DMA instructions per stage: waves 0-3 issue three, waves 4-7 two and
+// a third with an out-of-range offset (no memory access) into a 1 KB dummy slot of their own,
+// so every wave issues five and the wait counts stay constant.
+constexpr int kWideN = 320;
+constexpr int WST = (kTileM + kWideN) * NCH4;           // chunks per stage (A then B)
+constexpr int WIDE_LDS_CHUNKS = 4 * WST + 4 * 64;        // four stages + four dummy slots = 148 KB
+
+struct WaveIdW {
+    int tid, lane, w, wm, wn, h, lr;
+    __device__ WaveIdW() {
+        tid = threadIdx.x;
+        lane = tid & 63;
+        w = __builtin_amdgcn_readfirstlane(tid >> 6);
+        wm = w >> 1;
+        wn = w & 1;
+        h = lane >> 5;
+        lr = lane & 31;
+    }
+    __device__ __forceinline__ WaveIdW fresh() const {
+        WaveIdW c = *this;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(c.tid) : "v"(tid));
+        c.lane = c.tid & 63;
+        c.h = c.lane >> 5;
+        c.lr = c.lane & 31;
+        return c;
+    }
+};
+
+// Operand of NI 16-row groups per wave (A: NI = 2 covers 256 rows; B: NI = 3 covers 320 rows,
+// the third group of waves 4-7 being the dummy). Layouts as KOperand4.
+template <typename T, bool BLK, int NI>
+struct KOperandW {
+    static constexpr int VEC = Elem<T>::VEC;
+    __amdgpu_buffer_rsrc_t rsrc;
+    const char* base;
+    int64_t blk_bytes;
+    uint32_t off[NI];
+    int dst[NI];  // chunk index of the instruction's destination within a stage, or -1 (dummy)
+    int chunk;
+    __device__ __forceinline__ void init(const T* src, int64_t ld, int64_t mn0, int64_t mn_lim, int stage_off,
+                                         int rows, const WaveIdW& id) {
+        const int64_t row_ld = BLK ? 256 : ld;
+        if constexpr (BLK) {
+            base = (const char*)uniform_ptr(src + mn0 * 256);
+            blk_bytes = ld * 256 * (int64_t)sizeof(T);
+        } else {
+            rsrc = make_rsrc(src + mn0 * ld);
+        }
+        chunk = (id.lane & 3) ^ (((id.lane >> 4) ^ (id.lane >> 3)) & 3);
+#pragma unroll
+        for (int t = 0; t < NI; ++t) {
+            const int g = 8 * t + id.w;  // 16-row group
+            const int row = 16 * g + (id.lane >> 2);
+            const bool real = 16 * g < rows;
+            off[t] = real && mn0 + row < mn_lim ? (uint32_t)((row * row_ld + chunk * VEC) * (int64_t)sizeof(T)) : kOOB;
+            dst[t] = real ? stage_off + 64 * g : -1;
+        }
+    }
+    __device__ __forceinline__ void issue_one(u32x4* L, int stage, int t, int64_t k0, int64_t k_lim, bool full,
+                                              bool live, const WaveIdW& id) const {
+        const bool in = live && dst[t] >= 0 && (full || (int64_t)chunk * VEC < k_lim - k0);
+        u32x4* d = dst[t] >= 0 ? L + stage * WST + dst[t] : L + 4 * WST + 64 * (id.w & 3);
+        if constexpr (BLK) {
+            const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (k0 >> 8) * blk_bytes);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)d, 16, (int)(in ? off[t] : kOOB),
+                                                     (int)((k0 & 255) * (int64_t)sizeof(T)), 0, 0);
+        } else {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)d, 16, (int)(in ? off[t] : kOOB),
+                                                     (int)(k0 * (int64_t)sizeof(T)), 0, 0);
+        }
+    }
+};
+
+template <typename T>
+__device__ __forceinline__ void read_frags_w(u32x4 (&fa)[2], u32x4 (&fb)[5], const u32x4* S, int g,
+                                             const WaveIdW& id) {
+    const int c = 2 * g + id.h;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = id.wm * 64 + i * 32 + id.lr;
+        fa[i] = S[row * NCH4 + swz4(row, c)];
+    }
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        const int row = id.wn * 160 + j * 32 + id.lr;
+        fb[j] = S[kTileM * NCH4 + row * NCH4 + swz4(row, c)];
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void mma_block_w(f32x16 (&acc)[2][5], const u32x4 (&fa)[2], const u32x4 (&fb)[5]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 5; ++j) mma<T>(acc[i][j], fa[i], fb[j]);
+}
+
+// Same contract as gemm_tile_kk with a 256 x 320 tile; acc[i][j] is the 32 x 32 block at tile
+// rows wm*64 + 32i, columns wn*160 + 32j. L must hold WIDE_LDS_CHUNKS chunks.
+template <typename T, bool BA = false, bool BB = false>
+__device__ __forceinline__ void gemm_tile_w(f32x16 (&acc)[2][5], u32x4* L, const WaveIdW& id, const T* A,
+                                            int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim, const T* B,
+                                            int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim, int64_t k_begin,
+                                            int64_t k_end) {
+    constexpr int BKH = Elem<T>::BK / 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 5; ++j) acc[i][j] = f32x16{};
+    const int nk = (int)((k_end - k_begin + BKH - 1) / BKH);
+    if (nk <= 0) return;
+    KOperandW<T, BA, 2> opA;
+    KOperandW<T, BB, 3> opB;
+    opA.init(A, lda, m0, m_lim, 0, kTileM, id);
+    opB.init(B, ldb, n0, n_lim, kTileM * NCH4, kWideN, id);
+    auto kof = [&](int s) { return k_begin + (int64_t)s * BKH; };
+    auto issue = [&](int s) {
+        const bool live = s < nk;
+        const bool fa = kof(s) + BKH <= ka_lim, fb = kof(s) + BKH <= kb_lim;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) opA.issue_one(L, s & 3, t, kof(s), ka_lim, fa, live, id);
+#pragma unroll
+        for (int t = 0; t < 3; ++t) opB.issue_one(L, s & 3, t, kof(s), kb_lim, fb, live, id);
+    };
+    // five DMA instructions per wave per stage
+#pragma unroll
+    for (int s = 0; s < 4; ++s) issue(s);
+    wait_vmem_le<15>();
+    __syncthreads();
+    u32x4 f0a[2], f0b[5], f1a[2], f1b[5];
+    read_frags_w<T>(f0a, f0b, L, 0, id);
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+        KD_SCHED_FENCE();
+        read_frags_w<T>(f1a, f1b, L + (kt & 3) * WST, 1, id);
+        mma_block_w<T>(acc, f0a, f0b);
+#pragma unroll
+        for (int q = 0; q < 7; ++q) {
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 3, 0);
+        KD_SCHED_FENCE();
+        wait_vmem_le<10>();  // stage kt+1 complete; kt+2 and kt+3 may be in flight
+        __syncthreads();
+        KD_SCHED_FENCE();
+        issue(kt + 4);
+        read_frags_w<T>(f0a, f0b, L + ((kt + 1) & 3) * WST, 0, id);
+        mma_block_w<T>(acc, f1a, f1b);
+        // 10 MFMAs carry 5 DMA issues and 7 fragment reads
+#pragma unroll
+        for (int q = 0; q < 5; ++q) {
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM_RD, 1, 1);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 2, 1);
+        }
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
+            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 1);
+        }
+        KD_SCHED_FENCE();
+    }
+    KD_SCHED_FENCE();
+    read_frags_w<T>(f1a, f1b, L + ((nk - 1) & 3) * WST, 1, id);
+    KD_SCHED_FENCE();
+    mma_block_w<T>(acc, f0a, f0b);
+    KD_SCHED_FENCE();
+    mma_block_w<T>(acc, f1a, f1b);
+    KD_SCHED_FENCE();
+    wait_vmem_le<0>();  // no zero-fill may land after the caller reuses the LDS
+    __syncthreads();
+}
+
 // Workgroups go to the 8 XCDs round robin (id % 8). Give XCD x the contiguous range
 // [x*per, (x+1)*per) of logical tiles, in dispatch order, so tiles that share operands run
 // on the same L2 at about the same time. Returns n (no work) for the padding ids.

@@ -26,6 +26,7 @@ using namespace kdkl;
 namespace {
 
 constexpr int64_t kAlign = 256;
+constexpr int64_t kMaxD = (int64_t)1 << 20;  // keeps a tile's 256 rows of d fp32 within 32-bit offsets
 constexpr int64_t kDwGroup = 4;  // chunks per dW pass
 
 struct Carve {
@@ -51,7 +52,7 @@ kd_status check_problem(const kd_problem* p) {
     if (!p) return KD_ERR_NULL;
     if (p->act != KD_FP32 && p->act != KD_BF16) return KD_ERR_DTYPE;
     if (p->tlogit != KD_FP32 && p->tlogit != KD_BF16) return KD_ERR_DTYPE;
-    if (p->N < 1 || p->d < 8 || p->d % 8 != 0 || p->V < 1 || p->V > (int64_t)kTileN * kMaxVTiles) return KD_ERR_SHAPE;
+    if (p->N < 1 || p->d < 8 || p->d % 8 != 0 || p->d > kMaxD || p->V < 1 || p->V > (int64_t)kTileN * kMaxVTiles) return KD_ERR_SHAPE;
     if (p->K < 1 || p->K > kMaxK || p->K > p->V || p->chunk < 1) return KD_ERR_SHAPE;
     const int64_t lim = (int64_t)1 << 31;
     if ((p->N + kTileM) * p->K >= lim || p->N * p->d >= lim || p->V * p->d >= lim) return KD_ERR_SHAPE;
@@ -106,7 +107,7 @@ FusedWs layout_fused(const kd_problem* p, void* ws) {
     const int64_t n_vt = n_vtiles(V), Vp = n_vt * kTileN;
     const int64_t C = chunk_rows(p);
     w.n_vsplit = fwd_vsplits(N, V);
-    w.n_split = dh_splits(C, d, V);
+    w.n_split = dh_splits(C, d, V, true);
     Carve f(ws);
     w.status = (uint32_t*)f.take(kAlign);
     w.plan_off = (int32_t*)f.take(sizeof(int32_t) * n_rblocks(N) * (n_vt + 1));
@@ -166,7 +167,7 @@ StoredWs layout_stored(const kd_problem* p, void* ws, bool all_rows) {
     const int64_t C = chunk_rows(p);
     const int64_t fwd_rows = all_rows ? N : C;
     w.n_vsplit = fwd_vsplits(fwd_rows, V);
-    w.n_split = dh_splits(C, d, V);
+    w.n_split = dh_splits(C, d, V, true);
     w.ldzt = round_up(fwd_rows, 4);
     w.ldgt = kDwGroup * round_up(C, 8);
     const int64_t n_chunks = (N + C - 1) / C;
@@ -208,7 +209,7 @@ DenseWs layout_dense(const kd_problem* p, void* ws) {
     DenseWs w{};
     const int64_t N = p->N, Vp = n_vtiles(p->V) * kTileN;
     w.ldz = Vp;
-    w.n_split = dh_splits(N, p->d, p->V);
+    w.n_split = dh_splits(N, p->d, p->V, false);
     Carve c(ws);
     w.status = (uint32_t*)c.take(kAlign);
     w.Z = (float*)c.take(sizeof(float) * N * Vp);
@@ -326,7 +327,7 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
     if (!H || !W || !idx || !tlog || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
-    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16)) return KD_ERR_VALUE;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_fused_workspace_bytes(p)) return KD_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
@@ -376,7 +377,7 @@ kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const i
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
-    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16)) return KD_ERR_VALUE;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_dense_workspace_bytes(p)) return KD_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
@@ -428,7 +429,7 @@ kd_status kd_chunked_kl(const kd_problem* p, const void* H, const void* W, const
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
-    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16)) return KD_ERR_VALUE;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_chunked_workspace_bytes(p)) return KD_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
@@ -455,7 +456,7 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
-    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16)) return KD_ERR_VALUE;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_fused_fwdbwd_workspace_bytes(p)) return KD_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();

@@ -135,7 +135,7 @@ hipError_t launch_sum_rows(const Shape& sh, const double* row_sum, double* blk_s
                            hipStream_t s);
 
 int64_t round_up(int64_t x, int64_t m);
-int dh_splits(int64_t cc, int64_t d, int64_t V);
+int dh_splits(int64_t cc, int64_t d, int64_t V, bool wide);  // wide: 320-column dH tiles
 int fwd_vsplits(int64_t N, int64_t V);
 
 }  // namespace kdkl

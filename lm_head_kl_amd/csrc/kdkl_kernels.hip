@@ -793,6 +793,44 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dh(DhArgs a) {
         }
 }
 
+// Same product on 256 x 320 tiles (tokens x hidden) with K-blocked G_c and W^T.
+template <typename T>
+__global__ __launch_bounds__(512, 1) void k_dh_w(DhArgs a) {
+    __shared__ u32x4 L[WIDE_LDS_CHUNKS];
+    const WaveIdW id;
+    const int64_t n_tiles = (int64_t)a.n_split * a.n_nt * a.n_mt;
+    const int64_t t = xcd_tile(blockIdx.x, n_tiles);
+    if (t >= n_tiles) return;
+    const int ks = (int)(t / ((int64_t)a.n_nt * a.n_mt));
+    const int rem = (int)(t % ((int64_t)a.n_nt * a.n_mt));
+    const int nt = rem / a.n_mt, mt = rem % a.n_mt;
+    const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kWideN;
+    const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
+    f32x16 acc[2][5];
+    gemm_tile_w<T, true, true>(acc, L, id, (const T*)a.G, a.cc, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d, k_end,
+                               k_begin, k_end);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int64_t row = m0 + id.wm * 64 + acc_row(i, e, id.h);
+            if (row >= a.cc) continue;
+#pragma unroll
+            for (int j = 0; j < 5; ++j) {
+                const int64_t col = n0 + id.wn * 160 + j * 32 + id.lr;
+                if (col >= a.d) continue;
+                const float v = acc[i][j][e];
+                if (a.n_split > 1) {
+                    a.part[((int64_t)ks * a.cc + row) * a.d + col] = v;
+                } else if constexpr (sizeof(T) == 2) {
+                    ((bf16_t*)a.dH)[(a.c0 + row) * a.d + col] = (bf16_t)f2bf(v);
+                } else {
+                    ((float*)a.dH)[(a.c0 + row) * a.d + col] = v;
+                }
+            }
+        }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ part, int n_split, int64_t cc,
                                                    int64_t d, int64_t c0, void* __restrict__ dH) {
@@ -896,6 +934,84 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dw(DwArgs a) {
         load_old(pq, 1, old1);
         add_store(pq, 0, old0);
         add_store(pq, 1, old1);
+        __syncthreads();
+    }
+}
+
+// Same product on 256 x 320 tiles (vocabulary x hidden), operands G_c^T and H_c^T (K contiguous).
+// Read-modify-write through LDS in four passes of 64 rows: pass (i, eh) stages acc[i][*][e] for
+// e in [8 eh, 8 eh + 8), which is 16 rows of each wave's 64 (stage row wm*16 + r, tile row
+// wm*64 + 32 i + 16 eh + r). Stage rows are kWSS floats apart; kWSS % 16 == 8 keeps the two
+// lane halves (rows 4 apart) on different banks. Each thread then handles ten 16-byte items
+// per pass, in two batches; old values are requested ahead of the LDS work that hides them.
+constexpr int kWSS = 328;
+
+template <typename T>
+__global__ __launch_bounds__(512, 1) void k_dw_w(DwArgs a) {
+    constexpr int NT = 512, IB = 5;  // items per thread per batch; 2 batches x 512 x 5 = 64 rows x 80
+    __shared__ u32x4 L[WIDE_LDS_CHUNKS];
+    const WaveIdW id;
+    const int64_t n_tiles = (int64_t)a.n_mt * a.n_nt;
+    const int64_t t = xcd_tile(blockIdx.x, n_tiles);
+    if (t >= n_tiles) return;
+    const int mt = (int)(t / a.n_nt), nt = (int)(t % a.n_nt);
+    const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kWideN;
+    f32x16 acc[2][5];
+    gemm_tile_w<T>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.ccp, (const T*)a.H, a.ldh, n0, a.d, a.ccp, 0, a.ccp);
+    const WaveIdW ie = id.fresh();
+    float* stage = (float*)L;
+    // dW is addressed through a descriptor at the tile origin with 32-bit offsets (d <= 2^20
+    // keeps 256 rows of a tile below 2^31 bytes); items past V or d get an out-of-range offset,
+    // which loads zero and drops the store.
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.dW + m0 * a.d + n0);
+    const int64_t rows_left = a.V - m0, cols_left = a.d - n0;
+    auto item = [&](int p, int bt, int k, int& soff) -> uint32_t {
+        const int it = ie.tid + NT * (IB * bt + k);
+        const int sr = it / 80, c4 = it % 80;
+        const int r = (sr >> 4) * 64 + (p >> 1) * 32 + (p & 1) * 16 + (sr & 15);
+        soff = sr * kWSS + c4 * 4;
+        return (r < rows_left && c4 * 4 < cols_left) ? (uint32_t)((r * a.d + c4 * 4) * 4) : kOOB;
+    };
+    auto load_old = [&](int p, int bt, f32x4 (&old)[IB]) {
+#pragma unroll
+        for (int k = 0; k < IB; ++k) {
+            int soff;
+            const uint32_t o = item(p, bt, k, soff);
+            old[k] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)o, 0, 0));
+        }
+    };
+    auto add_store = [&](int p, int bt, const f32x4 (&old)[IB]) {
+#pragma unroll
+        for (int k = 0; k < IB; ++k) {
+            int soff;
+            const uint32_t o = item(p, bt, k, soff);
+            const f32x4 v = old[k] + *(const f32x4*)(stage + soff);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, (int)o, 0, 0);
+        }
+    };
+    const bool acc_old = a.accumulate != 0;
+    f32x4 old0[IB], old1[IB];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int i = p >> 1, eh = p & 1;
+        if (acc_old) load_old(p, 0, old0);
+        else
+#pragma unroll
+            for (int k = 0; k < IB; ++k) old0[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e8 = 0; e8 < 8; ++e8) {
+            const int e = 8 * eh + e8;
+            const int sr = ie.wm * 16 + 8 * ((e >> 2) & 1) + 4 * ie.h + (e & 3);
+#pragma unroll
+            for (int j = 0; j < 5; ++j) stage[sr * kWSS + ie.wn * 160 + j * 32 + ie.lr] = acc[i][j][e];
+        }
+        __syncthreads();
+        if (acc_old) load_old(p, 1, old1);
+        else
+#pragma unroll
+            for (int k = 0; k < IB; ++k) old1[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        add_store(p, 0, old0);
+        add_store(p, 1, old1);
         __syncthreads();
     }
 }
@@ -1305,15 +1421,29 @@ static int device_cus() {
 
 static unsigned grid_xcd(int64_t n_tiles) { return (unsigned)(8 * ((n_tiles + 7) / 8)); }
 
-int dh_splits(int64_t cc, int64_t d, int64_t V) {
-    const int64_t tiles = ((cc + kTileM - 1) / kTileM) * ((d + kTileN - 1) / kTileN);
+int dh_splits(int64_t cc, int64_t d, int64_t V, bool wide) {
+    const int64_t tiles = ((cc + kTileM - 1) / kTileM) * ((d + (wide ? kWideN : kTileN) - 1) / (wide ? kWideN : kTileN));
     if (tiles >= 512) return 1;
-    int64_t s = (768 + tiles - 1) / tiles;
     const int64_t ksteps = (V + 63) / 64;
-    if (s > ksteps / 4) s = ksteps / 4;
-    if (s > 32) s = 32;
-    if (s < 1) s = 1;
-    return (int)s;
+    const int64_t s_max = std::max<int64_t>(1, std::min<int64_t>(32, ksteps / 4));
+    if (!wide) {
+        const int64_t s = std::min<int64_t>((768 + tiles - 1) / tiles, s_max);
+        return (int)std::max<int64_t>(s, 1);
+    }
+    // Fewest splits that fill the 256 compute units in whole rounds to within 5 % (each split
+    // adds a partial of cc x d floats to write and reduce); else the best fill up to 3 rounds.
+    int64_t best = 1;
+    double best_fill = 0.0;
+    for (int64_t s = 1; s <= s_max; ++s) {
+        const int64_t n = tiles * s;
+        const double fill = (double)n / (double)(((n + 255) / 256) * 256);
+        if (n >= 256 && fill >= 0.95) return (int)s;
+        if (n <= 768 && fill > best_fill + 1e-9) {
+            best = s;
+            best_fill = fill;
+        }
+    }
+    return (int)best;
 }
 
 int combine_blocks(int64_t N) { return (int)((N + kCombRows - 1) / kCombRows); }
@@ -1516,17 +1646,17 @@ hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W
     a.kper = round_up((a.Vp + n_split - 1) / n_split, 64);
     a.part = part;
     a.dH = dH;
-    a.n_nt = (int)((sh.d + kTileN - 1) / kTileN);
+    a.n_nt = (int)((sh.d + (WT ? kWideN : kTileN) - 1) / (WT ? kWideN : kTileN));
     a.n_mt = (int)((cc + kTileM - 1) / kTileM);
     const dim3 grid(grid_xcd((int64_t)n_split * a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16) {
         if (WT)
-            KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, true, kDhWaves>), grid, dim3(64 * kDhWaves), 0, s, a);
+            KD_LAUNCH(kKindDh, s, k_dh_w<bf16_t>, grid, dim3(512), 0, s, a);
         else
             KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, false, 4>), grid, dim3(NTHR), 0, s, a);
     } else {
         if (WT)
-            KD_LAUNCH(kKindDh, s, (k_dh<float, true, kDhWaves>), grid, dim3(64 * kDhWaves), 0, s, a);
+            KD_LAUNCH(kKindDh, s, k_dh_w<float>, grid, dim3(512), 0, s, a);
         else
             KD_LAUNCH(kKindDh, s, (k_dh<float, false, 4>), grid, dim3(NTHR), 0, s, a);
     }
@@ -1581,13 +1711,13 @@ hipError_t launch_dw_t(const Shape& sh, const void* GT, int64_t ldgt, const void
     a.ccp = round_up(cc, 8);
     a.accumulate = accumulate ? 1 : 0;
     a.dW = dW;
-    a.n_nt = (int)((sh.d + kTileN - 1) / kTileN);
+    a.n_nt = (int)((sh.d + kWideN - 1) / kWideN);
     a.n_mt = (int)(a.Vp / kTileM);
     const dim3 grid(grid_xcd((int64_t)a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16)
-        KD_LAUNCH(kKindDw, s, (k_dw<bf16_t, true, kDwWaves>), grid, dim3(64 * kDwWaves), 0, s, a);
+        KD_LAUNCH(kKindDw, s, k_dw_w<bf16_t>, grid, dim3(512), 0, s, a);
     else
-        KD_LAUNCH(kKindDw, s, (k_dw<float, true, kDwWaves>), grid, dim3(64 * kDwWaves), 0, s, a);
+        KD_LAUNCH(kKindDw, s, k_dw_w<float>, grid, dim3(512), 0, s, a);
     return hipGetLastError();
 }
 

@@ -139,6 +139,7 @@ def dense(p, H=F, dH=F, ws=F, nbytes=None):
 @pytest.mark.parametrize("bad,code", [
     (dict(N=0), 2), (dict(d=0), 2), (dict(d=12), 2), (dict(V=0), 2), (dict(K=0), 2), (dict(K=1025, V=4000), 2),
     (dict(V=50, K=60), 2), (dict(chunk=0), 2), (dict(V=256 * 16384 + 1), 2), (dict(N=1 << 30, d=8), 2),
+    (dict(d=(1 << 20) + 8, V=1000, N=1000), 2),
     (dict(act=2), 3), (dict(tlogit=-1), 3),
     (dict(T=0.0), 4), (dict(T=-1.0), 4), (dict(T=float("nan")), 4), (dict(T=float("inf")), 4),
     (dict(n_norm=float("nan")), 4), (dict(flags=4), 4), (dict(reserved=1), 4),
@@ -171,6 +172,7 @@ def test_workspace_and_alignment_rejected():
     assert fwd(p, ws=ctypes.c_void_p(0x10000 + 128)) == 5  # not 256-byte aligned
     assert fwd(p, H=ctypes.c_void_p(0x10008)) == 4          # vector loads need 16-byte alignment
     assert bwd(p, dH=ctypes.c_void_p(0x10004)) == 4
+    assert bwd(p, dW=ctypes.c_void_p(0x10008)) == 4
     dn = _lib.lib().kd_dense_workspace_bytes(ctypes.byref(p))
     assert dense(p, nbytes=dn - 1) == 5
 
