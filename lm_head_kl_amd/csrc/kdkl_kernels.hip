@@ -734,7 +734,9 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, in
 }
 
 // ------------------------------------------------------------------------------------------
-// dH = G W (A = G_c with the vocabulary contiguous, B = W with d contiguous).
+// dH = G W. The dense path multiplies G [rows][ldg] (vocabulary contiguous) by W [V][d]
+// (d contiguous) on 256 x 256 tiles; the chunked paths use K-blocked G_c and W^T on
+// 256 x 320 tiles (k_dh_w).
 
 struct DhArgs {
     const void* G;   // G_c [cc][ldg] row-major, or K-blocked [Vp/256][cc][256] (with W^T)
@@ -748,12 +750,10 @@ struct DhArgs {
     void* dH;
 };
 
-template <typename T, bool WT, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void k_dh(DhArgs a) {
-    static_assert(WT || NW == 4, "the M/N-contiguous path runs on four waves");
-    constexpr int JN = 16 / NW;
+template <typename T>
+__global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
-    const WaveIdN<NW> id;
+    const WaveId id;
     // Logical tiles are split major, then column tile, then row tile: an XCD's band shares one
     // vocabulary slice of G_c and W.
     const int64_t n_tiles = (int64_t)a.n_split * a.n_nt * a.n_mt;
@@ -764,13 +764,9 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dh(DhArgs a) {
     const int nt = rem / a.n_mt, mt = rem % a.n_mt;
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
     const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
-    f32x16 acc[4][JN];
-    if constexpr (WT)
-        gemm_tile_kk<T, true, true, NW>(acc, L, id, (const T*)a.G, a.cc, m0, a.cc, k_end, (const T*)a.W, a.d, n0,
-                                        a.d, k_end, k_begin, k_end);
-    else
-        gemm_tile<T, true, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
-                                  min(a.V, k_end), k_begin, k_end);
+    f32x16 acc[4][4];
+    gemm_tile<T, true, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
+                              min(a.V, k_end), k_begin, k_end);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -778,8 +774,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dh(DhArgs a) {
             const int64_t row = m0 + id.wm * 128 + acc_row(i, e, id.h);
             if (row >= a.cc) continue;
 #pragma unroll
-            for (int j = 0; j < JN; ++j) {
-                const int64_t col = n0 + id.wn * WaveIdN<NW>::NSPAN + j * 32 + id.lr;
+            for (int j = 0; j < 4; ++j) {
+                const int64_t col = n0 + id.wn * 128 + j * 32 + id.lr;
                 if (col >= a.d) continue;
                 const float v = acc[i][j][e];
                 if (a.n_split > 1) {
@@ -851,7 +847,9 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
 }
 
 // ------------------------------------------------------------------------------------------
-// dW (+)= G_c^T H_c (A = G_c^T: vocabulary contiguous; B = H_c: d contiguous).
+// dW (+)= G^T H. The dense path reads G [rows][ldg] and H [rows][d] as stored (vocabulary and
+// d contiguous) on 256 x 256 tiles; the chunked paths use G_c^T and H_c^T on 256 x 320 tiles
+// (k_dw_w).
 
 struct DwArgs {
     const void* G;   // G_c [cc][ldg], or G_c^T [Vp][ldg] (K contiguous)
@@ -865,13 +863,12 @@ struct DwArgs {
     float* dW;
 };
 
-template <typename T, bool KK, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void k_dw(DwArgs a) {
-    static_assert(KK || NW == 4, "the M/N-contiguous path runs on four waves");
-    constexpr int NT = 64 * NW, JN = 16 / NW;
+template <typename T>
+__global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
+    constexpr int NT = 256, JN = 4;
     constexpr int IB = 8192 / NT / 2;  // 16-byte items per thread per batch (two batches per pass)
     __shared__ u32x4 L[LDS_CHUNKS];
-    const WaveIdN<NW> id;
+    const WaveId id;
     // Logical tiles are vocab-row major: an XCD's band shares a few G_c column slabs and H_c.
     const int64_t n_tiles = (int64_t)a.n_mt * a.n_nt;
     const int64_t t = xcd_tile(blockIdx.x, n_tiles);
@@ -879,17 +876,13 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dw(DwArgs a) {
     const int mt = (int)(t / a.n_nt), nt = (int)(t % a.n_nt);
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
     f32x16 acc[4][JN];
-    if constexpr (KK)
-        gemm_tile_kk<T, false, false, NW>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.ccp, (const T*)a.H, a.ldh,
-                                          n0, a.d, a.ccp, 0, a.ccp);
-    else
-        gemm_tile<T, false, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.cc, (const T*)a.H + a.c0 * a.d,
-                                   a.d, n0, a.d, a.cc, 0, a.cc);
+    gemm_tile<T, false, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.cc, (const T*)a.H + a.c0 * a.d, a.d,
+                               n0, a.d, a.cc, 0, a.cc);
     // Read-modify-write through LDS, in two passes of 128 rows. Every dW access is a 16-byte
     // vector and a wave covers 1 KB of one row. The old values of a pass's first half are
     // requested before its staging writes and those of the second half before the first half
     // is added, so the load latency hides behind LDS work.
-    const WaveIdN<NW> ie = id.fresh();
+    const WaveId ie = id.fresh();
     float* stage = (float*)L;
     auto item = [&](int pq, int bt, int k, int& sr, int64_t& row, int64_t& col) {
         const int it = ie.tid + NT * (IB * bt + k);
@@ -928,7 +921,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_dw(DwArgs a) {
                 const int sr = ie.wm * 64 + ii * 32 + blk_row(e, ie.h);
 #pragma unroll
                 for (int j = 0; j < JN; ++j)
-                    stage[st_idx(sr, ie.wn * WaveIdN<NW>::NSPAN + j * 32 + ie.lr)] = acc[2 * pq + ii][j][e];
+                    stage[st_idx(sr, ie.wn * 128 + j * 32 + ie.lr)] = acc[2 * pq + ii][j][e];
             }
         __syncthreads();
         load_old(pq, 1, old1);
@@ -1395,7 +1388,7 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Waves per workgroup of the dW and dH GEMMs: eight (two per SIMD) hide more of the operand
 // latency than four.
-constexpr int kDwWaves = 8, kDhWaves = 8, kGradWaves = 8, kFwdWaves = 8;
+constexpr int kGradWaves = 8, kFwdWaves = 8;
 
 // Vocab lanes of the forward: at least 8, and enough units to give every CU one.
 int fwd_vsplits(int64_t N, int64_t V) {
@@ -1653,12 +1646,12 @@ hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W
         if (WT)
             KD_LAUNCH(kKindDh, s, k_dh_w<bf16_t>, grid, dim3(512), 0, s, a);
         else
-            KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, false, 4>), grid, dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindDh, s, k_dh<bf16_t>, grid, dim3(NTHR), 0, s, a);
     } else {
         if (WT)
             KD_LAUNCH(kKindDh, s, k_dh_w<float>, grid, dim3(512), 0, s, a);
         else
-            KD_LAUNCH(kKindDh, s, (k_dh<float, false, 4>), grid, dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindDh, s, k_dh<float>, grid, dim3(NTHR), 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split <= 1) return e;
@@ -1690,9 +1683,9 @@ hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H
     a.n_mt = (int)(a.Vp / kTileM);
     const dim3 grid(grid_xcd((int64_t)a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16)
-        KD_LAUNCH(kKindDw, s, (k_dw<bf16_t, false, 4>), grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindDw, s, k_dw<bf16_t>, grid, dim3(NTHR), 0, s, a);
     else
-        KD_LAUNCH(kKindDw, s, (k_dw<float, false, 4>), grid, dim3(NTHR), 0, s, a);
+        KD_LAUNCH(kKindDw, s, k_dw<float>, grid, dim3(NTHR), 0, s, a);
     return hipGetLastError();
 }
 
