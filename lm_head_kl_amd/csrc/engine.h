@@ -416,6 +416,12 @@ __device__ __forceinline__ void mma_block(f32x16 (&acc)[4][JN], const u32x4 (&fa
 
 template <int N> __device__ __forceinline__ void wait_vmem_le() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
+// Barrier for an LDS hand-off only. __syncthreads() also fences global memory at workgroup
+// scope, so after global stores (a previous tile's epilogue) it waits for all of them and for
+// every DMA load still in flight; this waits for the wave's LDS operations alone. DMA writes
+// into LDS are covered by the caller's vmcnt wait.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 #define KD_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 // sched_group_barrier masks
 #define KD_SG_MFMA 0x008
@@ -462,7 +468,7 @@ __device__ __forceinline__ void gemm_tile_kk(f32x16 (&acc)[4][16 / NW], u32x4* L
         opB.issue(stageB(s), kof(s), kb_lim, s < nk, id);
     }
     wait_vmem_le<6 * TPI>();
-    __syncthreads();
+    lds_barrier();
     u32x4 f0a[4], f0b[JN], f1a[4], f1b[JN];
     read_frags4<T, NW>(f0a, f0b, stageA(0), stageB(0), 0, id);
     for (int kt = 0; kt + 1 < nk; ++kt) {
@@ -477,7 +483,7 @@ __device__ __forceinline__ void gemm_tile_kk(f32x16 (&acc)[4][16 / NW], u32x4* L
         __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, NMM - NFR, 0);
         KD_SCHED_FENCE();
         wait_vmem_le<4 * TPI>();  // stage kt+1 complete; kt+2 and kt+3 may be in flight
-        __syncthreads();
+        lds_barrier();
         KD_SCHED_FENCE();
         {
             const int s = kt + 4;
@@ -664,7 +670,7 @@ __device__ __forceinline__ void gemm_tile_w(f32x16 (&acc)[2][5], u32x4* L, const
 #pragma unroll
     for (int s = 0; s < 4; ++s) issue(s);
     wait_vmem_le<15>();
-    __syncthreads();
+    lds_barrier();
     u32x4 f0a[2], f0b[5], f1a[2], f1b[5];
     read_frags_w<T>(f0a, f0b, L, 0, id);
     for (int kt = 0; kt + 1 < nk; ++kt) {
@@ -679,7 +685,7 @@ __device__ __forceinline__ void gemm_tile_w(f32x16 (&acc)[2][5], u32x4* L, const
         __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 3, 0);
         KD_SCHED_FENCE();
         wait_vmem_le<10>();  // stage kt+1 complete; kt+2 and kt+3 may be in flight
-        __syncthreads();
+        lds_barrier();
         KD_SCHED_FENCE();
         issue(kt + 4);
         read_frags_w<T>(f0a, f0b, L + ((kt + 1) & 3) * WST, 0, id);
