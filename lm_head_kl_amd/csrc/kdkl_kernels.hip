@@ -500,16 +500,18 @@ struct GradArgs {
     int64_t ldzt, zt_col0;
 };
 
+// Non-temporal: G and G^T (1.65 GB per chunk) would otherwise evict the W and H_c lines the
+// next tiles' operand loads hit in L2 (about 1% faster gradient kernel).
 template <typename T>
 __device__ __forceinline__ void store8(T* dst, const float (&x)[8]) {
     if constexpr (sizeof(T) == 2) {
         u32x4 o;
 #pragma unroll
         for (int u = 0; u < 4; ++u) o[u] = pack_bf16x2(x[2 * u], x[2 * u + 1]);
-        *(u32x4*)dst = o;
+        __builtin_nontemporal_store(o, (u32x4*)dst);
     } else {
-        *(f32x4*)dst = f32x4{x[0], x[1], x[2], x[3]};
-        *(f32x4*)(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
+        __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, (f32x4*)dst);
+        __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, (f32x4*)(dst + 4));
     }
 }
 
