@@ -86,6 +86,7 @@ def test_small_bf16_dense_path():
     dict(N=257, d=136, V=513, K=128, chunk=256, T=2.0),     # two lanes' worth of K, one row past a block
     dict(N=64, d=32, V=40, K=40, chunk=64, T=1.0),          # K = V: every token cached
     dict(N=300, d=64, V=3000, K=1024, chunk=256, T=1.0),    # K at its maximum
+    dict(N=520, d=648, V=5000, K=33, chunk=512, T=1.1),     # last 320-wide hidden tile holds 8 columns
 ])
 def test_ragged_and_edge_shapes(dtype, shape):
     p = datagen.make("tiny", N=shape["N"], d=shape["d"], V=shape["V"], K=shape["K"], T=shape["T"],
