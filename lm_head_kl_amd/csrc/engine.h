@@ -537,6 +537,141 @@ __device__ __forceinline__ void gemm_tile_kk(f32x16 (&acc)[4][16 / NW], u32x4* L
 }
 
 // ------------------------------------------------------------------------------------------
+// 16 x 16 blocks for the 256 x 256 tile. v_mfma_f32_16x16x32_bf16 does half the work of a
+// 32x32x16 in half the cycles but draws less power per FLOP, so at the chip's power limit a
+// mainloop on it runs about 7% faster. Layout of a 16 x 16 fp32 block (f32x4): lane l holds
+// column l % 16 and rows 4 (l / 16) + 0..3. A fragment is one 16-byte chunk per lane: row
+// l % 16 of the block and chunk l / 16 of the stage's four (K32 bf16 or K16 fp32), so a stage
+// is one k-group. The fp32 path issues four v_mfma_f32_16x16x4_f32, instruction i taking
+// element i of every lane's chunk; lane group g then supplies k = 4g + i, the same k in A and B.
+template <typename T> __device__ __forceinline__ void mma16(f32x4& c, const u32x4& a, const u32x4& b);
+template <> __device__ __forceinline__ void mma16<bf16_t>(f32x4& c, const u32x4& a, const u32x4& b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                0, 0);
+}
+template <> __device__ __forceinline__ void mma16<float>(f32x4& c, const u32x4& a, const u32x4& b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[i]), __uint_as_float(b[i]), c, 0, 0, 0);
+}
+template <typename T> struct Mfma16Count { static constexpr int N = sizeof(T) == 2 ? 1 : 4; };
+
+// Fragment of the 16-row block whose first row is r0 (in a stage's A or B region).
+__device__ __forceinline__ u32x4 frag16(const u32x4* S, int r0, int lane) {
+    const int row = r0 + (lane & 15);
+    return S[row * NCH4 + swz4(row, lane >> 4)];
+}
+
+// Same contract as gemm_tile_kk on eight waves, 16 x 16 blocks: each wave holds 128 x 64 as
+// 8 x 4 blocks, acc[i][j] at tile rows wm*128 + 16i, columns wn*64 + 16j. Stage k splits by A
+// rows: part 0 = rows 0-3 (A rows 4-7 of the stage read meanwhile), barrier, part 1 = rows 4-7
+// (the DMA of stage k+4 issued, A rows 0-3 and B of stage k+1 read meanwhile). B alternates
+// between two register sets, so the loop runs two stages per trip.
+template <typename T, bool BA = false, bool BB = false>
+__device__ __forceinline__ void gemm_tile_kk16(f32x4 (&acc)[8][4], u32x4* L, const WaveIdN<8>& id, const T* A,
+                                               int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim, const T* B,
+                                               int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim,
+                                               int64_t k_begin, int64_t k_end) {
+    constexpr int BKH = Elem<T>::BK / 2;
+    constexpr int TPI = 2;  // DMA instructions per operand per wave per stage
+    constexpr int MM = Mfma16Count<T>::N;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int nk = (int)((k_end - k_begin + BKH - 1) / BKH);
+    if (nk <= 0) return;
+    KOperand4<T, BA, 8> opA;
+    KOperand4<T, BB, 8> opB;
+    opA.init(A, lda, m0, m_lim, id);
+    opB.init(B, ldb, n0, n_lim, id);
+    auto stageA = [&](int s) { return L + (2 * (s & 3)) * TILE4; };
+    auto stageB = [&](int s) { return L + (2 * (s & 3) + 1) * TILE4; };
+    auto kof = [&](int s) { return k_begin + (int64_t)s * BKH; };
+    u32x4 fa[8], fb[2][4];
+    auto rdA = [&](int i0, int s) {
+#pragma unroll
+        for (int i = i0; i < i0 + 4; ++i) fa[i] = frag16(stageA(s), id.wm * 128 + 16 * i, id.lane);
+    };
+    auto rdB = [&](u32x4 (&b)[4], int s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) b[j] = frag16(stageB(s), id.wn * 64 + 16 * j, id.lane);
+    };
+    auto stage = [&](int k, const u32x4 (&bc)[4], u32x4 (&bn)[4], bool more) {
+        KD_SCHED_FENCE();
+        rdA(4, k);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mma16<T>(acc[i][j], fa[i], bc[j]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 3 * MM, 0);
+            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 4 * MM, 0);
+        KD_SCHED_FENCE();
+        if (more)
+            wait_vmem_le<4 * TPI>();  // stage k+1 complete; k+2 and k+3 may be in flight
+        else
+            wait_vmem_le<0>();
+        lds_barrier();
+        KD_SCHED_FENCE();
+        if (more) {
+            const int s = k + 4;
+            const bool live = s < nk;
+            const bool fa_ = kof(s) + BKH <= ka_lim, fb_ = kof(s) + BKH <= kb_lim;
+#pragma unroll
+            for (int t = 0; t < TPI; ++t) {
+                opA.issue_one(stageA(s), t, kof(s), ka_lim, fa_, live, id);
+                opB.issue_one(stageB(s), t, kof(s), kb_lim, fb_, live, id);
+            }
+            rdA(0, k + 1);
+            rdB(bn, k + 1);
+        }
+#pragma unroll
+        for (int i = 4; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mma16<T>(acc[i][j], fa[i], bc[j]);
+        if (more) {
+            // 16 MFMAs carry 4 DMA issues and 8 fragment reads
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, MM, 1);
+                __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM_RD, 1, 1);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, MM, 1);
+                __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 4 * MM, 1);
+        }
+        KD_SCHED_FENCE();
+    };
+    // Every stage slot issues its 2 TPI loads, live or not, so the wait counts are constant.
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        opA.issue(stageA(s), kof(s), ka_lim, s < nk, id);
+        opB.issue(stageB(s), kof(s), kb_lim, s < nk, id);
+    }
+    wait_vmem_le<6 * TPI>();
+    lds_barrier();
+    rdA(0, 0);
+    rdB(fb[0], 0);
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+        stage(kt, fb[0], fb[1], true);
+        stage(kt + 1, fb[1], fb[0], true);
+    }
+    // the last one or two stages
+    stage(kt, fb[0], fb[1], kt + 1 < nk);
+    if (kt + 1 < nk) stage(kt + 1, fb[1], fb[0], false);
+    wait_vmem_le<0>();  // no zero-fill may land after the caller reuses the LDS
+    __syncthreads();
+}
+
+// ------------------------------------------------------------------------------------------
 // Wide tile: 256 x 320 (M x N), for products whose N is the hidden size d. d = 2880 is 9 x 320
 // but 11.25 x 256, so 256-wide column tiles waste a quarter of their last tile; a 320-wide tile
 // also moves about 10 % fewer operand bytes per FLOP. Eight waves in a 4 x 2 grid, 64 x 160 per

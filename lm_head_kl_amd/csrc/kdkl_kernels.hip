@@ -109,10 +109,10 @@ __device__ __forceinline__ int blk_row(int e, int h) { return 8 * (e >> 2) + 4 *
 // (tokens) of fp32. Stage row sr holds tile row (sr/64)*128 + pass*64 + sr%64. Column t of row
 // r sits at t ^ st_swz(r); the XOR touches bits 2..5 only, so runs of 4 columns stay
 // contiguous and 16-byte aligned. With 64 four-byte banks it is conflict free for the
-// accumulator writes (rows r and r+4 of a wave land in opposite bank halves) and for column
-// reads of 16 rows 8 apart by 4 tokens.
+// accumulator writes of 16 x 16 blocks (rows r, r+4, r+8, r+12 by 16 tokens: bits 4..5 of the
+// XOR differ) and for column reads of 16 rows 8 apart by 4 tokens (bits 2..5 differ).
 constexpr int SST = kTileN;
-__device__ __forceinline__ int st_swz(int r) { return (((r >> 3) ^ (((r >> 2) & 1) << 3)) & 15) << 2; }
+__device__ __forceinline__ int st_swz(int r) { return (((r >> 3) ^ (((r >> 2) & 3) << 2)) & 15) << 2; }
 __device__ __forceinline__ int st_idx(int r, int t) { return r * SST + (t ^ st_swz(r)); }
 // Stage row of tile row c in the pass that holds it (pass (c >> 6) & 1).
 __device__ __forceinline__ int st_row(int c) { return (c >> 7) * 64 + (c & 63); }
@@ -264,7 +264,8 @@ struct FwdArgs {
 // and lanes only meet once per unit.
 template <typename T, bool ZT, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void k_fwd(FwdArgs a) {
-    constexpr int NT = 64 * NW, JN = 16 / NW, NSPAN = WaveIdN<NW>::NSPAN;
+    static_assert(NW == 8, "the forward runs on eight waves with 16 x 16 blocks");
+    constexpr int NT = 64 * NW;
     __shared__ u32x4 L[LDS_CHUNKS];
     const WaveIdN<NW> id;
     const int64_t P = gridDim.x;
@@ -277,11 +278,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(FwdArgs a) {
         const int rb = (int)(u / a.Q), q = (int)(u % a.Q);
         const int64_t m0 = (int64_t)rb * kTileM;  // first token of the row block
         const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
-        // Running (max, sum) in units of y = z*log2(e)/T for this lane's token columns j, over
-        // the vocabulary rows the lane holds.
-        float run_m[JN], run_s[JN];
+        // Running (max, sum) in units of y = z*log2(e)/T for this lane's 4 token columns
+        // wn*64 + 16j + lane%16, over the vocabulary rows the lane holds.
+        float run_m[4], run_s[4];
 #pragma unroll
-        for (int j = 0; j < JN; ++j) {
+        for (int j = 0; j < 4; ++j) {
             run_m[j] = -INFINITY;
             run_s[j] = 0.f;
         }
@@ -292,10 +293,11 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(FwdArgs a) {
             // mainloop, so their load latency hides behind it.
             const int e0 = off[vt], e1 = off[vt + 1];
             const uint32_t my_en = e0 + id.tid < e1 ? a.ent[e0 + id.tid] : 0xffffffffu;
-            f32x16 acc[4][JN];
-            gemm_tile_kk<T, false, false, NW>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, (const T*)a.H, a.d, m0,
-                                              a.N, a.d, 0, a.d);
+            f32x4 acc[8][4];
+            gemm_tile_kk16<T>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, (const T*)a.H, a.d, m0, a.N, a.d, 0,
+                              a.d);
             const WaveIdN<NW> ie = id.fresh();
+            const int g4 = 4 * (ie.lane >> 4), c16 = ie.lane & 15;
 
             // Gather z at the cached ids of this (row block, vocab tile): two passes of 128
             // vocabulary rows staged in LDS. The paths that keep the logits also store the
@@ -304,15 +306,15 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(FwdArgs a) {
 #pragma unroll
                 for (int pq = 0; pq < 2; ++pq) {
 #pragma unroll
-                    for (int ii = 0; ii < 2; ++ii)
+                    for (int i4 = 0; i4 < 4; ++i4)
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const int sr = ie.wm * 64 + ii * 32 + blk_row(e, ie.h);
+                        for (int v = 0; v < 4; ++v) {
+                            const int sr = ie.wm * 64 + 16 * i4 + g4 + v;
 #pragma unroll
-                            for (int j = 0; j < JN; ++j)
-                                stage[st_idx(sr, ie.wn * NSPAN + j * 32 + ie.lr)] = acc[2 * pq + ii][j][e];
+                            for (int j = 0; j < 4; ++j)
+                                stage[st_idx(sr, ie.wn * 64 + 16 * j + c16)] = acc[4 * pq + i4][j][v];
                         }
-                    __syncthreads();
+                    lds_barrier();
                     if (my_en != 0xffffffffu && ((my_en >> 14) & 1) == (uint32_t)pq) {
                         const int r = my_en & 255, c = (my_en >> 8) & 255, k = (int)(my_en >> 16);
                         a.zk[(m0 + r) * a.K + k] = stage[st_idx(st_row(c), r)];
@@ -334,55 +336,52 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(FwdArgs a) {
                                 *(f32x4*)(a.zt + v * a.ldzt + m0 + tok) = *(const f32x4*)(stage + st_idx(sr, tok));
                         }
                     }
-                    __syncthreads();
+                    lds_barrier();
                 }
             }
 
-            // Tile (max, sum) per token column, folded over the lane's 64 vocabulary rows, then
+            // Tile (max, sum) per token column, folded over the lane's 32 vocabulary rows, then
             // merged into the running pair. Rows past V (last tile only) count as -inf.
             const bool vfull = n0 + kTileN <= a.V;
-            const int rows_left = (int)min<int64_t>(kTileN, a.V - n0) - ie.wm * 128 - 4 * ie.h;
+            const int rows_left = (int)min<int64_t>(kTileN, a.V - n0) - ie.wm * 128 - g4;
 #pragma unroll
-            for (int j = 0; j < JN; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 float mx = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 8; ++i)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        const bool ok = vfull || i * 32 + 8 * (e >> 2) + (e & 3) < rows_left;
-                        mx = fmaxf(mx, ok ? acc[i][j][e] : -INFINITY);
+                    for (int v = 0; v < 4; ++v) {
+                        const bool ok = vfull || 16 * i + v < rows_left;
+                        mx = fmaxf(mx, ok ? acc[i][j][v] : -INFINITY);
                     }
-                // With the accumulators in AGPRs (four waves), re-read them for the sum instead of
-                // keeping 64 VGPR copies live.
-                if constexpr (NW == 4) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) asm volatile("" : "+a"(acc[i][j]));
-                }
                 const float mt = mx * a.c;
                 float s = 0.f;
                 if (mx != -INFINITY) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                    for (int i = 0; i < 8; ++i)
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) {
-                            const bool ok = vfull || i * 32 + 8 * (e >> 2) + (e & 3) < rows_left;
-                            s += ok ? exp2_fast(fmaf(acc[i][j][e], a.c, -mt)) : 0.f;
+                        for (int v = 0; v < 4; ++v) {
+                            const bool ok = vfull || 16 * i + v < rows_left;
+                            s += ok ? exp2_fast(fmaf(acc[i][j][v], a.c, -mt)) : 0.f;
                         }
                 }
                 ms_merge(run_m[j], run_s[j], mt, s);
             }
         }
 
-        // Lanes l and l^32 hold the same token columns over different vocabulary rows.
+        // Lanes l, l^16, l^32, l^48 hold the same token columns over different vocabulary rows.
 #pragma unroll
-        for (int j = 0; j < JN; ++j) {
-            const float m2 = __shfl_xor(run_m[j], 32), s2 = __shfl_xor(run_s[j], 32);
+        for (int j = 0; j < 4; ++j) {
+            float m2 = __shfl_xor(run_m[j], 16), s2 = __shfl_xor(run_s[j], 16);
+            ms_merge(run_m[j], run_s[j], m2, s2);
+            m2 = __shfl_xor(run_m[j], 32);
+            s2 = __shfl_xor(run_s[j], 32);
             ms_merge(run_m[j], run_s[j], m2, s2);
         }
-        if (id.h == 0) {
+        if (id.lane < 16) {
 #pragma unroll
-            for (int j = 0; j < JN; ++j) {
-                const int64_t g = m0 + id.wn * NSPAN + j * 32 + id.lr;
+            for (int j = 0; j < 4; ++j) {
+                const int64_t g = m0 + id.wn * 64 + 16 * j + id.lane;
                 if (g < a.N) a.part[(int64_t)(q * 2 + id.wm) * a.N + g] = make_float2(run_m[j], run_s[j]);
             }
         }
@@ -573,7 +572,8 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
 
 template <typename T, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
-    constexpr int NT = 64 * NW, JN = 16 / NW, NSPAN = WaveIdN<NW>::NSPAN;
+    static_assert(NW == 8, "the gradient kernel runs on eight waves with 16 x 16 blocks");
+    constexpr int NT = 64 * NW;
     __shared__ u32x4 L[LDS_CHUNKS];
     const WaveIdN<NW> id;
     // Persistent when launched with fewer workgroups than tiles. Logical tiles are vocab-tile
@@ -590,11 +590,12 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
         const int64_t r0 = (int64_t)rb * kTileM;  // token offset within the chunk
         const int64_t n0 = (int64_t)vt * kTileN;
         const float gs = (a.grad ? a.grad[0] : 1.f) * a.gsc;
-        float l2[JN];
-        bool tok_ok[JN];
+        // lse (log2 units) of the lane's 4 token columns wn*64 + 16j + lane%16
+        float l2[4];
+        bool tok_ok[4];
 #pragma unroll
-        for (int j = 0; j < JN; ++j) {
-            const int64_t tr = r0 + id.wn * NSPAN + j * 32 + id.lr;
+        for (int j = 0; j < 4; ++j) {
+            const int64_t tr = r0 + id.wn * 64 + 16 * j + (id.lane & 15);
             tok_ok[j] = tr < a.cc;
             l2[j] = tok_ok[j] ? a.lse[a.c0 + tr] * kLog2e : 0.f;
         }
@@ -608,24 +609,24 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
             my_en = a.ent[e0 + id.tid];
             my_pt = a.pt[(r0 + (my_en & 255)) * a.K + (my_en >> 16)];
         }
-        f32x16 acc[4][JN];
-        gemm_tile_kk<T, false, false, NW>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, Hc, a.d, r0, a.cc, a.d, 0,
-                                          a.d);
+        f32x4 acc[8][4];
+        gemm_tile_kk16<T>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, Hc, a.d, r0, a.cc, a.d, 0, a.d);
         const WaveIdN<NW> ie = id.fresh();
+        const int g4 = 4 * (ie.lane >> 4), c16 = ie.lane & 15;
 
 #pragma unroll
         for (int pq = 0; pq < 2; ++pq) {
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
-                const int i = 2 * pq + ii;
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int i = 4 * pq + i4;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const bool vok = n0 + ie.wm * 128 + i * 32 + blk_row(e, ie.h) < a.V;
-                    const int sr = ie.wm * 64 + ii * 32 + blk_row(e, ie.h);
+                for (int v = 0; v < 4; ++v) {
+                    const bool vok = n0 + ie.wm * 128 + 16 * i + g4 + v < a.V;
+                    const int sr = ie.wm * 64 + 16 * i4 + g4 + v;
 #pragma unroll
-                    for (int j = 0; j < JN; ++j) {
-                        const float v = (vok && tok_ok[j]) ? gs * exp2_fast(fmaf(acc[i][j][e], a.c, -l2[j])) : 0.f;
-                        stage[st_idx(sr, ie.wn * NSPAN + j * 32 + ie.lr)] = v;
+                    for (int j = 0; j < 4; ++j) {
+                        const float x = (vok && tok_ok[j]) ? gs * exp2_fast(fmaf(acc[i][j][v], a.c, -l2[j])) : 0.f;
+                        stage[st_idx(sr, ie.wn * 64 + 16 * j + c16)] = x;
                     }
                 }
             }
