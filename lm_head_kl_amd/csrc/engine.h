@@ -1,29 +1,38 @@
 // MFMA tile engine for gfx950, shared by every GEMM-shaped kernel of libkdkl.
 //
-// A workgroup of 256 threads computes one 256 x 256 fp32 tile of C = A B^T over a K range.
-// The threads form four 64-wide waves in a 2 x 2 grid. Each wave owns 128 x 128 of the tile
-// as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16, or of v_mfma_f32_32x32x2_f32 for fp32
-// inputs. The accumulators (256 per lane) live in AGPRs.
+// A workgroup computes one fp32 tile of C = A B^T over a K range, with the accumulators in
+// registers. Four variants:
+//   gemm_tile       256 x 256, four waves (2 x 2, 128 x 128 each as 4 x 4 blocks of
+//                   v_mfma_f32_32x32x16_bf16 / 32x32x2_f32, accumulators in AGPRs), two LDS
+//                   stages of a full K step; takes M/N-contiguous operands (dense path).
+//   gemm_tile_kk    same tile on K-contiguous operands, four LDS stages of half a K step,
+//                   four or eight waves (dense logits).
+//   gemm_tile_kk16  same tile and stages, eight waves (2 x 4, 128 x 64 each as 8 x 4 blocks of
+//                   v_mfma_f32_16x16x32_bf16 / 16x16x4_f32): forward and gradient kernels.
+//   gemm_tile_w     256 x 320, eight waves (4 x 2, 64 x 160 each as 2 x 5 32x32 blocks): dH, dW.
 //
-// Operands reach LDS in 16-byte chunks, double-buffered over K (two stages of 2 x 32 KB):
+// Operands reach LDS in 16-byte chunks:
 //   - K contiguous (element (mn, k) at src[mn*ld + k]): buffer_load_dwordx4 with the LDS
 //     destination bit, straight from memory into LDS. No VGPRs and no ds_write are used.
 //     A wave instruction fills 64 consecutive LDS chunks, so each lane fetches the global
-//     chunk that belongs at its destination under the swizzle below.
-//   - M/N contiguous (element (mn, k) at src[k*ld + mn]): buffer loads of 8 x 8 (bf16) or
-//     4 x 4 (fp32) blocks into VGPRs, transposed in registers and written with ds_write_b128.
+//     chunk that belongs at its destination under the stage's swizzle.
+//   - M/N contiguous (element (mn, k) at src[k*ld + mn], gemm_tile only): buffer loads of
+//     8 x 8 (bf16) or 4 x 4 (fp32) blocks into VGPRs, transposed in registers and written with
+//     ds_write_b128.
 // Rows and k beyond the operand's limits are read through an out-of-range offset of the
 // buffer descriptor. The hardware returns zeros for those, so the loop has no branches.
 //
-// LDS tile layout: [256 rows][8 chunks of 16 bytes]. Chunk c of row r sits at
+// gemm_tile's LDS layout: [256 rows][8 chunks of 16 bytes]. Chunk c of row r sits at
 // c ^ ((r ^ (r >> 3)) & 7). This is conflict free for the MFMA fragment reads (32 rows, one
 // chunk column), for the DMA fill (8 rows x 8 chunks per 1 KB), and for the transposed
-// writes (rows 8 apart).
+// writes (rows 8 apart). The half-K stages use [rows][4 chunks] with their own swizzle (swz4).
 //
 // MFMA lane layouts (checked on gfx950 hardware):
 //   32x32x16 bf16: lane l supplies A[m = l%32][k = 8*(l/32) + 0..7], and B likewise with n.
 //   32x32x2 f32:   lane l supplies A[m = l%32][k = l/32].
 //   Accumulator element e of lane l: row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+//   16x16x32 bf16: lane l supplies A[m = l%16][k = 8*(l/16) + 0..7]; accumulator element v of
+//                  lane l: row 4*(l/16) + v, column l%16.
 // The DMA fill places lane l's 16 bytes at M0 + 16*l; an out-of-range offset writes zeros
 // (also checked on hardware).
 #pragma once
