@@ -9,7 +9,7 @@
 //                   four or eight waves (dense logits).
 //   gemm_tile_kk16  same tile and stages, eight waves (2 x 4, 128 x 64 each as 8 x 4 blocks of
 //                   v_mfma_f32_16x16x32_bf16 / 16x16x4_f32): forward and gradient kernels.
-//   gemm_tile_w     256 x 320, eight waves (4 x 2, 64 x 160 each as 2 x 5 32x32 blocks): dH, dW.
+//   gemm_tile_w16   256 x 320, eight waves (2 x 4, 128 x 80 each as 8 x 5 16x16 blocks): dH, dW.
 //
 // Operands reach LDS in 16-byte chunks:
 //   - K contiguous (element (mn, k) at src[mn*ld + k]): buffer_load_dwordx4 with the LDS
@@ -683,36 +683,14 @@ __device__ __forceinline__ void gemm_tile_kk16(f32x4 (&acc)[8][4], u32x4* L, con
 // ------------------------------------------------------------------------------------------
 // Wide tile: 256 x 320 (M x N), for products whose N is the hidden size d. d = 2880 is 9 x 320
 // but 11.25 x 256, so 256-wide column tiles waste a quarter of their last tile; a 320-wide tile
-// also moves about 10 % fewer operand bytes per FLOP. Eight waves in a 4 x 2 grid, 64 x 160 per
-// wave (2 x 5 MFMA blocks, two waves per SIMD). The stage layout, swizzle, pipeline and schedule
-// are those of gemm_tile_kk: four stages of half a K step, A [256][4 chunks] + B [320][4 chunks]
+// also moves about 10 % fewer operand bytes per FLOP. The stage layout, swizzle and pipeline are
+// those of gemm_tile_kk: four stages of half a K step, A [256][4 chunks] + B [320][4 chunks]
 // = 36 KB each. B takes 20 DMA instructions per stage: waves 0-3 issue three, waves 4-7 two and
 // a third with an out-of-range offset (no memory access) into a 1 KB dummy slot of their own,
 // so every wave issues five and the wait counts stay constant.
 constexpr int kWideN = 320;
 constexpr int WST = (kTileM + kWideN) * NCH4;           // chunks per stage (A then B)
 constexpr int WIDE_LDS_CHUNKS = 4 * WST + 4 * 64;        // four stages + four dummy slots = 148 KB
-
-struct WaveIdW {
-    int tid, lane, w, wm, wn, h, lr;
-    __device__ WaveIdW() {
-        tid = threadIdx.x;
-        lane = tid & 63;
-        w = __builtin_amdgcn_readfirstlane(tid >> 6);
-        wm = w >> 1;
-        wn = w & 1;
-        h = lane >> 5;
-        lr = lane & 31;
-    }
-    __device__ __forceinline__ WaveIdW fresh() const {
-        WaveIdW c = *this;
-        asm volatile("v_mov_b32 %0, %1" : "=v"(c.tid) : "v"(tid));
-        c.lane = c.tid & 63;
-        c.h = c.lane >> 5;
-        c.lr = c.lane & 31;
-        return c;
-    }
-};
 
 // Operand of NI 16-row groups per wave (A: NI = 2 covers 256 rows; B: NI = 3 covers 320 rows,
 // the third group of waves 4-7 being the dummy). Layouts as KOperand4.
@@ -725,8 +703,9 @@ struct KOperandW {
     uint32_t off[NI];
     int dst[NI];  // chunk index of the instruction's destination within a stage, or -1 (dummy)
     int chunk;
+    template <typename Id>
     __device__ __forceinline__ void init(const T* src, int64_t ld, int64_t mn0, int64_t mn_lim, int stage_off,
-                                         int rows, const WaveIdW& id) {
+                                         int rows, const Id& id) {
         const int64_t row_ld = BLK ? 256 : ld;
         if constexpr (BLK) {
             base = (const char*)uniform_ptr(src + mn0 * 256);
@@ -744,8 +723,9 @@ struct KOperandW {
             dst[t] = real ? stage_off + 64 * g : -1;
         }
     }
+    template <typename Id>
     __device__ __forceinline__ void issue_one(u32x4* L, int stage, int t, int64_t k0, int64_t k_lim, bool full,
-                                              bool live, const WaveIdW& id) const {
+                                              bool live, const Id& id) const {
         const bool in = live && dst[t] >= 0 && (full || (int64_t)chunk * VEC < k_lim - k0);
         u32x4* d = dst[t] >= 0 ? L + stage * WST + dst[t] : L + 4 * WST + 64 * (id.w & 3);
         if constexpr (BLK) {
@@ -759,42 +739,22 @@ struct KOperandW {
     }
 };
 
-template <typename T>
-__device__ __forceinline__ void read_frags_w(u32x4 (&fa)[2], u32x4 (&fb)[5], const u32x4* S, int g,
-                                             const WaveIdW& id) {
-    const int c = 2 * g + id.h;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = id.wm * 64 + i * 32 + id.lr;
-        fa[i] = S[row * NCH4 + swz4(row, c)];
-    }
-#pragma unroll
-    for (int j = 0; j < 5; ++j) {
-        const int row = id.wn * 160 + j * 32 + id.lr;
-        fb[j] = S[kTileM * NCH4 + row * NCH4 + swz4(row, c)];
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ void mma_block_w(f32x16 (&acc)[2][5], const u32x4 (&fa)[2], const u32x4 (&fb)[5]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 5; ++j) mma<T>(acc[i][j], fa[i], fb[j]);
-}
-
-// Same contract as gemm_tile_kk with a 256 x 320 tile; acc[i][j] is the 32 x 32 block at tile
-// rows wm*64 + 32i, columns wn*160 + 32j. L must hold WIDE_LDS_CHUNKS chunks.
+// Wide tile on 16 x 16 blocks: eight waves in a 2 x 4 grid, 128 x 80 per wave = 8 x 5 blocks,
+// acc[i][j] at tile rows wm*128 + 16i, columns wn*80 + 16j (WaveIdN<8>). The stage layout and
+// DMA are those above; the schedule is gemm_tile_kk16's: part 0 = A rows 0-3 while A rows 4-7
+// of the stage are read, barrier, part 1 = A rows 4-7 with the DMA of stage k+4 and the reads of
+// stage k+1 (A rows 0-3, and B into the other of two register sets).
 template <typename T, bool BA = false, bool BB = false>
-__device__ __forceinline__ void gemm_tile_w(f32x16 (&acc)[2][5], u32x4* L, const WaveIdW& id, const T* A,
-                                            int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim, const T* B,
-                                            int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim, int64_t k_begin,
-                                            int64_t k_end) {
+__device__ __forceinline__ void gemm_tile_w16(f32x4 (&acc)[8][5], u32x4* L, const WaveIdN<8>& id, const T* A,
+                                              int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim, const T* B,
+                                              int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim, int64_t k_begin,
+                                              int64_t k_end) {
     constexpr int BKH = Elem<T>::BK / 2;
+    constexpr int MM = Mfma16Count<T>::N;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 5; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < 5; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nk = (int)((k_end - k_begin + BKH - 1) / BKH);
     if (nk <= 0) return;
     KOperandW<T, BA, 2> opA;
@@ -810,55 +770,76 @@ __device__ __forceinline__ void gemm_tile_w(f32x16 (&acc)[2][5], u32x4* L, const
 #pragma unroll
         for (int t = 0; t < 3; ++t) opB.issue_one(L, s & 3, t, kof(s), kb_lim, fb, live, id);
     };
+    u32x4 fa[8], fb[2][5];
+    auto rdA = [&](int i0, int s) {
+        const u32x4* S = L + (s & 3) * WST;
+#pragma unroll
+        for (int i = i0; i < i0 + 4; ++i) fa[i] = frag16(S, id.wm * 128 + 16 * i, id.lane);
+    };
+    auto rdB = [&](u32x4 (&b)[5], int s) {
+        const u32x4* S = L + (s & 3) * WST + kTileM * NCH4;
+#pragma unroll
+        for (int j = 0; j < 5; ++j) b[j] = frag16(S, id.wn * 80 + 16 * j, id.lane);
+    };
+    auto stage = [&](int k, const u32x4 (&bc)[5], u32x4 (&bn)[5], bool more) {
+        KD_SCHED_FENCE();
+        rdA(4, k);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 5; ++j) mma16<T>(acc[i][j], fa[i], bc[j]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 4 * MM, 0);
+            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 4 * MM, 0);
+        KD_SCHED_FENCE();
+        if (more)
+            wait_vmem_le<10>();  // stage k+1 complete; k+2 and k+3 may be in flight
+        else
+            wait_vmem_le<0>();
+        lds_barrier();
+        KD_SCHED_FENCE();
+        if (more) {
+            issue(k + 4);
+            rdA(0, k + 1);
+            rdB(bn, k + 1);
+        }
+#pragma unroll
+        for (int i = 4; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 5; ++j) mma16<T>(acc[i][j], fa[i], bc[j]);
+        if (more) {
+            // 20 MFMAs carry 5 DMA issues and 9 fragment reads
+#pragma unroll
+            for (int q = 0; q < 5; ++q) {
+                __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, MM, 1);
+                __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM_RD, 1, 1);
+            }
+#pragma unroll
+            for (int q = 0; q < 9; ++q) {
+                __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, MM, 1);
+                __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 1);
+            }
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 6 * MM, 1);
+        }
+        KD_SCHED_FENCE();
+    };
     // five DMA instructions per wave per stage
 #pragma unroll
     for (int s = 0; s < 4; ++s) issue(s);
     wait_vmem_le<15>();
     lds_barrier();
-    u32x4 f0a[2], f0b[5], f1a[2], f1b[5];
-    read_frags_w<T>(f0a, f0b, L, 0, id);
-    for (int kt = 0; kt + 1 < nk; ++kt) {
-        KD_SCHED_FENCE();
-        read_frags_w<T>(f1a, f1b, L + (kt & 3) * WST, 1, id);
-        mma_block_w<T>(acc, f0a, f0b);
-#pragma unroll
-        for (int q = 0; q < 7; ++q) {
-            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 3, 0);
-        KD_SCHED_FENCE();
-        wait_vmem_le<10>();  // stage kt+1 complete; kt+2 and kt+3 may be in flight
-        lds_barrier();
-        KD_SCHED_FENCE();
-        issue(kt + 4);
-        read_frags_w<T>(f0a, f0b, L + ((kt + 1) & 3) * WST, 0, id);
-        mma_block_w<T>(acc, f1a, f1b);
-        // 10 MFMAs carry 5 DMA issues and 7 fragment reads
-#pragma unroll
-        for (int q = 0; q < 5; ++q) {
-            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM_RD, 1, 1);
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 2, 1);
-        }
-#pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 1, 1);
-            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 1);
-        }
-        KD_SCHED_FENCE();
+    rdA(0, 0);
+    rdB(fb[0], 0);
+    int kt = 0;
+    for (; kt + 2 < nk; kt += 2) {
+        stage(kt, fb[0], fb[1], true);
+        stage(kt + 1, fb[1], fb[0], true);
     }
-    KD_SCHED_FENCE();
-    read_frags_w<T>(f1a, f1b, L + ((nk - 1) & 3) * WST, 1, id);
-    KD_SCHED_FENCE();
-    mma_block_w<T>(acc, f0a, f0b);
-    KD_SCHED_FENCE();
-    mma_block_w<T>(acc, f1a, f1b);
-    KD_SCHED_FENCE();
+    stage(kt, fb[0], fb[1], kt + 1 < nk);
+    if (kt + 1 < nk) stage(kt + 1, fb[1], fb[0], false);
     wait_vmem_le<0>();  // no zero-fill may land after the caller reuses the LDS
     __syncthreads();
 }

@@ -796,7 +796,7 @@ __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
 template <typename T>
 __global__ __launch_bounds__(512, 1) void k_dh_w(DhArgs a) {
     __shared__ u32x4 L[WIDE_LDS_CHUNKS];
-    const WaveIdW id;
+    const WaveIdN<8> id;
     const int64_t n_tiles = (int64_t)a.n_split * a.n_nt * a.n_mt;
     const int64_t t = xcd_tile(blockIdx.x, n_tiles);
     if (t >= n_tiles) return;
@@ -805,18 +805,18 @@ __global__ __launch_bounds__(512, 1) void k_dh_w(DhArgs a) {
     const int nt = rem / a.n_mt, mt = rem % a.n_mt;
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kWideN;
     const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
-    f32x16 acc[2][5];
-    gemm_tile_w<T, true, true>(acc, L, id, (const T*)a.G, a.cc, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d, k_end,
-                               k_begin, k_end);
+    f32x4 acc[8][5];
+    gemm_tile_w16<T, true, true>(acc, L, id, (const T*)a.G, a.cc, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
+                                 k_end, k_begin, k_end);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t row = m0 + id.wm * 64 + acc_row(i, e, id.h);
+        for (int e = 0; e < 4; ++e) {
+            const int64_t row = m0 + id.wm * 128 + 16 * i + 4 * (id.lane >> 4) + e;
             if (row >= a.cc) continue;
 #pragma unroll
             for (int j = 0; j < 5; ++j) {
-                const int64_t col = n0 + id.wn * 160 + j * 32 + id.lr;
+                const int64_t col = n0 + id.wn * 80 + 16 * j + (id.lane & 15);
                 if (col >= a.d) continue;
                 const float v = acc[i][j][e];
                 if (a.n_split > 1) {
@@ -935,26 +935,27 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
 }
 
 // Same product on 256 x 320 tiles (vocabulary x hidden), operands G_c^T and H_c^T (K contiguous).
-// Read-modify-write through LDS in four passes of 64 rows: pass (i, eh) stages acc[i][*][e] for
-// e in [8 eh, 8 eh + 8), which is 16 rows of each wave's 64 (stage row wm*16 + r, tile row
-// wm*64 + 32 i + 16 eh + r). Stage rows are kWSS floats apart; kWSS % 16 == 8 keeps the two
-// lane halves (rows 4 apart) on different banks. Each thread then handles ten 16-byte items
+// Read-modify-write through LDS in four passes of 64 rows: pass p stages block rows 2p and 2p+1
+// of every wave, 32 rows of its 128 (stage row wm*32 + r, tile row wm*128 + 32p + r). Stage rows
+// are kWSS floats apart; kWSS % 16 == 4 puts the four row groups a write touches (rows 4 apart)
+// on distinct banks. Each thread then handles ten 16-byte items
 // per pass, in two batches; old values are requested ahead of the LDS work that hides them.
-constexpr int kWSS = 328;
+constexpr int kWSS = 324;
 
 template <typename T>
 __global__ __launch_bounds__(512, 1) void k_dw_w(DwArgs a) {
     constexpr int NT = 512, IB = 5;  // items per thread per batch; 2 batches x 512 x 5 = 64 rows x 80
     __shared__ u32x4 L[WIDE_LDS_CHUNKS];
-    const WaveIdW id;
+    const WaveIdN<8> id;
     const int64_t n_tiles = (int64_t)a.n_mt * a.n_nt;
     const int64_t t = xcd_tile(blockIdx.x, n_tiles);
     if (t >= n_tiles) return;
     const int mt = (int)(t / a.n_nt), nt = (int)(t % a.n_nt);
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kWideN;
-    f32x16 acc[2][5];
-    gemm_tile_w<T>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.ccp, (const T*)a.H, a.ldh, n0, a.d, a.ccp, 0, a.ccp);
-    const WaveIdW ie = id.fresh();
+    f32x4 acc[8][5];
+    gemm_tile_w16<T>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.ccp, (const T*)a.H, a.ldh, n0, a.d, a.ccp, 0,
+                     a.ccp);
+    const WaveIdN<8> ie = id.fresh();
     float* stage = (float*)L;
     // dW is addressed through a descriptor at the tile origin with 32-bit offsets (d <= 2^20
     // keeps 256 rows of a tile below 2^31 bytes); items past V or d get an out-of-range offset,
@@ -964,7 +965,7 @@ __global__ __launch_bounds__(512, 1) void k_dw_w(DwArgs a) {
     auto item = [&](int p, int bt, int k, int& soff) -> uint32_t {
         const int it = ie.tid + NT * (IB * bt + k);
         const int sr = it / 80, c4 = it % 80;
-        const int r = (sr >> 4) * 64 + (p >> 1) * 32 + (p & 1) * 16 + (sr & 15);
+        const int r = (sr >> 5) * 128 + 32 * p + (sr & 31);
         soff = sr * kWSS + c4 * 4;
         return (r < rows_left && c4 * 4 < cols_left) ? (uint32_t)((r * a.d + c4 * 4) * 4) : kOOB;
     };
@@ -989,18 +990,19 @@ __global__ __launch_bounds__(512, 1) void k_dw_w(DwArgs a) {
     f32x4 old0[IB], old1[IB];
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
-        const int i = p >> 1, eh = p & 1;
         if (acc_old) load_old(p, 0, old0);
         else
 #pragma unroll
             for (int k = 0; k < IB; ++k) old0[k] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e8 = 0; e8 < 8; ++e8) {
-            const int e = 8 * eh + e8;
-            const int sr = ie.wm * 16 + 8 * ((e >> 2) & 1) + 4 * ie.h + (e & 3);
+        for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-            for (int j = 0; j < 5; ++j) stage[sr * kWSS + ie.wn * 160 + j * 32 + ie.lr] = acc[i][j][e];
-        }
+            for (int e = 0; e < 4; ++e) {
+                const int sr = ie.wm * 32 + 16 * i2 + 4 * (ie.lane >> 4) + e;
+#pragma unroll
+                for (int j = 0; j < 5; ++j)
+                    stage[sr * kWSS + ie.wn * 80 + 16 * j + (ie.lane & 15)] = acc[2 * p + i2][j][e];
+            }
         __syncthreads();
         if (acc_old) load_old(p, 1, old1);
         else
