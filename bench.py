@@ -16,6 +16,8 @@ Prints one JSON line. Along with the throughput it carries:
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gptoss] [--chunk C]
        [--no-cpu-baseline] [--no-dense] [--no-formulations]
+       python bench.py --sweep   (per-config timings and the peak-memory sweep over S; not the
+                                  headline line)
 """
 
 import argparse
@@ -46,6 +48,9 @@ def parse():
                     help="skip timing the single-pass and forward-chunked formulations")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="rows of the workload the oracle is timed on (about 10-30 s on 16 host threads)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the fused path at every timed config (small, the Qwen-like head over its "
+                         "chunk sweep, gpt-oss, the pages' full shape) and sweep S for peak memory")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device-to-device once (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -107,6 +112,82 @@ def cpu_baseline(p, n_rows):
     }
 
 
+def sweep(dev, steps: int):
+    """Fused forward + backward at every timed config, and peak device memory over S.
+
+    Timings: one warm-up step, then `steps` steps between HIP events on the current stream.
+    Peak memory: torch's allocator peak over one fused forward + backward, counted from the
+    inputs (H, W, idx, t) up, so it holds the workspace, lse, row_kl, dH and dW. The S sweep
+    runs the gpt-oss head at N in {4096, 8192, 16384, 32768}; what grows with N is dH (2d
+    bytes a row) and the O(N*K) cache-side buffers (plan entries, p_t, zk), nothing of size
+    N x V."""
+    import torch
+
+    import datagen
+    import lm_head_kl_amd as kd
+
+    stream = torch.cuda.current_stream(dev)
+
+    def to_dev(a):
+        import numpy as np
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    def run(cfg, chunk=None, N=None, n_steps=steps):
+        p = datagen.make(cfg, N=N)
+        c = chunk or p.chunk
+        H, W, idx, t = to_dev(p.H), to_dev(p.W), to_dev(p.idx), to_dev(p.tlog)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
+        dW = torch.empty(W.shape, dtype=torch.float32, device=dev)
+
+        def step():
+            f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=c, want_row_kl=True)
+            return kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=c, dW=dW)
+
+        step()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated(dev) - base
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(n_steps):
+            step()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        ms = e[0].elapsed_time(e[1]) / n_steps
+        fl = 8.0 * p.N * p.d * p.V
+        r = {"config": cfg, "N": p.N, "d": p.d, "V": p.V, "K": p.K, "T": p.T, "chunk": c, "ms": ms,
+             "tokens_per_s": p.N / (ms / 1e3), "pct_bf16_peak": 100.0 * fl / (ms / 1e3) / (PEAK_BF16_TFLOPS * 1e12),
+             "peak_beyond_inputs_gb": peak / 1e9, "dH_gb": H.numel() * H.element_size() / 1e9}
+        del H, W, idx, t, dW
+        torch.cuda.empty_cache()
+        print(json.dumps(r), flush=True)
+        return r
+
+    rows = [run("small")]
+    rows += [run("qwen", chunk=c) for c in (512, 1024, 2048, 4096)]
+    rows.append(run("gptoss"))
+    rows.append(run("full", n_steps=max(1, steps // 2)))
+    srows = [run("gptoss", N=n, n_steps=1) for n in (4096, 8192, 16384, 32768)]
+    print("| config | N | d | V | K | T | chunk | ms per step | tokens/s | % bf16 peak | peak beyond inputs GB |")
+    print("|---|---|---|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['config']} | {r['N']} | {r['d']} | {r['V']} | {r['K']} | {r['T']} | {r['chunk']} | "
+              f"{r['ms']:.2f} | {r['tokens_per_s']:,.0f} | {r['pct_bf16_peak']:.1f} | {r['peak_beyond_inputs_gb']:.3f} |")
+    print()
+    print("| N (gpt-oss head, chunk 2048) | peak beyond inputs GB | minus dH GB | growth per added row, bytes |")
+    print("|---|---|---|---|")
+    prev = None
+    for r in srows:
+        grow = "" if prev is None else f"{(r['peak_beyond_inputs_gb'] - prev['peak_beyond_inputs_gb']) * 1e9 / (r['N'] - prev['N']):.0f}"
+        print(f"| {r['N']} | {r['peak_beyond_inputs_gb']:.3f} | {r['peak_beyond_inputs_gb'] - r['dH_gb']:.3f} | {grow} |")
+        prev = r
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -130,6 +211,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": 1 << 30}))
+        return
+    if args.sweep:
+        sweep(dev, args.steps)
         return
     t_gen = time.perf_counter()
     p = datagen.make(args.config, N=args.rows or None)
