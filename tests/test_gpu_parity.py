@@ -87,11 +87,26 @@ def test_small_bf16_dense_path():
     dict(N=64, d=32, V=40, K=40, chunk=64, T=1.0),          # K = V: every token cached
     dict(N=300, d=64, V=3000, K=1024, chunk=256, T=1.0),    # K at its maximum
     dict(N=520, d=648, V=5000, K=33, chunk=512, T=1.1),     # last 320-wide hidden tile holds 8 columns
+    dict(N=200, d=96, V=700, K=20, chunk=64, T=0.25),       # sharp: tempered logits ~ N(0, 16)
+    dict(N=200, d=96, V=700, K=20, chunk=64, T=8.0),        # soft: student nearly uniform, scale T^2 = 64
 ])
 def test_ragged_and_edge_shapes(dtype, shape):
     p = datagen.make("tiny", N=shape["N"], d=shape["d"], V=shape["V"], K=shape["K"], T=shape["T"],
                      dtype=dtype, chunk=shape["chunk"])
     compare_full(p, shape["chunk"], TOL[dtype], grad=0.75, label=f"edge {shape} {dtype}")
+
+
+@pytest.mark.parametrize("dtype,scale", [("bf16", 40.0), ("fp32", 4.0)])
+def test_large_logits(dtype, scale):
+    """H and the teacher logits scaled up. At 40x (bf16) the lse is about 200, so exp of an
+    unshifted logit would overflow fp32; the online max shift keeps every term finite. fp32
+    runs at 4x: its 1e-5 gradient tolerance leaves room for rounding errors in z that grow
+    with |z| (fp32 accumulation over d), and 40x would exceed it for that reason alone."""
+    p = datagen.make("tiny", N=300, d=128, V=1500, K=24, T=1.0, dtype=dtype, chunk=128)
+    for name in ("H", "tlog"):
+        a = p.f32(name) * scale
+        setattr(p, name, datagen.bf16_bits(a) if getattr(p, name).dtype == np.uint16 else a.astype(np.float32))
+    compare_full(p, 128, TOL[dtype], grad=1.0, label=f"logits x{scale:g} {dtype}")
 
 
 def test_nnorm_and_grad_scaling():
