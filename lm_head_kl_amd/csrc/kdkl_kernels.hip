@@ -638,12 +638,19 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
 
 // Gradient tile from stored logits z^T (forward-chunked and single-pass paths): the same G and
 // G^T as k_bwd_grad, with the tile read from memory instead of recomputed. HBM-bound: it reads
-// 4 bytes and writes 2 x 2 bytes per entry.
+// 4 bytes and writes 2 x 2 bytes per entry. The tile goes through LDS in four passes of 64
+// vocabulary rows (64 KB), so two workgroups share a CU and the loads of one overlap the
+// stores of the other; each pass's z^T rows are requested before the previous pass is staged.
+// G is formed with the same operations as in k_bwd_grad (the exp2 of the tempered logit minus
+// lse, times gs, then gs*p_t subtracted in fp32), so both kernels give the same bits.
+constexpr int kGzRows = 64;  // vocabulary rows per pass
+
 template <typename T>
-__global__ __launch_bounds__(256) void k_grad_z(GradArgs a) {
-    __shared__ u32x4 L[LDS_CHUNKS + kTileM / 4];
+__global__ __launch_bounds__(256, 2) void k_grad_z(GradArgs a) {
+    constexpr int IT = kGzRows * kTileM / 4 / NTHR;  // 16-byte items per thread per pass (16)
+    __shared__ u32x4 L[kGzRows * SST / 4 + kTileM / 4];
     float* stage = (float*)L;
-    float* lse2 = (float*)(L + LDS_CHUNKS);
+    float* lse2 = (float*)(L + kGzRows * SST / 4);
     const WaveId id;
     const int64_t n_tiles = (int64_t)a.n_vt * a.n_rbc;
     const int64_t t = xcd_tile(blockIdx.x, n_tiles);
@@ -664,18 +671,16 @@ __global__ __launch_bounds__(256) void k_grad_z(GradArgs a) {
         my_en = a.ent[e0 + id.tid];
         my_pt = a.pt[(r0 + (my_en & 255)) * a.K + (my_en >> 16)];
     }
-    __syncthreads();
     // Vector loads when every chunk column offset is 16-byte aligned (uniform).
     const bool vec = ((a.ldzt | (a.zt_col0 + r0)) & 3) == 0;
-    for (int pq = 0; pq < 2; ++pq) {
-        // 128 vocabulary rows x 256 tokens; a wave reads 1 KB of one z^T row per step. All
-        // of a pass's loads are issued before the first is used.
-        f32x4 z[32];
+    // Pass pq holds tile rows pq*64 .. pq*64+63; item k of a thread is stage row it/64, tokens
+    // 4*(it%64) .. +3, so a wave reads 1 KB of one z^T row per item.
+    auto load = [&](int pq, f32x4 (&z)[IT]) {
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
+        for (int k = 0; k < IT; ++k) {
             const int it = id.tid + NTHR * k;
             const int sr = it >> 6, tok = (it & 63) * 4;
-            const int64_t v = n0 + (sr >> 6) * 128 + pq * 64 + (sr & 63);
+            const int64_t v = n0 + pq * kGzRows + sr;
             z[k] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (v < a.V && r0 + tok < a.cc) {
                 const float* zr = a.zt + v * a.ldzt + a.zt_col0 + r0 + tok;
@@ -688,11 +693,13 @@ __global__ __launch_bounds__(256) void k_grad_z(GradArgs a) {
                 }
             }
         }
+    };
+    auto pass = [&](int pq, const f32x4 (&z)[IT]) {
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
+        for (int k = 0; k < IT; ++k) {
             const int it = id.tid + NTHR * k;
             const int sr = it >> 6, tok = (it & 63) * 4;
-            const int64_t v = n0 + (sr >> 6) * 128 + pq * 64 + (sr & 63);
+            const int64_t v = n0 + pq * kGzRows + sr;
             f32x4 g = {0.f, 0.f, 0.f, 0.f};
             if (v < a.V) {
 #pragma unroll
@@ -702,8 +709,62 @@ __global__ __launch_bounds__(256) void k_grad_z(GradArgs a) {
             *(f32x4*)(stage + st_idx(sr, tok)) = g;
         }
         __syncthreads();
-        grad_pass_out<T, 4>(a, stage, pq, id, vt, r0, n0, e0, e1, my_en, my_pt, gs);
-    }
+        // gs*p_t at the cached ids whose vocabulary row is in this pass (bits 6-7 of the column)
+        if (my_en != 0xffffffffu && ((my_en >> 14) & 3) == (uint32_t)pq) {
+            const int r = my_en & 255, c = (my_en >> 8) & 255;
+            stage[st_idx(c & 63, r)] -= gs * my_pt;
+        }
+        for (int i = e0 + NTHR + id.tid; i < e1; i += NTHR) {
+            const uint32_t en = a.ent[i];
+            const int c = (en >> 8) & 255;
+            if ((c >> 6) != pq) continue;
+            const int r = en & 255, k = (int)(en >> 16);
+            stage[st_idx(c & 63, r)] -= gs * a.pt[(r0 + r) * a.K + k];
+        }
+        __syncthreads();
+        // G rows: token tl, group g of 8 vocabulary entries; 8 lanes write a token's 64 entries
+        // of the pass, one 128-byte line.
+#pragma unroll 4
+        for (int q = 0; q < kGzRows * kTileM / 8 / NTHR; ++q) {
+            const int it = id.tid + NTHR * q;
+            const int g = it & 7, tl = it >> 3;
+            const int64_t tr = r0 + tl;
+            if (tr < a.cc) {
+                float x[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) x[u] = stage[st_idx(8 * g + u, tl)];
+                store8<T>((T*)a.G + ((int64_t)vt * a.cc + tr) * kTileN + pq * kGzRows + 8 * g, x);
+            }
+        }
+        // G^T rows: vocabulary row sr of the pass, group cb of 8 tokens; 32 lanes write a row's
+        // 256 tokens.
+        if (a.GT) {
+#pragma unroll 4
+            for (int q = 0; q < kGzRows * kTileM / 8 / NTHR; ++q) {
+                const int it = id.tid + NTHR * q;
+                const int sr = it >> 5, cb = it & 31;
+                const int64_t tr = r0 + cb * 8;
+                if (tr < a.ccp) {
+                    const float* row = stage + sr * SST;
+                    const f32x4 v0 = *(const f32x4*)(row + ((cb * 8) ^ st_swz(sr)));
+                    const f32x4 v1 = *(const f32x4*)(row + ((cb * 8 + 4) ^ st_swz(sr)));
+                    const float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+                    store8<T>((T*)a.GT + (n0 + pq * kGzRows + sr) * a.ldgt + tr, x);
+                }
+            }
+        }
+        __syncthreads();
+    };
+    f32x4 za[IT], zb[IT];
+    load(0, za);
+    load(1, zb);
+    __syncthreads();  // lse2
+    pass(0, za);
+    load(2, za);
+    pass(1, zb);
+    load(3, zb);
+    pass(2, za);
+    pass(3, zb);
 }
 
 // ------------------------------------------------------------------------------------------
