@@ -774,25 +774,40 @@ __global__ __launch_bounds__(256, 2) void k_grad_z(GradArgs a) {
 template <typename T, bool BLK>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, int64_t lds, int64_t rows,
                                                    int64_t cols, T* __restrict__ dst, int64_t ldd, int64_t rows_pad) {
-    __shared__ T tile[64][65];
+    // 16-byte global accesses: VEC elements of a source row per load, VEC consecutive rows of
+    // one column per store. cols, lds, ldd and rows_pad are multiples of 8, so a vector never
+    // leaves its row. The LDS tile is padded to an odd word stride.
+    constexpr int VEC = 16 / (int)sizeof(T);
+    constexpr int LDW = 64 + 4 / (int)sizeof(T);  // row stride in elements: 33 (bf16) or 65 (fp32) words
+    constexpr int CPR = 64 / VEC;                 // vectors per tile row
+    __shared__ T tile[64][LDW];
     const int64_t c0 = (int64_t)blockIdx.x * 64, r0 = (int64_t)blockIdx.y * 64;
-    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = ty + 4 * i;
-        const int64_t gr = r0 + r, gc = c0 + tx;
-        tile[r][tx] = (gr < rows && gc < cols) ? src[gr * lds + gc] : (T)0;
+    for (int i = 0; i < 64 * CPR / NTHR; ++i) {
+        const int it = threadIdx.x + NTHR * i;
+        const int r = it / CPR, cv = (it % CPR) * VEC;
+        const int64_t gr = r0 + r, gc = c0 + cv;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (gr < rows && gc < cols) v = *(const u32x4*)(src + gr * lds + gc);
+        const T* e = (const T*)&v;
+#pragma unroll
+        for (int u = 0; u < VEC; ++u) tile[r][cv + u] = e[u];
     }
     __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int c = ty + 4 * i;
-        const int64_t gc = c0 + c, gr = r0 + tx;
+    for (int i = 0; i < 64 * CPR / NTHR; ++i) {
+        const int it = threadIdx.x + NTHR * i;
+        const int c = it / CPR, rv = (it % CPR) * VEC;
+        const int64_t gc = c0 + c, gr = r0 + rv;
         if (gc < cols && gr < rows_pad) {
+            u32x4 v;
+            T* e = (T*)&v;
+#pragma unroll
+            for (int u = 0; u < VEC; ++u) e[u] = tile[rv + u][c];
             if constexpr (BLK)
-                dst[((gr >> 8) * cols + gc) * 256 + (gr & 255)] = tile[tx][c];
+                *(u32x4*)(dst + ((gr >> 8) * cols + gc) * 256 + (gr & 255)) = v;
             else
-                dst[gc * ldd + gr] = tile[tx][c];
+                *(u32x4*)(dst + gc * ldd + gr) = v;
         }
     }
 }
