@@ -1250,9 +1250,7 @@ __device__ __forceinline__ void topk_scan(const T* x, int V, F&& f) {
     if (tid < h) f(tid, fp32_bits<T>(x[tid]), 0);
     const int nvec = (V - h) / VEC;
     const u32x4* xv = (const u32x4*)(x + h);
-    int j = 0;
-    for (int q = tid; q < nvec; q += NTHR, ++j) {
-        const u32x4 c = xv[q];
+    auto each = [&](const u32x4& c, int q, int j) {
         const int v0 = h + q * VEC;
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -1264,12 +1262,23 @@ __device__ __forceinline__ void topk_scan(const T* x, int V, F&& f) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) f(v0 + u, c[u], j);
         }
+    };
+    // eight 16-byte loads in flight per lane
+    int j = 0;
+    int q = tid;
+    for (; q + 7 * NTHR < nvec; q += 8 * NTHR, j += 8) {
+        u32x4 c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c[u] = xv[q + u * NTHR];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) each(c[u], q + u * NTHR, j + u);
     }
+    for (; q < nvec; q += NTHR, ++j) each(xv[q], q, j);
     for (int v = h + nvec * VEC + tid; v < V; v += NTHR) f(v, fp32_bits<T>(x[v]), 0);
 }
 
 // Largest value of each of m interleaved groups of this thread's entries (load j of the thread
-// goes to group j % m), four 16-byte loads in flight per lane.
+// goes to group j % m), eight 16-byte loads in flight per lane.
 template <typename T>
 __device__ __forceinline__ void topk_scan_max(const T* x, int V, int m, float (&gmax)[kTopkMaxGroups]) {
     constexpr int VEC = 16 / sizeof(T);
@@ -1295,11 +1304,15 @@ __device__ __forceinline__ void topk_scan_max(const T* x, int V, int m, float (&
     };
     int j = 0;
     int q = tid;
-    for (; q + 3 * NTHR < nvec; q += 4 * NTHR) {
-        const u32x4 c0 = xv[q], c1 = xv[q + NTHR], c2 = xv[q + 2 * NTHR], c3 = xv[q + 3 * NTHR];
-        const float r[4] = {vmax(c0), vmax(c1), vmax(c2), vmax(c3)};
+    for (; q + 7 * NTHR < nvec; q += 8 * NTHR) {
+        u32x4 c[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u, ++j) {
+        for (int u = 0; u < 8; ++u) c[u] = xv[q + u * NTHR];
+        float r[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) r[u] = vmax(c[u]);
+#pragma unroll
+        for (int u = 0; u < 8; ++u, ++j) {
             const int g = j % m;
 #pragma unroll
             for (int t = 0; t < kTopkMaxGroups; ++t)
@@ -1342,7 +1355,7 @@ __device__ __forceinline__ void bitonic_desc(uint64_t* a, int P) {
 template <typename T>
 __global__ __launch_bounds__(256) void k_topk(const T* __restrict__ X, int64_t ld, int64_t N, int V, int K,
                                               int32_t* __restrict__ idx_out, T* __restrict__ val_out) {
-    __shared__ uint32_t hist[4][kTopkBins];
+    __shared__ uint32_t hist[2][kTopkBins];  // two copies (waves 0, 2 and 1, 3): 49 KB of LDS, three rows per CU
     __shared__ uint64_t cand[kTopkSort];
     __shared__ uint32_t wsum[NTHR];
     __shared__ int s_bin, s_above, s_cnt, s_ncoll;
@@ -1394,11 +1407,11 @@ __global__ __launch_bounds__(256) void k_topk(const T* __restrict__ X, int64_t l
         while (true) {
             const int wd = shift < kTopkBits ? shift : kTopkBits;
             const int s = shift - wd;
-            for (int i = tid; i < 4 * kTopkBins; i += NTHR) (&hist[0][0])[i] = 0u;
+            for (int i = tid; i < 2 * kTopkBins; i += NTHR) (&hist[0][0])[i] = 0u;
             __syncthreads();
             topk_scan<T>(x, V, [&](int v, uint32_t bits, int) {
                 const uint64_t ck = topk_ck(v, bits);
-                if ((ck >> shift) == prefix) atomicAdd(&hist[w][(uint32_t)(ck >> s) & ((1u << wd) - 1u)], 1u);
+                if ((ck >> shift) == prefix) atomicAdd(&hist[w & 1][(uint32_t)(ck >> s) & ((1u << wd) - 1u)], 1u);
             });
             __syncthreads();
             // Bins of this level, highest first: thread t owns bins [8t, 8t+8) counted from the top.
@@ -1407,7 +1420,7 @@ __global__ __launch_bounds__(256) void k_topk(const T* __restrict__ X, int64_t l
 #pragma unroll
             for (int q = 0; q < PER; ++q) {
                 const int b = kTopkBins - 1 - (tid * PER + q);
-                mine[q] = hist[0][b] + hist[1][b] + hist[2][b] + hist[3][b];
+                mine[q] = hist[0][b] + hist[1][b];
                 tot += mine[q];
             }
             wsum[tid] = tot;
