@@ -590,27 +590,31 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
         const int64_t r0 = (int64_t)rb * kTileM;  // token offset within the chunk
         const int64_t n0 = (int64_t)vt * kTileN;
         const float gs = (a.grad ? a.grad[0] : 1.f) * a.gsc;
-        // lse (log2 units) of the lane's 4 token columns wn*64 + 16j + lane%16
-        float l2[4];
+        // Everything below up to the mainloop is needed only by the epilogue: the loads are
+        // issued without branches so that their latency hides behind the mainloop's first DMA
+        // stages instead of being waited for one by one.
+        // lse of the lane's 4 token columns wn*64 + 16j + lane%16 (a clamped index past the chunk)
+        float lse_raw[4];
         bool tok_ok[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int64_t tr = r0 + id.wn * 64 + 16 * j + (id.lane & 15);
             tok_ok[j] = tr < a.cc;
-            l2[j] = tok_ok[j] ? a.lse[a.c0 + tr] * kLog2e : 0.f;
+            lse_raw[j] = a.lse[a.c0 + (tok_ok[j] ? tr : 0)];
         }
         // This tile's cached-id entries: the first NT are loaded into registers (one per
-        // thread) before the mainloop; more only occur on Zipf-hot tiles.
+        // thread) before the mainloop; more only occur on Zipf-hot tiles. Their p_t is
+        // loaded after the mainloop, ahead of its first use.
         const int32_t* off = a.off + (int64_t)rb * (a.n_vt + 1);
         const int e0 = off[vt], e1 = off[vt + 1];
-        uint32_t my_en = 0xffffffffu;
-        float my_pt = 0.f;
-        if (e0 + id.tid < e1) {
-            my_en = a.ent[e0 + id.tid];
-            my_pt = a.pt[(r0 + (my_en & 255)) * a.K + (my_en >> 16)];
-        }
+        const bool has_en = e0 + id.tid < e1;
+        const uint32_t my_en = a.ent[has_en ? e0 + id.tid : 0] | (has_en ? 0u : 0xffffffffu);
         f32x4 acc[8][4];
         gemm_tile_kk16<T>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, Hc, a.d, r0, a.cc, a.d, 0, a.d);
+        const float my_pt = my_en != 0xffffffffu ? a.pt[(r0 + (my_en & 255)) * a.K + (my_en >> 16)] : 0.f;
+        float l2[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) l2[j] = tok_ok[j] ? lse_raw[j] * kLog2e : 0.f;
         const WaveIdN<NW> ie = id.fresh();
         const int g4 = 4 * (ie.lane >> 4), c16 = ie.lane & 15;
 
