@@ -534,19 +534,26 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
         stage[st_idx(st_row(c), r)] -= gs * a.pt[(r0 + r) * a.K + k];
     }
     __syncthreads();
-    // G rows: token tl, group g of 8 vocabulary entries (stage rows 8g .. 8g+7). Eight
-    // consecutive lanes cover one token's 64 entries of a half: a whole 128-byte line.
-#pragma unroll 4
-    for (int it8 = 0; it8 < IT; ++it8) {
-        const int it = ie.tid + NT * it8;
-        const int g = it & 15, tl = it >> 4;
-        const int64_t tr = r0 + tl;
-        if (tr < a.cc) {
-            float x[8];
+    // G rows: group g of 8 vocabulary entries (stage rows 8g .. 8g+7) by a group of 4 tokens.
+    // A lane reads the 8 x 4 block with 16-byte LDS reads (4 tokens of one stage row each) and
+    // writes the 4 tokens' 8-entry segments; 16 consecutive lanes cover one token's 128
+    // entries of the pass: two whole 128-byte lines.
+#pragma unroll 2
+    for (int ib = 0; ib < 1024 / NT; ++ib) {
+        const int it = ie.tid + NT * ib;
+        const int g = it & 15, tq = it >> 4;
+        f32x4 blk[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) x[u] = stage[st_idx(8 * g + u, tl)];
-            const int vb = (g >> 3) * 128 + pq * 64 + (g & 7) * 8;
-            store8<T>((T*)a.G + ((int64_t)vt * a.cc + tr) * kTileN + vb, x);
+        for (int u = 0; u < 8; ++u) blk[u] = *(const f32x4*)(stage + st_idx(8 * g + u, 4 * tq));
+        const int vb = (g >> 3) * 128 + pq * 64 + (g & 7) * 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int64_t tr = r0 + 4 * tq + j;
+            if (tr < a.cc) {
+                const float x[8] = {blk[0][j], blk[1][j], blk[2][j], blk[3][j],
+                                    blk[4][j], blk[5][j], blk[6][j], blk[7][j]};
+                store8<T>((T*)a.G + ((int64_t)vt * a.cc + tr) * kTileN + vb, x);
+            }
         }
     }
     // G^T rows: vocabulary entry of stage row sr, group cb of 8 tokens; 32 lanes write a row's
