@@ -62,6 +62,8 @@ __all__ = [
     "kl_chunked",
     "kl_fused",
     "kl_rows",
+    "lse_all_rows",
+    "dw_rows",
     "topk_cache",
 ]
 
@@ -250,6 +252,39 @@ def kl_rows(H, W, idx, tlog, T: float, rows, n_norm, g: float = 1.0, *, H_rows=N
     G[r, ir] -= pt
     G *= gs
     return dict(lse=lse, row_kl=row_kl, zk=zk, dH=G @ W)
+
+
+def lse_all_rows(H, W, T: float, block: int = 512) -> np.ndarray:
+    """lse_n = logsumexp_v z_nv/T for every row of a large batch. Each row's value is the
+    definition applied to that row alone (as in ``kl_rows``); rows are taken ``block`` at a time
+    only to bound the size of the logit slab held in memory."""
+    W = _f64(W)
+    H = np.asarray(H)
+    out = np.empty(H.shape[0])
+    for r0 in range(0, H.shape[0], block):
+        out[r0:r0 + block] = logsumexp_rows((_f64(H[r0:r0 + block]) @ W.T) / T)
+    return out
+
+
+def dw_rows(H, W, idx, tlog, T: float, vocab, lse, n_norm, g: float = 1.0) -> np.ndarray:
+    """Rows ``vocab`` of dW = G^T H, where G = g*(T/n_norm)*(softmax(z/T) - P_t) and P_t is
+    the teacher distribution scattered at the cached ids (zero elsewhere). Column v of G needs
+    z[:, v] and every row's lse, which is passed in (``lse_all_rows``). This is the dense
+    definition restricted to those columns."""
+    H = _f64(H)
+    V = np.asarray(W).shape[0]
+    vocab = np.asarray(vocab, np.int64)
+    Wv = _f64(np.asarray(W)[vocab])                       # only the rows asked for
+    idx = np.asarray(idx, np.int64)
+    _check(idx, V)
+    zc = H @ Wv.T                                         # z[:, vocab]
+    Pc = np.exp(zc / T - np.asarray(lse, np.float64)[:, None])
+    pt = np.exp(teacher_logp(tlog, T))
+    col = np.full(V, -1, np.int64)
+    col[vocab] = np.arange(len(vocab))
+    n, k = np.nonzero(col[idx] >= 0)                      # cached entries that fall in vocab
+    Pc[n, col[idx[n, k]]] -= pt[n, k]
+    return (g * T / float(n_norm)) * (Pc.T @ H)
 
 
 def topk_cache(logits, K: int):

@@ -85,6 +85,13 @@ def test_brute_force(N, d, V, K, T, g, seed):
     rk = oracle.kl_rows(H, W, idx, t, T, rows=[N - 1, 0], n_norm=N, g=g)
     np.testing.assert_allclose(rk["dH"], ref["dH"][[N - 1, 0]], rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(rk["row_kl"], ref["row_kl"][[N - 1, 0]], rtol=1e-12, atol=1e-14)
+    # the per-row lse of a whole batch (any row block) and the vocab rows of dW from it
+    for block in (1, 3, N):
+        np.testing.assert_allclose(oracle.lse_all_rows(H, W, T, block=block), ref["lse"], rtol=1e-12, atol=1e-13)
+    vocab = [V - 1, 0, 2] + sorted({int(i) for i in idx[0]})[:2]
+    vocab = sorted(set(vocab))
+    dw = oracle.dw_rows(H, W, idx, t, T, vocab, ref["lse"], n_norm=N, g=g)
+    np.testing.assert_allclose(dw, ref["dW"][vocab], rtol=1e-12, atol=1e-13)
 
 
 # ---------------------------------------------------------- finite differences
@@ -256,6 +263,21 @@ def test_linear_in_upstream_gradient():
     c = oracle.kl_dense(H, W, idx, t, 1.0, n_norm=2 * N)
     np.testing.assert_allclose(c["dW"], 0.5 * a["dW"], rtol=1e-14, atol=1e-16)
     assert abs(c["loss"] - 0.5 * a["loss"]) <= 1e-15
+
+
+def test_dw_rows_equals_dense_dw():
+    """dW restricted to chosen vocabulary rows, from the batch's lse, equals those rows of the
+    dense formulation's dW: all rows, cached and uncached ids, n_norm != N and g != 1."""
+    N, d, V, K = 40, 9, 57, 6
+    H, W, idx, t = rand_problem(N, d, V, K, 120)
+    a = oracle.kl_dense(H, W, idx, t, 1.7, n_norm=100.0, g=-0.6)
+    lse = oracle.lse_all_rows(H, W, 1.7, block=7)
+    np.testing.assert_allclose(lse, a["lse"], rtol=1e-13, atol=1e-14)
+    full = oracle.dw_rows(H, W, idx, t, 1.7, np.arange(V), lse, n_norm=100.0, g=-0.6)
+    np.testing.assert_allclose(full, a["dW"], rtol=1e-11, atol=1e-15)
+    some = np.array([0, 5, int(idx[3, 2]), V - 1])
+    np.testing.assert_allclose(oracle.dw_rows(H, W, idx, t, 1.7, some, lse, n_norm=100.0, g=-0.6), a["dW"][some],
+                               rtol=1e-11, atol=1e-15)
 
 
 def test_rejects_bad_ids():
