@@ -224,26 +224,26 @@ def test_gptoss_subbatch_dw():
     subbatch_dw_check("gptoss")
 
 
-GOLDEN_LSE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "gptoss_lse.npy")
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-def test_gptoss_full_batch_lse_and_dw_rows():
-    """The whole gpt-oss batch (N = 32768), not a sub-batch: lse at every row against the stored
-    fp64 oracle lse (tests/golden/make_gptoss_lse.py), and 256 rows of the full-batch dW (ids
-    0..3 and V-1, the Zipf-hot and masked-tail columns, plus 251 seeded) against oracle.dw_rows
-    built from that lse."""
-    p = datagen.make("gptoss")
-    lse_ref = np.load(GOLDEN_LSE, allow_pickle=False)
+@pytest.mark.parametrize("name", ["gptoss", "full"])
+def test_full_batch_lse_and_dw_rows(name):
+    """The whole batch, not a sub-batch, at the gpt-oss head (N = 32768) and the pages' shape
+    (N = 131072): lse at every row against the stored fp64 oracle lse (tests/golden/make_lse.py),
+    and 256 rows of the full-batch dW (ids 0..3 and V-1, the Zipf-hot and masked-tail columns,
+    plus 251 seeded) against oracle.dw_rows built from that lse."""
+    p = datagen.make(name)
+    lse_ref = np.load(os.path.join(GOLDEN, f"{name}_lse.npy"), allow_pickle=False)
     assert lse_ref.shape == (p.N,)
-    say("full-batch lse and dW rows", f"N={p.N} chunk={p.chunk}")
+    say("full-batch lse and dW rows", name, f"N={p.N} chunk={p.chunk}")
     H, W, idx, t = device_inputs(p)
     f, dH, dW = run_fused(H, W, idx, t, p.T, p.chunk)
     e_lse = max_rel(host(f.lse), lse_ref)
     vocab = datagen.sample_vocab(p.V, 256, p.extra["seed"])
     got = host(dW[torch.from_numpy(vocab).to(dW.device)])
     del dH, dW, f
-    want = oracle.dw_rows(p.f32("H"), p.W if p.W.dtype != np.uint16 else datagen.bf16_to_f32(p.W), p.idx,
-                          p.f64("tlog"), p.T, vocab, lse_ref, n_norm=p.N)
+    want = oracle.dw_rows(p.f32("H"), p.f32("W"), p.idx, p.f64("tlog"), p.T, vocab, lse_ref, n_norm=p.N)
     e_dw = rel_l2(got, want)
     say(f"  lse max rel {e_lse:.2e}  dW rows relL2 {e_dw:.2e}")
     assert e_lse <= TOL["bf16"]["lse"]
