@@ -1,12 +1,13 @@
 """Writes <config>_lse.npy: the fp64 log-sum-exp of z/T for every row of a large workload
 (seeded inputs from datagen), computed by oracle.lse_all_rows. Configs: "gptoss" (N = 32768)
-and "full" (the pages' shape, N = 131072), both at d = 2880, V = 201,088, T = 1.
+and "full" (the pages' shape, N = 131072), both at d = 2880, V = 201,088, T = 1; "qwen"
+(N = 8192, d = 2048, V = 151,936, T = 2).
 
 With it, a GPU test checks the full-batch lse of the fused forward at every row and derives
 sampled rows of the full-batch dW on the host (oracle.dw_rows needs every row's lse, which
 takes minutes of fp64 matrix products and so is stored here instead of recomputed).
 
-Run from the repository root: python tests/golden/make_lse.py gptoss full
+Run from the repository root: python tests/golden/make_lse.py gptoss full qwen
 """
 
 import os
@@ -35,4 +36,4 @@ def main(names):
 
 
 if __name__ == "__main__":
-    main(sys.argv[1:] or ["gptoss", "full"])
+    main(sys.argv[1:] or ["gptoss", "full", "qwen"])

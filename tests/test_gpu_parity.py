@@ -227,18 +227,28 @@ def test_gptoss_subbatch_dw():
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
-@pytest.mark.parametrize("name", ["gptoss", "full"])
-def test_full_batch_lse_and_dw_rows(name):
-    """The whole batch, not a sub-batch, at the gpt-oss head (N = 32768) and the pages' shape
-    (N = 131072): lse at every row against the stored fp64 oracle lse (tests/golden/make_lse.py),
-    and 256 rows of the full-batch dW (ids 0..3 and V-1, the Zipf-hot and masked-tail columns,
-    plus 251 seeded) against oracle.dw_rows built from that lse."""
-    p = datagen.make(name)
-    lse_ref = np.load(os.path.join(GOLDEN, f"{name}_lse.npy"), allow_pickle=False)
+@pytest.mark.parametrize("name,N,chunk", [
+    ("gptoss", None, None),
+    ("full", None, None),
+    ("qwen", None, 512),
+    ("qwen", None, 4096),
+    ("gptoss", 5000, None),   # ragged: chunks of 2048, 2048, 904
+    ("gptoss", 5000, 1000),   # chunks off the 256-row blocks: a plan per chunk
+])
+def test_full_batch_lse_and_dw_rows(name, N, chunk):
+    """The whole batch, not a sub-batch, at the gpt-oss head (N = 32768), the pages' shape
+    (N = 131072), the Qwen-like head (T = 2) and a ragged prefix of the gpt-oss batch: lse at
+    every row against the stored fp64 oracle lse (tests/golden/make_lse.py; rows are drawn in
+    fixed blocks, so a prefix of the batch has the prefix of its lse), and 256 rows of the
+    full-batch dW (ids 0..3 and V-1, the Zipf-hot and masked-tail columns, plus 251 seeded)
+    against oracle.dw_rows built from that lse."""
+    p = datagen.make(name, N=N)
+    chunk = chunk or p.chunk
+    lse_ref = np.load(os.path.join(GOLDEN, f"{name}_lse.npy"), allow_pickle=False)[:p.N]
     assert lse_ref.shape == (p.N,)
-    say("full-batch lse and dW rows", name, f"N={p.N} chunk={p.chunk}")
+    say("full-batch lse and dW rows", name, f"N={p.N} chunk={chunk}")
     H, W, idx, t = device_inputs(p)
-    f, dH, dW = run_fused(H, W, idx, t, p.T, p.chunk)
+    f, dH, dW = run_fused(H, W, idx, t, p.T, chunk)
     e_lse = max_rel(host(f.lse), lse_ref)
     vocab = datagen.sample_vocab(p.V, 256, p.extra["seed"])
     got = host(dW[torch.from_numpy(vocab).to(dW.device)])
