@@ -119,14 +119,18 @@ def test_nnorm_and_grad_scaling():
 # --------------------------------------------------------------- gather bit-exactness
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_gather_bit_exact_on_exact_arithmetic(dtype):
+@pytest.mark.parametrize("cfg,N,d,V", [
+    ("small", 512, 1024, 4096),     # 2 row blocks x 16 vocab tiles; Zipf-hot first tile
+    ("gptoss", 256, 2880, 201088),  # every vocab tile of the gpt-oss head, padded last tile
+])
+def test_gather_bit_exact_on_exact_arithmetic(dtype, cfg, N, d, V):
     """Small-integer H and W make every logit an exact fp32 integer whatever the summation
-    order, so the gathered zk must equal the oracle bit for bit."""
-    N, d, V, K = 512, 1024, 4096, 100
+    order (|z| <= 4d < 2^24), so the gathered zk must equal the oracle bit for bit."""
+    K = 100
     g = np.random.default_rng(7)
-    Hn = g.integers(-2, 3, size=(N, d)).astype(np.float32)
-    Wn = g.integers(-2, 3, size=(V, d)).astype(np.float32)
-    p = datagen.make("small", N=N, d=d, V=V, K=K, dtype=dtype)
+    Hn = g.integers(-2, 3, size=(N, d), dtype=np.int8).astype(np.float32)
+    Wn = g.integers(-2, 3, size=(V, d), dtype=np.int8).astype(np.float32)
+    p = datagen.make(cfg, N=N, d=d, V=V, K=K, dtype=dtype)
     if dtype == "bf16":
         p.H, p.W = datagen.bf16_bits(Hn), datagen.bf16_bits(Wn)
     else:
@@ -135,8 +139,8 @@ def test_gather_bit_exact_on_exact_arithmetic(dtype):
     H, W, idx, t = device_inputs(p)
     f = kd.fused_kl_fwd(H, W, idx, t, T=1.0, chunk=256, want_zk=True)
     torch.cuda.synchronize()
-    z = Hn.astype(np.float64) @ Wn.astype(np.float64).T
-    want = np.take_along_axis(z, p.idx.astype(np.int64), axis=1).astype(np.float32)
+    ii = p.idx.astype(np.int64)
+    want = np.einsum("nd,nkd->nk", Hn.astype(np.float64), Wn[ii].astype(np.float64)).astype(np.float32)
     got = f.zk.cpu().numpy()
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
