@@ -1496,12 +1496,28 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 constexpr int kGradWaves = 8, kFwdWaves = 8;
 
 // Vocab lanes of the forward: at least 8, and enough units to give every CU one.
+// Vocabulary lanes Q of the persistent forward: unit (row block, lane q) walks vocab tiles q,
+// q + Q, ... The grid's workgroup w takes units w, w + P, w + 2P, ... of its XCD band, so the
+// busiest workgroup does ceil(units / P) units of up to ceil(n_vt / Q) tiles. Among Q in
+// 4..16 pick the one with the least of that, preferring Q near 8 (4 row blocks x 8 lanes per
+// XCD share operands in L2 best); at least 256 units when the rows are few.
 int fwd_vsplits(int64_t N, int64_t V) {
     const int64_t n_rb = (N + kTileM - 1) / kTileM;
     const int64_t n_vt = (V + kTileN - 1) / kTileN;
-    int64_t q = std::max<int64_t>(8, (256 + n_rb - 1) / n_rb);
-    if (q > n_vt) q = n_vt;
-    return (int)q;
+    const int64_t q_min = std::max<int64_t>(4, (256 + n_rb - 1) / n_rb);
+    if (q_min >= n_vt) return (int)n_vt;
+    const int64_t P = 256;
+    int64_t best_q = std::min<int64_t>(std::max<int64_t>(8, q_min), n_vt), best = INT64_MAX;
+    for (int64_t q = q_min; q <= std::min<int64_t>(16, n_vt); ++q) {
+        const int64_t load = ((n_rb * q + P - 1) / P) * ((n_vt + q - 1) / q);
+        const int64_t dist = q > 8 ? q - 8 : 8 - q;
+        const int64_t best_dist = best_q > 8 ? best_q - 8 : 8 - best_q;
+        if (load < best || (load == best && dist < best_dist)) {
+            best = load;
+            best_q = q;
+        }
+    }
+    return (int)best_q;
 }
 
 // Compute units of the current device (cached per device id).
