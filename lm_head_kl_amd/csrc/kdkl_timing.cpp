@@ -3,7 +3,9 @@
 // While enabled, every launch the library makes is bracketed by two events recorded on the
 // launch's own stream. kd_timing_read synchronises the recorded pairs and adds up, per kernel
 // kind, the launches and their elapsed time. Events come from a pool that grows on demand and
-// is reused after kd_timing_reset. The state is process-wide and guarded by a mutex.
+// is reused after kd_timing_reset. The totals and the event pool are process-wide and guarded
+// by a mutex; the bracket of the launch being enqueued is per thread, so calls made from
+// several threads at once each time their own launches.
 
 #include <hip/hip_runtime_api.h>
 
@@ -34,9 +36,10 @@ struct State {
     std::vector<Rec> recs;         // recorded, not yet read
     int64_t launches[kNumKinds] = {0};
     double ms[kNumKinds] = {0};
-    // open bracket of the current launch (launches are enqueued one at a time per call)
-    Rec open{-1, nullptr, nullptr};
 };
+
+// Bracket of the launch this thread is enqueueing (begin and end come from the same thread).
+thread_local Rec t_open{-1, nullptr, nullptr};
 
 State& st() {
     static State s;
@@ -74,17 +77,30 @@ void timing_begin(int kind, hipStream_t stream) {
     std::lock_guard<std::mutex> g(s.mu);
     if (!s.on) return;
     hipEvent_t a = take_event(s), b = take_event(s);
-    if (!a || !b) return;
-    if (hipEventRecord(a, stream) != hipSuccess) return;
-    s.open = Rec{kind, a, b};
+    if (!a || !b) {
+        if (a) s.pool.push_back(a);
+        if (b) s.pool.push_back(b);
+        return;
+    }
+    if (hipEventRecord(a, stream) != hipSuccess) {
+        s.pool.push_back(a);
+        s.pool.push_back(b);
+        return;
+    }
+    t_open = Rec{kind, a, b};
 }
 
 void timing_end(int kind, hipStream_t stream) {
     State& s = st();
     std::lock_guard<std::mutex> g(s.mu);
-    if (!s.on || s.open.kind != kind) return;
-    if (hipEventRecord(s.open.b, stream) == hipSuccess) s.recs.push_back(s.open);
-    s.open = Rec{-1, nullptr, nullptr};
+    if (t_open.kind != kind) return;
+    if (s.on && hipEventRecord(t_open.b, stream) == hipSuccess) {
+        s.recs.push_back(t_open);
+    } else {
+        s.pool.push_back(t_open.a);
+        s.pool.push_back(t_open.b);
+    }
+    t_open = Rec{-1, nullptr, nullptr};
 }
 
 }  // namespace kdkl
