@@ -330,8 +330,15 @@ def main():
     # inputs up, like the fused path's.
     del ws, dW
     forms = {"fused_recompute": {"ms": ms_step, "peak_hbm_gb": peak_fused / 1e9, "counted_flops": flops_step}}
+    def frozen_head():
+        f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=chunk, want_row_kl=True)
+        return kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=chunk, flags=kd.KD_SKIP_DW)
+
+    # counted FLOPs of each: single pass and forward-chunked compute the logits once (6 N d V);
+    # the frozen head (KD_SKIP_DW) recomputes them but skips dW (6 N d V)
     others = [("single_pass", lambda: kd.fused_kl_fwdbwd(H, W, idx, t, T=p.T, chunk=chunk), 6.0),
-              ("forward_chunked", lambda: kd.chunked_kl(H, W, idx, t, T=p.T, chunk=chunk), 6.0)]
+              ("forward_chunked", lambda: kd.chunked_kl(H, W, idx, t, T=p.T, chunk=chunk), 6.0),
+              ("fused_frozen_head", frozen_head, 6.0)]
     if not args.no_dense:
         others.append(("dense", lambda: kd.dense_kl(H, W, idx, t, T=p.T), 8.0))
     for name, call, fl in others:

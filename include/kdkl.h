@@ -97,6 +97,9 @@ typedef enum kd_dtype {
 /* flags */
 #define KD_VALIDATE_IDX  0x1u /* check idx on the device first; this syncs the stream once */
 #define KD_ACCUMULATE_DW 0x2u /* kd_fused_kl_bwd / kd_dense_kl add into dW instead of overwriting */
+#define KD_SKIP_DW       0x4u /* kd_fused_kl_bwd computes dH only (dW may be NULL): for a frozen head.
+                                 Ignored by kd_fused_kl_fwd; KD_ERR_VALUE for the other calls and
+                                 together with KD_ACCUMULATE_DW */
 
 /*
  * Problem descriptor (host memory).
@@ -111,7 +114,7 @@ typedef enum kd_dtype {
  *                one batch is split over several calls.
  *   act          dtype of H, W and dH: KD_BF16 (fp32 accumulation) or KD_FP32 (fp32 products).
  *   tlogit       dtype of the cached teacher logits t: KD_BF16 or KD_FP32.
- *   flags        KD_VALIDATE_IDX | KD_ACCUMULATE_DW.
+ *   flags        KD_VALIDATE_IDX | KD_ACCUMULATE_DW | KD_SKIP_DW.
  */
 typedef struct kd_problem {
     int64_t N;

@@ -19,7 +19,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import KD_ACCUMULATE_DW, KD_BF16, KD_FP32, KD_VALIDATE_IDX, KdError, KdProblem
+from ._lib import KD_ACCUMULATE_DW, KD_BF16, KD_FP32, KD_SKIP_DW, KD_VALIDATE_IDX, KdError, KdProblem
 
 __all__ = [
     "FusedKL",
@@ -41,6 +41,7 @@ __all__ = [
     "KdError",
     "KD_VALIDATE_IDX",
     "KD_ACCUMULATE_DW",
+    "KD_SKIP_DW",
 ]
 
 _DT = {torch.bfloat16: KD_BF16, torch.float32: KD_FP32}
@@ -125,11 +126,14 @@ def fused_kl_bwd(H, W, idx, tlog, lse, grad_loss=None, T: float = 1.0, chunk: in
                  n_norm: float = 0.0, flags: int = 0, dW: torch.Tensor | None = None,
                  workspace: torch.Tensor | None = None):
     """kd_fused_kl_bwd. Returns (dH [N,d] in H's dtype, dW [V,d] fp32). grad_loss is a device
-    scalar tensor or None (= 1). With KD_ACCUMULATE_DW, pass dW to add into."""
+    scalar tensor or None (= 1). With KD_ACCUMULATE_DW, pass dW to add into. With KD_SKIP_DW
+    only dH is computed and dW is returned as None."""
     dev = _need_device(H, W, idx, tlog, lse)
     p = make_problem(H, W, idx, tlog, T, chunk, n_norm, flags)
     dH = torch.empty_like(H)
-    if dW is None:
+    if flags & KD_SKIP_DW:
+        dW = None
+    elif dW is None:
         if flags & KD_ACCUMULATE_DW:
             raise KdError(1, "fused_kl_bwd", "KD_ACCUMULATE_DW needs a dW tensor")
         dW = torch.empty(W.shape, dtype=torch.float32, device=dev)
@@ -252,8 +256,10 @@ class FusedKL(torch.autograd.Function):
     def backward(ctx, g):
         H, W, idx, tlog, lse = ctx.saved_tensors
         T, chunk, n_norm = ctx.cfg
-        dH, dW = fused_kl_bwd(H, W, idx, tlog, lse, grad_loss=g, T=T, chunk=chunk, n_norm=n_norm)
-        return dH, dW.to(W.dtype), None, None, None, None, None
+        # a frozen head (W without a gradient) skips dW and the work that only it needs
+        flags = 0 if ctx.needs_input_grad[1] else KD_SKIP_DW
+        dH, dW = fused_kl_bwd(H, W, idx, tlog, lse, grad_loss=g, T=T, chunk=chunk, n_norm=n_norm, flags=flags)
+        return dH, (dW.to(W.dtype) if dW is not None else None), None, None, None, None, None
 
 
 def fused_kl(H, W, idx, tlog, T: float = 1.0, chunk: int = 2048, n_norm: float = 0.0):

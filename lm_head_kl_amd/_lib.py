@@ -13,7 +13,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkdkl.so")
 
 KD_FP32, KD_BF16 = 0, 1
-KD_VALIDATE_IDX, KD_ACCUMULATE_DW = 0x1, 0x2
+KD_VALIDATE_IDX, KD_ACCUMULATE_DW, KD_SKIP_DW = 0x1, 0x2, 0x4
 
 STATUS = {
     0: "KD_OK",

@@ -58,7 +58,8 @@ kd_status check_problem(const kd_problem* p) {
     if ((p->N + kTileM) * p->K >= lim || p->N * p->d >= lim || p->V * p->d >= lim) return KD_ERR_SHAPE;
     if (!std::isfinite(p->T) || !(p->T > 0.f)) return KD_ERR_VALUE;
     if (!std::isfinite(p->n_norm)) return KD_ERR_VALUE;
-    if ((p->flags & ~(KD_VALIDATE_IDX | KD_ACCUMULATE_DW)) != 0 || p->reserved != 0) return KD_ERR_VALUE;
+    if ((p->flags & ~(KD_VALIDATE_IDX | KD_ACCUMULATE_DW | KD_SKIP_DW)) != 0 || p->reserved != 0) return KD_ERR_VALUE;
+    if ((p->flags & KD_SKIP_DW) && (p->flags & KD_ACCUMULATE_DW)) return KD_ERR_VALUE;
     return KD_OK;
 }
 
@@ -326,8 +327,9 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
                           kd_stream stream) {
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
-    if (!H || !W || !idx || !tlog || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
-    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
+    const bool want_dw = (p->flags & KD_SKIP_DW) == 0;
+    if (!H || !W || !idx || !tlog || !lse || !dH || (want_dw && !dW) || !ws) return KD_ERR_NULL;
+    if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || (want_dw && !aligned(dW, 16))) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_fused_workspace_bytes(p)) return KD_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
@@ -357,13 +359,15 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
         // The chunk's row blocks in the plan; entry offsets in it are absolute.
         const int32_t* c_off = w.cplan_off + (one_plan ? (c0 / kTileM) * plan_stride : 0);
         // H_c^T into its slot, so that dW = G^T H reads both operands with the rows contiguous
-        KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
-                                (char*)w.HT + slot * C8 * es, w.ldgt, round_up(cc, 8), s));
+        if (want_dw)
+            KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
+                                    (char*)w.HT + slot * C8 * es, w.ldgt, round_up(cc, 8), s));
+        // Without dW, G^T is not needed: the gradient kernel skips those stores.
         KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.cplan_ent, w.Gc,
-                               (char*)w.GT + slot * C8 * es, w.ldgt, s));
+                               want_dw ? (char*)w.GT + slot * C8 * es : nullptr, w.ldgt, s));
         KD_TRY(launch_dh(sh, w.Gc, 0, W, w.WT, c0, cc, w.n_split, w.dh_part, dH, s));
         // One dW pass per group of chunks (K = the group's rows; the slots are zero-padded to 8)
-        if (slot == kDwGroup - 1 || c0 + cc >= p->N) {
+        if (want_dw && (slot == kDwGroup - 1 || c0 + cc >= p->N)) {
             KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * C8 + cc, acc0 || dw_written, dW, s));
             dw_written = true;
         }
@@ -376,6 +380,7 @@ kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const i
                       size_t ws_bytes, kd_stream stream) {
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
+    if (p->flags & KD_SKIP_DW) return KD_ERR_VALUE;  // only the fused backward can leave dW out
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_dense_workspace_bytes(p)) return KD_ERR_WORKSPACE;
@@ -428,6 +433,7 @@ kd_status kd_chunked_kl(const kd_problem* p, const void* H, const void* W, const
                         size_t ws_bytes, kd_stream stream) {
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
+    if (p->flags & KD_SKIP_DW) return KD_ERR_VALUE;  // only the fused backward can leave dW out
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_chunked_workspace_bytes(p)) return KD_ERR_WORKSPACE;
@@ -455,6 +461,7 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
                              void* ws, size_t ws_bytes, kd_stream stream) {
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
+    if (p->flags & KD_SKIP_DW) return KD_ERR_VALUE;  // only the fused backward can leave dW out
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_fused_fwdbwd_workspace_bytes(p)) return KD_ERR_WORKSPACE;

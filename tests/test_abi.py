@@ -142,7 +142,7 @@ def dense(p, H=F, dH=F, ws=F, nbytes=None):
     (dict(d=(1 << 20) + 8, V=1000, N=1000), 2),
     (dict(act=2), 3), (dict(tlogit=-1), 3),
     (dict(T=0.0), 4), (dict(T=-1.0), 4), (dict(T=float("nan")), 4), (dict(T=float("inf")), 4),
-    (dict(n_norm=float("nan")), 4), (dict(flags=4), 4), (dict(reserved=1), 4),
+    (dict(n_norm=float("nan")), 4), (dict(flags=8), 4), (dict(reserved=1), 4),
 ])
 def test_bad_problem_rejected(bad, code):
     p = prob(**bad)
@@ -194,3 +194,19 @@ def test_topk_bad_arguments(args, code):
     L = _lib.lib()
     assert L.kd_topk_cache(a["logits"], a["dtype"], a["N"], a["V"], a["ld"], a["K"], a["idx"], a["values"],
                            None) == code
+
+
+@nogpu
+def test_skip_dw_flag_rules():
+    """KD_SKIP_DW: only the fused backward may leave dW out; with KD_ACCUMULATE_DW it is
+    rejected by every call; without it the fused backward still needs dW."""
+    L = _lib.lib()
+    both = prob(flags=_lib.KD_SKIP_DW | _lib.KD_ACCUMULATE_DW)
+    assert fwd(both) == 4 and bwd(both) == 4 and dense(both) == 4
+    p = prob(flags=_lib.KD_SKIP_DW)
+    assert dense(p) == 4
+    for fn, query in (("kd_chunked_kl", "kd_chunked_workspace_bytes"),
+                      ("kd_fused_kl_fwdbwd", "kd_fused_fwdbwd_workspace_bytes")):
+        nb = max(1, getattr(L, query)(ctypes.byref(p)))
+        assert getattr(L, fn)(ctypes.byref(p), F, F, F, F, None, F, F, None, F, F, F, nb, None) == 4
+    assert bwd(prob(), dW=None) == 1

@@ -176,3 +176,24 @@ def test_fused_peak_memory_flat_in_sequence():
         del H, idx, t
     # dW (fp32, 2.3 GB) and the gradient tile (C x V bf16, 0.82 GB) dominate; no growth with S
     assert max(extra) - min(extra) <= 0.02 * max(extra)
+
+
+def test_skip_dw_frozen_head():
+    """KD_SKIP_DW computes the same dH bit for bit and leaves dW alone; the autograd term uses it
+    when W does not require a gradient."""
+    p = datagen.make("small", N=1536)
+    say("KD_SKIP_DW")
+    H, W, idx, t = device_inputs(p)
+    f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=512)
+    dH_full, dW_full = kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=512)
+    dH_skip, dW_none = kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=512, flags=kd.KD_SKIP_DW)
+    torch.cuda.synchronize()
+    assert dW_none is None
+    assert torch.equal(dH_full.view(torch.int16), dH_skip.view(torch.int16))
+    # autograd: frozen head
+    Hg = H.clone().requires_grad_(True)
+    loss = kd.fused_kl(Hg, W, idx, t, T=p.T, chunk=512)
+    loss.backward()
+    torch.cuda.synchronize()
+    assert torch.equal(Hg.grad.view(torch.int16), dH_full.view(torch.int16))
+    assert W.grad is None
