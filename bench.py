@@ -186,6 +186,20 @@ def sweep(dev, steps: int):
         grow = "" if prev is None else f"{(r['peak_beyond_inputs_gb'] - prev['peak_beyond_inputs_gb']) * 1e9 / (r['N'] - prev['N']):.0f}"
         print(f"| {r['N']} | {r['peak_beyond_inputs_gb']:.3f} | {r['peak_beyond_inputs_gb'] - r['dH_gb']:.3f} | {grow} |")
         prev = r
+    # The oracle as it stands on each config: the whole tiny and small batches, and the first
+    # 1024 rows at full V and d for the larger heads (cost is linear in rows).
+    gpu_rate = {}
+    for r in rows:
+        if r["config"] not in gpu_rate or r["chunk"] == datagen.CONFIGS[r["config"]]["chunk"]:
+            gpu_rate[r["config"]] = r["tokens_per_s"]
+    print()
+    print("| config | oracle rows | oracle s | oracle tokens/s | threads | GPU fused step tokens/s | GPU / oracle |")
+    print("|---|---|---|---|---|---|---|")
+    for name, n in (("tiny", 256), ("small", 4096), ("qwen", 1024), ("gptoss", 1024), ("full", 1024)):
+        cb = cpu_baseline(datagen.make(name, N=n), n)
+        g = gpu_rate.get(name)
+        print(f"| {name} | {n} | {n / cb['value']:.2f} | {cb['value']:,.0f} | {cb['cores']} | "
+              + (f"{g:,.0f} | {g / cb['value']:,.0f} |" if g else "— | — |"), flush=True)
 
 
 def main():
