@@ -205,8 +205,8 @@ def sweep(dev, steps: int):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported by this build "
-              f"(the path is measured on one GPU's share; see the sharding notes)", file=sys.stderr)
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported: the path is "
+              f"measured on one GPU's share of a token-parallel job", file=sys.stderr)
         sys.exit(2)
 
     import torch

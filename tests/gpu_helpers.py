@@ -9,7 +9,7 @@ import torch
 import datagen
 
 TOL = {
-    # the benchmark spec tolerances: loss/lse relative, dH/dW relative L2
+    # the stated tolerances: loss and lse relative, dH and dW relative L2
     "fp32": dict(loss=1e-6, lse=1e-6, grad=1e-5),
     "bf16": dict(loss=2e-3, lse=2e-3, grad=1e-2),
 }
