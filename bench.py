@@ -339,6 +339,32 @@ def main():
         },
     }
 
+    # The same step replayed from a HIP graph (torch.cuda.CUDAGraph): every launch of the
+    # forward and backward captured once with the step's buffers, then replayed. Shows what
+    # launch overhead the eager step carries; the headline figure stays the eager one.
+    if not args.no_formulations:
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        out["graph_replay_ms_per_step"] = e[0].elapsed_time(e[1]) / args.steps
+        del graph
+        torch.cuda.empty_cache()
+        print("[bench] graph replay done", file=sys.stderr, flush=True)
+
     # The other formulations on the same inputs: one call each does forward and backward.
     # Each is warmed up once and timed over a few calls; peak memory is measured from the
     # inputs up, like the fused path's.
