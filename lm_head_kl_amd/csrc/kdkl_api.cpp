@@ -27,7 +27,13 @@ namespace {
 
 constexpr int64_t kAlign = 256;
 constexpr int64_t kMaxD = (int64_t)1 << 20;  // keeps a tile's 256 rows of d fp32 within 32-bit offsets
-constexpr int64_t kDwGroup = 4;  // chunks per dW pass
+// Chunks per dW pass: as many as make about 8192 tokens (4 chunks of 2048). Each pass reads and
+// writes all of dW once, so few tokens per pass multiply that traffic; many make each
+// vocabulary tile's G^T slab outgrow the L2 (16384 tokens measured 4% slower than 8192, and 4096
+// tokens 6% slower). It depends on the chunk only, so the workspace does not grow with N; a
+// group the batch does not fill ends with the last chunk.
+constexpr int64_t kDwTokens = 8192;
+int64_t dw_group(const kd_problem*, int64_t C) { return std::max<int64_t>(1, kDwTokens / round_up(C, 8)); }
 
 struct Carve {
     uintptr_t base;
@@ -97,7 +103,7 @@ struct FusedWs {
     void* WT;   // K-blocked W^T [Vp/256][d][256], entries past V zero
     void* HT;   // [d][ldgt]: H_c transposed
     float* dh_part;
-    int64_t ldgt;
+    int64_t ldgt, group;
     int n_vsplit, n_split;
     size_t fwd_bytes, bwd_bytes;
 };
@@ -125,9 +131,10 @@ FusedWs layout_fused(const kd_problem* p, void* ws) {
     w.cplan_off = (int32_t*)b.take(sizeof(int32_t) * n_rblocks(plan_rows) * (n_vt + 1));
     w.cplan_ent = (uint32_t*)b.take(sizeof(uint32_t) * n_rblocks(plan_rows) * kTileM * K);
     w.pt = (float*)b.take(sizeof(float) * N * K);
-    // G_c^T and H_c^T hold kDwGroup chunks side by side (slot s at columns s*round_up(C, 8)), so
-    // one dW pass reduces over kDwGroup chunks and dW is read and written once per group.
-    w.ldgt = kDwGroup * round_up(C, 8);
+    // G_c^T and H_c^T hold a group of chunks side by side (slot s at columns s*round_up(C, 8)),
+    // so one dW pass reduces over the group and dW is read and written once per group.
+    w.group = dw_group(p, C);
+    w.ldgt = w.group * round_up(C, 8);
     w.Gc = b.take(esize(p->act) * C * Vp);
     w.GT = b.take(esize(p->act) * Vp * w.ldgt);
     w.WT = b.take(esize(p->act) * d * Vp);
@@ -156,7 +163,7 @@ struct StoredWs {
     void* WT;
     void* HT;
     float* dh_part;
-    int64_t ldgt;
+    int64_t ldgt, group;
     int n_vsplit, n_split;
     size_t bytes;
 };
@@ -170,7 +177,8 @@ StoredWs layout_stored(const kd_problem* p, void* ws, bool all_rows) {
     w.n_vsplit = fwd_vsplits(fwd_rows, V);
     w.n_split = dh_splits(C, d, V, true);
     w.ldzt = round_up(fwd_rows, 4);
-    w.ldgt = kDwGroup * round_up(C, 8);
+    w.group = dw_group(p, C);
+    w.ldgt = w.group * round_up(C, 8);
     const int64_t n_chunks = (N + C - 1) / C;
     Carve c(ws);
     w.status = (uint32_t*)c.take(kAlign);
@@ -249,7 +257,7 @@ kd_status stored_backward(const kd_problem* p, const Shape& sh, const StoredWs& 
     bool dw_written = false;
     for (int64_t c0 = 0; c0 < p->N; c0 += C, ++ci) {
         const int64_t cc = std::min(C, p->N - c0);
-        const int64_t slot = ci % kDwGroup;
+        const int64_t slot = ci % w.group;
         if (!one_plan) KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.plan_off, w.plan_ent, s));
         const int32_t* c_off = w.plan_off + (one_plan ? (c0 / kTileM) * plan_stride : 0);
         KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
@@ -257,7 +265,7 @@ kd_status stored_backward(const kd_problem* p, const Shape& sh, const StoredWs& 
         KD_TRY(launch_grad_z(sh, w.zt, w.ldzt, c0, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.plan_ent, w.Gc,
                              (char*)w.GT + slot * C8 * es, w.ldgt, s));
         KD_TRY(launch_dh(sh, w.Gc, 0, nullptr, w.WT, c0, cc, w.n_split, w.dh_part, dH, s));
-        if (slot == kDwGroup - 1 || c0 + cc >= p->N) {
+        if (slot == w.group - 1 || c0 + cc >= p->N) {
             KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * C8 + cc, acc0 || dw_written, dW, s));
             dw_written = true;
         }
@@ -354,7 +362,7 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
     bool dw_written = false;
     for (int64_t c0 = 0; c0 < p->N; c0 += C, ++ci) {
         const int64_t cc = std::min(C, p->N - c0);
-        const int64_t slot = ci % kDwGroup;
+        const int64_t slot = ci % w.group;
         if (!one_plan) KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.cplan_off, w.cplan_ent, s));
         // The chunk's row blocks in the plan; entry offsets in it are absolute.
         const int32_t* c_off = w.cplan_off + (one_plan ? (c0 / kTileM) * plan_stride : 0);
@@ -367,7 +375,7 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
                                want_dw ? (char*)w.GT + slot * C8 * es : nullptr, w.ldgt, s));
         KD_TRY(launch_dh(sh, w.Gc, 0, W, w.WT, c0, cc, w.n_split, w.dh_part, dH, s));
         // One dW pass per group of chunks (K = the group's rows; the slots are zero-padded to 8)
-        if (want_dw && (slot == kDwGroup - 1 || c0 + cc >= p->N)) {
+        if (want_dw && (slot == w.group - 1 || c0 + cc >= p->N)) {
             KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * C8 + cc, acc0 || dw_written, dW, s));
             dw_written = true;
         }
@@ -487,7 +495,7 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
     bool dw_written = false;
     for (int64_t c0 = 0; c0 < p->N; c0 += C, ++ci) {
         const int64_t cc = std::min(C, p->N - c0);
-        const int64_t slot = ci % kDwGroup;
+        const int64_t slot = ci % w.group;
         if (!one_plan) KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.plan_off, w.plan_ent, s));
         const int32_t* c_off = w.plan_off + (one_plan ? (c0 / kTileM) * plan_stride : 0);
         // The chunk's logits, once: loss terms and z^T, which the gradient tile then reads.
@@ -505,7 +513,7 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
         KD_TRY(launch_grad_z(sh, w.zt, w.ldzt, 0, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.plan_ent, w.Gc,
                              (char*)w.GT + slot * C8 * es, w.ldgt, s));
         KD_TRY(launch_dh(sh, w.Gc, 0, nullptr, w.WT, c0, cc, w.n_split, w.dh_part, dH, s));
-        if (slot == kDwGroup - 1 || c0 + cc >= p->N) {
+        if (slot == w.group - 1 || c0 + cc >= p->N) {
             KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * C8 + cc, acc0 || dw_written, dW, s));
             dw_written = true;
         }
