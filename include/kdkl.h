@@ -161,7 +161,8 @@ kd_status kd_fused_kl_fwd(const kd_problem* p, const void* H, const void* W, con
  *   lse [N] fp32           from kd_fused_kl_fwd on the same inputs
  *   grad_loss [1] fp32     upstream gradient g of the scalar loss (device), or NULL for 1
  *   dH [N,d] act           written (overwritten)
- *   dW [V,d] fp32          overwritten, or incremented under KD_ACCUMULATE_DW
+ *   dW [V,d] fp32          overwritten, incremented under KD_ACCUMULATE_DW,
+ *                          or untouched (and may be NULL) under KD_SKIP_DW
  * Source: same paragraph (the backward recomputes each chunk on the fly); dailyai.com.br
  * launch note, section "As duas inovacoes", item 2.
  */
