@@ -343,27 +343,31 @@ def main():
     # forward and backward captured once with the step's buffers, then replayed. Shows what
     # launch overhead the eager step carries; the headline figure stays the eager one.
     if not args.no_formulations:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            step()
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        graph.replay()
-        torch.cuda.synchronize()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        e[0].record(stream)
-        for _ in range(args.steps):
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                step()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
             graph.replay()
-        e[1].record(stream)
-        torch.cuda.synchronize()
-        out["graph_replay_ms_per_step"] = e[0].elapsed_time(e[1]) / args.steps
-        del graph
-        torch.cuda.empty_cache()
-        print("[bench] graph replay done", file=sys.stderr, flush=True)
+            torch.cuda.synchronize()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            for _ in range(args.steps):
+                graph.replay()
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            out["graph_replay_ms_per_step"] = e[0].elapsed_time(e[1]) / args.steps
+            del graph
+            torch.cuda.empty_cache()
+            print("[bench] graph replay done", file=sys.stderr, flush=True)
+        except (RuntimeError, torch.OutOfMemoryError) as ex:
+            out["graph_replay_ms_per_step"] = None
+            out["graph_replay_error"] = str(ex)[:200]
 
     # The other formulations on the same inputs: one call each does forward and backward.
     # Each is warmed up once and timed over a few calls; peak memory is measured from the
@@ -415,34 +419,40 @@ def main():
         out["peak_hbm_dense_gb"] = forms["dense"]["peak_hbm_gb"]
 
     if not args.no_formulations:
-        # The offline top-K cache producer on teacher logits of the workload's shape: seeded
-        # synthetic bf16 rows N(0, 4), K = the cache width. HBM-bound; reported against one read
-        # of the logits.
-        torch.cuda.empty_cache()
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(p.extra.get("seed", 0) + 9)
-        tl = torch.empty((N, V), dtype=torch.bfloat16, device=dev)
-        for r0 in range(0, N, 4096):
-            tl[r0:r0 + 4096] = (torch.randn((min(4096, N - r0), V), generator=gen, device=dev) * 2.0).to(torch.bfloat16)
-        kd.topk_cache(tl[:256], p.K)
-        torch.cuda.synchronize()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        e[0].record(stream)
-        kd.topk_cache(tl, p.K)
-        e[1].record(stream)
-        torch.cuda.synchronize()
-        ms_tk = e[0].elapsed_time(e[1])
-        read_gb = N * V * 2 / 1e9
-        out["topk_producer"] = {"rows": N, "V": V, "K": p.K, "dtype": "bf16", "ms": ms_tk,
-                                "rows_per_s": N / (ms_tk / 1e3), "logits_read_once_gb_s": read_gb / (ms_tk / 1e3),
-                                "frac_of_hbm_peak": read_gb / (ms_tk / 1e3) / PEAK_HBM_GBS}
-        del tl
-        torch.cuda.empty_cache()
-        print("[bench] top-K producer done", file=sys.stderr, flush=True)
+        try:
+            # The offline top-K cache producer on teacher logits of the workload's shape: seeded
+            # synthetic bf16 rows N(0, 4), K = the cache width. HBM-bound; reported against one read
+            # of the logits.
+            torch.cuda.empty_cache()
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(p.extra.get("seed", 0) + 9)
+            tl = torch.empty((N, V), dtype=torch.bfloat16, device=dev)
+            for r0 in range(0, N, 4096):
+                tl[r0:r0 + 4096] = (torch.randn((min(4096, N - r0), V), generator=gen, device=dev) * 2.0).to(torch.bfloat16)
+            kd.topk_cache(tl[:256], p.K)
+            torch.cuda.synchronize()
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record(stream)
+            kd.topk_cache(tl, p.K)
+            e[1].record(stream)
+            torch.cuda.synchronize()
+            ms_tk = e[0].elapsed_time(e[1])
+            read_gb = N * V * 2 / 1e9
+            out["topk_producer"] = {"rows": N, "V": V, "K": p.K, "dtype": "bf16", "ms": ms_tk,
+                                    "rows_per_s": N / (ms_tk / 1e3), "logits_read_once_gb_s": read_gb / (ms_tk / 1e3),
+                                    "frac_of_hbm_peak": read_gb / (ms_tk / 1e3) / PEAK_HBM_GBS}
+            del tl
+            torch.cuda.empty_cache()
+            print("[bench] top-K producer done", file=sys.stderr, flush=True)
+        except (RuntimeError, torch.OutOfMemoryError) as ex:
+            out["topk_producer"] = {"error": str(ex)[:200]}
 
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline on {args.cpu_rows} rows", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(p, args.cpu_rows)
+        try:
+            out["cpu_baseline"] = cpu_baseline(p, args.cpu_rows)
+        except Exception as ex:  # the headline line is printed whatever happens here
+            out["cpu_baseline"] = {"value": None, "error": str(ex)[:200]}
 
     print(json.dumps(out), flush=True)
 
