@@ -517,6 +517,9 @@ __device__ __forceinline__ void store8(T* dst, const float (&x)[8]) {
 // Second half of a gradient pass, once the pass's 128 vocabulary rows of gs*softmax are staged:
 // subtract gs*p_t at the cached ids that fall in the pass, then write the rows of G (K-blocked)
 // and of G^T. Ends with a barrier, so the stage may be refilled.
+// The plan fills each bucket in atomic order, so whether an entry is among the first NT (held
+// in registers) or comes from the loop changes between calls; both paths subtract with one
+// explicit fused multiply-add, so G does not depend on that order.
 template <typename T, int NW>
 __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, int pq, const WaveIdN<NW>& ie, int vt,
                                               int64_t r0, int64_t n0, int e0, int e1, uint32_t my_en, float my_pt,
@@ -524,14 +527,16 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
     constexpr int NT = 64 * NW, IT = 4096 / NT;  // items per thread of each output layout
     if (my_en != 0xffffffffu && ((my_en >> 14) & 1) == (uint32_t)pq) {
         const int r = my_en & 255, c = (my_en >> 8) & 255;
-        stage[st_idx(st_row(c), r)] -= gs * my_pt;
+        float& x = stage[st_idx(st_row(c), r)];
+        x = fmaf(-gs, my_pt, x);
     }
     for (int i = e0 + NT + ie.tid; i < e1; i += NT) {
         const uint32_t en = a.ent[i];
         const int c = (en >> 8) & 255;
         if (((c >> 6) & 1) != pq) continue;
         const int r = en & 255, k = (int)(en >> 16);
-        stage[st_idx(st_row(c), r)] -= gs * a.pt[(r0 + r) * a.K + k];
+        float& x = stage[st_idx(st_row(c), r)];
+        x = fmaf(-gs, a.pt[(r0 + r) * a.K + k], x);
     }
     __syncthreads();
     // G rows: group g of 8 vocabulary entries (stage rows 8g .. 8g+7) by a group of 4 tokens.
@@ -653,7 +658,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
 // vocabulary rows (64 KB), so two workgroups share a CU and the loads of one overlap the
 // stores of the other; each pass's z^T rows are requested before the previous pass is staged.
 // G is formed with the same operations as in k_bwd_grad (the exp2 of the tempered logit minus
-// lse, times gs, then gs*p_t subtracted in fp32), so both kernels give the same bits.
+// lse, times gs, then gs*p_t subtracted with one fused multiply-add), so both kernels give the
+// same bits.
 constexpr int kGzRows = 64;  // vocabulary rows per pass
 
 template <typename T>
@@ -723,14 +729,16 @@ __global__ __launch_bounds__(256, 2) void k_grad_z(GradArgs a) {
         // gs*p_t at the cached ids whose vocabulary row is in this pass (bits 6-7 of the column)
         if (my_en != 0xffffffffu && ((my_en >> 14) & 3) == (uint32_t)pq) {
             const int r = my_en & 255, c = (my_en >> 8) & 255;
-            stage[st_idx(c & 63, r)] -= gs * my_pt;
+            float& x = stage[st_idx(c & 63, r)];
+            x = fmaf(-gs, my_pt, x);
         }
         for (int i = e0 + NTHR + id.tid; i < e1; i += NTHR) {
             const uint32_t en = a.ent[i];
             const int c = (en >> 8) & 255;
             if ((c >> 6) != pq) continue;
             const int r = en & 255, k = (int)(en >> 16);
-            stage[st_idx(c & 63, r)] -= gs * a.pt[(r0 + r) * a.K + k];
+            float& x = stage[st_idx(c & 63, r)];
+            x = fmaf(-gs, a.pt[(r0 + r) * a.K + k], x);
         }
         __syncthreads();
         // G rows: token tl, group g of 8 vocabulary entries; 8 lanes write a token's 64 entries

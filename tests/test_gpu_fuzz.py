@@ -1,0 +1,111 @@
+"""Seeded random problems: sizes, dtype, temperature, teacher recipe, id recipe, chunk,
+normaliser and upstream weight are drawn per case, and each formulation is compared in full
+with the fp64 oracle at the stated tolerances. The fixed edge list elsewhere names the
+boundaries one at a time; here they are combined the way a caller might combine them
+(a ragged chunk with K near its maximum, d just past a hidden tile, V below one vocab tile).
+
+The draws are fixed by the case number, so a failing case is reproduced by its id."""
+
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+import lm_head_kl_amd as kd
+from gpu_helpers import TOL, device_inputs, host, max_rel, rel_l2, say
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 16
+
+
+def draw_case(i: int) -> dict:
+    g = np.random.Generator(np.random.PCG64([4242, i]))
+    d = 8 * int(g.integers(1, 81))                        # 8 .. 648
+    V = int(g.choice([int(g.integers(1, 256)), int(g.integers(256, 6000))]))
+    kmax = min(V, 1024)
+    K = int(g.choice([1, int(g.integers(1, kmax + 1)), kmax]))
+    N = int(g.integers(1, 700))
+    chunk = int(g.choice([1, int(g.integers(1, N + 1)), 64, 256, 512, 2048]))
+    T = float(g.choice([0.5, 1.0, 1.7, 4.0]))
+    teacher = str(g.choice(["normal", "peaked", "flat", "mix"]))
+    # Zipf ids are drawn by rejection, so keep K well under V for them
+    ids = str(g.choice(["uniform", "zipf", "mix"])) if 4 * K <= V else "uniform"
+    dtype = str(g.choice(["fp32", "bf16"]))
+    n_norm = float(g.choice([0.0, float(g.integers(1, 2 * N + 2))]))
+    grad = float(g.choice([1.0, 0.37, -2.0]))
+    return dict(N=N, d=d, V=V, K=K, chunk=chunk, T=T, teacher=teacher, ids=ids, dtype=dtype,
+                n_norm=n_norm, grad=grad, seed=5000 + i)
+
+
+def make_problem(c: dict) -> datagen.Problem:
+    return datagen.make("tiny", N=c["N"], seed=c["seed"], d=c["d"], V=c["V"], K=c["K"], T=c["T"],
+                        dtype=c["dtype"], chunk=c["chunk"], teacher=c["teacher"], ids=c["ids"])
+
+
+def check(label, c, ref, loss, lse, row_kl, dH, dW=None, zk=None):
+    tol = TOL[c["dtype"]]
+    got = float(loss.item()) * c["grad"]  # the oracle's loss carries the upstream weight
+    assert abs(got - ref["loss"]) <= tol["loss"] * max(abs(ref["loss"]), 1e-30), (label, got, ref["loss"])
+    assert max_rel(host(lse), ref["lse"]) <= tol["lse"], label
+    scale = max(np.abs(ref["row_kl"]).max(), 1e-30)
+    assert np.max(np.abs(host(row_kl) - ref["row_kl"])) <= tol["loss"] * scale, label
+    if zk is not None:
+        np.testing.assert_allclose(host(zk), ref["zk"], rtol=tol["lse"], atol=tol["lse"] * 4, err_msg=label)
+    e_dh = rel_l2(host(dH), ref["dH"])
+    e_dw = None if dW is None else rel_l2(host(dW), ref["dW"])
+    say(f"  {label}: dH relL2 {e_dh:.2e}" + ("" if e_dw is None else f"  dW relL2 {e_dw:.2e}"))
+    assert e_dh <= tol["grad"], label
+    if e_dw is not None:
+        assert e_dw <= tol["grad"], label
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_fuzz_case(i):
+    c = draw_case(i)
+    say(f"fuzz case {i}:", {k: v for k, v in c.items()})
+    p = make_problem(c)
+    H, W, idx, t = device_inputs(p)
+    nn = None if c["n_norm"] == 0.0 else c["n_norm"]
+    ref = oracle.kl_chunked(p.f64("H"), p.f64("W"), p.idx, p.f64("tlog"), p.T, chunk=256, n_norm=nn, g=c["grad"])
+    gt = torch.tensor(c["grad"], dtype=torch.float32, device=H.device)
+
+    # fused pair
+    f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=c["chunk"], n_norm=c["n_norm"], want_zk=True)
+    dH, dW = kd.fused_kl_bwd(H, W, idx, t, f.lse, grad_loss=gt, T=p.T, chunk=c["chunk"], n_norm=c["n_norm"])
+    torch.cuda.synchronize()
+    check("fused", c, ref, f.loss, f.lse, f.row_kl, dH, dW, zk=f.zk)
+
+    # frozen head: the same dH, dW left alone
+    dH2, none = kd.fused_kl_bwd(H, W, idx, t, f.lse, grad_loss=gt, T=p.T, chunk=c["chunk"], n_norm=c["n_norm"],
+                                flags=kd.KD_SKIP_DW)
+    torch.cuda.synchronize()
+    assert none is None
+    assert torch.equal(dH2, dH), "frozen-head dH differs from the full backward's"
+
+    # accumulate: a second backward added into the first dW doubles it, up to fp32 rounding of
+    # the running sum where several dW passes add in turn
+    dW_acc = dW.clone()
+    kd.fused_kl_bwd(H, W, idx, t, f.lse, grad_loss=gt, T=p.T, chunk=c["chunk"], n_norm=c["n_norm"],
+                    dW=dW_acc, flags=kd.KD_ACCUMULATE_DW)
+    torch.cuda.synchronize()
+    assert rel_l2(host(dW_acc), 2.0 * host(dW)) <= 1e-6, "accumulated dW is not twice the overwritten one"
+
+    # the two other formulations
+    for name, fn in (("chunked", kd.chunked_kl), ("fwdbwd", kd.fused_kl_fwdbwd)):
+        loss, lse, row_kl, dHx, dWx = fn(H, W, idx, t, T=p.T, chunk=c["chunk"], grad_loss=gt, n_norm=c["n_norm"])
+        torch.cuda.synchronize()
+        check(name, c, ref, loss, lse, row_kl, dHx, dWx)
+
+
+def test_fuzz_draws_cover_the_boundaries():
+    """The fixed draws reach both dtypes, K = 1, K at min(V, 1024), V below one vocab tile,
+    chunk = 1, and a non-default normaliser."""
+    cs = [draw_case(i) for i in range(N_CASES)]
+    assert {c["dtype"] for c in cs} == {"fp32", "bf16"}
+    assert any(c["K"] == 1 for c in cs)
+    assert any(c["K"] == min(c["V"], 1024) and c["K"] > 1 for c in cs)
+    assert any(c["V"] < 256 for c in cs)
+    assert any(c["chunk"] == 1 for c in cs)
+    assert any(c["n_norm"] != 0.0 for c in cs)

@@ -29,6 +29,28 @@ def test_bitwise_deterministic():
                            if b.dtype == torch.bfloat16 else b)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_backward_reproducible_across_plan_order(dtype):
+    """The plan fills each (row block, vocab tile) bucket in atomic order, so an entry's place in
+    its bucket changes between calls. With K = 1024 over 12 vocab tiles a bucket's 512th entry
+    falls in rows 5-6, whose entries are therefore subtracted by the in-register path in one call
+    and by the loop in the next: the fp32 gradients must still come out bit for bit the same."""
+    p = datagen.make("tiny", N=505, d=584, V=3038, K=1024, T=1.0, chunk=256, dtype=dtype,
+                     teacher="flat", ids="uniform", seed=5009)
+    say("backward reproducible over plan order", dtype)
+    H, W, idx, t = device_inputs(p)
+    f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=256)
+    outs = []
+    for _ in range(4):
+        dH, dW = kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=256)
+        torch.cuda.synchronize()
+        outs.append((dH.clone(), dW.clone()))
+    for dH, dW in outs[1:]:
+        assert torch.equal(dH.view(torch.int16) if dtype == "bf16" else dH,
+                           outs[0][0].view(torch.int16) if dtype == "bf16" else outs[0][0])
+        assert torch.equal(dW, outs[0][1])
+
+
 def test_accumulate_dw_doubles():
     p = datagen.make("tiny")
     say("KD_ACCUMULATE_DW")
