@@ -115,3 +115,55 @@ def test_fuzz_draws_cover_the_boundaries():
     assert any(c["V"] < 256 for c in cs)
     assert any(c["chunk"] == 1 for c in cs)
     assert any(c["n_norm"] != 0.0 for c in cs)
+
+
+# Medium shapes: more tiles than the chip has workgroup slots, so the persistent loops, the
+# forward's vocabulary split and the dW chunk groups all take their general paths. Every row's
+# lse, zk, KL_n and dH row is compared; dW on 64 vocabulary rows (ids 0-3, V-1 and seeded).
+N_MEDIUM = 6
+
+
+def draw_medium(i: int) -> dict:
+    g = np.random.Generator(np.random.PCG64([4243, i]))
+    N = int(g.integers(1000, 3000))
+    d = 8 * int(g.integers(16, 97))                       # 128 .. 768
+    V = int(g.integers(16000, 48000))
+    K = int(g.choice([int(g.integers(1, 129)), int(g.integers(129, 1025))]))
+    chunk = int(g.choice([int(g.integers(100, N)), 256, 512, 1024, 4096]))
+    T = float(g.choice([0.5, 1.0, 2.0]))
+    teacher = str(g.choice(["peaked", "flat", "mix"]))
+    ids = str(g.choice(["uniform", "zipf", "mix"]))
+    dtype = "fp32" if i % 3 == 2 else "bf16"
+    return dict(N=N, d=d, V=V, K=K, chunk=chunk, T=T, teacher=teacher, ids=ids, dtype=dtype,
+                n_norm=0.0, grad=1.0, seed=6000 + i)
+
+
+@pytest.mark.parametrize("i", range(N_MEDIUM))
+def test_fuzz_medium(i):
+    c = draw_medium(i)
+    say(f"medium case {i}:", {k: v for k, v in c.items()})
+    p = make_problem(c)
+    H, W, idx, t = device_inputs(p)
+    tol = TOL[c["dtype"]]
+    f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=c["chunk"], want_zk=True)
+    dH, dW = kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=c["chunk"])
+    torch.cuda.synchronize()
+    Hf, Wf, tl = p.f64("H"), p.f64("W"), p.f64("tlog")
+    ref = {k: [] for k in ("lse", "row_kl", "zk", "dH")}
+    for r0 in range(0, p.N, 512):
+        rows = np.arange(r0, min(p.N, r0 + 512))
+        part = oracle.kl_rows(Hf, Wf, p.idx, tl, p.T, rows, n_norm=p.N)
+        for k in ref:
+            ref[k].append(part[k])
+    ref = {k: np.concatenate(v) for k, v in ref.items()}
+    loss = p.T * p.T / p.N * float(np.sum(ref["row_kl"]))
+    assert abs(f.loss.item() - loss) <= tol["loss"] * abs(loss)
+    assert max_rel(host(f.lse), ref["lse"]) <= tol["lse"]
+    assert np.max(np.abs(host(f.row_kl) - ref["row_kl"])) <= tol["loss"] * np.abs(ref["row_kl"]).max()
+    np.testing.assert_allclose(host(f.zk), ref["zk"], rtol=tol["lse"], atol=tol["lse"] * 4)
+    e_dh = rel_l2(host(dH), ref["dH"])
+    vocab = datagen.sample_vocab(p.V, 64, c["seed"])
+    want = oracle.dw_rows(Hf, Wf, p.idx, tl, p.T, vocab, ref["lse"], n_norm=p.N)
+    e_dw = rel_l2(host(dW[torch.from_numpy(vocab).to(dW.device)]), want)
+    say(f"  dH relL2 {e_dh:.2e}  dW rows relL2 {e_dw:.2e}")
+    assert e_dh <= tol["grad"] and e_dw <= tol["grad"]
