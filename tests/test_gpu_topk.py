@@ -99,3 +99,42 @@ def test_cache_feeds_the_loss():
     ci, cv = oracle.topk_cache(teacher, p.K)
     ref = oracle.kl_dense(p.f64("H"), p.f64("W"), ci, cv, p.T)
     assert abs(f.loss.item() - ref["loss"]) <= 1e-6 * abs(ref["loss"])
+
+
+def draw_rows(g: np.random.Generator, N: int, V: int, K: int) -> np.ndarray:
+    """Rows of mixed kinds: scaled normals, small integers (many ties), normals with signed zeros
+    and infinities planted, and rows where many entries equal the value at the cutoff."""
+    x = np.empty((N, V), np.float32)
+    for n in range(N):
+        kind = int(g.integers(0, 4))
+        if kind == 0:
+            x[n] = g.standard_normal(V) * float(g.choice([1e-3, 1.0, 100.0]))
+        elif kind == 1:
+            r = int(g.integers(0, 11))
+            x[n] = g.integers(-r, r + 1, V)
+        elif kind == 2:
+            x[n] = g.standard_normal(V)
+            m = int(g.integers(0, min(V, 40) + 1))
+            pos = g.choice(V, size=m, replace=False)
+            x[n, pos] = g.choice(np.array([0.0, -0.0, np.inf, -np.inf], np.float32), size=m)
+        else:
+            x[n] = g.standard_normal(V)
+            cut = np.sort(x[n])[::-1][min(K, V) - 1]
+            m = int(g.integers(1, V + 1))
+            x[n, g.choice(V, size=m, replace=False)] = cut
+    return x
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes(i):
+    """Seeded random (N, V, K, row stride, dtype, row kinds); ids and values bit for bit."""
+    g = np.random.Generator(np.random.PCG64([4244, i]))
+    V = int(g.choice([int(g.integers(1, 300)), int(g.integers(300, 5000)), int(g.integers(5000, 70000))]))
+    N = int(g.integers(1, max(2, min(300, 4_000_000 // V))))
+    K = int(g.choice([1, int(g.integers(1, min(V, 1024) + 1)), min(V, 1024)]))
+    ld = V + int(g.choice([0, int(g.integers(1, 64))]))
+    dtype = "bf16" if i % 2 else "fp32"
+    x = draw_rows(g, N, V, K)
+    if dtype == "bf16":
+        x = bf16_values(x)
+    check(x, K, dtype, f"random shape {i}", ld=ld)
