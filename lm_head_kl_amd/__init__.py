@@ -55,6 +55,8 @@ def make_problem(H: torch.Tensor, W: torch.Tensor, idx: torch.Tensor, tlog: torc
         raise KdError(3, "make_problem", "teacher logits must be bfloat16 or float32")
     if idx.dtype != torch.int32:
         raise KdError(3, "make_problem", "idx must be int32")
+    if H.dim() != 2 or W.dim() != 2 or idx.dim() != 2 or tlog.dim() != 2:
+        raise KdError(2, "make_problem", "H, W, idx and the teacher logits must be 2-D")
     N, d = H.shape
     V, d2 = W.shape
     if d2 != d or tuple(idx.shape) != tuple(tlog.shape) or idx.shape[0] != N:
@@ -96,6 +98,30 @@ def _workspace(nbytes: int, dev) -> torch.Tensor:
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
 
 
+def _take_workspace(workspace, nbytes: int, dev, where: str):
+    """(tensor, size in bytes): the caller's workspace after checks, or a new one. A caller who
+    passes one means to avoid an allocation, so one that is too small is an error, not a cue to
+    allocate."""
+    if workspace is None:
+        ws = _workspace(nbytes, dev)
+        return ws, ws.numel()
+    _need_device(workspace)
+    if workspace.device != dev:
+        raise KdError(1, where, "the workspace must be on the inputs' GPU")
+    size = workspace.numel() * workspace.element_size()
+    if size < nbytes:
+        raise KdError(5, where, f"workspace holds {size} bytes, the call needs {nbytes}")
+    return workspace, size
+
+
+def _check_dw(dW, W, dev, where: str):
+    if dW.dtype != torch.float32 or tuple(dW.shape) != tuple(W.shape):
+        raise KdError(3, where, "dW must be float32 with W's shape")
+    _need_device(dW)
+    if dW.device != dev:
+        raise KdError(1, where, "dW must be on the inputs' GPU")
+
+
 @dataclass
 class FwdOut:
     loss: torch.Tensor    # [] fp32
@@ -114,10 +140,9 @@ def fused_kl_fwd(H, W, idx, tlog, T: float = 1.0, chunk: int = 2048, n_norm: flo
     lse = torch.empty(p.N, dtype=torch.float32, device=dev)
     row_kl = torch.empty(p.N, dtype=torch.float32, device=dev) if want_row_kl else None
     zk = torch.empty((p.N, p.K), dtype=torch.float32, device=dev) if want_zk else None
-    nb = fused_workspace_bytes(p)
-    ws = workspace if workspace is not None and workspace.numel() >= nb else _workspace(nb, dev)
+    ws, ws_bytes = _take_workspace(workspace, fused_workspace_bytes(p), dev, "fused_kl_fwd")
     code = _lib.lib().kd_fused_kl_fwd(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlog), _ptr(loss),
-                                      _ptr(lse), _ptr(row_kl), _ptr(zk), _ptr(ws), ws.numel(), _stream(dev))
+                                      _ptr(lse), _ptr(row_kl), _ptr(zk), _ptr(ws), ws_bytes, _stream(dev))
     _lib.check(code, "kd_fused_kl_fwd")
     return FwdOut(loss, lse, row_kl, zk)
 
@@ -130,6 +155,8 @@ def fused_kl_bwd(H, W, idx, tlog, lse, grad_loss=None, T: float = 1.0, chunk: in
     only dH is computed and dW is returned as None."""
     dev = _need_device(H, W, idx, tlog, lse)
     p = make_problem(H, W, idx, tlog, T, chunk, n_norm, flags)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (p.N,):
+        raise KdError(3, "fused_kl_bwd", "lse must be float32 [N], as the forward returns it")
     dH = torch.empty_like(H)
     if flags & KD_SKIP_DW:
         dW = None
@@ -137,15 +164,14 @@ def fused_kl_bwd(H, W, idx, tlog, lse, grad_loss=None, T: float = 1.0, chunk: in
         if flags & KD_ACCUMULATE_DW:
             raise KdError(1, "fused_kl_bwd", "KD_ACCUMULATE_DW needs a dW tensor")
         dW = torch.empty(W.shape, dtype=torch.float32, device=dev)
-    elif dW.dtype != torch.float32 or tuple(dW.shape) != tuple(W.shape):
-        raise KdError(3, "fused_kl_bwd", "dW must be float32 with W's shape")
+    else:
+        _check_dw(dW, W, dev, "fused_kl_bwd")
     g = None
     if grad_loss is not None:
         g = grad_loss.detach().to(device=dev, dtype=torch.float32).reshape(1).contiguous()
-    nb = fused_workspace_bytes(p)
-    ws = workspace if workspace is not None and workspace.numel() >= nb else _workspace(nb, dev)
+    ws, ws_bytes = _take_workspace(workspace, fused_workspace_bytes(p), dev, "fused_kl_bwd")
     code = _lib.lib().kd_fused_kl_bwd(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlog), _ptr(lse),
-                                      _ptr(g), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream(dev))
+                                      _ptr(g), _ptr(dH), _ptr(dW), _ptr(ws), ws_bytes, _stream(dev))
     _lib.check(code, "kd_fused_kl_bwd")
     return dH, dW
 
@@ -183,16 +209,15 @@ def _one_call(fn_name: str, ws_name: str, H, W, idx, tlog, T, chunk, grad_loss, 
         if flags & KD_ACCUMULATE_DW:
             raise KdError(1, fn_name, "KD_ACCUMULATE_DW needs a dW tensor")
         dW = torch.empty(W.shape, dtype=torch.float32, device=dev)
-    elif dW.dtype != torch.float32 or tuple(dW.shape) != tuple(W.shape):
-        raise KdError(3, fn_name, "dW must be float32 with W's shape")
+    else:
+        _check_dw(dW, W, dev, fn_name)
     g = None
     if grad_loss is not None:
         g = grad_loss.detach().to(device=dev, dtype=torch.float32).reshape(1).contiguous()
     L = _lib.lib()
-    nb = int(getattr(L, ws_name)(ctypes.byref(p)))
-    ws = workspace if workspace is not None and workspace.numel() >= nb else _workspace(nb, dev)
+    ws, ws_bytes = _take_workspace(workspace, int(getattr(L, ws_name)(ctypes.byref(p))), dev, fn_name)
     code = getattr(L, fn_name)(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlog), _ptr(g), _ptr(loss),
-                               _ptr(lse), _ptr(row_kl), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream(dev))
+                               _ptr(lse), _ptr(row_kl), _ptr(dH), _ptr(dW), _ptr(ws), ws_bytes, _stream(dev))
     _lib.check(code, fn_name)
     return loss, lse, row_kl, dH, dW
 

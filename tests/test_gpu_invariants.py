@@ -113,6 +113,44 @@ def test_workspace_too_small_is_rejected():
     assert code == 5
 
 
+def test_binding_rejects_bad_buffers():
+    """The binding checks what the C ABI cannot (device, layout, size of caller tensors) and
+    raises before anything is enqueued."""
+    p = datagen.make("tiny")
+    H, W, idx, t = device_inputs(p)
+    f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=64)
+    prob = kd.make_problem(H, W, idx, t, p.T, 64)
+    need = kd.fused_workspace_bytes(prob)
+    bad = {
+        "dW on the host": dict(dW=torch.empty(W.shape, dtype=torch.float32)),
+        "dW not contiguous": dict(dW=torch.empty((W.shape[1], W.shape[0]), dtype=torch.float32,
+                                                  device="cuda").t()),
+        "dW of another dtype": dict(dW=torch.empty(W.shape, dtype=torch.bfloat16, device="cuda")),
+        "workspace on the host": dict(workspace=torch.empty(need, dtype=torch.uint8)),
+        "workspace too small": dict(workspace=torch.empty(need - 256, dtype=torch.uint8, device="cuda")),
+    }
+    for label, kw in bad.items():
+        with pytest.raises(kd.KdError):
+            kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=64, **kw)
+        say("  rejected:", label)
+    with pytest.raises(kd.KdError):
+        kd.fused_kl_bwd(H, W, idx, t, f.lse[:-1], T=p.T, chunk=64)
+    with pytest.raises(kd.KdError):
+        kd.fused_kl_bwd(H, W, idx, t, f.lse.double(), T=p.T, chunk=64)
+    with pytest.raises(kd.KdError):
+        kd.chunked_kl(H, W, idx, t, T=p.T, chunk=64, dW=torch.empty(W.shape, dtype=torch.float32))
+    with pytest.raises(kd.KdError):
+        kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=64, workspace=torch.empty(16, device="cuda"))
+    with pytest.raises(kd.KdError):
+        kd.fused_kl_fwd(H[None], W, idx, t, T=p.T, chunk=64)
+    # a workspace of another element type counts in bytes
+    ws = torch.empty((need + 3) // 4, dtype=torch.float32, device="cuda")
+    dH, dW = kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=64, workspace=ws)
+    dH0, dW0 = kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=64)
+    torch.cuda.synchronize()
+    assert torch.equal(dH, dH0) and torch.equal(dW, dW0)
+
+
 @pytest.mark.parametrize("T", [1.0, 2.0])
 def test_k1_matches_torch_cross_entropy(T):
     """One cached entry per row: the loss is T^2 times cross entropy of z/T at that id."""
