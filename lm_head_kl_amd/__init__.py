@@ -254,10 +254,12 @@ def topk_cache(logits: torch.Tensor, K: int):
         raise KdError(3, "topk_cache", "logits must be bfloat16 or float32")
     if logits.dim() != 2 or logits.stride(1) != 1:
         raise KdError(2, "topk_cache", "logits must be [N, V] with contiguous rows")
+    N, V = logits.shape
+    if not 1 <= int(K) <= min(V, 1024):
+        raise KdError(2, "topk_cache", f"K = {K} outside 1 .. min(V, 1024) = {min(V, 1024)}")
     if logits.device.type != "cuda":
         raise KdError(1, "topk_cache", "logits must be on a GPU")
     dev = logits.device
-    N, V = logits.shape
     idx = torch.empty((N, K), dtype=torch.int32, device=dev)
     vals = torch.empty((N, K), dtype=logits.dtype, device=dev)
     code = _lib.lib().kd_topk_cache(_ptr(logits), _DT[logits.dtype], N, V, logits.stride(0), int(K), _ptr(idx),

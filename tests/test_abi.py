@@ -210,3 +210,15 @@ def test_skip_dw_flag_rules():
         nb = max(1, getattr(L, query)(ctypes.byref(p)))
         assert getattr(L, fn)(ctypes.byref(p), F, F, F, F, None, F, F, None, F, F, F, nb, None) == 4
     assert bwd(prob(), dW=None) == 1
+
+
+@pytest.mark.parametrize("K", [0, -3, 11, 2000])
+def test_topk_binding_checks_k(K):
+    """The binding rejects K outside 1 .. min(V, 1024) before it allocates or calls anything."""
+    import torch
+
+    import lm_head_kl_amd as kd
+
+    with pytest.raises(kd.KdError) as e:
+        kd.topk_cache(torch.zeros((4, 10)), K)
+    assert e.value.code == 2
