@@ -108,7 +108,9 @@ typedef enum kd_dtype {
  *   chunk        rows per backward chunk (>= 1; N need not be a multiple). It bounds the
  *                backward's per-chunk gradient tile G_c [chunk, V] in the workspace. The
  *                forward keeps each projected tile in registers only, so its memory does not
- *                depend on chunk.
+ *                depend on chunk. Values above 1048576 (2^20) are taken as 2^20, which keeps
+ *                the chunk-strided operands of the dW product within 32-bit buffer offsets;
+ *                the chunk changes memory use and summation order only, never the result.
  *   T            temperature, finite and > 0.
  *   n_norm       denominator of the mean; <= 0 means N. Set it to the global row count when
  *                one batch is split over several calls.
@@ -171,7 +173,7 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
                           float* dW, void* ws, size_t ws_bytes, kd_stream stream);
 
 /* Workspace bytes for kd_dense_kl: two fp32 [N, V] grids (rounded up to whole tiles) plus a
- * small remainder. Returns 0 if p is NULL or invalid. */
+ * small remainder. Returns 0 if p is NULL or invalid, or V exceeds the dense limit below. */
 size_t kd_dense_workspace_bytes(const kd_problem* p);
 
 /*
@@ -180,6 +182,8 @@ size_t kd_dense_workspace_bytes(const kd_problem* p);
  * full [N, V] student log-probability grid, so two vocabulary-by-sequence grids are resident
  * at once. Source: aiexpert.news article, paragraph on the three formulations (dense KL).
  *   Arguments as in the two fused calls; row_kl may be NULL. Same results up to rounding.
+ *   Limit: V <= 2097152 (2^21), so that a tile's 256 rows of the logit grid stay within
+ *   32-bit buffer offsets; KD_ERR_SHAPE above it (the fused calls take V up to 4194304).
  */
 kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const int32_t* idx,
                       const void* tlog, const float* grad_loss, float* loss, float* lse,

@@ -82,7 +82,14 @@ Shape make_shape(const kd_problem* p) {
     return s;
 }
 
-int64_t chunk_rows(const kd_problem* p) { return std::min(p->chunk, p->N); }
+// Rows per chunk: the caller's chunk, at most N and at most 2^20. G_c^T and H_c^T have a row
+// stride of max(8192, chunk) elements and the dW product reads 320 of their rows per tile
+// through 32-bit buffer offsets: 320 * 2^20 * 4 bytes stays below the descriptor range.
+constexpr int64_t kMaxChunk = (int64_t)1 << 20;
+int64_t chunk_rows(const kd_problem* p) { return std::min({p->chunk, p->N, kMaxChunk}); }
+// The dense grids have a row stride of 4 * Vp bytes (fp32 Z, or bf16 G at twice the element
+// stride), and a 256-row tile of them is read through 32-bit buffer offsets.
+constexpr int64_t kMaxDenseV = (int64_t)1 << 21;
 bool whole_plan(const kd_problem* p) { return chunk_rows(p) % kTileM == 0; }
 
 // Workspace of the fused calls. The forward and backward parts are disjoint in time, so they
@@ -301,7 +308,7 @@ size_t kd_fused_workspace_bytes(const kd_problem* p) {
 }
 
 size_t kd_dense_workspace_bytes(const kd_problem* p) {
-    if (check_problem(p) != KD_OK) return 0;
+    if (check_problem(p) != KD_OK || p->V > kMaxDenseV) return 0;
     return layout_dense(p, nullptr).bytes;
 }
 
@@ -389,6 +396,7 @@ kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const i
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
     if (p->flags & KD_SKIP_DW) return KD_ERR_VALUE;  // only the fused backward can leave dW out
+    if (p->V > kMaxDenseV) return KD_ERR_SHAPE;
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_dense_workspace_bytes(p)) return KD_ERR_WORKSPACE;

@@ -222,3 +222,26 @@ def test_topk_binding_checks_k(K):
     with pytest.raises(kd.KdError) as e:
         kd.topk_cache(torch.zeros((4, 10)), K)
     assert e.value.code == 2
+
+
+def test_chunk_is_capped_at_2_20_rows():
+    """Chunks longer than 2^20 rows are taken as 2^20 (the dW product's chunk-strided operands
+    stay within 32-bit buffer offsets): the workspace stops growing there."""
+    big = dict(N=1 << 22, d=8, V=256, K=1)
+    a = ws_bytes(chunk=1 << 20, **big)
+    assert a > 0
+    assert ws_bytes(chunk=(1 << 20) + 1, **big) == a
+    assert ws_bytes(chunk=1 << 22, **big) == a
+    assert ws_bytes(chunk=(1 << 20) - 8, **big) < a
+
+
+@nogpu
+def test_dense_vocabulary_limit():
+    """The dense path reads 256-row tiles of grids whose rows are 4 * Vp bytes through 32-bit
+    buffer offsets, so it stops at V = 2^21; the fused calls take the full range."""
+    L = _lib.lib()
+    ok, over = prob(N=8, d=8, V=1 << 21, K=4), prob(N=8, d=8, V=(1 << 21) + 1, K=4)
+    assert L.kd_dense_workspace_bytes(ctypes.byref(ok)) > 0
+    assert L.kd_dense_workspace_bytes(ctypes.byref(over)) == 0
+    assert dense(over) == 2
+    assert ws_bytes(N=8, d=8, V=(1 << 21) + 1, K=4) > 0
