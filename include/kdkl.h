@@ -95,7 +95,8 @@ typedef enum kd_dtype {
 } kd_dtype;
 
 /* flags */
-#define KD_VALIDATE_IDX  0x1u /* check idx on the device first; this syncs the stream once */
+#define KD_VALIDATE_IDX  0x1u /* check idx on the device first; this syncs the stream once
+                                 (kd_validate_ids is the same check without the sync) */
 #define KD_ACCUMULATE_DW 0x2u /* kd_fused_kl_bwd / kd_dense_kl add into dW instead of overwriting */
 #define KD_SKIP_DW       0x4u /* kd_fused_kl_bwd computes dH only (dW may be NULL): for a frozen head.
                                  Ignored by kd_fused_kl_fwd; KD_ERR_VALUE for the other calls and
@@ -240,6 +241,24 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
  */
 kd_status kd_topk_cache(const void* logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, int64_t K,
                         int32_t* idx, void* values, kd_stream stream);
+
+/*
+ * Check of a cached id table that does not synchronise: the test KD_VALIDATE_IDX runs, as two
+ * kernel launches on `stream` with the verdict left in device memory. Every row of the cache
+ * holds K distinct token ids of the vocabulary, the most probable tokens of one position
+ * (aiexpert.news "Making knowledge distillation cheap enough to run in production", paragraph
+ * on the first fix); this checks exactly that.
+ *   idx [N][K]   device int32, read
+ *   status       device, one uint32 owned by the caller: cleared by a kernel, then bit 0x1 is
+ *                set if some id lies outside [0, V) and bit 0x2 if some row repeats an id.
+ *   limits: 1 <= N < 2^31, 1 <= K <= 1024, V >= 1. KD_ERR_NULL if idx or status is NULL.
+ * Nothing is copied to the host or waited for, so the call can be captured into a HIP graph
+ * next to the loss calls; the caller reads *status once the stream has passed it. The loss
+ * calls skip ids outside [0, V) without dereferencing them, and a repeated id gives wrong
+ * values for its row but no fault, so a step may run before its verdict is read.
+ */
+kd_status kd_validate_ids(const int32_t* idx, int64_t N, int64_t K, int64_t V, uint32_t* status,
+                          kd_stream stream);
 
 /*
  * Per-kernel timing (profiling; off by default). While enabled, every kernel the library

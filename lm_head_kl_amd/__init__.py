@@ -30,6 +30,7 @@ __all__ = [
     "chunked_kl",
     "fused_kl_fwdbwd",
     "topk_cache",
+    "validate_ids",
     "fused_workspace_bytes",
     "dense_workspace_bytes",
     "chunked_workspace_bytes",
@@ -266,6 +267,23 @@ def topk_cache(logits: torch.Tensor, K: int):
                                     _ptr(vals), _stream(dev))
     _lib.check(code, "kd_topk_cache")
     return idx, vals
+
+
+def validate_ids(idx: torch.Tensor, V: int, status: torch.Tensor | None = None) -> torch.Tensor:
+    """kd_validate_ids: checks the cached ids without synchronising. Returns the device status
+    word (uint32 viewed as int32, one element): 0 if every row holds K distinct ids in [0, V),
+    else bit 1 (an id out of range) and/or bit 2 (a repeated id). Pass `status` to reuse one
+    word, e.g. inside a captured graph."""
+    if idx.dtype != torch.int32 or idx.dim() != 2:
+        raise KdError(3, "validate_ids", "idx must be int32 [N, K]")
+    dev = _need_device(idx)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    elif status.dtype != torch.int32 or status.numel() < 1 or status.device != dev or not status.is_contiguous():
+        raise KdError(3, "validate_ids", "status must be a contiguous int32 tensor on idx's GPU")
+    code = _lib.lib().kd_validate_ids(_ptr(idx), idx.shape[0], idx.shape[1], int(V), _ptr(status), _stream(dev))
+    _lib.check(code, "kd_validate_ids")
+    return status
 
 
 class FusedKL(torch.autograd.Function):

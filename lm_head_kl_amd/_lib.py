@@ -41,6 +41,7 @@ EXPORTS = (
     "kd_fused_fwdbwd_workspace_bytes",
     "kd_fused_kl_fwdbwd",
     "kd_topk_cache",
+    "kd_validate_ids",
     "kd_timing_enable",
     "kd_timing_kinds",
     "kd_timing_name",
@@ -107,6 +108,8 @@ def lib() -> ctypes.CDLL:
     i64 = ctypes.c_int64
     L.kd_topk_cache.restype = ctypes.c_int
     L.kd_topk_cache.argtypes = [vp, ctypes.c_int32, i64, i64, i64, i64, vp, vp, vp]
+    L.kd_validate_ids.restype = ctypes.c_int
+    L.kd_validate_ids.argtypes = [vp, i64, i64, i64, vp, vp]
     L.kd_timing_enable.restype = ctypes.c_int
     L.kd_timing_enable.argtypes = [ctypes.c_int]
     L.kd_timing_kinds.restype = ctypes.c_int

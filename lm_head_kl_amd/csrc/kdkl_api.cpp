@@ -421,6 +421,15 @@ kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const i
     return KD_OK;
 }
 
+kd_status kd_validate_ids(const int32_t* idx, int64_t N, int64_t K, int64_t V, uint32_t* status,
+                          kd_stream stream) {
+    if (!idx || !status) return KD_ERR_NULL;
+    if (N < 1 || N > 0x7FFFFFFF || K < 1 || K > kMaxK || V < 1) return KD_ERR_SHAPE;
+    (void)hipGetLastError();
+    KD_TRY(launch_validate(idx, N, K, V, status, (hipStream_t)stream));
+    return KD_OK;
+}
+
 kd_status kd_topk_cache(const void* logits, int32_t dtype, int64_t N, int64_t V, int64_t ld, int64_t K,
                         int32_t* idx, void* values, kd_stream stream) {
     if (!logits || !idx || !values) return KD_ERR_NULL;

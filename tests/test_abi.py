@@ -245,3 +245,14 @@ def test_dense_vocabulary_limit():
     assert L.kd_dense_workspace_bytes(ctypes.byref(over)) == 0
     assert dense(over) == 2
     assert ws_bytes(N=8, d=8, V=(1 << 21) + 1, K=4) > 0
+
+
+@nogpu
+@pytest.mark.parametrize("args,code", [
+    (dict(idx=None), 1), (dict(status=None), 1),
+    (dict(N=0), 2), (dict(K=0), 2), (dict(K=1025), 2), (dict(V=0), 2), (dict(N=1 << 31), 2),
+])
+def test_validate_ids_bad_arguments(args, code):
+    a = dict(idx=F, N=4, K=10, V=100, status=F)
+    a.update(args)
+    assert _lib.lib().kd_validate_ids(a["idx"], a["N"], a["K"], a["V"], a["status"], None) == code

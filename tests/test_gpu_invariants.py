@@ -257,3 +257,47 @@ def test_skip_dw_frozen_head():
     torch.cuda.synchronize()
     assert torch.equal(Hg.grad.view(torch.int16), dH_full.view(torch.int16))
     assert W.grad is None
+
+
+def test_validate_ids_without_sync():
+    """kd_validate_ids leaves its verdict in a device word: 0 for a sound cache, bit 1 for an id
+    out of range, bit 2 for a repeated id. It enqueues only kernels, so it can sit in a captured
+    graph in front of the loss; each replay clears the word and checks the ids as they are then."""
+    p = datagen.make("tiny")
+    say("kd_validate_ids")
+    H, W, idx, t = device_inputs(p)
+    assert int(kd.validate_ids(idx, p.V).item()) == 0
+    dup = idx.clone()
+    dup[5, 3] = dup[5, 0]
+    oob = idx.clone()
+    oob[7, 1] = p.V
+    both = dup.clone()
+    both[9, 2] = -1
+    assert int(kd.validate_ids(dup, p.V).item()) == 2
+    assert int(kd.validate_ids(oob, p.V).item()) == 1
+    assert int(kd.validate_ids(both, p.V).item()) == 3
+    # in a graph with the forward
+    st = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(kd.fused_workspace_bytes(kd.make_problem(H, W, idx, t, p.T, 64)), dtype=torch.uint8,
+                     device="cuda")
+    work = idx.clone()
+    eager = kd.fused_kl_fwd(H, W, work, t, T=p.T, chunk=64, workspace=ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        kd.validate_ids(work, p.V, st)
+        kd.fused_kl_fwd(H, W, work, t, T=p.T, chunk=64, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        kd.validate_ids(work, p.V, st)
+        f = kd.fused_kl_fwd(H, W, work, t, T=p.T, chunk=64, workspace=ws)
+    for ids, want in ((idx, 0), (both, 3), (dup, 2), (idx, 0)):
+        work.copy_(ids)
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(st.item()) == want
+        if want == 0:
+            assert torch.equal(f.lse, eager.lse) and torch.equal(f.loss, eager.loss)
