@@ -166,3 +166,46 @@ def test_timing_from_two_threads():
     assert k["fwd"][0] == 6
     assert k["bwd_grad"][0] == 3 * (4 + 2) and k["dh"][0] == 3 * (4 + 2)
     assert k["dw"][0] == 6
+
+
+@pytest.mark.parametrize("path", ["chunked", "fwdbwd", "topk"])
+def test_other_calls_capture_and_replay(path):
+    """The forward-chunked and single-pass calls and the top-K producer enqueue kernels only as
+    well: captured into a graph, each of three replays (with eager library calls between them)
+    gives the eager result bit for bit."""
+    say("graph capture", path)
+    p = datagen.make("small", N=1024, seed=21)
+    H, W, idx, t = device_inputs(p)
+    if path == "topk":
+        logits = (H[:256].float() @ W.float().t()).to(torch.bfloat16).contiguous()
+
+        def call():
+            return list(kd.topk_cache(logits, 100))
+    else:
+        fn = kd.chunked_kl if path == "chunked" else kd.fused_kl_fwdbwd
+        prob = kd.make_problem(H, W, idx, t, p.T, CHUNK)
+        nb = (kd.chunked_workspace_bytes if path == "chunked" else kd.fused_fwdbwd_workspace_bytes)(prob)
+        ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        dW = torch.empty(W.shape, dtype=torch.float32, device="cuda")
+
+        def call():
+            return list(fn(H, W, idx, t, T=p.T, chunk=CHUNK, dW=dW, workspace=ws))
+    eager = snapshot(call())
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        static_out = call()
+    other = Step(datagen.make("small", N=512, seed=5))
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for x, y in zip(static_out, eager):
+            assert same(x, y), f"{path} replay {rep}"
+        other()
+        torch.cuda.synchronize()
