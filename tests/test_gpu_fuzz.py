@@ -1,8 +1,9 @@
 """Seeded random problems: sizes, dtype, temperature, teacher recipe, id recipe, chunk,
-normaliser and upstream weight are drawn per case, and each formulation is compared in full
-with the fp64 oracle at the stated tolerances. The fixed edge list elsewhere names the
-boundaries one at a time; here they are combined the way a caller might combine them
-(a ragged chunk with K near its maximum, d just past a hidden tile, V below one vocab tile).
+normaliser and upstream weight are drawn per case, and each of the four formulations is
+compared in full with the fp64 oracle at the stated tolerances. The fixed edge list
+elsewhere names the boundaries one at a time; here they are combined the way a caller might
+combine them (a ragged chunk with K near its maximum, d just past a hidden tile, V below one
+vocab tile).
 
 The draws are fixed by the case number, so a failing case is reproduced by its id."""
 
@@ -98,11 +99,14 @@ def test_fuzz_case(i):
     torch.cuda.synchronize()
     assert rel_l2(host(dW_acc), 2.0 * host(dW)) <= 1e-6, "accumulated dW is not twice the overwritten one"
 
-    # the two other formulations
+    # the other three formulations
     for name, fn in (("chunked", kd.chunked_kl), ("fwdbwd", kd.fused_kl_fwdbwd)):
         loss, lse, row_kl, dHx, dWx = fn(H, W, idx, t, T=p.T, chunk=c["chunk"], grad_loss=gt, n_norm=c["n_norm"])
         torch.cuda.synchronize()
         check(name, c, ref, loss, lse, row_kl, dHx, dWx)
+    loss, lse, row_kl, dHx, dWx = kd.dense_kl(H, W, idx, t, T=p.T, grad_loss=gt, n_norm=c["n_norm"])
+    torch.cuda.synchronize()
+    check("dense", c, ref, loss, lse, row_kl, dHx, dWx)
 
 
 def test_fuzz_draws_cover_the_boundaries():
