@@ -71,7 +71,9 @@
 extern "C" {
 #endif
 
-#define KDKL_ABI_VERSION 1
+/* 1: first release. 2: kd_validate_ids added; chunks capped at 2^20 rows; kd_dense_kl limited
+ * to V <= 2^21. Calls and structures of version 1 are unchanged. */
+#define KDKL_ABI_VERSION 2
 
 /* Same type as hipStream_t; declared here so that this header does not need the HIP headers. */
 typedef struct ihipStream_t* kd_stream;
