@@ -246,7 +246,7 @@ kd_status kd_topk_cache(const void* logits, int32_t dtype, int64_t N, int64_t V,
 
 /*
  * Check of a cached id table that does not synchronise: the test KD_VALIDATE_IDX runs, as two
- * kernel launches on `stream` with the verdict left in device memory. Every row of the cache
+ * kernel launches on `stream` with the result left in device memory. Every row of the cache
  * holds K distinct token ids of the vocabulary, the most probable tokens of one position
  * (aiexpert.news "Making knowledge distillation cheap enough to run in production", paragraph
  * on the first fix); this checks exactly that.
@@ -257,7 +257,7 @@ kd_status kd_topk_cache(const void* logits, int32_t dtype, int64_t N, int64_t V,
  * Nothing is copied to the host or waited for, so the call can be captured into a HIP graph
  * next to the loss calls; the caller reads *status once the stream has passed it. The loss
  * calls skip ids outside [0, V) without dereferencing them, and a repeated id gives wrong
- * values for its row but no fault, so a step may run before its verdict is read.
+ * values for its row but no fault, so a step may run before its result is read.
  */
 kd_status kd_validate_ids(const int32_t* idx, int64_t N, int64_t K, int64_t V, uint32_t* status,
                           kd_stream stream);

@@ -260,7 +260,7 @@ def test_skip_dw_frozen_head():
 
 
 def test_validate_ids_without_sync():
-    """kd_validate_ids leaves its verdict in a device word: 0 for a sound cache, bit 1 for an id
+    """kd_validate_ids leaves its result in a device word: 0 for a sound cache, bit 1 for an id
     out of range, bit 2 for a repeated id. It enqueues only kernels, so it can sit in a captured
     graph in front of the loss; each replay clears the word and checks the ids as they are then."""
     p = datagen.make("tiny")
