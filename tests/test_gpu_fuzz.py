@@ -72,11 +72,16 @@ def test_fuzz_case(i):
     ref = oracle.kl_chunked(p.f64("H"), p.f64("W"), p.idx, p.f64("tlog"), p.T, chunk=256, n_norm=nn, g=c["grad"])
     gt = torch.tensor(c["grad"], dtype=torch.float32, device=H.device)
 
+    # the cache is sound: both forms of the id check pass it
+    assert int(kd.validate_ids(idx, p.V).item()) == 0
+    fv = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=c["chunk"], n_norm=c["n_norm"], flags=kd.KD_VALIDATE_IDX)
+
     # fused pair
     f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=c["chunk"], n_norm=c["n_norm"], want_zk=True)
     dH, dW = kd.fused_kl_bwd(H, W, idx, t, f.lse, grad_loss=gt, T=p.T, chunk=c["chunk"], n_norm=c["n_norm"])
     torch.cuda.synchronize()
     check("fused", c, ref, f.loss, f.lse, f.row_kl, dH, dW, zk=f.zk)
+    assert torch.equal(fv.lse, f.lse) and torch.equal(fv.loss, f.loss)
 
     # a second call gives the same bits (nothing depends on the plan's atomic fill order or on
     # which workgroup takes which tile)
