@@ -33,6 +33,10 @@ The pages leave the following open. The readings taken:
 (3) Mean over all N rows, with denominator n_norm (default N).
 (4) The student is normalised over all V, not over the K cached ids.
 (5) Cached ids are distinct and in [0, V).
+(6) A cached teacher logit may be -inf (a masked entry). Its probability is 0 and it adds
+    nothing to the KL sum (0 log 0 = 0, as in the dense formulation's full-vocabulary sum).
+    Every row needs at least one finite cached logit; +inf and NaN logits are outside the
+    domain.
 
 Notation: H [N,d] hidden states, W [V,d] LM-head weight, z = H W^T logits, u = z/T,
 lse_n = logsumexp_v u_nv, t [N,K] cached teacher logits with ids idx [N,K],
@@ -63,6 +67,7 @@ __all__ = [
     "kl_fused",
     "kl_rows",
     "lse_all_rows",
+    "kl_rows_all",
     "dw_rows",
     "topk_cache",
 ]
@@ -88,6 +93,15 @@ def teacher_logp(tlog, T: float) -> np.ndarray:
     return a - (m + np.log(np.exp(a - m).sum(axis=1, keepdims=True)))
 
 
+def _kl_terms(pt, lpt, zk, T: float, lse) -> np.ndarray:
+    """Per-row sum over the cached entries of p_t (log p_t - (z_k/T - lse)), where entries
+    with p_t = 0 (teacher logit -inf) add nothing: the 0 log 0 = 0 convention of the
+    full-vocabulary KL sum."""
+    with np.errstate(invalid="ignore"):
+        t = pt * (lpt - (zk / T - np.asarray(lse)[:, None]))
+    return np.where(pt > 0, t, 0.0).sum(axis=1)
+
+
 def logsumexp_rows(u) -> np.ndarray:
     """lse_n = log sum_v exp(u_nv), shifted by the row max for range."""
     u = _f64(u)
@@ -106,7 +120,7 @@ def kl_from_logits(z, idx, tlog, T: float):
     zk = np.take_along_axis(z, np.asarray(idx, np.int64), axis=1)
     lpt = teacher_logp(tlog, T)
     pt = np.exp(lpt)
-    row_kl = (pt * (lpt - (zk / T - lse[:, None]))).sum(axis=1)
+    row_kl = _kl_terms(pt, lpt, zk, T, lse)
     return row_kl, lse, zk
 
 
@@ -163,7 +177,7 @@ def kl_chunked(H, W, idx, tlog, T: float, chunk: int, n_norm=None, g: float = 1.
         kept.append(z)
         lse[r0:r1] = logsumexp_rows(z / T)
         zk[r0:r1] = np.take_along_axis(z, idx[r0:r1], axis=1)
-        row_kl[r0:r1] = (pt[r0:r1] * (lpt[r0:r1] - (zk[r0:r1] / T - lse[r0:r1, None]))).sum(axis=1)
+        row_kl[r0:r1] = _kl_terms(pt[r0:r1], lpt[r0:r1], zk[r0:r1], T, lse[r0:r1])
     for c, r0 in enumerate(range(0, N, chunk)):
         r1 = min(N, r0 + chunk)
         z = kept[c]
@@ -210,7 +224,7 @@ def kl_fused(H, W, idx, tlog, T: float, chunk: int, vtile: int, n_norm=None,
             rr, kk = np.nonzero(hit)
             zk[r0 + rr, kk] = z[rr, ic[rr, kk] - v0]
         lse[r0:r1] = m + np.log(s)
-        row_kl[r0:r1] = (pt[r0:r1] * (lpt[r0:r1] - (zk[r0:r1] / T - lse[r0:r1, None]))).sum(axis=1)
+        row_kl[r0:r1] = _kl_terms(pt[r0:r1], lpt[r0:r1], zk[r0:r1], T, lse[r0:r1])
     for r0 in range(0, N, chunk):
         r1 = min(N, r0 + chunk)
         Hc, ic = H[r0:r1], idx[r0:r1]
@@ -245,7 +259,7 @@ def kl_rows(H, W, idx, tlog, T: float, rows, n_norm, g: float = 1.0, *, H_rows=N
     lpt = teacher_logp(tr, T)
     pt = np.exp(lpt)
     zk = np.take_along_axis(z, ir, axis=1)
-    row_kl = (pt * (lpt - (zk / T - lse[:, None]))).sum(axis=1)
+    row_kl = _kl_terms(pt, lpt, zk, T, lse)
     gs = g * T / float(n_norm)
     G = np.exp(u - lse[:, None])
     r = np.arange(len(rows))[:, None]
@@ -264,6 +278,29 @@ def lse_all_rows(H, W, T: float, block: int = 512) -> np.ndarray:
     for r0 in range(0, H.shape[0], block):
         out[r0:r0 + block] = logsumexp_rows((_f64(H[r0:r0 + block]) @ W.T) / T)
     return out
+
+
+def kl_rows_all(H, W, idx, tlog, T: float, block: int = 512) -> dict:
+    """lse_n and KL_n for every row of a large batch. Each row's values are the definition
+    applied to that row alone, as in ``kl_rows`` (the row's logits over all V, its teacher
+    softmax over the K cached entries); rows are taken ``block`` at a time only to bound the
+    logit slab held in memory. Returns dict(lse [N], row_kl [N])."""
+    W = _f64(W)
+    H = np.asarray(H)
+    idx = np.asarray(idx, np.int64)
+    tlog = np.asarray(tlog)
+    N = H.shape[0]
+    _check(idx, W.shape[0])
+    lse = np.empty(N)
+    row_kl = np.empty(N)
+    for r0 in range(0, N, block):
+        r1 = min(N, r0 + block)
+        z = _f64(H[r0:r1]) @ W.T
+        lse[r0:r1] = logsumexp_rows(z / T)
+        lpt = teacher_logp(tlog[r0:r1], T)
+        zk = np.take_along_axis(z, idx[r0:r1], axis=1)
+        row_kl[r0:r1] = _kl_terms(np.exp(lpt), lpt, zk, T, lse[r0:r1])
+    return dict(lse=lse, row_kl=row_kl)
 
 
 def dw_rows(H, W, idx, tlog, T: float, vocab, lse, n_norm, g: float = 1.0) -> np.ndarray:

@@ -88,10 +88,59 @@ def test_brute_force(N, d, V, K, T, g, seed):
     # the per-row lse of a whole batch (any row block) and the vocab rows of dW from it
     for block in (1, 3, N):
         np.testing.assert_allclose(oracle.lse_all_rows(H, W, T, block=block), ref["lse"], rtol=1e-12, atol=1e-13)
+        every = oracle.kl_rows_all(H, W, idx, t, T, block=block)
+        np.testing.assert_allclose(every["lse"], ref["lse"], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(every["row_kl"], ref["row_kl"], rtol=1e-12, atol=1e-14)
     vocab = [V - 1, 0, 2] + sorted({int(i) for i in idx[0]})[:2]
     vocab = sorted(set(vocab))
     dw = oracle.dw_rows(H, W, idx, t, T, vocab, ref["lse"], n_norm=N, g=g)
     np.testing.assert_allclose(dw, ref["dW"][vocab], rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("T", [1.0, 1.9])
+def test_brute_force_masked_teacher_entries(T):
+    """Cached teacher logits of -inf (masked entries, one or all but one per row): such an
+    entry has p_t = 0 and adds nothing to the KL (the brute force's full-vocabulary sum skips
+    p = 0), and the gradient does not subtract at it. Every formulation must stay finite and
+    match the brute force."""
+    N, d, V, K = 4, 5, 9, 4
+    H, W, idx, t = rand_problem(N, d, V, K, 7)
+    t[0, 1] = -np.inf
+    t[1, [0, 2, 3]] = -np.inf        # one finite entry left
+    t[3, 3] = -np.inf
+    ref = brute(H.tolist(), W.tolist(), idx.tolist(), t.tolist(), T, N, 1.3)
+    assert np.all(np.isfinite(ref["row_kl"]))
+    outs = [oracle.kl_dense(H, W, idx, t, T, g=1.3),
+            oracle.kl_chunked(H, W, idx, t, T, chunk=3, g=1.3),
+            oracle.kl_fused(H, W, idx, t, T, chunk=2, vtile=4, g=1.3)]
+    for out in outs:
+        assert abs(out["loss"] - ref["loss"]) <= 1e-13 * max(1.0, abs(ref["loss"]))
+        for key in ("row_kl", "lse", "dH", "dW"):
+            np.testing.assert_allclose(out[key], ref[key], rtol=1e-12, atol=1e-13, err_msg=key)
+    rk = oracle.kl_rows(H, W, idx, t, T, rows=[1, 0, 3], n_norm=N, g=1.3)
+    np.testing.assert_allclose(rk["row_kl"], ref["row_kl"][[1, 0, 3]], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(rk["dH"], ref["dH"][[1, 0, 3]], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(oracle.kl_rows_all(H, W, idx, t, T, block=3)["row_kl"], ref["row_kl"],
+                               rtol=1e-12, atol=1e-14)
+    row_kl, lse, zk = oracle.kl_from_logits(H @ W.T, idx, t, T)
+    np.testing.assert_allclose(row_kl, ref["row_kl"], rtol=1e-12, atol=1e-14)
+    # a row whose only finite entry is id k: KL_n = -log p_s(k) = lse - z_k/T
+    np.testing.assert_allclose(ref["row_kl"][1], ref["lse"][1] - ref["zk"][1][1] / T, rtol=1e-12)
+
+
+@pytest.mark.parametrize("T", [1.0, 0.6, 2.5])
+def test_kl_from_logits_matches_dense(T):
+    """kl_from_logits on the logits z = H W^T gives the dense formulation's per-row KL, lse and
+    gathered logits: a dropped teacher weight, a missing temperature or a wrong sign in it
+    would break the equality on these non-degenerate rows."""
+    N, d, V, K = 9, 6, 37, 5
+    H, W, idx, t = rand_problem(N, d, V, K, 130, scale=1.5, tscale=2.0)
+    ref = oracle.kl_dense(H, W, idx, t, T)
+    row_kl, lse, zk = oracle.kl_from_logits(H @ W.T, idx, t, T)
+    np.testing.assert_allclose(row_kl, ref["row_kl"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, ref["lse"], rtol=1e-13)
+    np.testing.assert_allclose(zk, ref["zk"], rtol=1e-13, atol=1e-15)
+    assert np.all(row_kl > 1e-3)  # far from the exact-zero case
 
 
 # ---------------------------------------------------------- finite differences
@@ -292,6 +341,12 @@ def test_rejects_bad_ids():
         oracle.kl_fused(H, W, bad, t, 1.0, chunk=2, vtile=3)
 
 
+def _rank_key(x, v):
+    """Explicit order of the cache: larger values first, NaN below every number (even -inf),
+    equal values (NaN among NaN, -0 with +0) by the lower id."""
+    return (1, 0.0, v) if math.isnan(x) else (0, -x, v)
+
+
 def test_topk_cache_matches_sort():
     """The cache producer's oracle against a plain per-row sort, ties by lower id."""
     g = np.random.default_rng(120)
@@ -301,6 +356,36 @@ def test_topk_cache_matches_sort():
         pairs = sorted(range(50), key=lambda v: (-x[n, v], v))[:7]
         assert list(idx[n]) == pairs
         np.testing.assert_array_equal(vals[n], x[n, pairs])
+
+
+@pytest.mark.parametrize("K", [1, 5, 12, 30])
+def test_topk_cache_nan_and_signed_values(K):
+    """Rows with NaN: scattered, all NaN, next to +-inf, fewer than K numbers; and -0 beside +0.
+    The oracle must rank NaN last with ties by id, and treat -0 as equal to +0."""
+    g = np.random.default_rng(121)
+    V = 30
+    rows = []
+    r = np.round(g.standard_normal(V) * 2) / 2
+    r[[3, 11, 17]] = np.nan                                    # scattered NaN
+    rows.append(r)
+    rows.append(np.full(V, np.nan))                            # every entry NaN
+    r = g.standard_normal(V)
+    r[[0, 1, 2, 5]] = [np.nan, np.inf, -np.inf, np.nan]        # NaN next to +-inf
+    r[[6, 7]] = [np.inf, -np.inf]
+    rows.append(r)
+    r = np.full(V, np.nan)
+    r[[4, 9, 21]] = [1.5, -np.inf, 1.5]                        # three numbers, the rest NaN
+    rows.append(r)
+    r = np.zeros(V)
+    r[::2] = -0.0                                              # signed zeros only
+    r[[8, 13]] = [np.nan, -1.0]
+    rows.append(r)
+    x = np.stack(rows)
+    idx, vals = oracle.topk_cache(x, K)
+    for n in range(len(rows)):
+        want = sorted(range(V), key=lambda v: _rank_key(x[n, v], v))[:K]
+        assert list(idx[n]) == want, (n, list(idx[n]), want)
+        np.testing.assert_array_equal(vals[n], x[n, want])  # NaN == NaN in this comparison
 
 
 
