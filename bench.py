@@ -12,7 +12,8 @@ Prints one JSON line. Along with the throughput it carries:
     per-launch HIP events on its stream, and its HBM bytes from the committed counter summary;
   - cpu_baseline: the fp64 oracle timed on the host on a bounded slice of rows;
   - formulations: time and peak device memory of the same step through the other three
-    formulations (single pass, forward-chunked, dense) on the same inputs.
+    formulations (single pass, forward-chunked, dense), the frozen-head and memory-lean fused
+    backward, and the autograd term with an fp32 dW accumulator, on the same inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gptoss] [--chunk C]
        [--no-cpu-baseline] [--no-dense] [--no-formulations]
@@ -46,8 +47,8 @@ def parse():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-formulations", action="store_true",
                     help="skip timing the single-pass and forward-chunked formulations")
-    ap.add_argument("--cpu-rows", type=int, default=4096,
-                    help="rows of the workload the oracle is timed on (about 10-30 s on 16 host threads)")
+    ap.add_argument("--cpu-rows", type=int, default=2048,
+                    help="rows of the workload the oracle is timed on, three times (about 20 s on 16 host threads)")
     ap.add_argument("--sweep", action="store_true",
                     help="time the fused path at every timed config (small, the Qwen-like head over its "
                          "chunk sweep, gpt-oss, the pages' full shape) and sweep S for peak memory")
@@ -83,10 +84,10 @@ def measured_traffic(config: str, kernel: str):
     return None
 
 
-def cpu_baseline(p, n_rows):
+def cpu_baseline(p, n_rows, reps=3):
     """The oracle as it stands (fp64 numpy, forward-chunked formulation, forward + backward)
-    on the first n_rows rows at the config's full V and d; rows/s is tokens/s since the cost
-    is linear in rows."""
+    on the first n_rows rows at the config's full V and d, timed `reps` times (the median is
+    reported); rows/s is tokens/s since the cost is linear in rows."""
     import numpy as np
 
     import datagen
@@ -99,16 +100,20 @@ def cpu_baseline(p, n_rows):
         cores = os.cpu_count() or 1
     sub = datagen.make(p.name, N=n_rows)
     Hs, Ws, ts = sub.f64("H"), sub.f64("W"), sub.f64("tlog")
-    t0 = time.perf_counter()
-    oracle.kl_chunked(Hs, Ws, sub.idx, ts, sub.T, chunk=min(1024, n_rows), n_norm=p.N)
-    dt = time.perf_counter() - t0
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        oracle.kl_chunked(Hs, Ws, sub.idx, ts, sub.T, chunk=min(1024, n_rows), n_norm=p.N)
+        times.append(time.perf_counter() - t0)
+    dt = sorted(times)[len(times) // 2]
     return {
         "value": n_rows / dt,
         "unit": "tokens/s",
         "cores": int(cores),
         "kind": "oracle",
         "sample": f"{n_rows} rows of the same workload at full V={p.V}, d={p.d}, K={p.K}: fp64 numpy "
-                  f"oracle (forward-chunked formulation, forward and backward), {dt:.1f} s on the host",
+                  f"oracle (forward-chunked formulation, forward and backward), median of {reps} runs "
+                  f"({', '.join(f'{x:.1f}' for x in times)} s) on the host",
     }
 
 
@@ -196,7 +201,7 @@ def sweep(dev, steps: int):
     print("| config | oracle rows | oracle s | oracle tokens/s | threads | GPU fused step tokens/s | GPU / oracle |")
     print("|---|---|---|---|---|---|---|")
     for name, n in (("tiny", 256), ("small", 4096), ("qwen", 1024), ("gptoss", 1024), ("full", 1024)):
-        cb = cpu_baseline(datagen.make(name, N=n), n)
+        cb = cpu_baseline(datagen.make(name, N=n), n, reps=1)
         g = gpu_rate.get(name)
         print(f"| {name} | {n} | {n / cb['value']:.2f} | {cb['value']:,.0f} | {cb['cores']} | "
               + (f"{g:,.0f} | {g / cb['value']:,.0f} |" if g else "— | — |"), flush=True)
@@ -378,11 +383,31 @@ def main():
         f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=chunk, want_row_kl=True)
         return kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=chunk, flags=kd.KD_SKIP_DW)
 
+    def low_memory():
+        f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=chunk, want_row_kl=True, flags=kd.KD_LOW_MEMORY)
+        return kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=chunk, flags=kd.KD_LOW_MEMORY)
+
+    # The autograd term of a training step on a bf16 head: H and W as leaves, dW accumulated in a
+    # caller-owned fp32 buffer (allocated once, like an optimizer's main gradient; its 4 V d bytes
+    # count in the peak), dH returned to H.grad.
+    acc_box = []
+
+    def autograd_step():
+        if not acc_box:
+            acc_box.append(torch.zeros(W.shape, dtype=torch.float32, device=dev))
+        Hl = H.detach().requires_grad_(True)
+        loss = kd.fused_kl(Hl, W, idx, t, T=p.T, chunk=chunk, dw_accumulator=acc_box[0])
+        loss.backward()
+        return Hl.grad
+
     # counted FLOPs of each: single pass and forward-chunked compute the logits once (6 N d V);
-    # the frozen head (KD_SKIP_DW) recomputes them but skips dW (6 N d V)
+    # the frozen head (KD_SKIP_DW) recomputes them but skips dW (6 N d V); the memory-lean and
+    # autograd steps do the whole fused step (8 N d V)
     others = [("single_pass", lambda: kd.fused_kl_fwdbwd(H, W, idx, t, T=p.T, chunk=chunk), 6.0),
               ("forward_chunked", lambda: kd.chunked_kl(H, W, idx, t, T=p.T, chunk=chunk), 6.0),
-              ("fused_frozen_head", frozen_head, 6.0)]
+              ("fused_frozen_head", frozen_head, 6.0),
+              ("fused_low_memory", low_memory, 8.0),
+              ("fused_autograd_fp32_dw", autograd_step, 8.0)]
     if not args.no_dense:
         others.append(("dense", lambda: kd.dense_kl(H, W, idx, t, T=p.T), 8.0))
     for name, call, fl in others:
@@ -407,6 +432,7 @@ def main():
                            "counted_flops": fl * N * d * V}
         except (RuntimeError, torch.OutOfMemoryError) as ex:
             forms[name] = {"error": str(ex)[:200]}
+        acc_box.clear()
         torch.cuda.empty_cache()
         print(f"[bench] {name} path done", file=sys.stderr, flush=True)
     for f in forms.values():

@@ -43,9 +43,12 @@
  *
  * Conventions shared by every call:
  *   - Memory: every pointer argument except `p` is device memory on the current HIP
- *     device, allocated and owned by the caller. `p` is host memory. The library allocates,
- *     frees and keeps nothing across calls. Calls that do not share output or workspace
- *     buffers may run concurrently on different streams.
+ *     device, allocated and owned by the caller. `p` is host memory. The library never
+ *     allocates or frees device memory, and no result depends on an earlier call. Host-side
+ *     state is limited to the optional timing (kd_timing_*: a process-wide pool of HIP events
+ *     and running totals under a mutex) and a per-device cache of the compute-unit count.
+ *     Calls that do not share output or workspace buffers may run concurrently on different
+ *     streams.
  *   - Streams: work is enqueued on `stream`, an hipStream_t (NULL means the null stream).
  *     Outputs are valid once the caller has synchronised that stream. No call synchronises,
  *     except as noted for KD_VALIDATE_IDX.
@@ -54,8 +57,13 @@
  *     KD_ERR_HIP. A fault inside a kernel surfaces at the caller's next synchronisation of
  *     the stream. No C++ exception crosses this interface.
  *   - Preconditions the host cannot check without reading device memory: idx in [0,V) and
- *     distinct within each row. Out-of-range ids are skipped, never dereferenced. Results
- *     are undefined if the ids repeat. Set KD_VALIDATE_IDX to have them checked.
+ *     distinct within each row. An out-of-range id is never dereferenced (no fault), but the
+ *     zk slot of that entry is left unwritten, so the KL_n and zk of its row, and the loss,
+ *     are undefined; repeated ids give undefined values for their row. Set KD_VALIDATE_IDX
+ *     (or run kd_validate_ids) to have the ids checked.
+ *   - Teacher logits: finite, or -inf for a masked entry. A -inf entry has p_t = 0: it adds
+ *     nothing to KL_n (0 log 0 = 0) and nothing is subtracted at its id in the gradient. Every
+ *     row needs at least one finite cached logit; +inf or NaN logits give undefined values.
  *   - Alignment: H, W, dH and dW must be 16-byte aligned (KD_ERR_VALUE otherwise).
  *   - Workspace: the caller passes ws (256-byte aligned) of at least the bytes returned by
  *     the matching *_workspace_bytes query for the same problem. Its contents on entry do not
@@ -72,8 +80,9 @@ extern "C" {
 #endif
 
 /* 1: first release. 2: kd_validate_ids added; chunks capped at 2^20 rows; kd_dense_kl limited
- * to V <= 2^21. Calls and structures of version 1 are unchanged. */
-#define KDKL_ABI_VERSION 2
+ * to V <= 2^21. 3: KD_LOW_MEMORY and kd_chunked_logits added; a -inf teacher logit counts as a
+ * masked entry. Calls and structures of earlier versions are unchanged. */
+#define KDKL_ABI_VERSION 3
 
 /* Same type as hipStream_t; declared here so that this header does not need the HIP headers. */
 typedef struct ihipStream_t* kd_stream;
@@ -103,6 +112,13 @@ typedef enum kd_dtype {
 #define KD_SKIP_DW       0x4u /* kd_fused_kl_bwd computes dH only (dW may be NULL): for a frozen head.
                                  Ignored by kd_fused_kl_fwd; KD_ERR_VALUE for the other calls and
                                  together with KD_ACCUMULATE_DW */
+#define KD_LOW_MEMORY    0x8u /* memory-lean fused backward: of the default backward's buffers the
+                                 workspace keeps the chunk's gradient tile G_c [chunk, V], and none
+                                 of the transposed copies of W, G_c and H_c; dH and dW then read
+                                 their operands as stored, on a slower GEMM path, with one dW pass
+                                 per chunk. Same results up to rounding order. Changes
+                                 kd_fused_workspace_bytes; ignored by kd_fused_kl_fwd; KD_ERR_VALUE
+                                 for the other loss calls */
 
 /*
  * Problem descriptor (host memory).
@@ -119,7 +135,7 @@ typedef enum kd_dtype {
  *                one batch is split over several calls.
  *   act          dtype of H, W and dH: KD_BF16 (fp32 accumulation) or KD_FP32 (fp32 products).
  *   tlogit       dtype of the cached teacher logits t: KD_BF16 or KD_FP32.
- *   flags        KD_VALIDATE_IDX | KD_ACCUMULATE_DW | KD_SKIP_DW.
+ *   flags        KD_VALIDATE_IDX | KD_ACCUMULATE_DW | KD_SKIP_DW | KD_LOW_MEMORY.
  */
 typedef struct kd_problem {
     int64_t N;
@@ -209,6 +225,19 @@ kd_status kd_chunked_kl(const kd_problem* p, const void* H, const void* W, const
                         const void* tlog, const float* grad_loss, float* loss, float* lse,
                         float* row_kl, void* dH, float* dW, void* ws, size_t ws_bytes,
                         kd_stream stream);
+
+/*
+ * Where kd_chunked_kl keeps the student logits it materialises (the same paragraph: the
+ * forward-chunked formulation stores the full logit grid for the backward). Host-only: it
+ * enqueues nothing and reads no device memory. For a workspace `ws` of at least
+ * kd_chunked_workspace_bytes(p) bytes, sets *zt to the fp32 array z^T [Vp][*ldzt] inside it
+ * (Vp = V rounded up to a multiple of 256; element (v, n) = z[n, v] for n < N, v < V). After a
+ * kd_chunked_kl call on the same p and ws has completed on its stream, the array holds that
+ * call's logits, until the workspace is next written.
+ *   Errors: as kd_chunked_kl's argument checks; KD_ERR_NULL if ws, zt or ldzt is NULL.
+ */
+kd_status kd_chunked_logits(const kd_problem* p, const void* ws, size_t ws_bytes, const float** zt,
+                            int64_t* ldzt);
 
 /*
  * Single-pass fused formulation: each chunk of rows is taken end to end (logits, its loss

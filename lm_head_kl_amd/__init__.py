@@ -19,7 +19,8 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import KD_ACCUMULATE_DW, KD_BF16, KD_FP32, KD_SKIP_DW, KD_VALIDATE_IDX, KdError, KdProblem
+from ._lib import (KD_ACCUMULATE_DW, KD_BF16, KD_FP32, KD_LOW_MEMORY, KD_SKIP_DW, KD_VALIDATE_IDX, KdError,
+                   KdProblem)
 
 __all__ = [
     "FusedKL",
@@ -28,6 +29,7 @@ __all__ = [
     "fused_kl_bwd",
     "dense_kl",
     "chunked_kl",
+    "chunked_logits",
     "fused_kl_fwdbwd",
     "topk_cache",
     "validate_ids",
@@ -43,6 +45,7 @@ __all__ = [
     "KD_VALIDATE_IDX",
     "KD_ACCUMULATE_DW",
     "KD_SKIP_DW",
+    "KD_LOW_MEMORY",
 ]
 
 _DT = {torch.bfloat16: KD_BF16, torch.float32: KD_FP32}
@@ -227,6 +230,21 @@ def chunked_workspace_bytes(p: KdProblem) -> int:
     return int(_lib.lib().kd_chunked_workspace_bytes(ctypes.byref(p)))
 
 
+def chunked_logits(p: KdProblem, workspace: torch.Tensor) -> torch.Tensor:
+    """kd_chunked_logits: the student logits that kd_chunked_kl keeps, as a view of its
+    workspace: z^T [Vp, ldzt] fp32 (Vp = V rounded up to 256), element (v, n) = z[n, v]. Valid
+    once the kd_chunked_kl call that used this workspace has run, until the workspace is reused."""
+    if workspace.dtype != torch.uint8 or workspace.dim() != 1 or not workspace.is_contiguous():
+        raise KdError(3, "chunked_logits", "the workspace must be a contiguous uint8 tensor")
+    zp, ld = ctypes.c_void_p(0), ctypes.c_int64(0)
+    code = _lib.lib().kd_chunked_logits(ctypes.byref(p), _ptr(workspace), workspace.numel(), ctypes.byref(zp),
+                                        ctypes.byref(ld))
+    _lib.check(code, "kd_chunked_logits")
+    vp = (p.V + 255) // 256 * 256
+    off = int(zp.value) - workspace.data_ptr()
+    return workspace[off:off + vp * ld.value * 4].view(torch.float32).view(vp, ld.value)
+
+
 def fused_fwdbwd_workspace_bytes(p: KdProblem) -> int:
     return int(_lib.lib().kd_fused_fwdbwd_workspace_bytes(ctypes.byref(p)))
 
@@ -287,28 +305,48 @@ def validate_ids(idx: torch.Tensor, V: int, status: torch.Tensor | None = None) 
 
 
 class FusedKL(torch.autograd.Function):
-    """loss = FusedKL.apply(H, W, idx, tlog, T, chunk, n_norm): the KL term of a distillation
-    step. The forward saves only lse [N]; the backward recomputes the logits chunk by chunk."""
+    """loss = FusedKL.apply(H, W, idx, tlog, T, chunk, n_norm, dw_accumulator, low_memory): the
+    KL term of a distillation step. The forward saves only lse [N]; the backward recomputes the
+    logits chunk by chunk.
+
+    dW is always accumulated in fp32 by the library. Without `dw_accumulator` it becomes W's
+    gradient in W's dtype (autograd requires that dtype, so a bf16 head receives dW rounded to
+    bf16). With `dw_accumulator` (an fp32 tensor of W's shape) the backward adds dW into it
+    (KD_ACCUMULATE_DW) and gives W no autograd gradient, so micro-batches sum in fp32 in the
+    caller's buffer. A head that needs no gradient and has no accumulator skips the dW work
+    (KD_SKIP_DW). `low_memory` selects the memory-lean backward (KD_LOW_MEMORY)."""
 
     @staticmethod
-    def forward(ctx, H, W, idx, tlog, T=1.0, chunk=2048, n_norm=0.0):
+    def forward(ctx, H, W, idx, tlog, T=1.0, chunk=2048, n_norm=0.0, dw_accumulator=None, low_memory=False):
         out = fused_kl_fwd(H, W, idx, tlog, T=T, chunk=chunk, n_norm=n_norm, want_row_kl=False)
+        if dw_accumulator is not None:
+            _check_dw(dw_accumulator, W, H.device, "FusedKL")
+            if not dw_accumulator.is_contiguous():
+                raise KdError(2, "FusedKL", "dw_accumulator must be contiguous")
         ctx.save_for_backward(H, W, idx, tlog, out.lse)
-        ctx.cfg = (T, chunk, n_norm)
+        ctx.cfg = (T, chunk, n_norm, bool(low_memory))
+        ctx.dw_acc = dw_accumulator
         return out.loss
 
     @staticmethod
     def backward(ctx, g):
         H, W, idx, tlog, lse = ctx.saved_tensors
-        T, chunk, n_norm = ctx.cfg
-        # a frozen head (W without a gradient) skips dW and the work that only it needs
-        flags = 0 if ctx.needs_input_grad[1] else KD_SKIP_DW
-        dH, dW = fused_kl_bwd(H, W, idx, tlog, lse, grad_loss=g, T=T, chunk=chunk, n_norm=n_norm, flags=flags)
-        return dH, (dW.to(W.dtype) if dW is not None else None), None, None, None, None, None
+        T, chunk, n_norm, lean = ctx.cfg
+        acc = ctx.dw_acc
+        flags = KD_LOW_MEMORY if lean else 0
+        if acc is not None:
+            flags |= KD_ACCUMULATE_DW
+        elif not ctx.needs_input_grad[1]:
+            flags |= KD_SKIP_DW  # a frozen head skips dW and the work that only it needs
+        dH, dW = fused_kl_bwd(H, W, idx, tlog, lse, grad_loss=g, T=T, chunk=chunk, n_norm=n_norm, flags=flags,
+                              dW=acc)
+        dW_out = dW.to(W.dtype) if (acc is None and dW is not None) else None
+        return dH, dW_out, None, None, None, None, None, None, None
 
 
-def fused_kl(H, W, idx, tlog, T: float = 1.0, chunk: int = 2048, n_norm: float = 0.0):
-    return FusedKL.apply(H, W, idx, tlog, T, chunk, n_norm)
+def fused_kl(H, W, idx, tlog, T: float = 1.0, chunk: int = 2048, n_norm: float = 0.0,
+             dw_accumulator: torch.Tensor | None = None, low_memory: bool = False):
+    return FusedKL.apply(H, W, idx, tlog, T, chunk, n_norm, dw_accumulator, low_memory)
 
 
 def timing_enable(on: bool = True) -> bool:

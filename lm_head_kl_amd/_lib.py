@@ -13,7 +13,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkdkl.so")
 
 KD_FP32, KD_BF16 = 0, 1
-KD_VALIDATE_IDX, KD_ACCUMULATE_DW, KD_SKIP_DW = 0x1, 0x2, 0x4
+KD_VALIDATE_IDX, KD_ACCUMULATE_DW, KD_SKIP_DW, KD_LOW_MEMORY = 0x1, 0x2, 0x4, 0x8
 
 STATUS = {
     0: "KD_OK",
@@ -38,6 +38,7 @@ EXPORTS = (
     "kd_dense_kl",
     "kd_chunked_workspace_bytes",
     "kd_chunked_kl",
+    "kd_chunked_logits",
     "kd_fused_fwdbwd_workspace_bytes",
     "kd_fused_kl_fwdbwd",
     "kd_topk_cache",
@@ -106,6 +107,8 @@ def lib() -> ctypes.CDLL:
         getattr(L, name).restype = ctypes.c_int
         getattr(L, name).argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     i64 = ctypes.c_int64
+    L.kd_chunked_logits.restype = ctypes.c_int
+    L.kd_chunked_logits.argtypes = [P, vp, sz, ctypes.POINTER(ctypes.c_void_p), ctypes.POINTER(i64)]
     L.kd_topk_cache.restype = ctypes.c_int
     L.kd_topk_cache.argtypes = [vp, ctypes.c_int32, i64, i64, i64, i64, vp, vp, vp]
     L.kd_validate_ids.restype = ctypes.c_int

@@ -127,27 +127,34 @@ template <> __device__ __forceinline__ void mma<float>(f32x16& c, const u32x4& a
 // ------------------------------------------------------------------------------------------
 // K-contiguous operand, filled by DMA. Wave w's instruction t fills LDS chunks
 // 256t + 64w + lane, i.e. row 32t + 8w + lane/8, physical chunk lane%8.
-template <typename T>
+// BLK selects the K-blocked layout (K cut into blocks of 256, each a row-major [R][256] slab;
+// ld is then the row count R). A K step (64 bf16 / 32 fp32) never straddles a block.
+template <typename T, bool BLK = false>
 struct KOperand {
     static constexpr int VEC = Elem<T>::VEC;
-    const char* base;  // &src[mn0*ld] (uniform)
+    const char* base;  // &src[mn0*ld] (row-major) or &src[mn0*256] in block 0 (uniform)
+    int64_t blk_bytes; // K-blocked: bytes per block
     uint32_t off[8];   // byte offset of this lane's chunk for instruction t at k = 0, or kOOB
     int chunk[2];      // logical chunk (k/VEC within the step) for even / odd t
 
     __device__ __forceinline__ void init(const T* src, int64_t ld, int64_t mn0, int64_t mn_lim, const WaveId& id) {
-        base = (const char*)(src + mn0 * ld);
+        const int64_t row_ld = BLK ? 256 : ld;
+        base = (const char*)(src + mn0 * row_ld);
+        blk_bytes = BLK ? ld * 256 * (int64_t)sizeof(T) : 0;
         const int r8 = id.lane >> 3, p = id.lane & 7;
 #pragma unroll
         for (int t = 0; t < 2; ++t) chunk[t] = p ^ ((r8 ^ (4 * t + id.w)) & 7);
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
             const int row = 32 * t + 8 * id.w + r8;
-            off[t] = mn0 + row < mn_lim ? (uint32_t)((row * ld + chunk[t & 1] * VEC) * (int64_t)sizeof(T)) : kOOB;
+            off[t] = mn0 + row < mn_lim ? (uint32_t)((row * row_ld + chunk[t & 1] * VEC) * (int64_t)sizeof(T)) : kOOB;
         }
     }
     // Enqueue the K step starting at k0 into the LDS tile (no wait).
     __device__ __forceinline__ void issue(u32x4* tile, int64_t k0, int64_t k_lim, const WaveId& id) const {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(base + k0 * (int64_t)sizeof(T));
+        const char* b = BLK ? base + (k0 >> 8) * blk_bytes + (k0 & 255) * (int64_t)sizeof(T)
+                            : base + k0 * (int64_t)sizeof(T);
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(b);
         const int64_t kc = (k_lim - k0 + VEC - 1) / VEC;  // chunks of this step inside the K range
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
@@ -251,8 +258,8 @@ struct MNOperand<float> {
     }
 };
 
-template <typename T, bool KMAJ> struct OperandSel { using type = KOperand<T>; };
-template <typename T> struct OperandSel<T, false> { using type = MNOperand<T>; };
+template <typename T, bool KMAJ, bool BLK = false> struct OperandSel { using type = KOperand<T, BLK>; };
+template <typename T, bool BLK> struct OperandSel<T, false, BLK> { using type = MNOperand<T>; };
 
 // One K step from LDS: for each of the 4 k-groups, 4 A and 4 B fragments and 16 MFMAs.
 // Fragments are double-buffered so the reads of group g+1 overlap the MFMAs of group g.
@@ -287,8 +294,9 @@ __device__ __forceinline__ void compute_stage(f32x16 (&acc)[4][4], const u32x4* 
 // acc = A[m0:m0+256, k_begin:k_end] B[n0:n0+256, k_begin:k_end]^T.
 // AK / BK: operand is K contiguous. ka_lim / kb_lim: first k each operand may not read
 // (multiples of the 16-byte vector width). Rows at or past m_lim / n_lim read as zero.
+// BLKA: A is K contiguous in the K-blocked layout (lda = its row count).
 // Ends with a barrier, so the LDS may be reused right away.
-template <typename T, bool AK, bool BKM>
+template <typename T, bool AK, bool BKM, bool BLKA = false>
 __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], u32x4* L, const WaveId& id,
                                           const T* A, int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim,
                                           const T* B, int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim,
@@ -300,7 +308,8 @@ __device__ __forceinline__ void gemm_tile(f32x16 (&acc)[4][4], u32x4* L, const W
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
     const int nk = (int)((k_end - k_begin + BK - 1) / BK);
     if (nk <= 0) return;
-    typename OperandSel<T, AK>::type opA;
+    static_assert(AK || !BLKA, "the K-blocked layout is for K-contiguous operands");
+    typename OperandSel<T, AK, BLKA>::type opA;
     typename OperandSel<T, BKM>::type opB;
     opA.init(A, lda, m0, m_lim, id);
     opB.init(B, ldb, n0, n_lim, id);

@@ -64,7 +64,8 @@ kd_status check_problem(const kd_problem* p) {
     if ((p->N + kTileM) * p->K >= lim || p->N * p->d >= lim || p->V * p->d >= lim) return KD_ERR_SHAPE;
     if (!std::isfinite(p->T) || !(p->T > 0.f)) return KD_ERR_VALUE;
     if (!std::isfinite(p->n_norm)) return KD_ERR_VALUE;
-    if ((p->flags & ~(KD_VALIDATE_IDX | KD_ACCUMULATE_DW | KD_SKIP_DW)) != 0 || p->reserved != 0) return KD_ERR_VALUE;
+    if ((p->flags & ~(KD_VALIDATE_IDX | KD_ACCUMULATE_DW | KD_SKIP_DW | KD_LOW_MEMORY)) != 0 || p->reserved != 0)
+        return KD_ERR_VALUE;
     if ((p->flags & KD_SKIP_DW) && (p->flags & KD_ACCUMULATE_DW)) return KD_ERR_VALUE;
     return KD_OK;
 }
@@ -115,13 +116,16 @@ struct FusedWs {
     size_t fwd_bytes, bwd_bytes;
 };
 
+bool low_memory(const kd_problem* p) { return (p->flags & KD_LOW_MEMORY) != 0; }
+
 FusedWs layout_fused(const kd_problem* p, void* ws) {
     FusedWs w{};
     const int64_t N = p->N, K = p->K, V = p->V, d = p->d;
     const int64_t n_vt = n_vtiles(V), Vp = n_vt * kTileN;
     const int64_t C = chunk_rows(p);
+    const bool lean = low_memory(p);
     w.n_vsplit = fwd_vsplits(N, V);
-    w.n_split = dh_splits(C, d, V, true);
+    w.n_split = dh_splits(C, d, V, !lean);
     Carve f(ws);
     w.status = (uint32_t*)f.take(kAlign);
     w.plan_off = (int32_t*)f.take(sizeof(int32_t) * n_rblocks(N) * (n_vt + 1));
@@ -138,14 +142,18 @@ FusedWs layout_fused(const kd_problem* p, void* ws) {
     w.cplan_off = (int32_t*)b.take(sizeof(int32_t) * n_rblocks(plan_rows) * (n_vt + 1));
     w.cplan_ent = (uint32_t*)b.take(sizeof(uint32_t) * n_rblocks(plan_rows) * kTileM * K);
     w.pt = (float*)b.take(sizeof(float) * N * K);
-    // G_c^T and H_c^T hold a group of chunks side by side (slot s at columns s*round_up(C, 8)),
-    // so one dW pass reduces over the group and dW is read and written once per group.
-    w.group = dw_group(p, C);
-    w.ldgt = w.group * round_up(C, 8);
     w.Gc = b.take(esize(p->act) * C * Vp);
-    w.GT = b.take(esize(p->act) * Vp * w.ldgt);
-    w.WT = b.take(esize(p->act) * d * Vp);
-    w.HT = b.take(esize(p->act) * d * w.ldgt);
+    if (!lean) {
+        // G_c^T and H_c^T hold a group of chunks side by side (slot s at columns
+        // s*round_up(C, 8)), so one dW pass reduces over the group and dW is read and written
+        // once per group. The memory-lean backward keeps none of these copies (nor W^T): dH and
+        // dW read G_c, W and H as they are.
+        w.group = dw_group(p, C);
+        w.ldgt = w.group * round_up(C, 8);
+        w.GT = b.take(esize(p->act) * Vp * w.ldgt);
+        w.WT = b.take(esize(p->act) * d * Vp);
+        w.HT = b.take(esize(p->act) * d * w.ldgt);
+    }
     w.dh_part = w.n_split > 1 ? (float*)b.take(sizeof(float) * w.n_split * C * d) : nullptr;
     w.bwd_bytes = b.used;
     return w;
@@ -357,8 +365,9 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
     const int64_t C = chunk_rows(p);
     const int64_t Vp = n_vtiles(p->V) * kTileN;
     const bool acc0 = (p->flags & KD_ACCUMULATE_DW) != 0;
+    const bool lean = low_memory(p);
     // W^T once per call: dH = G_c W then reads both operands with the vocabulary contiguous.
-    KD_TRY(launch_transpose_blocked(sh.act, W, p->d, p->V, p->d, w.WT, Vp, s));
+    if (!lean) KD_TRY(launch_transpose_blocked(sh.act, W, p->d, p->V, p->d, w.WT, Vp, s));
     const int64_t C8 = round_up(C, 8);
     const size_t es = esize(p->act);
     const bool one_plan = whole_plan(p);
@@ -373,6 +382,17 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
         if (!one_plan) KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.cplan_off, w.cplan_ent, s));
         // The chunk's row blocks in the plan; entry offsets in it are absolute.
         const int32_t* c_off = w.cplan_off + (one_plan ? (c0 / kTileM) * plan_stride : 0);
+        if (lean) {
+            // G_c only; dH reads W as stored and dW reads G_c and H_c as they are.
+            KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.cplan_ent, w.Gc,
+                                   nullptr, 0, s));
+            KD_TRY(launch_dh(sh, w.Gc, 0, W, nullptr, c0, cc, w.n_split, w.dh_part, dH, s, true));
+            if (want_dw) {
+                KD_TRY(launch_dw(sh, w.Gc, 0, H, c0, cc, acc0 || dw_written, dW, s, true));
+                dw_written = true;
+            }
+            continue;
+        }
         // H_c^T into its slot, so that dW = G^T H reads both operands with the rows contiguous
         if (want_dw)
             KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
@@ -395,7 +415,8 @@ kd_status kd_dense_kl(const kd_problem* p, const void* H, const void* W, const i
                       size_t ws_bytes, kd_stream stream) {
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
-    if (p->flags & KD_SKIP_DW) return KD_ERR_VALUE;  // only the fused backward can leave dW out
+    // only the fused backward can leave dW out or run memory-lean
+    if (p->flags & (KD_SKIP_DW | KD_LOW_MEMORY)) return KD_ERR_VALUE;
     if (p->V > kMaxDenseV) return KD_ERR_SHAPE;
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
@@ -448,6 +469,18 @@ size_t kd_chunked_workspace_bytes(const kd_problem* p) {
     return layout_stored(p, nullptr, true).bytes;
 }
 
+kd_status kd_chunked_logits(const kd_problem* p, const void* ws, size_t ws_bytes, const float** zt,
+                            int64_t* ldzt) {
+    kd_status st = check_problem(p);
+    if (st != KD_OK) return st;
+    if (!ws || !zt || !ldzt) return KD_ERR_NULL;
+    if (!aligned(ws, kAlign) || ws_bytes < kd_chunked_workspace_bytes(p)) return KD_ERR_WORKSPACE;
+    const StoredWs w = layout_stored(p, const_cast<void*>(ws), true);
+    *zt = w.zt;
+    *ldzt = w.ldzt;
+    return KD_OK;
+}
+
 size_t kd_fused_fwdbwd_workspace_bytes(const kd_problem* p) {
     if (check_problem(p) != KD_OK) return 0;
     return layout_stored(p, nullptr, false).bytes;
@@ -458,7 +491,8 @@ kd_status kd_chunked_kl(const kd_problem* p, const void* H, const void* W, const
                         size_t ws_bytes, kd_stream stream) {
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
-    if (p->flags & KD_SKIP_DW) return KD_ERR_VALUE;  // only the fused backward can leave dW out
+    // only the fused backward can leave dW out or run memory-lean
+    if (p->flags & (KD_SKIP_DW | KD_LOW_MEMORY)) return KD_ERR_VALUE;
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_chunked_workspace_bytes(p)) return KD_ERR_WORKSPACE;
@@ -486,7 +520,8 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
                              void* ws, size_t ws_bytes, kd_stream stream) {
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
-    if (p->flags & KD_SKIP_DW) return KD_ERR_VALUE;  // only the fused backward can leave dW out
+    // only the fused backward can leave dW out or run memory-lean
+    if (p->flags & (KD_SKIP_DW | KD_LOW_MEMORY)) return KD_ERR_VALUE;
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_fused_fwdbwd_workspace_bytes(p)) return KD_ERR_WORKSPACE;

@@ -112,15 +112,18 @@ hipError_t launch_transpose_blocked(Dt dt, const void* src, int64_t lds, int64_t
                                     void* dst, int64_t rows_pad, hipStream_t s);
 
 // dH rows [c0, c0+cc) = G_c W. With WT not null, G_c is the K-blocked tile written by
-// launch_bwd_grad and WT is W^T K-blocked [Vp/256][d][256]; with WT null, G_c is [cc][ldg]
-// row-major and W is read as stored. Split over the vocabulary into n_split fp32 partials when
-// n_split > 1 (part: [n_split][cc][d]), then reduced in a fixed order.
+// launch_bwd_grad and WT is W^T K-blocked [Vp/256][d][256]; with WT null, W is read as stored
+// and G_c is either that K-blocked tile (g_blocked) or row-major [cc][ldg]. Split over the
+// vocabulary into n_split fp32 partials when n_split > 1 (part: [n_split][cc][d]), then
+// reduced in a fixed order.
 hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, const void* WT,
-                     int64_t c0, int64_t cc, int n_split, float* part, void* dH, hipStream_t s);
+                     int64_t c0, int64_t cc, int n_split, float* part, void* dH, hipStream_t s,
+                     bool g_blocked = false);
 
-// dW (+)= G_c^T H[c0:c0+cc] from G_c [cc][ldg] and H (both M/N contiguous).
+// dW (+)= G_c^T H[c0:c0+cc] from G_c and H, both M/N contiguous: G_c row-major [cc][ldg], or
+// the gradient kernel's K-blocked tile [Vp/256][cc][256] (g_blocked; ldg unused).
 hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H, int64_t c0,
-                     int64_t cc, bool accumulate, float* dW, hipStream_t s);
+                     int64_t cc, bool accumulate, float* dW, hipStream_t s, bool g_blocked = false);
 // dW (+)= G_c^T H_c from G_c^T [Vp][ldgt] and H_c^T [d][ldht] (both K contiguous).
 hipError_t launch_dw_t(const Shape& sh, const void* GT, int64_t ldgt, const void* HT, int64_t ldht,
                        int64_t cc, bool accumulate, float* dW, hipStream_t s);

@@ -421,10 +421,12 @@ __global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ part
         double se = 0.0;
         for (int k = lane; k < K; k += 64) se += exp((double)load_t(tl, tdt, n * K + k) / T - mx);
         const double lz = mx + log(wave_sum_d(se));
+        // An entry whose teacher logit is -inf has p_t = 0 and adds nothing (0 log 0 = 0).
         double term = 0.0;
         for (int k = lane; k < K; k += 64) {
             const double lp = (double)load_t(tl, tdt, n * K + k) / T - lz;
-            term += exp(lp) * (lp - (double)zk[n * K + k] / T + lse_d);
+            const double pk = exp(lp);
+            if (pk > 0.0) term += pk * (lp - (double)zk[n * K + k] / T + lse_d);
         }
         const double kl = wave_sum_d(term);
         if (lane == 0) {
@@ -848,7 +850,10 @@ struct DhArgs {
     void* dH;
 };
 
-template <typename T>
+// BLK: G_c is the K-blocked tile of the gradient kernel ([Vp/256][cc][256]) instead of
+// row-major [cc][ldg]; W is read as stored either way (the memory-lean backward, which keeps
+// no W^T).
+template <typename T, bool BLK>
 __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
     const WaveId id;
@@ -863,8 +868,8 @@ __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
     const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
     f32x16 acc[4][4];
-    gemm_tile<T, true, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
-                              min(a.V, k_end), k_begin, k_end);
+    gemm_tile<T, true, false, BLK>(acc, L, id, (const T*)a.G, BLK ? a.cc : a.ldg, m0, a.cc, k_end, (const T*)a.W,
+                                   a.d, n0, a.d, min(a.V, k_end), k_begin, k_end);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -950,8 +955,9 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
 // (k_dw_w).
 
 struct DwArgs {
-    const void* G;   // G_c [cc][ldg], or G_c^T [Vp][ldg] (K contiguous)
+    const void* G;   // G_c [cc][ldg], G_c K-blocked [Vp/256][cc][256] (g_blk), or G_c^T [Vp][ldg] (K contiguous)
     int64_t ldg, Vp;
+    int g_blk;
     const void* H;   // H (rows from c0), or H_c^T [d][ldh] (K contiguous)
     int64_t ldh;
     int64_t d, V;
@@ -974,8 +980,11 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
     const int mt = (int)(t / a.n_nt), nt = (int)(t % a.n_nt);
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kTileN;
     f32x16 acc[4][JN];
-    gemm_tile<T, false, false>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.cc, (const T*)a.H + a.c0 * a.d, a.d,
-                               n0, a.d, a.cc, 0, a.cc);
+    // A K-blocked G_c holds this tile's 256 vocabulary columns as one row-major [cc][256] slab.
+    const T* Ga = a.g_blk ? (const T*)a.G + m0 * a.cc : (const T*)a.G;
+    gemm_tile<T, false, false>(acc, L, id, Ga, a.g_blk ? (int64_t)kTileN : a.ldg, a.g_blk ? 0 : m0,
+                               a.g_blk ? (int64_t)kTileM : a.Vp, a.cc, (const T*)a.H + a.c0 * a.d, a.d, n0, a.d, a.cc,
+                               0, a.cc);
     // Read-modify-write through LDS, in two passes of 128 rows. Every dW access is a 16-byte
     // vector and a wave covers 1 KB of one row. The old values of a pass's first half are
     // requested before its staging writes and those of the second half before the first half
@@ -1754,7 +1763,7 @@ hipError_t launch_transpose_blocked(Dt dt, const void* src, int64_t lds, int64_t
 }
 
 hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, const void* WT, int64_t c0,
-                     int64_t cc, int n_split, float* part, void* dH, hipStream_t s) {
+                     int64_t cc, int n_split, float* part, void* dH, hipStream_t s, bool g_blocked) {
     DhArgs a;
     a.G = Gc;
     a.ldg = ldg;
@@ -1774,13 +1783,17 @@ hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W
     if (sh.act == Dt::BF16) {
         if (WT)
             KD_LAUNCH(kKindDh, s, k_dh_w<bf16_t>, grid, dim3(512), 0, s, a);
+        else if (g_blocked)
+            KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, true>), grid, dim3(NTHR), 0, s, a);
         else
-            KD_LAUNCH(kKindDh, s, k_dh<bf16_t>, grid, dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, false>), grid, dim3(NTHR), 0, s, a);
     } else {
         if (WT)
             KD_LAUNCH(kKindDh, s, k_dh_w<float>, grid, dim3(512), 0, s, a);
+        else if (g_blocked)
+            KD_LAUNCH(kKindDh, s, (k_dh<float, true>), grid, dim3(NTHR), 0, s, a);
         else
-            KD_LAUNCH(kKindDh, s, k_dh<float>, grid, dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindDh, s, (k_dh<float, false>), grid, dim3(NTHR), 0, s, a);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || n_split <= 1) return e;
@@ -1794,10 +1807,11 @@ hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W
 }
 
 hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H, int64_t c0, int64_t cc,
-                     bool accumulate, float* dW, hipStream_t s) {
+                     bool accumulate, float* dW, hipStream_t s, bool g_blocked) {
     DwArgs a;
     a.G = Gc;
     a.ldg = ldg;
+    a.g_blk = g_blocked ? 1 : 0;
     a.Vp = round_up(sh.V, kTileN);
     a.H = H;
     a.ldh = sh.d;
@@ -1823,6 +1837,7 @@ hipError_t launch_dw_t(const Shape& sh, const void* GT, int64_t ldgt, const void
     DwArgs a;
     a.G = GT;
     a.ldg = ldgt;
+    a.g_blk = 0;
     a.Vp = round_up(sh.V, kTileN);
     a.H = HT;
     a.ldh = ldht;

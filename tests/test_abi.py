@@ -142,7 +142,7 @@ def dense(p, H=F, dH=F, ws=F, nbytes=None):
     (dict(d=(1 << 20) + 8, V=1000, N=1000), 2),
     (dict(act=2), 3), (dict(tlogit=-1), 3),
     (dict(T=0.0), 4), (dict(T=-1.0), 4), (dict(T=float("nan")), 4), (dict(T=float("inf")), 4),
-    (dict(n_norm=float("nan")), 4), (dict(flags=8), 4), (dict(reserved=1), 4),
+    (dict(n_norm=float("nan")), 4), (dict(flags=16), 4), (dict(reserved=1), 4),
 ])
 def test_bad_problem_rejected(bad, code):
     p = prob(**bad)
@@ -210,6 +210,57 @@ def test_skip_dw_flag_rules():
         nb = max(1, getattr(L, query)(ctypes.byref(p)))
         assert getattr(L, fn)(ctypes.byref(p), F, F, F, F, None, F, F, None, F, F, F, nb, None) == 4
     assert bwd(prob(), dW=None) == 1
+
+
+def test_low_memory_workspace():
+    """KD_LOW_MEMORY drops the transposed copies of W, G_c and H_c from the fused backward's
+    workspace: what is left is about the gradient tile G_c plus the dH partials and the
+    O(N*K) cache terms. The forward's part is unchanged."""
+    d, V, C = 2880, 201088, 2048
+    full = ws_bytes(N=32768, d=d, V=V, chunk=C)
+    lean = ws_bytes(N=32768, d=d, V=V, chunk=C, flags=_lib.KD_LOW_MEMORY)
+    vp = (V + 255) // 256 * 256
+    gc = C * vp * 2
+    assert gc <= lean < gc + 8 * C * d * 4 + 32768 * 100 * 12 + (1 << 24)
+    # the default adds W^T (V*d) and a four-chunk G^T slab (4*C*V) in bf16
+    assert full - lean >= (vp * d + 4 * C * vp) * 2
+    # N still enters only through O(N*K) terms
+    a, b, c = (ws_bytes(N=n, chunk=1024, flags=_lib.KD_LOW_MEMORY) for n in (8192, 16384, 24576))
+    assert abs((c - b) - (b - a)) <= 4096 and (b - a) / 8192 < 100 * 4 * 3 + 64
+
+
+@nogpu
+def test_low_memory_flag_rules():
+    """KD_LOW_MEMORY belongs to the fused calls; the other loss calls reject it."""
+    L = _lib.lib()
+    p = prob(flags=_lib.KD_LOW_MEMORY)
+    assert dense(p) == 4
+    for fn, query in (("kd_chunked_kl", "kd_chunked_workspace_bytes"),
+                      ("kd_fused_kl_fwdbwd", "kd_fused_fwdbwd_workspace_bytes")):
+        nb = max(1, getattr(L, query)(ctypes.byref(p)))
+        assert getattr(L, fn)(ctypes.byref(p), F, F, F, F, None, F, F, None, F, F, F, nb, None) == 4
+    # a workspace sized for the lean backward is too small for the default one
+    lean = L.kd_fused_workspace_bytes(ctypes.byref(p))
+    assert bwd(prob(), nbytes=lean) == 5
+
+
+def test_chunked_logits_view():
+    """kd_chunked_logits is host-only: it places z^T [Vp][ldzt] fp32 inside the workspace and
+    checks its arguments like the loss call."""
+    L = _lib.lib()
+    p = prob(N=1000, d=64, V=3000, K=10, chunk=256)
+    need = L.kd_chunked_workspace_bytes(ctypes.byref(p))
+    base = 0x100000
+    zp, ld = ctypes.c_void_p(0), ctypes.c_int64(0)
+    assert L.kd_chunked_logits(ctypes.byref(p), ctypes.c_void_p(base), need, ctypes.byref(zp), ctypes.byref(ld)) == 0
+    assert ld.value >= 1000 and ld.value % 4 == 0
+    off = zp.value - base
+    assert off % 256 == 0 and off + 3072 * ld.value * 4 <= need
+    assert L.kd_chunked_logits(ctypes.byref(p), ctypes.c_void_p(base), need - 1, ctypes.byref(zp),
+                               ctypes.byref(ld)) == 5
+    assert L.kd_chunked_logits(ctypes.byref(p), None, need, ctypes.byref(zp), ctypes.byref(ld)) == 1
+    assert L.kd_chunked_logits(ctypes.byref(prob(K=0)), ctypes.c_void_p(base), need, ctypes.byref(zp),
+                               ctypes.byref(ld)) == 2
 
 
 @pytest.mark.parametrize("K", [0, -3, 11, 2000])

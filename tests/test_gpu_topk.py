@@ -69,6 +69,45 @@ def test_ties_and_special_values(dtype):
         check(x, K, dtype, f"ties/special K={K}")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("V", [1000, 201088])
+def test_nan_rows(dtype, V):
+    """Rows with NaN: scattered, all NaN, NaN next to +-inf, fewer than K numbers, NaN of either
+    sign. NaN ranks below every number (-inf included), NaN among NaN by the lower id; the
+    oracle's order is pinned to that. Ids bit for bit, values as copies of the chosen entries."""
+    g = np.random.default_rng(16)
+    nan, nneg = np.float32(np.nan), -np.float32(np.nan)
+    rows = []
+    r = (g.standard_normal(V) * 3).astype(np.float32)
+    r[g.choice(V, V // 10, replace=False)] = nan                    # scattered NaN
+    rows.append(r)
+    rows.append(np.full(V, nan, np.float32))                         # every entry NaN
+    r = g.standard_normal(V).astype(np.float32)
+    r[:6] = [nan, np.inf, -np.inf, nneg, np.inf, -np.inf]              # NaN next to +-inf
+    r[g.choice(np.arange(6, V), 30, replace=False)] = nan
+    rows.append(r)
+    r = np.full(V, nneg, np.float32)
+    r[g.choice(V, 40, replace=False)] = g.integers(-2, 3, 40)         # 40 numbers with ties, rest NaN
+    rows.append(r)
+    r = g.standard_normal(V).astype(np.float32)
+    r[V // 2:] = nan                                                   # NaN tail
+    rows.append(r)
+    x = np.stack(rows)
+    store = datagen.bf16_bits(x) if dtype == "bf16" else x
+    dev = to_torch(store)
+    for K in (1, 7, 100, 1000):
+        say("topk NaN rows", dtype, f"V={V} K={K}")
+        idx, vals = kd.topk_cache(dev, K)
+        torch.cuda.synchronize()
+        xv = datagen.bf16_to_f32(store) if dtype == "bf16" else x
+        want_idx, _ = oracle.topk_cache(xv, K)
+        assert np.array_equal(idx.cpu().numpy(), want_idx), K
+        want_bits = np.take_along_axis(store, want_idx.astype(np.int64), 1)
+        got = vals.cpu()
+        got_bits = got.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else got.numpy()
+        assert np.array_equal(got_bits.view(want_bits.dtype).view(np.uint8), want_bits.view(np.uint8)), K
+
+
 def test_k_limits_and_padded_rows():
     g = np.random.default_rng(13)
     x = bf16_values(g.standard_normal((8, 3000)))
