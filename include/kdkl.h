@@ -81,8 +81,9 @@ extern "C" {
 
 /* 1: first release. 2: kd_validate_ids added; chunks capped at 2^20 rows; kd_dense_kl limited
  * to V <= 2^21. 3: KD_LOW_MEMORY and kd_chunked_logits added; a -inf teacher logit counts as a
- * masked entry. Calls and structures of earlier versions are unchanged. */
-#define KDKL_ABI_VERSION 3
+ * masked entry. 4: kd_fused_kl_fwd_noalloc added. Calls and structures of earlier versions are
+ * unchanged. */
+#define KDKL_ABI_VERSION 4
 
 /* Same type as hipStream_t; declared here so that this header does not need the HIP headers. */
 typedef struct ihipStream_t* kd_stream;
@@ -175,6 +176,27 @@ size_t kd_fused_workspace_bytes(const kd_problem* p);
 kd_status kd_fused_kl_fwd(const kd_problem* p, const void* H, const void* W, const int32_t* idx,
                           const void* tlog, float* loss, float* lse, float* row_kl, float* zk,
                           void* ws, size_t ws_bytes, kd_stream stream);
+
+/*
+ * The fused forward for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation. Same arguments, checks and
+ * results as kd_fused_kl_fwd (the same kernels run, bit for bit), without ws and ws_bytes: the
+ * forward's workspace is a static device array of KD_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU, held from the library's first use on that GPU until the process ends. The call
+ * allocates nothing; the caller passes every input and output.
+ *   Limit: the forward's share of kd_fused_workspace_bytes(p) (O(N*K + N) bytes: at K = 100 about
+ *   900 bytes a row, so N up to about 65,000 rows) must fit in KD_NOALLOC_SCRATCH_BYTES, else
+ *   KD_ERR_WORKSPACE with nothing enqueued. KD_VALIDATE_IDX gives KD_ERR_VALUE (it copies to the
+ *   host and waits; run kd_validate_ids first instead).
+ *   Calls on one GPU share its array: calls that overlap in time on one GPU (different streams
+ *   or threads, unsynchronised) race and give undefined results. Nothing in the array needs to
+ *   start at zero, so the contents an earlier call leaves do not matter.
+ *   KD_ERR_HIP if the array's device address cannot be obtained.
+ */
+#define KD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kd_status kd_fused_kl_fwd_noalloc(const kd_problem* p, const void* H, const void* W, const int32_t* idx,
+                                  const void* tlog, float* loss, float* lse, float* row_kl, float* zk,
+                                  kd_stream stream);
 
 /*
  * Fused backward: recomputes each chunk's logits instead of storing them.

@@ -26,6 +26,7 @@ __all__ = [
     "FusedKL",
     "fused_kl",
     "fused_kl_fwd",
+    "fused_kl_fwd_noalloc",
     "fused_kl_bwd",
     "dense_kl",
     "chunked_kl",
@@ -149,6 +150,22 @@ def fused_kl_fwd(H, W, idx, tlog, T: float = 1.0, chunk: int = 2048, n_norm: flo
                                       _ptr(lse), _ptr(row_kl), _ptr(zk), _ptr(ws), ws_bytes, _stream(dev))
     _lib.check(code, "kd_fused_kl_fwd")
     return FwdOut(loss, lse, row_kl, zk)
+
+
+def fused_kl_fwd_noalloc(H, W, idx, tlog, loss, lse, row_kl=None, zk=None, T: float = 1.0, chunk: int = 2048,
+                         n_norm: float = 0.0, flags: int = 0) -> None:
+    """kd_fused_kl_fwd_noalloc: the fused forward into caller-owned outputs (loss [] fp32,
+    lse [N] fp32, optionally row_kl [N] and zk [N,K] fp32), with the library's static device
+    scratch as its workspace. Neither this binding nor the library allocates device memory."""
+    dev = _need_device(H, W, idx, tlog, loss, lse, row_kl, zk)
+    p = make_problem(H, W, idx, tlog, T, chunk, n_norm, flags)
+    for name, t, shape in (("loss", loss, ()), ("lse", lse, (p.N,)), ("row_kl", row_kl, (p.N,)),
+                           ("zk", zk, (p.N, p.K))):
+        if t is not None and (t.dtype != torch.float32 or tuple(t.shape) != shape):
+            raise KdError(3, "fused_kl_fwd_noalloc", f"{name} must be float32 of shape {shape}")
+    code = _lib.lib().kd_fused_kl_fwd_noalloc(ctypes.byref(p), _ptr(H), _ptr(W), _ptr(idx), _ptr(tlog), _ptr(loss),
+                                              _ptr(lse), _ptr(row_kl), _ptr(zk), _stream(dev))
+    _lib.check(code, "kd_fused_kl_fwd_noalloc")
 
 
 def fused_kl_bwd(H, W, idx, tlog, lse, grad_loss=None, T: float = 1.0, chunk: int = 2048,

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libkdkl.so")
 
 KD_FP32, KD_BF16 = 0, 1
 KD_VALIDATE_IDX, KD_ACCUMULATE_DW, KD_SKIP_DW, KD_LOW_MEMORY = 0x1, 0x2, 0x4, 0x8
+KD_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 STATUS = {
     0: "KD_OK",
@@ -33,6 +34,7 @@ EXPORTS = (
     "kd_status_str",
     "kd_fused_workspace_bytes",
     "kd_fused_kl_fwd",
+    "kd_fused_kl_fwd_noalloc",
     "kd_fused_kl_bwd",
     "kd_dense_workspace_bytes",
     "kd_dense_kl",
@@ -96,6 +98,8 @@ def lib() -> ctypes.CDLL:
     L.kd_dense_workspace_bytes.argtypes = [P]
     L.kd_fused_kl_fwd.restype = ctypes.c_int
     L.kd_fused_kl_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.kd_fused_kl_fwd_noalloc.restype = ctypes.c_int
+    L.kd_fused_kl_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     L.kd_fused_kl_bwd.restype = ctypes.c_int
     L.kd_fused_kl_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.kd_dense_kl.restype = ctypes.c_int

@@ -11,17 +11,24 @@
 //             and dW += G_c^T H_c.
 // So peak memory depends on the sequence only through H, dH and the O(N*K) cache terms.
 
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "kdkl.h"
 #include "kdkl_internal.h"
 
 using namespace kdkl;
+
+// Device scratch of kd_fused_kl_fwd_noalloc: the forward's workspace for callers that cannot
+// allocate. Every GPU the library runs on holds its own copy until the process ends. Host code
+// never passes this name to a kernel or a copy (on the host it is only a stand-in for the
+// symbol); it uses the per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[KD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -288,6 +295,56 @@ kd_status stored_backward(const kd_problem* p, const Shape& sh, const StoredWs& 
     return KD_OK;
 }
 
+// The forward's launches, once the arguments have been checked; ws holds at least the
+// forward's part of the fused workspace layout.
+kd_status fused_forward(const kd_problem* p, const void* H, const void* W, const int32_t* idx, const void* tlog,
+                        float* loss, float* lse, float* row_kl, float* zk, void* ws, hipStream_t s) {
+    (void)hipGetLastError();  // start from a clean error state
+    const Shape sh = make_shape(p);
+    const FusedWs w = layout_fused(p, ws);
+    if (p->flags & KD_VALIDATE_IDX) {
+        const kd_status st = validate_ids(p, idx, w.status, s);
+        if (st != KD_OK) return st;
+    }
+    float* zk_out = zk ? zk : w.zk;
+    KD_TRY(launch_plan(idx, 0, p->N, p->K, p->V, w.plan_off, w.plan_ent, s));
+    KD_TRY(launch_fwd(sh, H, W, w.plan_off, w.plan_ent, w.n_vsplit, w.part, zk_out, nullptr, 0, s));
+    int n_blk = 0;
+    KD_TRY(launch_combine(sh, w.part, 2 * w.n_vsplit, zk_out, tlog, lse, row_kl, w.blk_sum, &n_blk, s));
+    KD_TRY(launch_loss_final(sh, w.blk_sum, n_blk, loss, s));
+    return KD_OK;
+}
+
+// Argument checks shared by the two forward entry points (nothing is enqueued).
+kd_status check_forward(const kd_problem* p, const void* H, const void* W, const int32_t* idx, const void* tlog,
+                        const float* loss, const float* lse) {
+    const kd_status st = check_problem(p);
+    if (st != KD_OK) return st;
+    if (!H || !W || !idx || !tlog || !loss || !lse) return KD_ERR_NULL;
+    if (!aligned(H, 16) || !aligned(W, 16)) return KD_ERR_VALUE;
+    return KD_OK;
+}
+
+// Address of `scratch` on the current device, looked up once per device with that device
+// current (each GPU holds its own copy of the array at its own address).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+kd_status scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KD_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return KD_ERR_INTERNAL;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return KD_ERR_HIP;
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = g_scratch_dev[dev];
+    return KD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -323,26 +380,26 @@ size_t kd_dense_workspace_bytes(const kd_problem* p) {
 kd_status kd_fused_kl_fwd(const kd_problem* p, const void* H, const void* W, const int32_t* idx, const void* tlog,
                           float* loss, float* lse, float* row_kl, float* zk, void* ws, size_t ws_bytes,
                           kd_stream stream) {
-    kd_status st = check_problem(p);
+    const kd_status st = check_forward(p, H, W, idx, tlog, loss, lse);
     if (st != KD_OK) return st;
-    if (!H || !W || !idx || !tlog || !loss || !lse || !ws) return KD_ERR_NULL;
-    if (!aligned(H, 16) || !aligned(W, 16)) return KD_ERR_VALUE;
+    if (!ws) return KD_ERR_NULL;
     if (!aligned(ws, kAlign) || ws_bytes < kd_fused_workspace_bytes(p)) return KD_ERR_WORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
-    (void)hipGetLastError();  // start from a clean error state
-    const Shape sh = make_shape(p);
-    const FusedWs w = layout_fused(p, ws);
-    if (p->flags & KD_VALIDATE_IDX) {
-        st = validate_ids(p, idx, w.status, s);
-        if (st != KD_OK) return st;
-    }
-    float* zk_out = zk ? zk : w.zk;
-    KD_TRY(launch_plan(idx, 0, p->N, p->K, p->V, w.plan_off, w.plan_ent, s));
-    KD_TRY(launch_fwd(sh, H, W, w.plan_off, w.plan_ent, w.n_vsplit, w.part, zk_out, nullptr, 0, s));
-    int n_blk = 0;
-    KD_TRY(launch_combine(sh, w.part, 2 * w.n_vsplit, zk_out, tlog, lse, row_kl, w.blk_sum, &n_blk, s));
-    KD_TRY(launch_loss_final(sh, w.blk_sum, n_blk, loss, s));
-    return KD_OK;
+    return fused_forward(p, H, W, idx, tlog, loss, lse, row_kl, zk, ws, (hipStream_t)stream);
+}
+
+kd_status kd_fused_kl_fwd_noalloc(const kd_problem* p, const void* H, const void* W, const int32_t* idx,
+                                  const void* tlog, float* loss, float* lse, float* row_kl, float* zk,
+                                  kd_stream stream) {
+    kd_status st = check_forward(p, H, W, idx, tlog, loss, lse);
+    if (st != KD_OK) return st;
+    // KD_VALIDATE_IDX copies a status word to the host and waits for it; kd_validate_ids is the
+    // check that needs neither.
+    if (p->flags & KD_VALIDATE_IDX) return KD_ERR_VALUE;
+    if (layout_fused(p, nullptr).fwd_bytes > KD_NOALLOC_SCRATCH_BYTES) return KD_ERR_WORKSPACE;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != KD_OK) return st;
+    return fused_forward(p, H, W, idx, tlog, loss, lse, row_kl, zk, ws, (hipStream_t)stream);
 }
 
 kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, const int32_t* idx, const void* tlog,
