@@ -7,31 +7,37 @@
 // backward pass recomputes each piece. The teacher side is the top-K cache from the
 // paragraph on the first fix.
 //
-// Everything here is built on one MFMA tile engine. A workgroup of 256 threads (four
-// 64-wide waves in a 2x2 grid) computes a 256 x 256 fp32 tile of C = A B^T:
-//   - each wave owns 128 x 128 as 4 x 4 blocks of v_mfma_f32_32x32x16_bf16
-//     (v_mfma_f32_32x32x2_f32 for fp32 inputs);
-//   - both operands are staged through LDS, double-buffered over K, in 16-byte chunks;
-//   - the chunk position is XOR-swizzled by row so that fragment reads and tile writes are
-//     free of bank conflicts.
-// An operand stored with K contiguous is copied chunk by chunk. An operand stored with its
-// M/N index contiguous (W in dH = G W; G and H in dW = G^T H) is loaded as 8x8 (bf16) or
-// 4x4 (fp32) blocks and transposed in registers on the way to LDS. So every GEMM of the
-// path reads K-contiguous fragments, and no transposed copy of W, H or G is ever made.
+// Every GEMM-shaped kernel runs on the MFMA tile engine of engine.h. A workgroup owns a fp32
+// tile of C = A B^T with its accumulators in registers:
+//   - forward and gradient kernels: 256 x 256, eight 64-wide waves in a 2 x 4 grid, each wave
+//     128 x 64 as 8 x 4 blocks of v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x4_f32 for fp32);
+//   - dH and dW: 256 x 320 (the hidden size on the 320 side), eight waves of 128 x 80;
+//   - the dense comparison path and the memory-lean backward: 256 x 256 on four waves of
+//     32x32x16 blocks.
+// Operands reach LDS straight from memory (buffer_load ... lds) in 16-byte chunks, XOR-swizzled
+// by row so that fragment reads are free of bank conflicts, four stages of half a K step deep.
+// Every operand of the fast path is K contiguous. Where the natural layout is not, a copy is
+// made: W^T once per backward call (K-blocked, for dH = G W), H_c^T per chunk and G_c^T from the
+// gradient tile (for dW = G^T H). The dense and memory-lean paths read M/N-contiguous operands
+// through registers instead (8 x 8 bf16 blocks transposed on the way to LDS).
 //
 // Epilogues:
-//   forward   online (max, sum) per row in the log2 domain, reduced across lanes with a
-//             reduce-scatter butterfly; gather of z at the cached ids through an LDS-staged
-//             copy of the tile;
-//   backward  G = g*T/n_norm*(softmax(z/T) - P_t), with P_t subtracted in the LDS-staged
-//             tile, then stored row-major in the activation dtype;
-//   dH        fp32 split-K partials or a direct store;
-//   dW        fp32 read-modify-write.
+//   forward   logit tiles are computed transposed (vocabulary x tokens), so each lane keeps the
+//             running (max, sum) of its token columns in the log2 domain without shuffles; the
+//             gather of z at the cached ids goes through an LDS-staged half tile;
+//   backward  G = g*T/n_norm*(softmax(z/T) - P_t), P_t subtracted in the LDS-staged tile, then
+//             stored twice in the activation dtype: K-blocked G_c for dH and G_c^T for dW;
+//   dH        fp32 split-K partials, reduced in a fixed order, or a direct store;
+//   dW        fp32 read-modify-write through LDS.
+// Hand-offs of staged LDS data inside an epilogue use an LDS-only barrier: a full workgroup
+// barrier would also wait for the global stores already issued.
 //
 // MFMA lane layouts (checked on gfx950 hardware):
 //   32x32x16 bf16: lane l supplies A[m = l%32][k = 8*(l/32) + 0..7], B likewise with n.
 //   32x32x2 f32:   lane l supplies A[m = l%32][k = l/32].
 //   Accumulator element e of lane l: row 8*(e/4) + 4*(l/32) + e%4, column l%32.
+//   16x16x32 bf16: lane l supplies A[m = l%16][k = 8*(l/16) + 0..7]; accumulator element v of
+//                  lane l: row 4*(l/16) + v, column l%16.
 
 #include <hip/hip_runtime.h>
 
@@ -540,7 +546,7 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
         float& x = stage[st_idx(st_row(c), r)];
         x = fmaf(-gs, a.pt[(r0 + r) * a.K + k], x);
     }
-    __syncthreads();
+    lds_barrier();
     // G rows: group g of 8 vocabulary entries (stage rows 8g .. 8g+7) by a group of 4 tokens.
     // A lane reads the 8 x 4 block with 16-byte LDS reads (4 tokens of one stage row each) and
     // writes the 4 tokens' 8-entry segments; 16 consecutive lanes cover one token's 128
@@ -581,7 +587,7 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
 }
 
 template <typename T, int NW>
@@ -648,7 +654,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
                     }
                 }
             }
-            __syncthreads();
+            lds_barrier();
             grad_pass_out<T, NW>(a, stage, pq, ie, vt, r0, n0, e0, e1, my_en, my_pt, gs);
         }
     }
@@ -727,7 +733,7 @@ __global__ __launch_bounds__(256, 2) void k_grad_z(GradArgs a) {
             }
             *(f32x4*)(stage + st_idx(sr, tok)) = g;
         }
-        __syncthreads();
+        lds_barrier();
         // gs*p_t at the cached ids whose vocabulary row is in this pass (bits 6-7 of the column)
         if (my_en != 0xffffffffu && ((my_en >> 14) & 3) == (uint32_t)pq) {
             const int r = my_en & 255, c = (my_en >> 8) & 255;
@@ -742,7 +748,7 @@ __global__ __launch_bounds__(256, 2) void k_grad_z(GradArgs a) {
             float& x = stage[st_idx(c & 63, r)];
             x = fmaf(-gs, a.pt[(r0 + r) * a.K + k], x);
         }
-        __syncthreads();
+        lds_barrier();
         // G rows: token tl, group g of 8 vocabulary entries; 8 lanes write a token's 64 entries
         // of the pass, one 128-byte line.
 #pragma unroll 4
@@ -774,12 +780,12 @@ __global__ __launch_bounds__(256, 2) void k_grad_z(GradArgs a) {
                 }
             }
         }
-        __syncthreads();
+        lds_barrier();
     };
     f32x4 za[IT], zb[IT];
     load(0, za);
     load(1, zb);
-    __syncthreads();  // lse2
+    lds_barrier();  // lse2
     pass(0, za);
     load(2, za);
     pass(1, zb);
@@ -1030,11 +1036,11 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
                 for (int j = 0; j < JN; ++j)
                     stage[st_idx(sr, ie.wn * 128 + j * 32 + ie.lr)] = acc[2 * pq + ii][j][e];
             }
-        __syncthreads();
+        lds_barrier();
         load_old(pq, 1, old1);
         add_store(pq, 0, old0);
         add_store(pq, 1, old1);
-        __syncthreads();
+        lds_barrier();
     }
 }
 
@@ -1107,14 +1113,14 @@ __global__ __launch_bounds__(512, 1) void k_dw_w(DwArgs a) {
                 for (int j = 0; j < 5; ++j)
                     stage[sr * kWSS + ie.wn * 80 + 16 * j + (ie.lane & 15)] = acc[2 * p + i2][j][e];
             }
-        __syncthreads();
+        lds_barrier();
         if (acc_old) load_old(p, 1, old1);
         else
 #pragma unroll
             for (int k = 0; k < IB; ++k) old1[k] = f32x4{0.f, 0.f, 0.f, 0.f};
         add_store(p, 0, old0);
         add_store(p, 1, old1);
-        __syncthreads();
+        lds_barrier();
     }
 }
 
