@@ -1273,10 +1273,31 @@ __device__ __forceinline__ uint32_t fp32_bits(T x);
 template <> __device__ __forceinline__ uint32_t fp32_bits<bf16_t>(bf16_t x) { return (uint32_t)x << 16; }
 template <> __device__ __forceinline__ uint32_t fp32_bits<float>(float x) { return __float_as_uint(x); }
 
+// Largest of the entries of a 16-byte chunk, as fp32 (a NaN entry is ignored unless all are NaN).
+template <typename T>
+__device__ __forceinline__ float chunk_max(const u32x4& c) {
+    if constexpr (sizeof(T) == 2) {
+        const float a = fmaxf(__uint_as_float(c[0] << 16), __uint_as_float(c[0] & 0xFFFF0000u));
+        const float b = fmaxf(__uint_as_float(c[1] << 16), __uint_as_float(c[1] & 0xFFFF0000u));
+        const float e = fmaxf(__uint_as_float(c[2] << 16), __uint_as_float(c[2] & 0xFFFF0000u));
+        const float f = fmaxf(__uint_as_float(c[3] << 16), __uint_as_float(c[3] & 0xFFFF0000u));
+        return fmaxf(fmaxf(a, b), fmaxf(e, f));
+    } else {
+        return fmaxf(fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1])),
+                     fmaxf(__uint_as_float(c[2]), __uint_as_float(c[3])));
+    }
+}
+
+struct KeepAll {
+    __device__ __forceinline__ bool operator()(float) const { return true; }
+};
+
 // Calls f(v, bits) for every entry of row x[0..V) handled by this thread, with 16-byte loads
-// for the aligned body; j counts this thread's loads (for the group choice).
-template <typename T, typename F>
-__device__ __forceinline__ void topk_scan(const T* x, int V, F&& f) {
+// for the aligned body; j counts this thread's loads (for the group choice). With a `keep`
+// test, the entries of a body chunk are visited only if keep(largest entry of the chunk) holds:
+// a caller that wants the entries >= L skips whole chunks below L with one comparison.
+template <typename T, typename F, typename Keep = KeepAll>
+__device__ __forceinline__ void topk_scan(const T* x, int V, F&& f, Keep keep = Keep()) {
     constexpr int VEC = 16 / sizeof(T);
     const int tid = threadIdx.x;
     const int head = (int)(((16 - ((uintptr_t)x & 15)) & 15) / sizeof(T));
@@ -1285,6 +1306,7 @@ __device__ __forceinline__ void topk_scan(const T* x, int V, F&& f) {
     const int nvec = (V - h) / VEC;
     const u32x4* xv = (const u32x4*)(x + h);
     auto each = [&](const u32x4& c, int q, int j) {
+        if (!keep(chunk_max<T>(c))) return;
         const int v0 = h + q * VEC;
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -1311,10 +1333,11 @@ __device__ __forceinline__ void topk_scan(const T* x, int V, F&& f) {
     for (int v = h + nvec * VEC + tid; v < V; v += NTHR) f(v, fp32_bits<T>(x[v]), 0);
 }
 
-// Largest value of each of m interleaved groups of this thread's entries (load j of the thread
-// goes to group j % m), eight 16-byte loads in flight per lane.
-template <typename T>
-__device__ __forceinline__ void topk_scan_max(const T* x, int V, int m, float (&gmax)[kTopkMaxGroups]) {
+// Largest value of each of M interleaved groups of this thread's entries (load j of the thread
+// goes to group j % M), eight 16-byte loads in flight per lane. M is a power of two up to 8, so
+// within a batch of eight loads the group of each is known at compile time.
+template <typename T, int M>
+__device__ __forceinline__ void topk_scan_max(const T* x, int V, float (&gmax)[kTopkMaxGroups]) {
     constexpr int VEC = 16 / sizeof(T);
     const int tid = threadIdx.x;
     const int head = (int)(((16 - ((uintptr_t)x & 15)) & 15) / sizeof(T));
@@ -1322,42 +1345,20 @@ __device__ __forceinline__ void topk_scan_max(const T* x, int V, int m, float (&
     if (tid < h) gmax[0] = fmaxf(gmax[0], __uint_as_float(fp32_bits<T>(x[tid])));
     const int nvec = (V - h) / VEC;
     const u32x4* xv = (const u32x4*)(x + h);
-    auto vmax = [](const u32x4& c) {
-        float r;
-        if constexpr (sizeof(T) == 2) {
-            float a = fmaxf(__uint_as_float(c[0] << 16), __uint_as_float(c[0] & 0xFFFF0000u));
-            float b = fmaxf(__uint_as_float(c[1] << 16), __uint_as_float(c[1] & 0xFFFF0000u));
-            float e = fmaxf(__uint_as_float(c[2] << 16), __uint_as_float(c[2] & 0xFFFF0000u));
-            float f = fmaxf(__uint_as_float(c[3] << 16), __uint_as_float(c[3] & 0xFFFF0000u));
-            r = fmaxf(fmaxf(a, b), fmaxf(e, f));
-        } else {
-            r = fmaxf(fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1])),
-                      fmaxf(__uint_as_float(c[2]), __uint_as_float(c[3])));
-        }
-        return r;
-    };
     int j = 0;
     int q = tid;
-    for (; q + 7 * NTHR < nvec; q += 8 * NTHR) {
+    for (; q + 7 * NTHR < nvec; q += 8 * NTHR, j += 8) {
         u32x4 c[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) c[u] = xv[q + u * NTHR];
-        float r[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) r[u] = vmax(c[u]);
-#pragma unroll
-        for (int u = 0; u < 8; ++u, ++j) {
-            const int g = j % m;
-#pragma unroll
-            for (int t = 0; t < kTopkMaxGroups; ++t)
-                if (t == g) gmax[t] = fmaxf(gmax[t], r[u]);
-        }
+        for (int u = 0; u < 8; ++u) gmax[u % M] = fmaxf(gmax[u % M], chunk_max<T>(c[u]));
     }
     for (; q < nvec; q += NTHR, ++j) {
-        const float r = vmax(xv[q]);
-        const int g = j % m;
+        const float r = chunk_max<T>(xv[q]);
+        const int g = j & (M - 1);
 #pragma unroll
-        for (int t = 0; t < kTopkMaxGroups; ++t)
+        for (int t = 0; t < M; ++t)
             if (t == g) gmax[t] = fmaxf(gmax[t], r);
     }
     for (int v = h + nvec * VEC + tid; v < V; v += NTHR) gmax[0] = fmaxf(gmax[0], __uint_as_float(fp32_bits<T>(x[v])));
@@ -1403,11 +1404,17 @@ __global__ __launch_bounds__(256) void k_topk(const T* __restrict__ X, int64_t l
     // work on fp32 values (max and compare treat -0 as +0, as the key does); only the
     // collected entries get their 54-bit keys.
     {
-        const int m = min(kTopkMaxGroups, max(1, (4 * K + NTHR - 1) / NTHR));
+        int m = 1;  // groups per thread: the power of two with 256 m >= 4K, at most 8
+        while (m < kTopkMaxGroups && NTHR * m < 4 * K) m <<= 1;
         float gmax[kTopkMaxGroups];
 #pragma unroll
         for (int g = 0; g < kTopkMaxGroups; ++g) gmax[g] = -INFINITY;
-        topk_scan_max<T>(x, V, m, gmax);
+        switch (m) {
+            case 1: topk_scan_max<T, 1>(x, V, gmax); break;
+            case 2: topk_scan_max<T, 2>(x, V, gmax); break;
+            case 4: topk_scan_max<T, 4>(x, V, gmax); break;
+            default: topk_scan_max<T, 8>(x, V, gmax); break;
+        }
         const int G = NTHR * m;  // <= 2048 <= kTopkSort
         int P = 1;
         while (P < G) P <<= 1;
@@ -1422,12 +1429,15 @@ __global__ __launch_bounds__(256) void k_topk(const T* __restrict__ X, int64_t l
         const float L = __uint_as_float(Lk & 0x80000000u ? (Lk & 0x7FFFFFFFu) : ~Lk);
         if (tid == 0) s_ncoll = 0;
         __syncthreads();
-        topk_scan<T>(x, V, [&](int v, uint32_t bits, int) {
-            if (__uint_as_float(bits) >= L) {
-                const int pos = atomicAdd(&s_ncoll, 1);
-                if (pos < kTopkSort) cand[pos] = topk_ck(v, bits);
-            }
-        });
+        topk_scan<T>(
+            x, V,
+            [&](int v, uint32_t bits, int) {
+                if (__uint_as_float(bits) >= L) {
+                    const int pos = atomicAdd(&s_ncoll, 1);
+                    if (pos < kTopkSort) cand[pos] = topk_ck(v, bits);
+                }
+            },
+            [L](float mx) { return mx >= L; });
         __syncthreads();
         nc = s_ncoll;
         done = nc >= K && nc <= kTopkSort;  // fewer than K only if NaNs were skipped
