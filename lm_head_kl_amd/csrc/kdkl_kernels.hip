@@ -1368,11 +1368,14 @@ __device__ __forceinline__ uint64_t topk_ck(int v, uint32_t bits) {
     return ((uint64_t)order_key(bits) << 22) | (uint64_t)(0x3FFFFF - v);
 }
 
-// Bitonic sort of a[0..P) descending (P a power of two), by all threads of the block.
+// Bitonic sort of a[0..P) descending (P a power of two), by all NT threads of the block. With
+// LDS_ONLY the steps are separated by barriers that wait for this wave's LDS operations only, so
+// global loads issued before the sort stay in flight through it.
+template <int NT = NTHR, bool LDS_ONLY = false>
 __device__ __forceinline__ void bitonic_desc(uint64_t* a, int P) {
     for (int size = 2; size <= P; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int i = threadIdx.x; i < P / 2; i += NTHR) {
+            for (int i = threadIdx.x; i < P / 2; i += NT) {
                 const int lo = 2 * i - (i & (stride - 1));
                 const int hi = lo + stride;
                 const bool desc = (lo & size) == 0;
@@ -1382,20 +1385,47 @@ __device__ __forceinline__ void bitonic_desc(uint64_t* a, int P) {
                     a[hi] = a0;
                 }
             }
-            __syncthreads();
+            if constexpr (LDS_ONLY)
+                lds_barrier();
+            else
+                __syncthreads();
         }
     }
 }
 
+// Bitonic sort of a[0..P) descending (P a power of two) by one wave, with no barriers: the LDS
+// runs one wave's accesses in issue order, so each step sees the previous step's writes.
+__device__ __forceinline__ void wave_bitonic_desc(uint64_t* a, int P) {
+    const int lane = threadIdx.x & 63;
+    for (int size = 2; size <= P; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int i = lane; i < P / 2; i += 64) {
+                const int lo = 2 * i - (i & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t a0 = a[lo], a1 = a[hi];
+                const bool swap = (a0 < a1) == desc;
+                a[lo] = swap ? a1 : a0;
+                a[hi] = swap ? a0 : a1;
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+// With only_flagged, a workgroup handles its row only if k_topk_reg left the row's first id at
+// -1 (the rows whose register-held bound did not settle them); the others keep their output.
 template <typename T>
 __global__ __launch_bounds__(256) void k_topk(const T* __restrict__ X, int64_t ld, int64_t N, int V, int K,
-                                              int32_t* __restrict__ idx_out, T* __restrict__ val_out) {
+                                              int32_t* __restrict__ idx_out, T* __restrict__ val_out,
+                                              int only_flagged) {
     __shared__ uint32_t hist[2][kTopkBins];  // two copies (waves 0, 2 and 1, 3): 49 KB of LDS, three rows per CU
     __shared__ uint64_t cand[kTopkSort];
     __shared__ uint32_t wsum[NTHR];
     __shared__ int s_bin, s_above, s_cnt, s_ncoll;
     const int tid = threadIdx.x, w = tid >> 6;
     const int64_t n = blockIdx.x;
+    if (only_flagged && idx_out[n * K] != -1) return;
     const T* x = X + n * ld;
     int nc = 0;
     bool done = false;
@@ -1516,6 +1546,259 @@ __global__ __launch_bounds__(256) void k_topk(const T* __restrict__ X, int64_t l
         const int v = 0x3FFFFF - (int)(cand[k] & 0x3FFFFFull);
         idx_out[n * K + k] = v;
         val_out[n * K + k] = x[v];
+    }
+}
+
+// One read of each row: a persistent grid, one workgroup of kTkrThreads per CU, holds a whole row
+// on chip. Thread t owns the 16-byte chunks t, t + 512, ... of the row, up to kTkrChunks of them
+// (204,800 bf16 or 102,400 fp32 entries); the last kTkrLds of its slots are loaded straight into
+// LDS, the others into registers. Per row:
+//   1. as the chunks land, each one's largest entry goes to LDS and into the thread's largest
+//      entry. Each wave finds the t-th largest of its 64 thread maxima, t = ceil(K / 8), and the
+//      bound L is the least of the 8 waves' values. Every wave has t threads whose largest entry
+//      is >= its value >= L, so at least 8 t >= K entries of the row are >= L: L bounds the K-th
+//      largest value from below;
+//   2. the chunks whose largest entry is >= L are copied to an LDS list, and the block takes the
+//      list apart into the candidates, the entries >= L (all of the row's top K among them);
+//   3. the next row's loads are issued into the same registers and LDS slots, and while they are
+//      in flight each candidate counts the candidates with a larger key. That count is its place
+//      in the output, which it writes if the count is below K.
+// Appends to the LDS lists take their places from a prefix count over the wave and one atomic
+// per wave, and step 3 needs no barrier: the next row's first barrier orders the reuse of the
+// lists. A row with fewer than K candidates (NaN), more than the buffers hold (many equal values)
+// or a bound of -inf is left with its first id at -1; k_topk then redoes those rows exactly.
+constexpr int kTkrThreads = 512, kTkrChunks = 50, kTkrCand = 1024, kTkrList = 1024, kTkrMaxK = 128;
+constexpr int kTkrLds = 6;  // slots loaded into LDS
+constexpr int kNonTemporal = 2;  // cache-policy operand of a buffer load: non-temporal
+
+// The pass's sort key: the 54-bit order (value, then lower id first) moved up one bit, and a last
+// bit that marks a -0 entry, which the order ranks with +0. Keys stay distinct and ordered as
+// before, and the stored value can be rebuilt from the key.
+__device__ __forceinline__ uint64_t tkr_key(int v, uint32_t bits) {
+    return (topk_ck(v, bits) << 1) | (uint64_t)(bits == 0x80000000u);
+}
+
+// Exclusive prefix sum over the wave of a count below 2^NB, and the wave's total, from one ballot
+// per bit (all lanes active).
+template <int NB>
+__device__ __forceinline__ int wave_prefix(int cnt, int& total) {
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const uint64_t m = __ballot((cnt >> b) & 1);
+        pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+        tot += __popcll(m) << b;
+    }
+    total = tot;
+    return pre;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kTkrThreads, 1) void k_topk_reg(const T* __restrict__ X, int64_t ld, int64_t N, int V,
+                                                             int K, int32_t* __restrict__ idx_out,
+                                                             T* __restrict__ val_out) {
+    constexpr int NT = kTkrThreads, VEC = 16 / (int)sizeof(T), NW = NT / 64, S = kTkrChunks;
+    constexpr int NL = kTkrLds, NR = S - NL;  // slots in LDS, in registers
+    // A chunk's largest entry is kept as a bf16 value: exactly for bf16 rows, rounded up for fp32
+    // rows (the test against the bound then lets through a few more chunks, whose entries are
+    // compared exactly). Eight go to a 16-byte LDS vector, thread-major, so that a thread writes
+    // and reads its own with a few wide accesses.
+    constexpr int CPV = 8, CMV = (S + CPV - 1) / CPV;
+    __shared__ u32x4 lslot[NL * NT];  // slots NR .. S-1, slot-major
+    __shared__ u32x4 cmv[NT * CMV];   // chunk maxima
+    __shared__ uint64_t cand[kTkrCand];
+    __shared__ u32x4 chl[kTkrList];  // chunks holding an entry >= the bound
+    __shared__ int chq[kTkrList];    // and their positions in the row (in chunks)
+    __shared__ uint32_t wkey[NW];
+    __shared__ int s_n[2], s_nch[2];  // list lengths; rows alternate between the two pairs
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int nvec = V / VEC, tail = V - nvec * VEC;  // row bases are 16-byte aligned (host check)
+    constexpr int kFull = 16;  // slots below this hold row entries in every thread (host check:
+                               // nvec >= kTkrChunks * NT / 3)
+    const int t_w = (K + NW - 1) / NW;  // <= 64 since K <= kTkrMaxK
+    // Every slot is loaded: a slot past the row's end reads the row's last chunk again and counts
+    // as -inf. Below kFull the slot offset goes in the scalar operand; above, the whole offset is
+    // clamped in the lane's. Each load is issued as soon as its offset exists, marked
+    // non-temporal (the row is read once; streaming reads ran about 3 % faster so). Values derived
+    // from the thread index are recomputed for each row from an opaque copy of it: held across
+    // rows they would take registers the row needs.
+    u32x4 c[NR];
+    T traw;  // an entry of the row's tail (past the last whole chunk): this thread's if it has one
+    auto load = [&](int64_t r) {
+        const T* x = X + r * ld;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(x);
+        int o = tid * 16, sb = 0, last = (nvec - 1) * 16, wb = __builtin_amdgcn_readfirstlane(w) * 64;
+        asm volatile("" : "+v"(o), "+s"(sb), "+s"(last), "+s"(wb));
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+            const int so = j < kFull ? sb + j * NT * 16 : sb;
+            const int vo = j < kFull ? o : min(o + j * NT * 16, last);
+            if (j < NR)
+                c[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, so, kNonTemporal));
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lslot + (j - NR) * NT + wb), 16, vo, so, 0,
+                                                         kNonTemporal);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // unconditional and in bounds, so that nothing waits for it before the chunks are used
+        int ti = tid;
+        asm volatile("" : "+v"(ti));
+        traw = x[tail > 0 ? nvec * VEC + min(ti, tail - 1) : 0];
+    };
+    if (tid < 2) s_n[tid] = 0, s_nch[tid] = 0;
+    int64_t r = blockIdx.x;
+    int par = 0;
+    if (r < N) load(r);
+    while (r < N) {
+        // 1. chunk maxima and the thread's largest entry (NaN ignored)
+        float mx = -INFINITY;
+        uint32_t tb;  // this thread's tail entry, or -inf
+        {
+            int tq = tid;
+            asm volatile("" : "+v"(tq));
+            uint32_t pk[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int j = 0; j < S; ++j) {
+                if (j == NR) wait_vmem();  // the LDS slots, loaded last, have landed (a lane reads its own)
+                float cm = chunk_max<T>(j < NR ? c[j < NR ? j : 0] : lslot[(j - NR) * NT + tq]);
+                if (j >= kFull && tq + j * NT >= nvec) cm = -INFINITY;
+                mx = fmaxf(mx, cm);
+                const int e = j % CPV;
+                const uint32_t cb = __float_as_uint(cm);
+                uint32_t h = cb >> 16;
+                if constexpr (sizeof(T) == 4) h += (cb < 0x7F800000u && (cb & 0xFFFFu) != 0u) ? 1u : 0u;
+                pk[e / 2] = (e & 1) ? (pk[e / 2] | (h << 16)) : h;
+                if (e == CPV - 1 || j == S - 1) cmv[tq * CMV + j / CPV] = u32x4{pk[0], pk[1], pk[2], pk[3]};
+            }
+            tb = tq < tail ? fp32_bits<T>(traw) : 0xFF800000u;
+            mx = fmaxf(mx, __uint_as_float(tb));
+        }
+        // The wave's t-th largest key, bit by bit from the top: a bit is set if at least `need`
+        // lanes match the prefix with it set. bf16 values fill the top 16 bits of the key; the
+        // rest then follows from the sign (0 for non-negative values, all ones for negative).
+        const uint32_t key = order_key(__float_as_uint(mx));
+        uint32_t kw = 0;
+        {
+            int need = t_w;
+            constexpr int LOW = sizeof(T) == 2 ? 16 : 0;
+#pragma unroll
+            for (int b = 31; b >= LOW; --b) {
+                const uint32_t want = (kw >> b) | 1u;
+                const int cnt = __popcll(__ballot((key >> b) == want));
+                if (cnt >= need)
+                    kw |= 1u << b;
+                else
+                    need -= cnt;
+            }
+            if constexpr (LOW > 0) kw |= (kw & 0x80000000u) ? 0u : 0xFFFFu;
+        }
+        if (lane == 0) wkey[w] = kw;
+        lds_barrier();
+        if (tid == 0) s_n[par ^ 1] = 0, s_nch[par ^ 1] = 0;  // the next row's; the last row read them
+        uint32_t lk = wkey[0];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) lk = min(lk, wkey[i]);
+        // back to the value: keys >= 2^31 are non-negative floats (mx is never NaN, so lk > 0).
+        // A bound of -inf would take in the padding slots: such a row is left to k_topk.
+        const bool ok_bound = lk > 0x007FFFFFu;
+        const float L = ok_bound ? __uint_as_float(lk & 0x80000000u ? (lk & 0x7FFFFFFFu) : ~lk) : INFINITY;
+        // 2. chunks with an entry >= L to the list (NaN compares false) ...
+        {
+            int qb = tid;
+            asm volatile("" : "+v"(qb));
+            uint64_t pm = 0;
+            {
+                u32x4 m[CMV];
+#pragma unroll
+                for (int v = 0; v < CMV; ++v) m[v] = cmv[qb * CMV + v];
+#pragma unroll
+                for (int j = 0; j < S; ++j) {
+                    const int e = j % CPV;
+                    const uint32_t word = m[j / CPV][e / 2];
+                    const float cm = __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
+                    pm |= (uint64_t)(cm >= L) << j;
+                }
+            }
+            int total;
+            int pos = wave_prefix<6>(__popcll(pm), total);
+            int base = 0;
+            if (lane == 0 && total > 0) base = atomicAdd(&s_nch[par], total);
+            pos += __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+            for (int j = 0; j < S; ++j) {
+                if ((pm >> j) & 1) {
+                    if (pos < kTkrList) {
+                        chl[pos] = j < NR ? c[j < NR ? j : 0] : lslot[(j - NR) * NT + qb];
+                        chq[pos] = qb + j * NT;
+                    }
+                    ++pos;
+                }
+            }
+            if (qb < tail && __uint_as_float(tb) >= L) {
+                const int p = atomicAdd(&s_n[par], 1);  // at most 7 lanes, before any other append
+                cand[p] = tkr_key(nvec * VEC + qb, tb);
+            }
+        }
+        lds_barrier();
+        // ... and its entries >= L to the candidates
+        const int nch = s_nch[par];
+        for (int i0 = 0; i0 < min(nch, kTkrList); i0 += NT) {
+            const int i = i0 + tid;
+            uint32_t bits[VEC];
+            uint32_t em = 0;
+            int v0 = 0;
+            if (i < min(nch, kTkrList)) {
+                const u32x4 ch = chl[i];
+                v0 = chq[i] * VEC;
+#pragma unroll
+                for (int u = 0; u < VEC; ++u) {
+                    bits[u] = sizeof(T) == 2 ? ((u & 1) ? (ch[u / 2] & 0xFFFF0000u) : (ch[u / 2] << 16)) : ch[u];
+                    em |= (uint32_t)(__uint_as_float(bits[u]) >= L) << u;
+                }
+            }
+            int total;
+            int pos = wave_prefix<4>(__popc(em), total);
+            int base = 0;
+            if (lane == 0 && total > 0) base = atomicAdd(&s_n[par], total);
+            pos += __builtin_amdgcn_readfirstlane(base);
+#pragma unroll
+            for (int u = 0; u < VEC; ++u) {
+                if ((em >> u) & 1) {
+                    if (pos < kTkrCand) cand[pos] = tkr_key(v0 + u, bits[u]);
+                    ++pos;
+                }
+            }
+        }
+        lds_barrier();
+        const int nc = s_n[par];
+        // 3. the registers and LDS slots are free: the next row's loads go out, then the ranks.
+        const int64_t rn = r + gridDim.x;
+        if (rn < N) load(rn);
+        if (!ok_bound || nc < K || nc > kTkrCand || nch > kTkrList) {
+            if (tid == 0) idx_out[r * K] = -1;  // left to k_topk
+        } else {
+            for (int i = tid; i < nc; i += NT) {
+                const uint64_t me = cand[i];
+                int rank = 0;
+                int j = 0;
+                for (; j + 2 <= nc; j += 2) {
+                    const uint64_t a0 = cand[j], a1 = cand[j + 1];
+                    rank += (int)(a0 > me) + (int)(a1 > me);
+                }
+                if (j < nc) rank += (int)(cand[j] > me);
+                if (rank < K) {
+                    const uint32_t ok = (uint32_t)(me >> 23);
+                    const uint32_t bits = (me & 1ull) ? 0x80000000u : (ok & 0x80000000u ? ok & 0x7FFFFFFFu : ~ok);
+                    idx_out[r * K + rank] = 0x3FFFFF - (int)((me >> 1) & 0x3FFFFFull);
+                    if constexpr (sizeof(T) == 2)
+                        val_out[r * K + rank] = (bf16_t)(bits >> 16);
+                    else
+                        val_out[r * K + rank] = __uint_as_float(bits);
+                }
+            }
+        }
+        par ^= 1;
+        r = rn;
     }
 }
 
@@ -1744,12 +2027,32 @@ hipError_t launch_grad_z(const Shape& sh, const float* zt, int64_t ldzt, int64_t
 hipError_t launch_topk(Dt dt, const void* X, int64_t ld, int64_t N, int64_t V, int64_t K, int32_t* idx, void* val,
                        hipStream_t s) {
     if (N > 0x7FFFFFFF) return hipErrorInvalidValue;
+    const int64_t es = dt == Dt::BF16 ? 2 : 4, vec = 16 / es;
+    // The register-resident pass takes rows that fill at least a third of its registers and
+    // whose bases are 16-byte aligned, with K <= kTkrMaxK; the rows it cannot settle, and every
+    // other problem, go through k_topk.
+    const int64_t nvec = V / vec;
+    const bool reg = K <= kTkrMaxK && nvec <= (int64_t)kTkrThreads * kTkrChunks &&
+                     nvec * 3 >= (int64_t)kTkrThreads * kTkrChunks && ((uintptr_t)X % 16) == 0 &&
+                     (ld * es) % 16 == 0;
+    if (reg) {
+        const unsigned grid = (unsigned)std::min<int64_t>(N, device_cus());
+        if (dt == Dt::BF16)
+            KD_LAUNCH(kKindTopk, s, k_topk_reg<bf16_t>, dim3(grid), dim3(kTkrThreads), 0, s, (const bf16_t*)X, ld, N,
+                      (int)V, (int)K, idx, (bf16_t*)val);
+        else
+            KD_LAUNCH(kKindTopk, s, k_topk_reg<float>, dim3(grid), dim3(kTkrThreads), 0, s, (const float*)X, ld, N,
+                      (int)V, (int)K, idx, (float*)val);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int flagged = reg ? 1 : 0;
     if (dt == Dt::BF16)
         KD_LAUNCH(kKindTopk, s, k_topk<bf16_t>, dim3((unsigned)N), dim3(NTHR), 0, s, (const bf16_t*)X, ld, N, (int)V,
-                  (int)K, idx, (bf16_t*)val);
+                  (int)K, idx, (bf16_t*)val, flagged);
     else
         KD_LAUNCH(kKindTopk, s, k_topk<float>, dim3((unsigned)N), dim3(NTHR), 0, s, (const float*)X, ld, N, (int)V,
-                  (int)K, idx, (float*)val);
+                  (int)K, idx, (float*)val, flagged);
     return hipGetLastError();
 }
 

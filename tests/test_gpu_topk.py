@@ -177,3 +177,62 @@ def test_random_shapes(i):
     if dtype == "bf16":
         x = bf16_values(x)
     check(x, K, dtype, f"random shape {i}", ld=ld)
+
+
+def single_read_rows(g: np.random.Generator, N: int, V: int, K: int) -> np.ndarray:
+    """Rows for the single-read pass (one workgroup per CU holds a whole row on chip): the kinds
+    of ``draw_rows``, peaked rows, rows of negative values only, signed zeros among the largest
+    entries, and rows that pass it back to the exact kernel (every entry -inf, all equal, a few
+    numbers among NaN)."""
+    x = draw_rows(g, N, V, K)
+    for n in range(N):
+        kind = n % 9
+        if kind == 4:
+            x[n] = g.standard_normal(V) * 2.0
+            x[n, g.integers(0, V, 8)] += 12.0
+        elif kind == 5:
+            x[n] = -np.abs(g.standard_normal(V)) - 1.0
+        elif kind == 6:
+            x[n] = -np.abs(g.standard_normal(V)) - 0.5
+            pos = g.choice(V, size=2 * K + 3, replace=False)
+            x[n, pos] = np.where(g.random(pos.size) < 0.5, np.float32(-0.0), np.float32(0.0))
+        elif kind == 7:
+            x[n] = -np.inf if n % 2 else np.float32(0.25)
+        elif kind == 8 and n % 4 == 0:
+            x[n] = np.nan
+            x[n, g.choice(V, size=max(1, K // 2), replace=False)] = g.standard_normal(max(1, K // 2))
+    return x
+
+
+@pytest.mark.parametrize(
+    "dtype,V,K,N,pad",
+    [
+        ("bf16", 201088, 100, 300, 0),   # the gpt-oss vocabulary; more rows than CUs
+        ("bf16", 201088, 128, 40, 8),    # the largest K of the pass; padded rows
+        ("bf16", 204800, 1, 40, 0),      # the longest row it holds
+        ("bf16", 201087, 13, 40, 1),     # ragged tail
+        ("bf16", 201087, 13, 40, 0),     # a row stride off 16-byte alignment: the exact kernel only
+        ("bf16", 68272, 64, 520, 0),     # the shortest row it takes; two rows per CU and more
+        ("fp32", 102400, 100, 40, 0),
+        ("fp32", 50001, 7, 300, 3),      # ragged tail, padded rows
+        ("fp32", 34136, 128, 40, 0),
+    ],
+)
+def test_single_read_pass(dtype, V, K, N, pad):
+    """kd_topk_cache at the row lengths where a whole row is held on chip and read once, with the
+    rows it cannot settle redone by the exact kernel; ids and values bit for bit."""
+    g = np.random.Generator(np.random.PCG64([4245, V, K]))
+    x = single_read_rows(g, N, V, K)
+    xs = datagen.bf16_bits(x) if dtype == "bf16" else x  # what the device holds
+    xv = datagen.bf16_to_f32(xs) if dtype == "bf16" else x
+    say("topk single read", dtype, f"N={N} V={V} K={K} ld={V + pad}")
+    buf = np.zeros((N, V + pad), xs.dtype)
+    buf[:, :V] = xs
+    idx, vals = kd.topk_cache(to_torch(buf)[:, :V], K)
+    torch.cuda.synchronize()
+    want_idx, _ = oracle.topk_cache(xv, K)
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+    want_bits = np.take_along_axis(xs, want_idx.astype(np.int64), 1)
+    got = vals.cpu()
+    got_bits = got.view(torch.int16).numpy().view(np.uint16) if dtype == "bf16" else got.numpy()
+    assert np.array_equal(got_bits.view(np.uint8), want_bits.view(np.uint8))
