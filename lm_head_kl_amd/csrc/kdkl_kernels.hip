@@ -1564,11 +1564,11 @@ __global__ __launch_bounds__(256) void k_topk(const T* __restrict__ X, int64_t l
 //      in flight each candidate counts the candidates with a larger key. That count is its place
 //      in the output, which it writes if the count is below K.
 // Appends to the LDS lists take their places from a prefix count over the wave and one atomic
-// per wave, and step 3 needs no barrier: the next row's first barrier orders the reuse of the
-// lists. A row with fewer than K candidates (NaN), more than the buffers hold (many equal values)
-// or a bound of -inf is left with its first id at -1; k_topk then redoes those rows exactly.
+// per wave. A row with fewer than K candidates (NaN), more than the buffers hold (many equal
+// values) or a bound of -inf is left with its first id at -1; k_topk then redoes those rows
+// exactly.
 constexpr int kTkrThreads = 512, kTkrChunks = 50, kTkrCand = 1024, kTkrList = 1024, kTkrMaxK = 128;
-constexpr int kTkrLds = 6;  // slots loaded into LDS
+constexpr int kTkrLds = 8;  // slots loaded into LDS
 constexpr int kNonTemporal = 2;  // cache-policy operand of a buffer load: non-temporal
 
 // The pass's sort key: the 54-bit order (value, then lower id first) moved up one bit, and a last
@@ -1607,8 +1607,8 @@ __global__ __launch_bounds__(kTkrThreads, 1) void k_topk_reg(const T* __restrict
     __shared__ u32x4 lslot[NL * NT];  // slots NR .. S-1, slot-major
     __shared__ u32x4 cmv[NT * CMV];   // chunk maxima
     __shared__ uint64_t cand[kTkrCand];
-    __shared__ u32x4 chl[kTkrList];  // chunks holding an entry >= the bound
-    __shared__ int chq[kTkrList];    // and their positions in the row (in chunks)
+    __shared__ u32x4 chl[kTkrList];   // chunks holding an entry >= the bound
+    __shared__ int chq[kTkrList];     // and their positions in the row (in chunks)
     __shared__ uint32_t wkey[NW];
     __shared__ int s_n[2], s_nch[2];  // list lengths; rows alternate between the two pairs
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1706,31 +1706,34 @@ __global__ __launch_bounds__(kTkrThreads, 1) void k_topk_reg(const T* __restrict
         {
             int qb = tid;
             asm volatile("" : "+v"(qb));
-            uint64_t pm = 0;
-            {
-                u32x4 m[CMV];
+            // Both passes read the maxima from LDS: held between them they would take registers
+            // the row needs.
+            auto passes = [&](const u32x4& mv, int j) {
+                const int e = j % CPV;
+                const uint32_t word = mv[e / 2];
+                return __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16)) >= L;
+            };
+            int cnt = 0;
 #pragma unroll
-                for (int v = 0; v < CMV; ++v) m[v] = cmv[qb * CMV + v];
+            for (int v = 0; v < CMV; ++v) {
+                const u32x4 mv = cmv[qb * CMV + v];
 #pragma unroll
-                for (int j = 0; j < S; ++j) {
-                    const int e = j % CPV;
-                    const uint32_t word = m[j / CPV][e / 2];
-                    const float cm = __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16));
-                    pm |= (uint64_t)(cm >= L) << j;
-                }
+                for (int j = v * CPV; j < min((v + 1) * CPV, S); ++j) cnt += passes(mv, j) ? 1 : 0;
             }
+            asm volatile("" ::: "memory");
             int total;
-            int pos = wave_prefix<6>(__popcll(pm), total);
+            int pos = wave_prefix<6>(cnt, total);
             int base = 0;
             if (lane == 0 && total > 0) base = atomicAdd(&s_nch[par], total);
             pos += __builtin_amdgcn_readfirstlane(base);
+            // past the list's end every chunk lands on its last entry: the row then goes to k_topk
 #pragma unroll
             for (int j = 0; j < S; ++j) {
-                if ((pm >> j) & 1) {
-                    if (pos < kTkrList) {
-                        chl[pos] = j < NR ? c[j < NR ? j : 0] : lslot[(j - NR) * NT + qb];
-                        chq[pos] = qb + j * NT;
-                    }
+                const u32x4 mv = cmv[qb * CMV + j / CPV];
+                if (passes(mv, j)) {
+                    const int at = min(pos, kTkrList - 1);
+                    chl[at] = j < NR ? c[j < NR ? j : 0] : lslot[(j - NR) * NT + qb];
+                    chq[at] = qb + j * NT;
                     ++pos;
                 }
             }
@@ -1740,16 +1743,16 @@ __global__ __launch_bounds__(kTkrThreads, 1) void k_topk_reg(const T* __restrict
             }
         }
         lds_barrier();
-        // ... and its entries >= L to the candidates
+        // ... and its entries >= L to the candidates (after the tail entries already there)
         const int nch = s_nch[par];
         for (int i0 = 0; i0 < min(nch, kTkrList); i0 += NT) {
             const int i = i0 + tid;
             uint32_t bits[VEC];
             uint32_t em = 0;
-            int v0 = 0;
+            int q = 0;
             if (i < min(nch, kTkrList)) {
                 const u32x4 ch = chl[i];
-                v0 = chq[i] * VEC;
+                q = chq[i];
 #pragma unroll
                 for (int u = 0; u < VEC; ++u) {
                     bits[u] = sizeof(T) == 2 ? ((u & 1) ? (ch[u / 2] & 0xFFFF0000u) : (ch[u / 2] << 16)) : ch[u];
@@ -1764,14 +1767,18 @@ __global__ __launch_bounds__(kTkrThreads, 1) void k_topk_reg(const T* __restrict
 #pragma unroll
             for (int u = 0; u < VEC; ++u) {
                 if ((em >> u) & 1) {
-                    if (pos < kTkrCand) cand[pos] = tkr_key(v0 + u, bits[u]);
+                    if (pos < kTkrCand) cand[pos] = tkr_key(q * VEC + u, bits[u]);
                     ++pos;
                 }
             }
         }
         lds_barrier();
         const int nc = s_n[par];
-        // 3. the registers and LDS slots are free: the next row's loads go out, then the ranks.
+        // 3. The registers and LDS slots are free: the next row's loads go out, then each wave
+        // places its candidates with no barrier (a wave waits at load issue while the CU's memory
+        // queue is full; work shared through barriers would wait for every wave's loads to be
+        // requested). A candidate's place is the number of candidates with a larger key. The
+        // next row's first barrier orders the reuse of the LDS lists and counters.
         const int64_t rn = r + gridDim.x;
         if (rn < N) load(rn);
         if (!ok_bound || nc < K || nc > kTkrCand || nch > kTkrList) {
@@ -1801,6 +1808,7 @@ __global__ __launch_bounds__(kTkrThreads, 1) void k_topk_reg(const T* __restrict
         r = rn;
     }
 }
+
 
 // ------------------------------------------------------------------------------------------
 // Launchers.
