@@ -54,7 +54,42 @@ def parse():
                          "chunk sweep, gpt-oss, the pages' full shape) and sweep S for peak memory")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device-to-device once (reference for the HBM byte counters)")
+    ap.add_argument("--producer", action="store_true",
+                    help="only time the top-K cache producer on the config's logits shape")
     return ap.parse_args()
+
+
+def producer(dev, stream, N: int, V: int, K: int, seed: int, reps: int = 5) -> dict:
+    """The offline top-K cache producer on teacher logits of the workload's shape: seeded
+    synthetic bf16 rows N(0, 4), K = the cache width. HBM-bound; reported against one read of
+    the logits, as the median of `reps` timed calls after one untimed call."""
+    import statistics
+
+    import torch
+
+    import lm_head_kl_amd as kd
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    tl = torch.empty((N, V), dtype=torch.bfloat16, device=dev)
+    for r0 in range(0, N, 4096):
+        tl[r0:r0 + 4096] = (torch.randn((min(4096, N - r0), V), generator=gen, device=dev) * 2.0).to(torch.bfloat16)
+    kd.topk_cache(tl, K)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record(stream)
+        kd.topk_cache(tl, K)
+        e[1].record(stream)
+        torch.cuda.synchronize()
+        times.append(e[0].elapsed_time(e[1]))
+    del tl
+    ms = statistics.median(times)
+    read_gb = N * V * 2 / 1e9
+    return {"rows": N, "V": V, "K": K, "dtype": "bf16", "ms": ms, "ms_calls": [round(t, 4) for t in times],
+            "rows_per_s": N / (ms / 1e3), "logits_read_once_gb_s": read_gb / (ms / 1e3),
+            "frac_of_hbm_peak": read_gb / (ms / 1e3) / PEAK_HBM_GBS}
 
 
 def kernel_sources_sha() -> str:
@@ -233,6 +268,11 @@ def main():
         return
     if args.sweep:
         sweep(dev, args.steps)
+        return
+    if args.producer:
+        p = datagen.make(args.config, N=args.rows or None)
+        res = producer(dev, torch.cuda.current_stream(), p.N, p.V, p.K, p.extra.get("seed", 0) + 9, reps=args.steps)
+        print(json.dumps({"topk_producer": res, "config": {"workload": p.name}}))
         return
     t_gen = time.perf_counter()
     p = datagen.make(args.config, N=args.rows or None)
@@ -446,28 +486,8 @@ def main():
 
     if not args.no_formulations:
         try:
-            # The offline top-K cache producer on teacher logits of the workload's shape: seeded
-            # synthetic bf16 rows N(0, 4), K = the cache width. HBM-bound; reported against one read
-            # of the logits.
             torch.cuda.empty_cache()
-            gen = torch.Generator(device=dev)
-            gen.manual_seed(p.extra.get("seed", 0) + 9)
-            tl = torch.empty((N, V), dtype=torch.bfloat16, device=dev)
-            for r0 in range(0, N, 4096):
-                tl[r0:r0 + 4096] = (torch.randn((min(4096, N - r0), V), generator=gen, device=dev) * 2.0).to(torch.bfloat16)
-            kd.topk_cache(tl[:256], p.K)
-            torch.cuda.synchronize()
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-            e[0].record(stream)
-            kd.topk_cache(tl, p.K)
-            e[1].record(stream)
-            torch.cuda.synchronize()
-            ms_tk = e[0].elapsed_time(e[1])
-            read_gb = N * V * 2 / 1e9
-            out["topk_producer"] = {"rows": N, "V": V, "K": p.K, "dtype": "bf16", "ms": ms_tk,
-                                    "rows_per_s": N / (ms_tk / 1e3), "logits_read_once_gb_s": read_gb / (ms_tk / 1e3),
-                                    "frac_of_hbm_peak": read_gb / (ms_tk / 1e3) / PEAK_HBM_GBS}
-            del tl
+            out["topk_producer"] = producer(dev, stream, N, V, p.K, p.extra.get("seed", 0) + 9)
             torch.cuda.empty_cache()
             print("[bench] top-K producer done", file=sys.stderr, flush=True)
         except (RuntimeError, torch.OutOfMemoryError) as ex:
