@@ -139,9 +139,19 @@ __global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ idx, i
     for (int t = tid; t < n_vt; t += NTHR) cnt[t] = 0;
     __syncthreads();
     const int n_e = rows * K;
-    for (int i = tid; i < n_e; i += NTHR) {
-        const int v = idx[r0 * K + i];
-        if (v >= 0 && v < V) atomicAdd(&cnt[v >> 8], 1);
+    // Entries go in batches of PB per thread, all loaded before any is used, so the loads'
+    // latency is paid once per batch rather than once per entry.
+    constexpr int PB = 8;
+    for (int i0 = 0; i0 < n_e; i0 += NTHR * PB) {
+        int v[PB];
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            const int i = i0 + u * NTHR + tid;
+            v[u] = i < n_e ? idx[r0 * K + i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < PB; ++u)
+            if (v[u] >= 0 && v[u] < V) atomicAdd(&cnt[v[u] >> 8], 1);
     }
     __syncthreads();
     // exclusive scan of cnt[0..n_vt): each thread owns a contiguous segment
@@ -170,12 +180,21 @@ __global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ idx, i
     }
     if (tid == NTHR - 1) o[n_vt] = (int32_t)(base + run);  // the last segment ends at the total
     __syncthreads();
-    for (int i = tid; i < n_e; i += NTHR) {
-        const int v = idx[r0 * K + i];
-        if (v >= 0 && v < V) {
-            const int pos = atomicAdd(&cnt[v >> 8], 1);
-            const int r = i / K, k = i - r * K;
-            ent[base + pos] = (uint32_t)r | ((uint32_t)(v & 255) << 8) | ((uint32_t)k << 16);
+    for (int i0 = 0; i0 < n_e; i0 += NTHR * PB) {
+        int v[PB];
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            const int i = i0 + u * NTHR + tid;
+            v[u] = i < n_e ? idx[r0 * K + i] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < PB; ++u) {
+            if (v[u] >= 0 && v[u] < V) {
+                const int i = i0 + u * NTHR + tid;
+                const int pos = atomicAdd(&cnt[v[u] >> 8], 1);
+                const int r = i / K, k = i - r * K;
+                ent[base + pos] = (uint32_t)r | ((uint32_t)(v[u] & 255) << 8) | ((uint32_t)k << 16);
+            }
         }
     }
 }
