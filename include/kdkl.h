@@ -180,12 +180,14 @@ kd_status kd_fused_kl_fwd(const kd_problem* p, const void* H, const void* W, con
 /*
  * The fused forward for callers that cannot allocate device memory: code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation. Same arguments, checks and
- * results as kd_fused_kl_fwd (the same kernels run, bit for bit), without ws and ws_bytes: the
+ * results as kd_fused_kl_fwd (the same arithmetic, bit for bit; kd_fused_kl_fwd reads W and H
+ * through stage-tiled copies in its workspace, this call as stored), without ws and ws_bytes: the
  * forward's workspace is a static device array of KD_NOALLOC_SCRATCH_BYTES inside the library,
  * one per GPU, held from the library's first use on that GPU until the process ends. The call
  * allocates nothing; the caller passes every input and output.
- *   Limit: the forward's share of kd_fused_workspace_bytes(p) (O(N*K + N) bytes: at K = 100 about
- *   900 bytes a row, so N up to about 65,000 rows) must fit in KD_NOALLOC_SCRATCH_BYTES, else
+ *   Limit: the forward's share of kd_fused_workspace_bytes(p) without the tiled copies (O(N*K + N)
+ *   bytes: at K = 100 and V = 201,088 about 815 bytes a row plus 1 MB, so N up to about 80,000
+ *   rows) must fit in KD_NOALLOC_SCRATCH_BYTES, else
  *   KD_ERR_WORKSPACE with nothing enqueued. KD_VALIDATE_IDX gives KD_ERR_VALUE (it copies to the
  *   host and waits; run kd_validate_ids first instead).
  *   Calls on one GPU share its array: calls that overlap in time on one GPU (different streams

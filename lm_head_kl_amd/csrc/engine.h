@@ -349,29 +349,42 @@ constexpr int NCH4 = 4;
 constexpr int TILE4 = kTileM * NCH4;  // 1024 chunks = 16 KB per operand per stage
 __device__ __forceinline__ int swz4(int r, int c) { return c ^ (((r >> 2) ^ (r >> 1)) & 3); }
 
-// Two operand layouts:
-//   row-major   element (mn, k) at src[mn*ld + k];
-//   K-blocked   the K axis cut into blocks of 256, each block a row-major [R][256] slab:
-//               element (mn, k) at src[((k >> 8)*R + mn)*256 + (k & 255)], with ld = R.
-// The K-blocked layout keeps the 256 rows of a tile within 128 KB (bf16) however long K is.
-// A row-major operand with a long K (the vocabulary) puts each of a tile's rows on its own
-// memory page, and its loads run about 15 % slower.
-template <typename T, bool BLK = false, int NW = 4>
+// Three operand layouts (LAY):
+//   kRow    row-major: element (mn, k) at src[mn*ld + k];
+//   kKBlk   K-blocked: the K axis cut into blocks of 256, each block a row-major [R][256] slab:
+//           element (mn, k) at src[((k >> 8)*R + mn)*256 + (k & 255)], with ld = R;
+//   kTiled  stage-tiled: rows cut into blocks of RB (the tile's rows) and K into stages of SW =
+//           64 bytes, each (row block, stage) a contiguous [RB][SW] block:
+//           element (mn, k) at src[((mn / RB)*S + k / SW)*RB*SW + (mn % RB)*SW + k % SW], with
+//           ld = S, the stages per row block; K is zero-padded to S*SW and rows to whole blocks.
+// One stage of a tile is 64 bytes of each of its rows. Row-major and K-blocked operands give it
+// as 64-byte pieces of separate 128-byte lines, the second half of each line following one stage
+// later; a stage-tiled operand gives it as one contiguous block, every line whole. At the
+// gpt-oss head the same mainloop runs 15-18 % faster on stage-tiled operands.
+enum Lay : int { kRow = 0, kKBlk = 1, kTiled = 2 };
+
+template <typename T, int LAY = kRow, int NW = 4>
 struct KOperand4 {
     static constexpr int TPI = 16 / NW;  // DMA instructions per wave per stage
     static constexpr int VEC = Elem<T>::VEC;
-    __amdgpu_buffer_rsrc_t rsrc;  // tile origin &src[mn0*ld] (row-major); k0 goes in the scalar offset
+    static constexpr bool BLK = LAY == kKBlk;
+    // row-major: tile origin &src[mn0*ld], k0 in the scalar offset; stage-tiled: the tile's
+    // first block, the stage's block in the scalar offset
+    __amdgpu_buffer_rsrc_t rsrc;
     const char* base;             // K-blocked: &src[mn0*256] in block 0
     int64_t blk_bytes;            // K-blocked: bytes per block
     uint32_t off[TPI];
     int chunk;
     // Wave w's instruction t fills chunks 64 NW t + 64w + lane: row 16 NW t + 16w + lane/4, slot lane%4.
+    // A stage-tiled operand needs mn0 % kTileM == 0.
     __device__ __forceinline__ void init(const T* src, int64_t ld, int64_t mn0, int64_t mn_lim,
                                          const WaveIdN<NW>& id) {
-        const int64_t row_ld = BLK ? 256 : ld;
+        const int64_t row_ld = BLK ? 256 : LAY == kTiled ? 4 * VEC : ld;
         if constexpr (BLK) {
             base = (const char*)uniform_ptr(src + mn0 * 256);
             blk_bytes = ld * 256 * (int64_t)sizeof(T);
+        } else if constexpr (LAY == kTiled) {
+            rsrc = make_rsrc(src + (mn0 / kTileM) * ld * (kTileM * 4 * VEC));
         } else {
             rsrc = make_rsrc(src + mn0 * ld);
         }
@@ -394,6 +407,10 @@ struct KOperand4 {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(tile + 64 * NW * t + 64 * id.w), 16,
                                                      (int)(in ? off[t] : kOOB), (int)((k0 & 255) * (int64_t)sizeof(T)),
                                                      0, 0);
+        } else if constexpr (LAY == kTiled) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + 64 * NW * t + 64 * id.w), 16,
+                                                     (int)(in ? off[t] : kOOB),
+                                                     (int)((k0 / (4 * VEC)) * (kTileM * 64)), 0, 0);
         } else {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(tile + 64 * NW * t + 64 * id.w), 16,
                                                      (int)(in ? off[t] : kOOB), (int)(k0 * (int64_t)sizeof(T)), 0, 0);
@@ -453,9 +470,10 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 //   [MFMA(F1) interleaved with DMA of stage kt+4 into stage kt's buffer and reads F0 <- (kt+1, g0)]
 // Stage kt's buffer is free after that barrier (its last fragments were read before it), so
 // the DMA runs four stages ahead. Every LDS read is issued one MFMA block ahead of its use.
-// BA / BB select the K-blocked layout for A / B (then lda / ldb is the operand's row count).
+// BA / BB select the layout of A / B (Lay; lda / ldb is then the row stride, the row count or
+// the stages per row block).
 // NW is the wave count of the workgroup (4 or 8, see WaveIdN); acc is [4][16/NW].
-template <typename T, bool BA = false, bool BB = false, int NW = 4>
+template <typename T, int BA = kRow, int BB = kRow, int NW = 4>
 __device__ __forceinline__ void gemm_tile_kk(f32x16 (&acc)[4][16 / NW], u32x4* L, const WaveIdN<NW>& id,
                                              const T* A, int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim,
                                              const T* B, int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim,
@@ -585,7 +603,7 @@ __device__ __forceinline__ u32x4 frag16(const u32x4* S, int r0, int lane) {
 // rows: part 0 = rows 0-3 (A rows 4-7 of the stage read meanwhile), barrier, part 1 = rows 4-7
 // (the DMA of stage k+4 issued, A rows 0-3 and B of stage k+1 read meanwhile). B alternates
 // between two register sets, so the loop runs two stages per trip.
-template <typename T, bool BA = false, bool BB = false>
+template <typename T, int BA = kRow, int BB = kRow>
 __device__ __forceinline__ void gemm_tile_kk16(f32x4 (&acc)[8][4], u32x4* L, const WaveIdN<8>& id, const T* A,
                                                int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim, const T* B,
                                                int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim,

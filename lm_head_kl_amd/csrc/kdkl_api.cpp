@@ -119,27 +119,58 @@ struct FusedWs {
     void* HT;   // [d][ldgt]: H_c transposed
     float* dh_part;
     int64_t ldgt, group;
-    int n_vsplit, n_split;
+    int n_split;
+    // stage-tiled copies of W and of one row chunk of H for the forward and gradient kernels
+    // (null: they read W and H as stored)
+    void* Wt;
+    void* Ht;   // kFwdRows rows
+    void* cWt;  // the backward's
+    void* cHt;  // one chunk of rows
+    int64_t tS;  // stages per row block
     size_t fwd_bytes, bwd_bytes;
 };
 
+// Rows per forward launch when H is read from a stage-tiled copy: the copy holds this many rows,
+// so the workspace stays independent of N. 8192 rows are 32 row blocks, which with 8 vocabulary
+// lanes give each of 256 compute units one unit of work.
+constexpr int64_t kFwdRows = 8192;
+int64_t fwd_rows(const kd_problem* p) { return std::min(p->N, kFwdRows); }
+int fwd_parts(const kd_problem* p) {
+    // per-row partials of the largest launch (the last may be shorter and use more lanes)
+    const int64_t F = fwd_rows(p), last = p->N - (p->N - 1) / F * F;
+    return (int)std::max(2 * fwd_vsplits(F, p->V) * F, 2 * fwd_vsplits(last, p->V) * last);
+}
+
 bool low_memory(const kd_problem* p) { return (p->flags & KD_LOW_MEMORY) != 0; }
 
-FusedWs layout_fused(const kd_problem* p, void* ws) {
+// The forward and gradient kernels read W and H from stage-tiled copies (engine.h, kTiled):
+// the copies cost one pass over W and H per call, and W's size plus a row chunk of H's in the
+// workspace; the kernels' operand loads then fetch whole 128-byte lines. The memory-lean
+// backward keeps none.
+bool tiled_fwd(const kd_problem* p) { return !low_memory(p); }
+bool tiled_bwd(const kd_problem* p) { return !low_memory(p); }
+
+FusedWs layout_fused(const kd_problem* p, void* ws, bool fwd_tiles = true) {
     FusedWs w{};
     const int64_t N = p->N, K = p->K, V = p->V, d = p->d;
     const int64_t n_vt = n_vtiles(V), Vp = n_vt * kTileN;
     const int64_t C = chunk_rows(p);
     const bool lean = low_memory(p);
-    w.n_vsplit = fwd_vsplits(N, V);
     w.n_split = dh_splits(C, d, V, !lean);
     Carve f(ws);
     w.status = (uint32_t*)f.take(kAlign);
     w.plan_off = (int32_t*)f.take(sizeof(int32_t) * n_rblocks(N) * (n_vt + 1));
     w.plan_ent = (uint32_t*)f.take(sizeof(uint32_t) * n_rblocks(N) * kTileM * K);
-    w.part = (float2*)f.take(sizeof(float2) * 2 * w.n_vsplit * N);
+    const bool ft = fwd_tiles && tiled_fwd(p);
+    w.part = (float2*)f.take(sizeof(float2) * fwd_parts(p));
     w.zk = (float*)f.take(sizeof(float) * N * K);
-    w.blk_sum = (double*)f.take(sizeof(double) * combine_blocks(N));
+    w.blk_sum = (double*)f.take(sizeof(double) * ((N + fwd_rows(p) - 1) / fwd_rows(p)) * combine_blocks(fwd_rows(p)));
+    const Dt act = p->act == KD_BF16 ? Dt::BF16 : Dt::F32;
+    w.tS = tiled_stages(act, d);
+    if (ft) {
+        w.Wt = f.take(tiled_bytes(act, V, d));
+        w.Ht = f.take(tiled_bytes(act, fwd_rows(p), d));
+    }
     w.fwd_bytes = f.used;
     Carve b(ws);
     b.take(kAlign);  // status word shared with the forward layout
@@ -162,6 +193,10 @@ FusedWs layout_fused(const kd_problem* p, void* ws) {
         w.HT = b.take(esize(p->act) * d * w.ldgt);
     }
     w.dh_part = w.n_split > 1 ? (float*)b.take(sizeof(float) * w.n_split * C * d) : nullptr;
+    if (tiled_bwd(p)) {
+        w.cWt = b.take(tiled_bytes(act, V, d));
+        w.cHt = b.take(tiled_bytes(act, C, d));
+    }
     w.bwd_bytes = b.used;
     return w;
 }
@@ -298,19 +333,44 @@ kd_status stored_backward(const kd_problem* p, const Shape& sh, const StoredWs& 
 // The forward's launches, once the arguments have been checked; ws holds at least the
 // forward's part of the fused workspace layout.
 kd_status fused_forward(const kd_problem* p, const void* H, const void* W, const int32_t* idx, const void* tlog,
-                        float* loss, float* lse, float* row_kl, float* zk, void* ws, hipStream_t s) {
+                        float* loss, float* lse, float* row_kl, float* zk, void* ws, hipStream_t s,
+                        bool tiles = true) {
     (void)hipGetLastError();  // start from a clean error state
     const Shape sh = make_shape(p);
-    const FusedWs w = layout_fused(p, ws);
+    const FusedWs w = layout_fused(p, ws, tiles);
     if (p->flags & KD_VALIDATE_IDX) {
         const kd_status st = validate_ids(p, idx, w.status, s);
         if (st != KD_OK) return st;
     }
     float* zk_out = zk ? zk : w.zk;
     KD_TRY(launch_plan(idx, 0, p->N, p->K, p->V, w.plan_off, w.plan_ent, s));
-    KD_TRY(launch_fwd(sh, H, W, w.plan_off, w.plan_ent, w.n_vsplit, w.part, zk_out, nullptr, 0, s));
+    // Rows in launches of kFwdRows (whole row blocks), with or without stage-tiled copies (of W,
+    // and of each launch's rows of H): the arithmetic, and so every result bit, is the same
+    // either way. Combined per launch; the fp64 block sums line up as for one launch over all
+    // rows.
+    if (w.Wt) KD_TRY(launch_tile_rows(sh.act, W, p->d, p->V, p->d, w.Wt, s));
+    const int64_t F = fwd_rows(p), plan_stride = n_vtiles(p->V) + 1;
+    const size_t es = esize(p->act), ets = esize(p->tlogit);
     int n_blk = 0;
-    KD_TRY(launch_combine(sh, w.part, 2 * w.n_vsplit, zk_out, tlog, lse, row_kl, w.blk_sum, &n_blk, s));
+    for (int64_t r0 = 0; r0 < p->N; r0 += F) {
+        const int64_t rows = std::min(F, p->N - r0);
+        Shape shc = sh;
+        shc.N = rows;
+        const int nvs = fwd_vsplits(rows, p->V);
+        const char* Hr = (const char*)H + r0 * p->d * es;
+        if (w.Wt) {
+            KD_TRY(launch_tile_rows(sh.act, Hr, p->d, rows, p->d, w.Ht, s));
+            KD_TRY(launch_fwd(shc, w.Ht, w.Wt, w.plan_off + (r0 / kTileM) * plan_stride, w.plan_ent, nvs, w.part,
+                              zk_out + r0 * p->K, nullptr, 0, s, w.tS));
+        } else {
+            KD_TRY(launch_fwd(shc, Hr, W, w.plan_off + (r0 / kTileM) * plan_stride, w.plan_ent, nvs, w.part,
+                              zk_out + r0 * p->K, nullptr, 0, s));
+        }
+        int nb = 0;
+        KD_TRY(launch_combine(shc, w.part, 2 * nvs, zk_out + r0 * p->K, (const char*)tlog + r0 * p->K * ets, lse + r0,
+                              row_kl ? row_kl + r0 : nullptr, w.blk_sum + n_blk, &nb, s));
+        n_blk += nb;
+    }
     KD_TRY(launch_loss_final(sh, w.blk_sum, n_blk, loss, s));
     return KD_OK;
 }
@@ -395,11 +455,11 @@ kd_status kd_fused_kl_fwd_noalloc(const kd_problem* p, const void* H, const void
     // KD_VALIDATE_IDX copies a status word to the host and waits for it; kd_validate_ids is the
     // check that needs neither.
     if (p->flags & KD_VALIDATE_IDX) return KD_ERR_VALUE;
-    if (layout_fused(p, nullptr).fwd_bytes > KD_NOALLOC_SCRATCH_BYTES) return KD_ERR_WORKSPACE;
+    if (layout_fused(p, nullptr, false).fwd_bytes > KD_NOALLOC_SCRATCH_BYTES) return KD_ERR_WORKSPACE;
     void* ws = nullptr;
     st = scratch_address(&ws);
     if (st != KD_OK) return st;
-    return fused_forward(p, H, W, idx, tlog, loss, lse, row_kl, zk, ws, (hipStream_t)stream);
+    return fused_forward(p, H, W, idx, tlog, loss, lse, row_kl, zk, ws, (hipStream_t)stream, false);
 }
 
 kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, const int32_t* idx, const void* tlog,
@@ -425,6 +485,10 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
     const bool lean = low_memory(p);
     // W^T once per call: dH = G_c W then reads both operands with the vocabulary contiguous.
     if (!lean) KD_TRY(launch_transpose_blocked(sh.act, W, p->d, p->V, p->d, w.WT, Vp, s));
+    // Stage-tiled W once per call, and each chunk's rows of H before its gradient kernel.
+    if (w.cWt) KD_TRY(launch_tile_rows(sh.act, W, p->d, p->V, p->d, w.cWt, s));
+    const void* gW = w.cWt ? w.cWt : W;
+    const int64_t gS = w.cWt ? w.tS : 0;
     const int64_t C8 = round_up(C, 8);
     const size_t es = esize(p->act);
     const bool one_plan = whole_plan(p);
@@ -455,8 +519,9 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
             KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
                                     (char*)w.HT + slot * C8 * es, w.ldgt, round_up(cc, 8), s));
         // Without dW, G^T is not needed: the gradient kernel skips those stores.
-        KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.cplan_ent, w.Gc,
-                               want_dw ? (char*)w.GT + slot * C8 * es : nullptr, w.ldgt, s));
+        if (w.cHt) KD_TRY(launch_tile_rows(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d, w.cHt, s));
+        KD_TRY(launch_bwd_grad(sh, w.cHt ? w.cHt : H, gW, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off,
+                               w.cplan_ent, w.Gc, want_dw ? (char*)w.GT + slot * C8 * es : nullptr, w.ldgt, s, gS));
         KD_TRY(launch_dh(sh, w.Gc, 0, W, w.WT, c0, cc, w.n_split, w.dh_part, dH, s));
         // One dW pass per group of chunks (K = the group's rows; the slots are zero-padded to 8)
         if (want_dw && (slot == w.group - 1 || c0 + cc >= p->N)) {

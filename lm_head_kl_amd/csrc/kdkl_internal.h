@@ -69,9 +69,11 @@ hipError_t launch_validate(const int32_t* idx, int64_t N, int64_t K, int64_t V, 
 // Fused forward over the sh.N rows of H: per (row block, vocab split) partial (max, sum) in
 // the log2 domain, and zk at every cached id. With zt not null the logits are also stored
 // transposed, z^T [Vp][ldzt] (columns: rows of H), for the paths that keep them.
+// tiled_S > 0: H and W are stage-tiled copies (launch_tile_rows) with tiled_S stages per row
+// block; 0: row-major [N][d] and [V][d].
 hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32_t* plan_off,
                       const uint32_t* plan_ent, int n_vsplit, float2* part, float* zk,
-                      float* zt, int64_t ldzt, hipStream_t s);
+                      float* zt, int64_t ldzt, hipStream_t s, int64_t tiled_S = 0);
 
 // Merge partials into lse, compute KL_n (row_kl) and per-block fp64 partial sums.
 hipError_t launch_combine(const Shape& sh, const float2* part, int n_part, const float* zk,
@@ -87,10 +89,11 @@ hipError_t launch_loss_final(const Shape& sh, const double* blk_sum, int n_blk, 
 //   G_c = g*T/n_norm*(softmax(z/T) - P_t) in the act dtype, K-blocked [Vp/256][cc][256] (entry
 //   (t, v) at ((v/256)*cc + t)*256 + v%256; entries v >= V zero), and, if GT is not null, its
 //   transpose G_c^T [Vp, ldgt] with columns [cc, round_up(cc, 8)) zero.
+// H and W as in launch_fwd; a stage-tiled H holds the chunk's cc rows alone (row 0 = row c0).
 hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const float* lse,
                            const float* pt, const float* grad_loss, int64_t c0, int64_t cc,
                            const int32_t* plan_off, const uint32_t* plan_ent, void* Gc,
-                           void* GT, int64_t ldgt, hipStream_t s);
+                           void* GT, int64_t ldgt, hipStream_t s, int64_t tiled_S = 0);
 
 // The same G_c and G_c^T as launch_bwd_grad, from stored logits z^T [Vp][ldzt] (chunk row r
 // in column zt_col0 + r) instead of recomputing them.
@@ -103,6 +106,14 @@ hipError_t launch_grad_z(const Shape& sh, const float* zt, int64_t ldzt, int64_t
 // first, ties in lower-id order.
 hipError_t launch_topk(Dt dt, const void* X, int64_t ld, int64_t N, int64_t V, int64_t K, int32_t* idx,
                        void* val, hipStream_t s);
+
+// Stage-tiled copy of a row-major src [rows][ld] (cols used; cols and ld multiples of 16 bytes):
+// blocks of 256 rows x 64 bytes, block (row block b, stage s) at dst + (b*S + s)*16 KB, S =
+// tiled_stages(dt, cols), zeros past rows and cols. tiled_bytes gives the size of dst.
+int64_t tiled_stages(Dt dt, int64_t cols);
+int64_t tiled_bytes(Dt dt, int64_t rows, int64_t cols);
+hipError_t launch_tile_rows(Dt dt, const void* src, int64_t ld, int64_t rows, int64_t cols, void* dst,
+                            hipStream_t s);
 
 // dst[c][r] = src[r][c] (r < rows), zero for rows <= r < rows_pad; cols, rows_pad multiples of 8.
 hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst,

@@ -263,8 +263,9 @@ __global__ __launch_bounds__(256) void k_validate(const int32_t* __restrict__ id
 // Fused forward.
 
 struct FwdArgs {
-    const void* H;
-    const void* W;
+    const void* H;  // row-major [N][d], or stage-tiled (ldh stages per row block)
+    const void* W;  // row-major [V][d], or stage-tiled (ldw stages per row block)
+    int64_t ldh, ldw;
     int64_t N, d, V, K;
     float c;  // log2(e)/T
     const int32_t* off;
@@ -287,7 +288,7 @@ struct FwdArgs {
 // entries and columns are tokens. Each lane then holds 64 vocabulary entries of each of its
 // 4 token columns, so the per-token (max, sum) over the vocabulary is folded inside the lane,
 // and lanes only meet once per unit.
-template <typename T, bool ZT, int NW>
+template <typename T, bool ZT, int NW, int LAY>
 __global__ __launch_bounds__(64 * NW, 1) void k_fwd(FwdArgs a) {
     static_assert(NW == 8, "the forward runs on eight waves with 16 x 16 blocks");
     constexpr int NT = 64 * NW;
@@ -319,8 +320,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(FwdArgs a) {
             const int e0 = off[vt], e1 = off[vt + 1];
             const uint32_t my_en = e0 + id.tid < e1 ? a.ent[e0 + id.tid] : 0xffffffffu;
             f32x4 acc[8][4];
-            gemm_tile_kk16<T>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, (const T*)a.H, a.d, m0, a.N, a.d, 0,
-                              a.d);
+            gemm_tile_kk16<T, LAY, LAY>(acc, L, id, (const T*)a.W, a.ldw, n0, a.V, a.d, (const T*)a.H, a.ldh, m0,
+                                        a.N, a.d, 0, a.d);
             const WaveIdN<NW> ie = id.fresh();
             const int g4 = 4 * (ie.lane >> 4), c16 = ie.lane & 15;
 
@@ -507,8 +508,9 @@ __global__ __launch_bounds__(256) void k_sum_rows(const double* __restrict__ v, 
 // and G^T (a vocabulary entry's 256 consecutive tokens).
 
 struct GradArgs {
-    const void* H;
-    const void* W;
+    const void* H;  // row-major [N][d], or stage-tiled (ldh stages per row block)
+    const void* W;  // row-major [V][d], or stage-tiled (ldw stages per row block)
+    int64_t ldh, ldw;
     int64_t d, V, K;
     float c;      // log2(e)/T
     float gsc;    // T/n_norm
@@ -609,7 +611,7 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
     lds_barrier();
 }
 
-template <typename T, int NW>
+template <typename T, int NW, int LAY>
 __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
     static_assert(NW == 8, "the gradient kernel runs on eight waves with 16 x 16 blocks");
     constexpr int NT = 64 * NW;
@@ -623,7 +625,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
     const int64_t band = (n_tiles + 7) / 8, per_xcd = gridDim.x / 8;
     const int64_t t_beg = (blockIdx.x % 8) * band, t_end = min(n_tiles, t_beg + band);
     float* stage = (float*)L;
-    const T* Hc = (const T*)a.H + a.c0 * a.d;
+    // The chunk's first row of H: row c0 of row-major H; a stage-tiled H holds the chunk alone.
+    const T* Hc = LAY == kTiled ? (const T*)a.H : (const T*)a.H + a.c0 * a.ldh;
     for (int64_t t = t_beg + blockIdx.x / 8; t < t_end; t += per_xcd) {
         const int vt = (int)(t / a.n_rbc), rb = (int)(t % a.n_rbc);
         const int64_t r0 = (int64_t)rb * kTileM;  // token offset within the chunk
@@ -649,7 +652,8 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
         const bool has_en = e0 + id.tid < e1;
         const uint32_t my_en = a.ent[has_en ? e0 + id.tid : 0] | (has_en ? 0u : 0xffffffffu);
         f32x4 acc[8][4];
-        gemm_tile_kk16<T>(acc, L, id, (const T*)a.W, a.d, n0, a.V, a.d, Hc, a.d, r0, a.cc, a.d, 0, a.d);
+        gemm_tile_kk16<T, LAY, LAY>(acc, L, id, (const T*)a.W, a.ldw, n0, a.V, a.d, Hc, a.ldh, r0, a.cc, a.d, 0,
+                                    a.d);
         const float my_pt = my_en != 0xffffffffu ? a.pt[(r0 + (my_en & 255)) * a.K + (my_en >> 16)] : 0.f;
         float l2[4];
 #pragma unroll
@@ -855,6 +859,28 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, in
             else
                 *(u32x4*)(dst + gc * ldd + gr) = v;
         }
+    }
+}
+
+// Stage-tiled copy (the kTiled operand layout of engine.h) of a row-major src [rows][ld]:
+// block (row block b, stage s) holds rows 256b .. 256b+255, columns s*SW .. s*SW+SW-1 (SW = 64
+// bytes of elements) as a contiguous [256][SW] array; entries past rows or cols are zero. A
+// workgroup writes eight consecutive blocks (128 KB) with consecutive 16-byte stores; its reads
+// are 64-byte pieces of 512-byte row segments, the rest of each line read by the same
+// workgroup's other blocks.
+template <typename T>
+__global__ __launch_bounds__(256) void k_tile_rows(const T* __restrict__ src, int64_t ld, int64_t rows, int64_t cols,
+                                                   int64_t S, T* __restrict__ dst) {
+    constexpr int VEC = 16 / (int)sizeof(T), SW = 4 * VEC;
+    const int64_t rb = blockIdx.y, s0 = (int64_t)blockIdx.x * 8;
+    const int nq = (int)min<int64_t>(8, S - s0) * 1024;  // 16-byte chunks to write
+    T* out = dst + (rb * S + s0) * (kTileM * SW);
+    for (int q = threadIdx.x; q < nq; q += 256) {
+        const int sb = q >> 10, r = (q >> 2) & 255, c = q & 3;
+        const int64_t gr = rb * kTileM + r, gc = (s0 + sb) * SW + c * VEC;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (gr < rows && gc < cols) v = *(const u32x4*)(src + gr * ld + gc);
+        *(u32x4*)(out + (int64_t)q * VEC) = v;
     }
 }
 
@@ -1929,10 +1955,11 @@ hipError_t launch_validate(const int32_t* idx, int64_t N, int64_t K, int64_t V, 
 
 hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32_t* plan_off,
                       const uint32_t* plan_ent, int n_vsplit, float2* part, float* zk, float* zt, int64_t ldzt,
-                      hipStream_t s) {
+                      hipStream_t s, int64_t tiled_S) {
     FwdArgs a;
     a.H = H;
     a.W = W;
+    a.ldh = a.ldw = tiled_S > 0 ? tiled_S : sh.d;
     a.N = sh.N;
     a.d = sh.d;
     a.V = sh.V;
@@ -1951,16 +1978,21 @@ hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32
     const int64_t cus = std::max(8, device_cus() / 8 * 8);
     const unsigned grid = (unsigned)std::min<int64_t>(cus, 8 * ((a.n_unit + 7) / 8));
     const dim3 blk(64 * kFwdWaves);
+    const bool t = tiled_S > 0;
     if (sh.act == Dt::BF16) {
         if (zt)
-            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, true, kFwdWaves>), dim3(grid), blk, 0, s, a);
+            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, true, kFwdWaves, kRow>), dim3(grid), blk, 0, s, a);
+        else if (t)
+            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, false, kFwdWaves, kTiled>), dim3(grid), blk, 0, s, a);
         else
-            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, false, kFwdWaves>), dim3(grid), blk, 0, s, a);
+            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, false, kFwdWaves, kRow>), dim3(grid), blk, 0, s, a);
     } else {
         if (zt)
-            KD_LAUNCH(kKindFwd, s, (k_fwd<float, true, kFwdWaves>), dim3(grid), blk, 0, s, a);
+            KD_LAUNCH(kKindFwd, s, (k_fwd<float, true, kFwdWaves, kRow>), dim3(grid), blk, 0, s, a);
+        else if (t)
+            KD_LAUNCH(kKindFwd, s, (k_fwd<float, false, kFwdWaves, kTiled>), dim3(grid), blk, 0, s, a);
         else
-            KD_LAUNCH(kKindFwd, s, (k_fwd<float, false, kFwdWaves>), dim3(grid), blk, 0, s, a);
+            KD_LAUNCH(kKindFwd, s, (k_fwd<float, false, kFwdWaves, kRow>), dim3(grid), blk, 0, s, a);
     }
     return hipGetLastError();
 }
@@ -1982,10 +2014,12 @@ hipError_t launch_loss_final(const Shape& sh, const double* blk_sum, int n_blk, 
 
 hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const float* lse, const float* pt,
                            const float* grad_loss, int64_t c0, int64_t cc, const int32_t* plan_off,
-                           const uint32_t* plan_ent, void* Gc, void* GT, int64_t ldgt, hipStream_t s) {
+                           const uint32_t* plan_ent, void* Gc, void* GT, int64_t ldgt, hipStream_t s,
+                           int64_t tiled_S) {
     GradArgs a;
     a.H = H;
     a.W = W;
+    a.ldh = a.ldw = tiled_S > 0 ? tiled_S : sh.d;
     a.zt = nullptr;
     a.ldzt = a.zt_col0 = 0;
     a.d = sh.d;
@@ -2009,10 +2043,18 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
     // One tile per workgroup: measured a little faster than the persistent launch, whose
     // workgroups stay in lockstep and so issue their tile stores all at once.
     const dim3 grid(grid_xcd((int64_t)a.n_vt * a.n_rbc));
-    if (sh.act == Dt::BF16)
-        KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<bf16_t, kGradWaves>), grid, dim3(64 * kGradWaves), 0, s, a);
-    else
-        KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<float, kGradWaves>), grid, dim3(64 * kGradWaves), 0, s, a);
+    const dim3 blk(64 * kGradWaves);
+    if (sh.act == Dt::BF16) {
+        if (tiled_S > 0)
+            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<bf16_t, kGradWaves, kTiled>), grid, blk, 0, s, a);
+        else
+            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<bf16_t, kGradWaves, kRow>), grid, blk, 0, s, a);
+    } else {
+        if (tiled_S > 0)
+            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<float, kGradWaves, kTiled>), grid, blk, 0, s, a);
+        else
+            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<float, kGradWaves, kRow>), grid, blk, 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -2022,6 +2064,7 @@ hipError_t launch_grad_z(const Shape& sh, const float* zt, int64_t ldzt, int64_t
     GradArgs a;
     a.H = nullptr;
     a.W = nullptr;
+    a.ldh = a.ldw = 0;
     a.zt = zt;
     a.ldzt = ldzt;
     a.zt_col0 = zt_col0;
@@ -2105,6 +2148,28 @@ hipError_t launch_transpose_blocked(Dt dt, const void* src, int64_t lds, int64_t
     else
         KD_LAUNCH(kKindTranspose, s, (k_transpose<float, true>), grid, dim3(NTHR), 0, s, (const float*)src, lds, rows,
                   cols, (float*)dst, (int64_t)0, rows_pad);
+    return hipGetLastError();
+}
+
+int64_t tiled_stages(Dt dt, int64_t cols) {
+    const int64_t sw = dt == Dt::BF16 ? 32 : 16;
+    return (cols + sw - 1) / sw;
+}
+
+int64_t tiled_bytes(Dt dt, int64_t rows, int64_t cols) {
+    return round_up(rows, kTileM) * tiled_stages(dt, cols) * 64;
+}
+
+hipError_t launch_tile_rows(Dt dt, const void* src, int64_t ld, int64_t rows, int64_t cols, void* dst,
+                            hipStream_t s) {
+    const int64_t S = tiled_stages(dt, cols);
+    const dim3 grid((unsigned)((S + 7) / 8), (unsigned)((rows + kTileM - 1) / kTileM));
+    if (dt == Dt::BF16)
+        KD_LAUNCH(kKindTranspose, s, k_tile_rows<bf16_t>, grid, dim3(NTHR), 0, s, (const bf16_t*)src, ld, rows, cols,
+                  S, (bf16_t*)dst);
+    else
+        KD_LAUNCH(kKindTranspose, s, k_tile_rows<float>, grid, dim3(NTHR), 0, s, (const float*)src, ld, rows, cols, S,
+                  (float*)dst);
     return hipGetLastError();
 }
 
