@@ -720,23 +720,29 @@ constexpr int WST = (kTileM + kWideN) * NCH4;           // chunks per stage (A t
 constexpr int WIDE_LDS_CHUNKS = 4 * WST + 4 * 64;        // four stages + four dummy slots = 148 KB
 
 // Operand of NI 16-row groups per wave (A: NI = 2 covers 256 rows; B: NI = 3 covers 320 rows,
-// the third group of waves 4-7 being the dummy). Layouts as KOperand4.
-template <typename T, bool BLK, int NI>
+// the third group of waves 4-7 being the dummy). Layouts as KOperand4; a stage-tiled operand has
+// row blocks of the tile's rows (256 or 320) and needs mn0 to be a multiple of them.
+template <typename T, int LAY, int NI, int ROWS>
 struct KOperandW {
     static constexpr int VEC = Elem<T>::VEC;
+    static constexpr bool BLK = LAY == kKBlk;
     __amdgpu_buffer_rsrc_t rsrc;
     const char* base;
     int64_t blk_bytes;
     uint32_t off[NI];
     int dst[NI];  // chunk index of the instruction's destination within a stage, or -1 (dummy)
     int chunk;
+    // ROWS: the operand's tile rows (256 or 320)
     template <typename Id>
     __device__ __forceinline__ void init(const T* src, int64_t ld, int64_t mn0, int64_t mn_lim, int stage_off,
-                                         int rows, const Id& id) {
-        const int64_t row_ld = BLK ? 256 : ld;
+                                         const Id& id) {
+        constexpr int rows = ROWS;
+        const int64_t row_ld = BLK ? 256 : LAY == kTiled ? 4 * VEC : ld;
         if constexpr (BLK) {
             base = (const char*)uniform_ptr(src + mn0 * 256);
             blk_bytes = ld * 256 * (int64_t)sizeof(T);
+        } else if constexpr (LAY == kTiled) {
+            rsrc = make_rsrc(src + (mn0 / rows) * ld * (rows * 4 * VEC));
         } else {
             rsrc = make_rsrc(src + mn0 * ld);
         }
@@ -759,6 +765,9 @@ struct KOperandW {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (k0 >> 8) * blk_bytes);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)d, 16, (int)(in ? off[t] : kOOB),
                                                      (int)((k0 & 255) * (int64_t)sizeof(T)), 0, 0);
+        } else if constexpr (LAY == kTiled) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)d, 16, (int)(in ? off[t] : kOOB),
+                                                     (int)((k0 / (4 * VEC)) * (ROWS * 64)), 0, 0);
         } else {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)d, 16, (int)(in ? off[t] : kOOB),
                                                      (int)(k0 * (int64_t)sizeof(T)), 0, 0);
@@ -771,7 +780,7 @@ struct KOperandW {
 // DMA are those above; the schedule is gemm_tile_kk16's: part 0 = A rows 0-3 while A rows 4-7
 // of the stage are read, barrier, part 1 = A rows 4-7 with the DMA of stage k+4 and the reads of
 // stage k+1 (A rows 0-3, and B into the other of two register sets).
-template <typename T, bool BA = false, bool BB = false>
+template <typename T, int BA = kRow, int BB = kRow>
 __device__ __forceinline__ void gemm_tile_w16(f32x4 (&acc)[8][5], u32x4* L, const WaveIdN<8>& id, const T* A,
                                               int64_t lda, int64_t m0, int64_t m_lim, int64_t ka_lim, const T* B,
                                               int64_t ldb, int64_t n0, int64_t n_lim, int64_t kb_lim, int64_t k_begin,
@@ -784,10 +793,10 @@ __device__ __forceinline__ void gemm_tile_w16(f32x4 (&acc)[8][5], u32x4* L, cons
         for (int j = 0; j < 5; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nk = (int)((k_end - k_begin + BKH - 1) / BKH);
     if (nk <= 0) return;
-    KOperandW<T, BA, 2> opA;
-    KOperandW<T, BB, 3> opB;
-    opA.init(A, lda, m0, m_lim, 0, kTileM, id);
-    opB.init(B, ldb, n0, n_lim, kTileM * NCH4, kWideN, id);
+    KOperandW<T, BA, 2, kTileM> opA;
+    KOperandW<T, BB, 3, kWideN> opB;
+    opA.init(A, lda, m0, m_lim, 0, id);
+    opB.init(B, ldb, n0, n_lim, kTileM * NCH4, id);
     auto kof = [&](int s) { return k_begin + (int64_t)s * BKH; };
     auto issue = [&](int s) {
         const bool live = s < nk;

@@ -40,7 +40,10 @@ constexpr int64_t kMaxD = (int64_t)1 << 20;  // keeps a tile's 256 rows of d fp3
 // tokens 6% slower). It depends on the chunk only, so the workspace does not grow with N; a
 // group the batch does not fill ends with the last chunk.
 constexpr int64_t kDwTokens = 8192;
-int64_t dw_group(const kd_problem*, int64_t C) { return std::max<int64_t>(1, kDwTokens / round_up(C, 8)); }
+// K columns per chunk in G_c^T and H_c^T: whole 32-column stages of the stage-tiled layout, the
+// columns past the chunk's rows zero.
+int64_t slot_cols(int64_t C) { return round_up(C, 32); }
+int64_t dw_group(const kd_problem*, int64_t C) { return std::max<int64_t>(1, kDwTokens / slot_cols(C)); }
 
 struct Carve {
     uintptr_t base;
@@ -113,10 +116,10 @@ struct FusedWs {
     int32_t* cplan_off;
     uint32_t* cplan_ent;
     float* pt;
-    void* Gc;   // K-blocked [Vp/256][cc][256]
-    void* GT;   // [Vp][ldgt]: G_c transposed
-    void* WT;   // K-blocked W^T [Vp/256][d][256], entries past V zero
-    void* HT;   // [d][ldgt]: H_c transposed
+    void* Gc;   // stage-tiled (K-blocked [Vp/256][cc][256] in the memory-lean backward)
+    void* GT;   // G_c^T stage-tiled, ldgt K columns: a group of chunks side by side
+    void* WT;   // W^T stage-tiled, Vp K columns, entries past V zero
+    void* HT;   // H_c^T stage-tiled, ldgt K columns
     float* dh_part;
     int64_t ldgt, group;
     int n_split;
@@ -180,17 +183,17 @@ FusedWs layout_fused(const kd_problem* p, void* ws, bool fwd_tiles = true) {
     w.cplan_off = (int32_t*)b.take(sizeof(int32_t) * n_rblocks(plan_rows) * (n_vt + 1));
     w.cplan_ent = (uint32_t*)b.take(sizeof(uint32_t) * n_rblocks(plan_rows) * kTileM * K);
     w.pt = (float*)b.take(sizeof(float) * N * K);
-    w.Gc = b.take(esize(p->act) * C * Vp);
+    w.Gc = b.take(esize(p->act) * round_up(C, kTileM) * Vp);
     if (!lean) {
         // G_c^T and H_c^T hold a group of chunks side by side (slot s at columns
         // s*round_up(C, 8)), so one dW pass reduces over the group and dW is read and written
         // once per group. The memory-lean backward keeps none of these copies (nor W^T): dH and
         // dW read G_c, W and H as they are.
         w.group = dw_group(p, C);
-        w.ldgt = w.group * round_up(C, 8);
+        w.ldgt = w.group * slot_cols(C);
         w.GT = b.take(esize(p->act) * Vp * w.ldgt);
-        w.WT = b.take(esize(p->act) * d * Vp);
-        w.HT = b.take(esize(p->act) * d * w.ldgt);
+        w.WT = b.take(esize(p->act) * round_up(d, 320) * Vp);
+        w.HT = b.take(esize(p->act) * round_up(d, 320) * w.ldgt);
     }
     w.dh_part = w.n_split > 1 ? (float*)b.take(sizeof(float) * w.n_split * C * d) : nullptr;
     if (tiled_bwd(p)) {
@@ -235,7 +238,7 @@ StoredWs layout_stored(const kd_problem* p, void* ws, bool all_rows) {
     w.n_split = dh_splits(C, d, V, true);
     w.ldzt = round_up(fwd_rows, 4);
     w.group = dw_group(p, C);
-    w.ldgt = w.group * round_up(C, 8);
+    w.ldgt = w.group * slot_cols(C);
     const int64_t n_chunks = (N + C - 1) / C;
     Carve c(ws);
     w.status = (uint32_t*)c.take(kAlign);
@@ -250,10 +253,10 @@ StoredWs layout_stored(const kd_problem* p, void* ws, bool all_rows) {
     w.part = (float2*)c.take(sizeof(float2) * 2 * n_part_rows);
     w.blk_sum = (double*)c.take(sizeof(double) * (all_rows ? combine_blocks(N) : n_chunks * combine_blocks(C)));
     w.zt = (float*)c.take(sizeof(float) * Vp * w.ldzt);
-    w.Gc = c.take(esize(p->act) * C * Vp);
+    w.Gc = c.take(esize(p->act) * round_up(C, kTileM) * Vp);
     w.GT = c.take(esize(p->act) * Vp * w.ldgt);
-    w.WT = c.take(esize(p->act) * d * Vp);
-    w.HT = c.take(esize(p->act) * d * w.ldgt);
+    w.WT = c.take(esize(p->act) * round_up(d, 320) * Vp);
+    w.HT = c.take(esize(p->act) * round_up(d, 320) * w.ldgt);
     w.dh_part = w.n_split > 1 ? (float*)c.take(sizeof(float) * w.n_split * C * d) : nullptr;
     w.bytes = c.used;
     return w;
@@ -307,7 +310,7 @@ kd_status stored_backward(const kd_problem* p, const Shape& sh, const StoredWs& 
     const int64_t C = chunk_rows(p);
     const bool one_plan = whole_plan(p);
     const int64_t plan_stride = n_vtiles(p->V) + 1;
-    const int64_t C8 = round_up(C, 8);
+    const int64_t SC = slot_cols(C);
     const size_t es = esize(p->act);
     const bool acc0 = (p->flags & KD_ACCUMULATE_DW) != 0;
     int64_t ci = 0;
@@ -317,13 +320,13 @@ kd_status stored_backward(const kd_problem* p, const Shape& sh, const StoredWs& 
         const int64_t slot = ci % w.group;
         if (!one_plan) KD_TRY(launch_plan(idx, c0, c0 + cc, p->K, p->V, w.plan_off, w.plan_ent, s));
         const int32_t* c_off = w.plan_off + (one_plan ? (c0 / kTileM) * plan_stride : 0);
-        KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
-                                (char*)w.HT + slot * C8 * es, w.ldgt, round_up(cc, 8), s));
+        KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d, w.HT, w.ldgt, slot * SC,
+                                round_up(cc, 32), s));
         KD_TRY(launch_grad_z(sh, w.zt, w.ldzt, c0, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.plan_ent, w.Gc,
-                             (char*)w.GT + slot * C8 * es, w.ldgt, s));
+                             w.GT, w.ldgt, slot * SC, s));
         KD_TRY(launch_dh(sh, w.Gc, 0, nullptr, w.WT, c0, cc, w.n_split, w.dh_part, dH, s));
         if (slot == w.group - 1 || c0 + cc >= p->N) {
-            KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * C8 + cc, acc0 || dw_written, dW, s));
+            KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * SC + cc, acc0 || dw_written, dW, s));
             dw_written = true;
         }
     }
@@ -484,12 +487,10 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
     const bool acc0 = (p->flags & KD_ACCUMULATE_DW) != 0;
     const bool lean = low_memory(p);
     // W^T once per call: dH = G_c W then reads both operands with the vocabulary contiguous.
-    if (!lean) KD_TRY(launch_transpose_blocked(sh.act, W, p->d, p->V, p->d, w.WT, Vp, s));
+    if (!lean) KD_TRY(launch_transpose(sh.act, W, p->d, p->V, p->d, w.WT, Vp, 0, Vp, s));
     // Stage-tiled W once per call, and each chunk's rows of H before its gradient kernel.
-    if (w.cWt) KD_TRY(launch_tile_rows(sh.act, W, p->d, p->V, p->d, w.cWt, s));
-    const void* gW = w.cWt ? w.cWt : W;
-    const int64_t gS = w.cWt ? w.tS : 0;
-    const int64_t C8 = round_up(C, 8);
+    if (!lean) KD_TRY(launch_tile_rows(sh.act, W, p->d, p->V, p->d, w.cWt, s));
+    const int64_t SC = slot_cols(C);
     const size_t es = esize(p->act);
     const bool one_plan = whole_plan(p);
     const int64_t plan_stride = n_vtiles(p->V) + 1;
@@ -506,7 +507,7 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
         if (lean) {
             // G_c only; dH reads W as stored and dW reads G_c and H_c as they are.
             KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.cplan_ent, w.Gc,
-                                   nullptr, 0, s));
+                                   false, nullptr, 0, 0, s));
             KD_TRY(launch_dh(sh, w.Gc, 0, W, nullptr, c0, cc, w.n_split, w.dh_part, dH, s, true));
             if (want_dw) {
                 KD_TRY(launch_dw(sh, w.Gc, 0, H, c0, cc, acc0 || dw_written, dW, s, true));
@@ -516,16 +517,16 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
         }
         // H_c^T into its slot, so that dW = G^T H reads both operands with the rows contiguous
         if (want_dw)
-            KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
-                                    (char*)w.HT + slot * C8 * es, w.ldgt, round_up(cc, 8), s));
+            KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d, w.HT, w.ldgt, slot * SC,
+                                    round_up(cc, 32), s));
         // Without dW, G^T is not needed: the gradient kernel skips those stores.
-        if (w.cHt) KD_TRY(launch_tile_rows(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d, w.cHt, s));
-        KD_TRY(launch_bwd_grad(sh, w.cHt ? w.cHt : H, gW, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off,
-                               w.cplan_ent, w.Gc, want_dw ? (char*)w.GT + slot * C8 * es : nullptr, w.ldgt, s, gS));
+        KD_TRY(launch_tile_rows(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d, w.cHt, s));
+        KD_TRY(launch_bwd_grad(sh, w.cHt, w.cWt, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.cplan_ent, w.Gc,
+                               true, want_dw ? w.GT : nullptr, w.ldgt, slot * SC, s, w.tS));
         KD_TRY(launch_dh(sh, w.Gc, 0, W, w.WT, c0, cc, w.n_split, w.dh_part, dH, s));
-        // One dW pass per group of chunks (K = the group's rows; the slots are zero-padded to 8)
+        // One dW pass per group of chunks (K = the group's rows; each slot zero-padded to 32)
         if (want_dw && (slot == w.group - 1 || c0 + cc >= p->N)) {
-            KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * C8 + cc, acc0 || dw_written, dW, s));
+            KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * SC + cc, acc0 || dw_written, dW, s));
             dw_written = true;
         }
     }
@@ -633,7 +634,7 @@ kd_status kd_chunked_kl(const kd_problem* p, const void* H, const void* W, const
     int n_blk = 0;
     KD_TRY(launch_combine(sh, w.part, 2 * w.n_vsplit, w.zk, tlog, lse, row_kl, w.blk_sum, &n_blk, s));
     KD_TRY(launch_loss_final(sh, w.blk_sum, n_blk, loss, s));
-    KD_TRY(launch_transpose_blocked(sh.act, W, p->d, p->V, p->d, w.WT, n_vtiles(p->V) * kTileN, s));
+    KD_TRY(launch_transpose(sh.act, W, p->d, p->V, p->d, w.WT, n_vtiles(p->V) * kTileN, 0, n_vtiles(p->V) * kTileN, s));
     return stored_backward(p, sh, w, H, idx, lse, grad_loss, dH, dW, s);
 }
 
@@ -658,12 +659,12 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
     const int64_t C = chunk_rows(p);
     const bool one_plan = whole_plan(p);
     const int64_t plan_stride = n_vtiles(p->V) + 1;
-    const int64_t C8 = round_up(C, 8);
+    const int64_t SC = slot_cols(C);
     const size_t es = esize(p->act), ets = esize(p->tlogit);
     const bool acc0 = (p->flags & KD_ACCUMULATE_DW) != 0;
     if (one_plan) KD_TRY(launch_plan(idx, 0, p->N, p->K, p->V, w.plan_off, w.plan_ent, s));
     KD_TRY(launch_teacher_prob(tlog, sh.tlog, 0, p->N, p->K, p->T, w.pt, s));
-    KD_TRY(launch_transpose_blocked(sh.act, W, p->d, p->V, p->d, w.WT, n_vtiles(p->V) * kTileN, s));
+    KD_TRY(launch_transpose(sh.act, W, p->d, p->V, p->d, w.WT, n_vtiles(p->V) * kTileN, 0, n_vtiles(p->V) * kTileN, s));
     int64_t ci = 0;
     int n_blk = 0;
     bool dw_written = false;
@@ -682,13 +683,13 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
         KD_TRY(launch_combine(shc, w.part, 2 * nvs, w.zk + c0 * p->K, (const char*)tlog + c0 * p->K * ets, lse + c0,
                               row_kl ? row_kl + c0 : nullptr, w.blk_sum + n_blk, &nb, s));
         n_blk += nb;
-        KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d,
-                                (char*)w.HT + slot * C8 * es, w.ldgt, round_up(cc, 8), s));
+        KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d, w.HT, w.ldgt, slot * SC,
+                                round_up(cc, 32), s));
         KD_TRY(launch_grad_z(sh, w.zt, w.ldzt, 0, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.plan_ent, w.Gc,
-                             (char*)w.GT + slot * C8 * es, w.ldgt, s));
+                             w.GT, w.ldgt, slot * SC, s));
         KD_TRY(launch_dh(sh, w.Gc, 0, nullptr, w.WT, c0, cc, w.n_split, w.dh_part, dH, s));
         if (slot == w.group - 1 || c0 + cc >= p->N) {
-            KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * C8 + cc, acc0 || dw_written, dW, s));
+            KD_TRY(launch_dw_t(sh, w.GT, w.ldgt, w.HT, w.ldgt, slot * SC + cc, acc0 || dw_written, dW, s));
             dw_written = true;
         }
     }

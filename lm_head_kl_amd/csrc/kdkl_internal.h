@@ -86,21 +86,25 @@ hipError_t launch_loss_final(const Shape& sh, const double* blk_sum, int n_blk, 
                              hipStream_t s);
 
 // Backward, one chunk of rows [c0, c0 + cc):
-//   G_c = g*T/n_norm*(softmax(z/T) - P_t) in the act dtype, K-blocked [Vp/256][cc][256] (entry
-//   (t, v) at ((v/256)*cc + t)*256 + v%256; entries v >= V zero), and, if GT is not null, its
-//   transpose G_c^T [Vp, ldgt] with columns [cc, round_up(cc, 8)) zero.
-// H and W as in launch_fwd; a stage-tiled H holds the chunk's cc rows alone (row 0 = row c0).
+//   G_c = g*T/n_norm*(softmax(z/T) - P_t) in the act dtype (entries v >= V zero), rows = the
+//   chunk's tokens, K = vocabulary: stage-tiled (g_tiled; row blocks of 256, Vp/SW stages) or
+//   K-blocked [Vp/256][cc][256] (entry (t, v) at ((v/256)*cc + t)*256 + v%256);
+//   if GT is not null, G_c^T stage-tiled (row blocks of 256, ldgt/SW stages), the chunk's tokens
+//   at K columns gt_col0 + [0, cc), zero for [cc, round_up(cc, 32)); ldgt and gt_col0 multiples
+//   of 32.
+// H and W as in launch_fwd (a stage-tiled H holds the chunk's cc rows alone: row 0 = row c0);
+// stage-tiled H and W go with a stage-tiled G_c, row-major ones with a K-blocked G_c.
 hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const float* lse,
                            const float* pt, const float* grad_loss, int64_t c0, int64_t cc,
-                           const int32_t* plan_off, const uint32_t* plan_ent, void* Gc,
-                           void* GT, int64_t ldgt, hipStream_t s, int64_t tiled_S = 0);
+                           const int32_t* plan_off, const uint32_t* plan_ent, void* Gc, bool g_tiled,
+                           void* GT, int64_t ldgt, int64_t gt_col0, hipStream_t s, int64_t tiled_S = 0);
 
-// The same G_c and G_c^T as launch_bwd_grad, from stored logits z^T [Vp][ldzt] (chunk row r
-// in column zt_col0 + r) instead of recomputing them.
+// The same stage-tiled G_c and G_c^T as launch_bwd_grad, from stored logits z^T [Vp][ldzt]
+// (chunk row r in column zt_col0 + r) instead of recomputing them.
 hipError_t launch_grad_z(const Shape& sh, const float* zt, int64_t ldzt, int64_t zt_col0,
                          const float* lse, const float* pt, const float* grad_loss, int64_t c0,
                          int64_t cc, const int32_t* plan_off, const uint32_t* plan_ent, void* Gc,
-                         void* GT, int64_t ldgt, hipStream_t s);
+                         void* GT, int64_t ldgt, int64_t gt_col0, hipStream_t s);
 
 // Offline cache: per row of X [N][ld] (V entries), the K largest values and their ids, largest
 // first, ties in lower-id order.
@@ -115,15 +119,15 @@ int64_t tiled_bytes(Dt dt, int64_t rows, int64_t cols);
 hipError_t launch_tile_rows(Dt dt, const void* src, int64_t ld, int64_t rows, int64_t cols, void* dst,
                             hipStream_t s);
 
-// dst[c][r] = src[r][c] (r < rows), zero for rows <= r < rows_pad; cols, rows_pad multiples of 8.
+// Transpose of src [rows][lds] (cols used) into a stage-tiled operand with row blocks of 320 and
+// kdst K columns (kdst/SW stages): result row c < cols holds src[r][c] at K column k0 + r for r <
+// rows, zero for rows <= r < rows_pad. cols, lds and rows_pad multiples of 8; kdst and k0
+// multiples of 32. The result takes round_up(cols, 320) * kdst elements.
 hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst,
-                            int64_t ldd, int64_t rows_pad, hipStream_t s);
-// The same transpose into the K-blocked layout [rows_pad/256][cols][256] (rows_pad % 256 == 0).
-hipError_t launch_transpose_blocked(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols,
-                                    void* dst, int64_t rows_pad, hipStream_t s);
+                            int64_t kdst, int64_t k0, int64_t rows_pad, hipStream_t s);
 
-// dH rows [c0, c0+cc) = G_c W. With WT not null, G_c is the K-blocked tile written by
-// launch_bwd_grad and WT is W^T K-blocked [Vp/256][d][256]; with WT null, W is read as stored
+// dH rows [c0, c0+cc) = G_c W. With WT not null, G_c is the stage-tiled tile written by
+// launch_bwd_grad and WT is W^T from launch_transpose (kdst = Vp); with WT null, W is read as stored
 // and G_c is either that K-blocked tile (g_blocked) or row-major [cc][ldg]. Split over the
 // vocabulary into n_split fp32 partials when n_split > 1 (part: [n_split][cc][d]), then
 // reduced in a fixed order.
@@ -135,7 +139,8 @@ hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W
 // the gradient kernel's K-blocked tile [Vp/256][cc][256] (g_blocked; ldg unused).
 hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H, int64_t c0,
                      int64_t cc, bool accumulate, float* dW, hipStream_t s, bool g_blocked = false);
-// dW (+)= G_c^T H_c from G_c^T [Vp][ldgt] and H_c^T [d][ldht] (both K contiguous).
+// dW (+)= G_c^T H_c over K columns [0, cc) from stage-tiled G_c^T (launch_bwd_grad, ldgt K
+// columns) and H_c^T (launch_transpose, kdst = ldht).
 hipError_t launch_dw_t(const Shape& sh, const void* GT, int64_t ldgt, const void* HT, int64_t ldht,
                        int64_t cc, bool accumulate, float* dW, hipStream_t s);
 

@@ -111,6 +111,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // Row of accumulator element e of lane half h inside its 32 x 32 MFMA block.
 __device__ __forceinline__ int blk_row(int e, int h) { return 8 * (e >> 2) + 4 * h + (e & 3); }
 
+// Element offset of (row, k) in a stage-tiled operand (engine.h, kTiled) with row blocks of RB
+// rows and S stages of SW = 64 bytes per row block.
+template <typename T, int RB>
+__device__ __forceinline__ int64_t tiled_at(int64_t row, int64_t k, int64_t S) {
+    constexpr int SW = 64 / (int)sizeof(T);
+    return ((row / RB) * S + k / SW) * (int64_t)(RB * SW) + (row % RB) * SW + k % SW;
+}
+
 // Staging of half a transposed tile in LDS: 128 rows (vocabulary entries) x 256 columns
 // (tokens) of fp32. Stage row sr holds tile row (sr/64)*128 + pass*64 + sr%64. Column t of row
 // r sits at t ^ st_swz(r); the XOR touches bits 2..5 only, so runs of 4 columns stay
@@ -521,9 +529,14 @@ struct GradArgs {
     const int32_t* off;
     const uint32_t* ent;
     int n_vt, n_rbc;
-    void* G;     // K-blocked [Vp/256][cc][256]: entry (t, v) at ((v/256)*cc + t)*256 + v%256
-    void* GT;    // [Vp][ldgt]: G transposed, columns [cc, ccp) zero; nullptr to skip
-    int64_t ldgt, ccp;
+    // G_c, rows = the chunk's tokens, K = vocabulary: stage-tiled (row blocks of 256, Vp/SW
+    // stages), or K-blocked [Vp/256][cc][256] (entry (t, v) at ((v/256)*cc + t)*256 + v%256)
+    void* G;
+    // G_c^T, rows = vocabulary, K = tokens of the dW group: stage-tiled (row blocks of 256, ldgt/SW
+    // stages), the chunk's tokens at K columns gt_col0 .. gt_col0 + cc, zero up to gt_col0 + ccp;
+    // nullptr to skip
+    void* GT;
+    int64_t ldgt, ccp, gt_col0;
     const float* zt;  // stored logits z^T [Vp][ldzt] (k_grad_z), chunk columns from zt_col0
     int64_t ldzt, zt_col0;
 };
@@ -549,10 +562,11 @@ __device__ __forceinline__ void store8(T* dst, const float (&x)[8]) {
 // The plan fills each bucket in atomic order, so whether an entry is among the first NT (held
 // in registers) or comes from the loop changes between calls; both paths subtract with one
 // explicit fused multiply-add, so G does not depend on that order.
-template <typename T, int NW>
+template <typename T, int NW, int GL>
 __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, int pq, const WaveIdN<NW>& ie, int vt,
                                               int64_t r0, int64_t n0, int e0, int e1, uint32_t my_en, float my_pt,
                                               float gs) {
+    constexpr int SW = 64 / (int)sizeof(T);
     constexpr int NT = 64 * NW, IT = 4096 / NT;  // items per thread of each output layout
     if (my_en != 0xffffffffu && ((my_en >> 14) & 1) == (uint32_t)pq) {
         const int r = my_en & 255, c = (my_en >> 8) & 255;
@@ -568,6 +582,25 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
         x = fmaf(-gs, a.pt[(r0 + r) * a.K + k], x);
     }
     lds_barrier();
+    if constexpr (GL == kTiled) {
+        // Stage-tiled G rows: token tl, group g of 8 vocabulary entries (stage rows 8g .. 8g+7,
+        // read one by one); 16 lanes write a token's 128 entries of the pass, 64 bytes in each of
+        // four stage blocks, and the next 16 lanes the next token's, the other half of each
+        // 128-byte line.
+#pragma unroll 4
+        for (int q = 0; q < 4096 / NT; ++q) {
+            const int it = ie.tid + NT * q;
+            const int g = it & 15, tl = it >> 4;
+            const int64_t tr = r0 + tl;
+            if (tr < a.cc) {
+                float x[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) x[u] = stage[st_idx(8 * g + u, tl)];
+                const int vb = (g >> 3) * 128 + pq * 64 + (g & 7) * 8;
+                store8<T>((T*)a.G + tiled_at<T, kTileM>(tr, n0 + vb, (int64_t)a.n_vt * (kTileN / SW)), x);
+            }
+        }
+    } else {
     // G rows: group g of 8 vocabulary entries (stage rows 8g .. 8g+7) by a group of 4 tokens.
     // A lane reads the 8 x 4 block with 16-byte LDS reads (4 tokens of one stage row each) and
     // writes the 4 tokens' 8-entry segments; 16 consecutive lanes cover one token's 128
@@ -590,6 +623,7 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
             }
         }
     }
+    }
     // G^T rows: vocabulary entry of stage row sr, group cb of 8 tokens; 32 lanes write a row's
     // 256 tokens.
     if (a.GT) {
@@ -604,14 +638,14 @@ __device__ __forceinline__ void grad_pass_out(const GradArgs& a, float* stage, i
                 const f32x4 v1 = *(const f32x4*)(row + ((cb * 8 + 4) ^ st_swz(sr)));
                 const float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
                 const int vr = (sr >> 6) * 128 + pq * 64 + (sr & 63);
-                store8<T>((T*)a.GT + (n0 + vr) * a.ldgt + tr, x);
+                store8<T>((T*)a.GT + tiled_at<T, kTileM>(n0 + vr, a.gt_col0 + tr, a.ldgt / SW), x);
             }
         }
     }
     lds_barrier();
 }
 
-template <typename T, int NW, int LAY>
+template <typename T, int NW, int LAY, int GL>
 __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
     static_assert(NW == 8, "the gradient kernel runs on eight waves with 16 x 16 blocks");
     constexpr int NT = 64 * NW;
@@ -678,7 +712,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_bwd_grad(GradArgs a) {
                 }
             }
             lds_barrier();
-            grad_pass_out<T, NW>(a, stage, pq, ie, vt, r0, n0, e0, e1, my_en, my_pt, gs);
+            grad_pass_out<T, NW, GL>(a, stage, pq, ie, vt, r0, n0, e0, e1, my_en, my_pt, gs);
         }
     }
 }
@@ -696,6 +730,7 @@ constexpr int kGzRows = 64;  // vocabulary rows per pass
 template <typename T>
 __global__ __launch_bounds__(256, 2) void k_grad_z(GradArgs a) {
     constexpr int IT = kGzRows * kTileM / 4 / NTHR;  // 16-byte items per thread per pass (16)
+    constexpr int SW = 64 / (int)sizeof(T);
     __shared__ u32x4 L[kGzRows * SST / 4 + kTileM / 4];
     float* stage = (float*)L;
     float* lse2 = (float*)(L + kGzRows * SST / 4);
@@ -783,7 +818,8 @@ __global__ __launch_bounds__(256, 2) void k_grad_z(GradArgs a) {
                 float x[8];
 #pragma unroll
                 for (int u = 0; u < 8; ++u) x[u] = stage[st_idx(8 * g + u, tl)];
-                store8<T>((T*)a.G + ((int64_t)vt * a.cc + tr) * kTileN + pq * kGzRows + 8 * g, x);
+                store8<T>((T*)a.G + tiled_at<T, kTileM>(tr, n0 + pq * kGzRows + 8 * g, (int64_t)a.n_vt * (kTileN / SW)),
+                          x);
             }
         }
         // G^T rows: vocabulary row sr of the pass, group cb of 8 tokens; 32 lanes write a row's
@@ -799,7 +835,7 @@ __global__ __launch_bounds__(256, 2) void k_grad_z(GradArgs a) {
                     const f32x4 v0 = *(const f32x4*)(row + ((cb * 8) ^ st_swz(sr)));
                     const f32x4 v1 = *(const f32x4*)(row + ((cb * 8 + 4) ^ st_swz(sr)));
                     const float x[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-                    store8<T>((T*)a.GT + (n0 + pq * kGzRows + sr) * a.ldgt + tr, x);
+                    store8<T>((T*)a.GT + tiled_at<T, kTileM>(n0 + pq * kGzRows + sr, a.gt_col0 + tr, a.ldgt / SW), x);
                 }
             }
         }
@@ -818,15 +854,19 @@ __global__ __launch_bounds__(256, 2) void k_grad_z(GradArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Transpose: dst[c*ldd + r] = src[r*lds + c] for r < rows, zero for rows <= r < rows_pad,
-// c < cols. 64 x 64 tiles through LDS. cols and rows_pad are multiples of 8.
+// Transpose into a stage-tiled operand with row blocks of 320 (engine.h, kTiled), for the wide
+// dH and dW tiles: result row c (c < cols) at K column k0 + r holds src[r*lds + c] for r < rows
+// and zero for rows <= r < rows_pad; the result has S stages per row block. 64 x 64 tiles
+// through LDS.
 
-template <typename T, bool BLK>
+template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, int64_t lds, int64_t rows,
-                                                   int64_t cols, T* __restrict__ dst, int64_t ldd, int64_t rows_pad) {
+                                                   int64_t cols, T* __restrict__ dst, int64_t S, int64_t k0,
+                                                   int64_t rows_pad) {
     // 16-byte global accesses: VEC elements of a source row per load, VEC consecutive rows of
-    // one column per store. cols, lds, ldd and rows_pad are multiples of 8, so a vector never
-    // leaves its row. The LDS tile is padded to an odd word stride.
+    // one column per store. cols, lds and rows_pad are multiples of VEC and k0 of the stage
+    // width, so a vector never leaves its row or its stage. The LDS tile is padded to an odd word
+    // stride.
     constexpr int VEC = 16 / (int)sizeof(T);
     constexpr int LDW = 64 + 4 / (int)sizeof(T);  // row stride in elements: 33 (bf16) or 65 (fp32) words
     constexpr int CPR = 64 / VEC;                 // vectors per tile row
@@ -854,10 +894,7 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, in
             T* e = (T*)&v;
 #pragma unroll
             for (int u = 0; u < VEC; ++u) e[u] = tile[rv + u][c];
-            if constexpr (BLK)
-                *(u32x4*)(dst + ((gr >> 8) * cols + gc) * 256 + (gr & 255)) = v;
-            else
-                *(u32x4*)(dst + gc * ldd + gr) = v;
+            *(u32x4*)(dst + tiled_at<T, kWideN>(gc, k0 + gr, S)) = v;
         }
     }
 }
@@ -890,9 +927,9 @@ __global__ __launch_bounds__(256) void k_tile_rows(const T* __restrict__ src, in
 // 256 x 320 tiles (k_dh_w).
 
 struct DhArgs {
-    const void* G;   // G_c [cc][ldg] row-major, or K-blocked [Vp/256][cc][256] (with W^T)
+    const void* G;   // G_c [cc][ldg] row-major or K-blocked [Vp/256][cc][256]; stage-tiled with W^T
     int64_t ldg, Vp;
-    const void* W;   // W [V][d], or W^T K-blocked [Vp/256][d][256], zero past V
+    const void* W;   // W [V][d], or W^T stage-tiled (row blocks of 320, Vp/SW stages), zero past V
     int64_t d, V;
     int64_t c0, cc;
     int64_t kper;
@@ -943,9 +980,10 @@ __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
         }
 }
 
-// Same product on 256 x 320 tiles (tokens x hidden) with K-blocked G_c and W^T.
+// Same product on 256 x 320 tiles (tokens x hidden) with stage-tiled G_c and W^T.
 template <typename T>
 __global__ __launch_bounds__(512, 1) void k_dh_w(DhArgs a) {
+    constexpr int SW = 64 / (int)sizeof(T);
     __shared__ u32x4 L[WIDE_LDS_CHUNKS];
     const WaveIdN<8> id;
     const int64_t n_tiles = (int64_t)a.n_split * a.n_nt * a.n_mt;
@@ -957,8 +995,8 @@ __global__ __launch_bounds__(512, 1) void k_dh_w(DhArgs a) {
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kWideN;
     const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
     f32x4 acc[8][5];
-    gemm_tile_w16<T, true, true>(acc, L, id, (const T*)a.G, a.cc, m0, a.cc, k_end, (const T*)a.W, a.d, n0, a.d,
-                                 k_end, k_begin, k_end);
+    gemm_tile_w16<T, kTiled, kTiled>(acc, L, id, (const T*)a.G, a.Vp / SW, m0, a.cc, k_end, (const T*)a.W, a.Vp / SW,
+                                     n0, a.d, k_end, k_begin, k_end);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -1006,10 +1044,12 @@ __global__ __launch_bounds__(256) void k_dh_reduce(const float* __restrict__ par
 // (k_dw_w).
 
 struct DwArgs {
-    const void* G;   // G_c [cc][ldg], G_c K-blocked [Vp/256][cc][256] (g_blk), or G_c^T [Vp][ldg] (K contiguous)
+    // G_c [cc][ldg], G_c K-blocked [Vp/256][cc][256] (g_blk), or G_c^T stage-tiled (row blocks of
+    // 256, ldg/SW stages)
+    const void* G;
     int64_t ldg, Vp;
     int g_blk;
-    const void* H;   // H (rows from c0), or H_c^T [d][ldh] (K contiguous)
+    const void* H;   // H (rows from c0), or H_c^T stage-tiled (row blocks of 320, ldh/SW stages)
     int64_t ldh;
     int64_t d, V;
     int64_t c0, cc, ccp;
@@ -1089,7 +1129,7 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
     }
 }
 
-// Same product on 256 x 320 tiles (vocabulary x hidden), operands G_c^T and H_c^T (K contiguous).
+// Same product on 256 x 320 tiles (vocabulary x hidden), operands G_c^T and H_c^T (stage-tiled).
 // Read-modify-write through LDS in four passes of 64 rows: pass p stages block rows 2p and 2p+1
 // of every wave, 32 rows of its 128 (stage row wm*32 + r, tile row wm*128 + 32p + r). Stage rows
 // are kWSS floats apart; kWSS % 16 == 4 puts the four row groups a write touches (rows 4 apart)
@@ -1100,6 +1140,7 @@ constexpr int kWSS = 324;
 template <typename T>
 __global__ __launch_bounds__(512, 1) void k_dw_w(DwArgs a) {
     constexpr int NT = 512, IB = 5;  // items per thread per batch; 2 batches x 512 x 5 = 64 rows x 80
+    constexpr int SW = 64 / (int)sizeof(T);
     __shared__ u32x4 L[WIDE_LDS_CHUNKS];
     const WaveIdN<8> id;
     const int64_t n_tiles = (int64_t)a.n_mt * a.n_nt;
@@ -1108,8 +1149,8 @@ __global__ __launch_bounds__(512, 1) void k_dw_w(DwArgs a) {
     const int mt = (int)(t / a.n_nt), nt = (int)(t % a.n_nt);
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kWideN;
     f32x4 acc[8][5];
-    gemm_tile_w16<T>(acc, L, id, (const T*)a.G, a.ldg, m0, a.Vp, a.ccp, (const T*)a.H, a.ldh, n0, a.d, a.ccp, 0,
-                     a.ccp);
+    gemm_tile_w16<T, kTiled, kTiled>(acc, L, id, (const T*)a.G, a.ldg / SW, m0, a.Vp, a.ccp, (const T*)a.H, a.ldh / SW,
+                                     n0, a.d, a.ccp, 0, a.ccp);
     const WaveIdN<8> ie = id.fresh();
     float* stage = (float*)L;
     // dW is addressed through a descriptor at the tile origin with 32-bit offsets (d <= 2^20
@@ -2014,8 +2055,8 @@ hipError_t launch_loss_final(const Shape& sh, const double* blk_sum, int n_blk, 
 
 hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const float* lse, const float* pt,
                            const float* grad_loss, int64_t c0, int64_t cc, const int32_t* plan_off,
-                           const uint32_t* plan_ent, void* Gc, void* GT, int64_t ldgt, hipStream_t s,
-                           int64_t tiled_S) {
+                           const uint32_t* plan_ent, void* Gc, bool g_tiled, void* GT, int64_t ldgt, int64_t gt_col0,
+                           hipStream_t s, int64_t tiled_S) {
     GradArgs a;
     a.H = H;
     a.W = W;
@@ -2039,28 +2080,35 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
     a.G = Gc;
     a.GT = GT;
     a.ldgt = ldgt;
-    a.ccp = round_up(cc, 8);
+    a.gt_col0 = gt_col0;
+    a.ccp = round_up(cc, 32);
+    if (GT && (ldgt % 32 != 0 || gt_col0 % 32 != 0)) return hipErrorInvalidValue;
     // One tile per workgroup: measured a little faster than the persistent launch, whose
     // workgroups stay in lockstep and so issue their tile stores all at once.
     const dim3 grid(grid_xcd((int64_t)a.n_vt * a.n_rbc));
     const dim3 blk(64 * kGradWaves);
+    // Operand layouts: stage-tiled H and W with a stage-tiled G_c, or as stored with a K-blocked
+    // G_c (the memory-lean backward).
+    if ((tiled_S > 0) != g_tiled) return hipErrorInvalidValue;
     if (sh.act == Dt::BF16) {
         if (tiled_S > 0)
-            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<bf16_t, kGradWaves, kTiled>), grid, blk, 0, s, a);
+            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<bf16_t, kGradWaves, kTiled, kTiled>), grid, blk, 0, s, a);
         else
-            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<bf16_t, kGradWaves, kRow>), grid, blk, 0, s, a);
+            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<bf16_t, kGradWaves, kRow, kKBlk>), grid, blk, 0, s, a);
     } else {
         if (tiled_S > 0)
-            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<float, kGradWaves, kTiled>), grid, blk, 0, s, a);
+            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<float, kGradWaves, kTiled, kTiled>), grid, blk, 0, s, a);
         else
-            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<float, kGradWaves, kRow>), grid, blk, 0, s, a);
+            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<float, kGradWaves, kRow, kKBlk>), grid, blk, 0, s, a);
     }
     return hipGetLastError();
 }
 
 hipError_t launch_grad_z(const Shape& sh, const float* zt, int64_t ldzt, int64_t zt_col0, const float* lse,
                          const float* pt, const float* grad_loss, int64_t c0, int64_t cc, const int32_t* plan_off,
-                         const uint32_t* plan_ent, void* Gc, void* GT, int64_t ldgt, hipStream_t s) {
+                         const uint32_t* plan_ent, void* Gc, void* GT, int64_t ldgt, int64_t gt_col0,
+                         hipStream_t s) {
+    if (GT && (ldgt % 32 != 0 || gt_col0 % 32 != 0)) return hipErrorInvalidValue;
     GradArgs a;
     a.H = nullptr;
     a.W = nullptr;
@@ -2085,7 +2133,8 @@ hipError_t launch_grad_z(const Shape& sh, const float* zt, int64_t ldzt, int64_t
     a.G = Gc;
     a.GT = GT;
     a.ldgt = ldgt;
-    a.ccp = round_up(cc, 8);
+    a.gt_col0 = gt_col0;
+    a.ccp = round_up(cc, 32);
     const dim3 grid(grid_xcd((int64_t)a.n_vt * a.n_rbc));
     if (sh.act == Dt::BF16)
         KD_LAUNCH(kKindGradZ, s, k_grad_z<bf16_t>, grid, dim3(NTHR), 0, s, a);
@@ -2126,28 +2175,17 @@ hipError_t launch_topk(Dt dt, const void* X, int64_t ld, int64_t N, int64_t V, i
     return hipGetLastError();
 }
 
-hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst, int64_t ldd,
-                            int64_t rows_pad, hipStream_t s) {
+hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst, int64_t kdst,
+                            int64_t k0, int64_t rows_pad, hipStream_t s) {
+    const int64_t sw = dt == Dt::BF16 ? 32 : 16;
+    if (kdst % sw != 0 || k0 % sw != 0 || k0 + rows_pad > kdst) return hipErrorInvalidValue;
     const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows_pad + 63) / 64));
     if (dt == Dt::BF16)
-        KD_LAUNCH(kKindTranspose, s, (k_transpose<bf16_t, false>), grid, dim3(NTHR), 0, s, (const bf16_t*)src, lds, rows,
-                  cols, (bf16_t*)dst, ldd, rows_pad);
+        KD_LAUNCH(kKindTranspose, s, k_transpose<bf16_t>, grid, dim3(NTHR), 0, s, (const bf16_t*)src, lds, rows, cols,
+                  (bf16_t*)dst, kdst / sw, k0, rows_pad);
     else
-        KD_LAUNCH(kKindTranspose, s, (k_transpose<float, false>), grid, dim3(NTHR), 0, s, (const float*)src, lds, rows,
-                  cols, (float*)dst, ldd, rows_pad);
-    return hipGetLastError();
-}
-
-hipError_t launch_transpose_blocked(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst,
-                                    int64_t rows_pad, hipStream_t s) {
-    if (rows_pad % 256 != 0) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows_pad + 63) / 64));
-    if (dt == Dt::BF16)
-        KD_LAUNCH(kKindTranspose, s, (k_transpose<bf16_t, true>), grid, dim3(NTHR), 0, s, (const bf16_t*)src, lds, rows,
-                  cols, (bf16_t*)dst, (int64_t)0, rows_pad);
-    else
-        KD_LAUNCH(kKindTranspose, s, (k_transpose<float, true>), grid, dim3(NTHR), 0, s, (const float*)src, lds, rows,
-                  cols, (float*)dst, (int64_t)0, rows_pad);
+        KD_LAUNCH(kKindTranspose, s, k_transpose<float>, grid, dim3(NTHR), 0, s, (const float*)src, lds, rows, cols,
+                  (float*)dst, kdst / sw, k0, rows_pad);
     return hipGetLastError();
 }
 
