@@ -93,7 +93,7 @@ hipError_t launch_loss_final(const Shape& sh, const double* blk_sum, int n_blk, 
 //   at K columns gt_col0 + [0, cc), zero for [cc, round_up(cc, 32)); ldgt and gt_col0 multiples
 //   of 32.
 // H and W as in launch_fwd (a stage-tiled H holds the chunk's cc rows alone: row 0 = row c0);
-// stage-tiled H and W go with a stage-tiled G_c, row-major ones with a K-blocked G_c.
+// stage-tiled H and W need a stage-tiled G_c.
 hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const float* lse,
                            const float* pt, const float* grad_loss, int64_t c0, int64_t cc,
                            const int32_t* plan_off, const uint32_t* plan_ent, void* Gc, bool g_tiled,

@@ -2087,17 +2087,21 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
     // workgroups stay in lockstep and so issue their tile stores all at once.
     const dim3 grid(grid_xcd((int64_t)a.n_vt * a.n_rbc));
     const dim3 blk(64 * kGradWaves);
-    // Operand layouts: stage-tiled H and W with a stage-tiled G_c, or as stored with a K-blocked
-    // G_c (the memory-lean backward).
-    if ((tiled_S > 0) != g_tiled) return hipErrorInvalidValue;
+    // Operand layouts: H and W stage-tiled or as stored; G_c stage-tiled, or K-blocked (the
+    // memory-lean backward, which reads H and W as stored).
+    if (tiled_S > 0 && !g_tiled) return hipErrorInvalidValue;
     if (sh.act == Dt::BF16) {
         if (tiled_S > 0)
             KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<bf16_t, kGradWaves, kTiled, kTiled>), grid, blk, 0, s, a);
+        else if (g_tiled)
+            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<bf16_t, kGradWaves, kRow, kTiled>), grid, blk, 0, s, a);
         else
             KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<bf16_t, kGradWaves, kRow, kKBlk>), grid, blk, 0, s, a);
     } else {
         if (tiled_S > 0)
             KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<float, kGradWaves, kTiled, kTiled>), grid, blk, 0, s, a);
+        else if (g_tiled)
+            KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<float, kGradWaves, kRow, kTiled>), grid, blk, 0, s, a);
         else
             KD_LAUNCH(kKindBwdGrad, s, (k_bwd_grad<float, kGradWaves, kRow, kKBlk>), grid, blk, 0, s, a);
     }

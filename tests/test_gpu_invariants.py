@@ -216,11 +216,12 @@ def _peak(fn):
 def test_fused_peak_memory_flat_in_sequence():
     """At the gpt-oss head (V = 201,088, d = 2880, chunk 2048) the fused call's peak beyond its
     inputs is the per-row buffers (lse, zk, dH, cache plan) plus a constant: growing S leaves
-    the constant unchanged."""
+    the constant unchanged. Below 8192 rows the calls keep no stage-tiled copy of W (1.16 GB),
+    so the constant there is smaller, never larger."""
     V, d, K = 201088, 2880, 100
     W = torch.randn(V, d, device="cuda", dtype=torch.bfloat16)
     extra = []
-    for S in (4096, 8192, 16384):
+    for S in (4096, 8192, 16384, 32768):
         H = torch.randn(S, d, device="cuda", dtype=torch.bfloat16)
         idx = torch.stack([torch.randperm(V, device="cuda")[:K] for _ in range(1)]).repeat(S, 1).int()
         t = torch.randn(S, K, device="cuda", dtype=torch.bfloat16)
@@ -234,8 +235,11 @@ def test_fused_peak_memory_flat_in_sequence():
         extra.append(pk - per_row)
         say(f"  S={S} fused peak {pk / 1e9:.3f} GB  minus per-row {extra[-1] / 1e9:.3f} GB")
         del H, idx, t
-    # dW (fp32, 2.3 GB) and the gradient tile (C x V bf16, 0.82 GB) dominate; no growth with S
-    assert max(extra) - min(extra) <= 0.02 * max(extra)
+    # dW (fp32, 2.3 GB), the tiled copy of W (1.16 GB) and the gradient tile (C x V bf16,
+    # 0.82 GB) dominate; no growth with S
+    big = extra[1:]
+    assert max(big) - min(big) <= 0.02 * max(big)
+    assert extra[0] <= min(big)
 
 
 def test_skip_dw_frozen_head():

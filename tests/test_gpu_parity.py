@@ -68,6 +68,17 @@ def test_small_bf16_full():
     compare_full(p, p.chunk, TOL["bf16"])
 
 
+@pytest.mark.parametrize("dtype,N,d,V,chunk", [("fp32", 8200, 136, 2100, 1024), ("bf16", 8192, 264, 3000, 2048),
+                                               ("bf16", 8448, 1032, 4100, 768)])
+def test_stage_tiled_operands_full(dtype, N, d, V, chunk):
+    """From 8192 rows the forward and gradient kernels read W and H through stage-tiled copies.
+    Full parity there: a ragged last row block, hidden sizes that leave a partial 64-byte stage
+    and a partial 320-row block, ragged vocabulary tiles, and a chunk that is not a multiple of
+    256 (per-chunk plans, 32-column dW slots)."""
+    p = datagen.make("tiny", N=N, d=d, V=V, dtype=dtype, chunk=chunk)
+    compare_full(p, p.chunk, TOL[dtype], label=f"tiled {dtype} N={N}")
+
+
 def test_small_bf16_dense_path():
     p = datagen.make("small", N=1024)
     say("dense path small bf16, 1024 rows")
