@@ -226,7 +226,10 @@ struct StoredWs {
     void* HT;
     float* dh_part;
     int64_t ldgt, group;
-    int n_vsplit, n_split;
+    int n_split;
+    void* Wt;   // stage-tiled W and a row chunk of H for the forward (null: as stored)
+    void* Ht;
+    int64_t tS;
     size_t bytes;
 };
 
@@ -236,7 +239,8 @@ StoredWs layout_stored(const kd_problem* p, void* ws, bool all_rows) {
     const int64_t n_vt = n_vtiles(V), Vp = n_vt * kTileN;
     const int64_t C = chunk_rows(p);
     const int64_t fwd_rows = all_rows ? N : C;
-    w.n_vsplit = fwd_vsplits(fwd_rows, V);
+    // the forward's launches: kFwdRows rows each (forward-chunked), one chunk each (single pass)
+    const int64_t F = all_rows ? std::min(N, kFwdRows) : C;
     w.n_split = dh_splits(C, d, V, true);
     w.ldzt = round_up(fwd_rows, 4);
     w.group = dw_group(p, C);
@@ -248,18 +252,23 @@ StoredWs layout_stored(const kd_problem* p, void* ws, bool all_rows) {
     w.plan_ent = (uint32_t*)c.take(sizeof(uint32_t) * n_rblocks(N) * kTileM * K);
     w.pt = (float*)c.take(sizeof(float) * N * K);
     w.zk = (float*)c.take(sizeof(float) * N * K);
-    // Per-row partials of one forward launch; the last chunk may use more vocab lanes.
-    const int64_t last = N - (n_chunks - 1) * C;
-    const int64_t n_part_rows =
-        all_rows ? w.n_vsplit * N : std::max(w.n_vsplit * C, (int64_t)fwd_vsplits(last, V) * last);
+    // Per-row partials of one forward launch; the last launch may use more vocab lanes.
+    const int64_t n_launch = (N + F - 1) / F, last = N - (n_launch - 1) * F;
+    const int64_t n_part_rows = std::max((int64_t)fwd_vsplits(F, V) * F, (int64_t)fwd_vsplits(last, V) * last);
     w.part = (float2*)c.take(sizeof(float2) * 2 * n_part_rows);
-    w.blk_sum = (double*)c.take(sizeof(double) * (all_rows ? combine_blocks(N) : n_chunks * combine_blocks(C)));
+    w.blk_sum = (double*)c.take(sizeof(double) * n_launch * combine_blocks(F));
     w.zt = (float*)c.take(sizeof(float) * Vp * w.ldzt);
     w.Gc = c.take(esize(p->act) * round_up(C, kTileM) * Vp);
     w.GT = c.take(esize(p->act) * Vp * w.ldgt);
     w.WT = c.take(esize(p->act) * round_up(d, 320) * Vp);
     w.HT = c.take(esize(p->act) * round_up(d, 320) * w.ldgt);
     w.dh_part = w.n_split > 1 ? (float*)c.take(sizeof(float) * w.n_split * C * d) : nullptr;
+    const Dt act = p->act == KD_BF16 ? Dt::BF16 : Dt::F32;
+    w.tS = tiled_stages(act, d);
+    if (tiled_fwd(p)) {
+        w.Wt = c.take(tiled_bytes(act, V, d));
+        w.Ht = c.take(tiled_bytes(act, F, d));
+    }
     w.bytes = c.used;
     return w;
 }
@@ -296,6 +305,23 @@ DenseWs layout_dense(const kd_problem* p, void* ws) {
     do {                                           \
         if ((x) != hipSuccess) return KD_ERR_HIP;  \
     } while (0)
+
+// The stored-logit paths' forward over rows [r0, r0 + rows): from stage-tiled copies when the
+// workspace holds them (the copy of W made by the caller), as stored otherwise; same arithmetic.
+kd_status stored_forward(const kd_problem* p, const Shape& sh, const StoredWs& w, const void* H, const void* W,
+                         int64_t r0, int64_t rows, const int32_t* plan_off, int nvs, float* zk, float* zt,
+                         hipStream_t s) {
+    Shape shc = sh;
+    shc.N = rows;
+    const char* Hr = (const char*)H + r0 * p->d * esize(p->act);
+    if (w.Wt) {
+        KD_TRY(launch_tile_rows(sh.act, Hr, p->d, rows, p->d, w.Ht, s));
+        KD_TRY(launch_fwd(shc, w.Ht, w.Wt, plan_off, w.plan_ent, nvs, w.part, zk, zt, w.ldzt, s, w.tS));
+    } else {
+        KD_TRY(launch_fwd(shc, Hr, W, plan_off, w.plan_ent, nvs, w.part, zk, zt, w.ldzt, s));
+    }
+    return KD_OK;
+}
 
 kd_status validate_ids(const kd_problem* p, const int32_t* idx, uint32_t* status, hipStream_t s) {
     KD_TRY(launch_validate(idx, p->N, p->K, p->V, status, s));
@@ -630,12 +656,26 @@ kd_status kd_chunked_kl(const kd_problem* p, const void* H, const void* W, const
         st = validate_ids(p, idx, w.status, s);
         if (st != KD_OK) return st;
     }
-    // Forward over all rows, keeping every logit (z^T) for the backward.
+    // Forward over all rows in launches of kFwdRows, keeping every logit (z^T) for the backward.
     KD_TRY(launch_plan(idx, 0, p->N, p->K, p->V, w.plan_off, w.plan_ent, s));
     KD_TRY(launch_teacher_prob(tlog, sh.tlog, 0, p->N, p->K, p->T, w.pt, s));
-    KD_TRY(launch_fwd(sh, H, W, w.plan_off, w.plan_ent, w.n_vsplit, w.part, w.zk, w.zt, w.ldzt, s));
+    if (w.Wt) KD_TRY(launch_tile_rows(sh.act, W, p->d, p->V, p->d, w.Wt, s));
+    const int64_t F = std::min(p->N, kFwdRows), plan_stride = n_vtiles(p->V) + 1;
+    const size_t ets = esize(p->tlogit);
     int n_blk = 0;
-    KD_TRY(launch_combine(sh, w.part, 2 * w.n_vsplit, w.zk, tlog, lse, row_kl, w.blk_sum, &n_blk, s));
+    for (int64_t r0 = 0; r0 < p->N; r0 += F) {
+        const int64_t rows = std::min(F, p->N - r0);
+        Shape shc = sh;
+        shc.N = rows;
+        const int nvs = fwd_vsplits(rows, p->V);
+        st = stored_forward(p, sh, w, H, W, r0, rows, w.plan_off + (r0 / kTileM) * plan_stride, nvs, w.zk + r0 * p->K,
+                            w.zt + r0, s);
+        if (st != KD_OK) return st;
+        int nb = 0;
+        KD_TRY(launch_combine(shc, w.part, 2 * nvs, w.zk + r0 * p->K, (const char*)tlog + r0 * p->K * ets, lse + r0,
+                              row_kl ? row_kl + r0 : nullptr, w.blk_sum + n_blk, &nb, s));
+        n_blk += nb;
+    }
     KD_TRY(launch_loss_final(sh, w.blk_sum, n_blk, loss, s));
     KD_TRY(launch_transpose(sh.act, W, p->d, p->V, p->d, w.WT, n_vtiles(p->V) * kTileN, 0, n_vtiles(p->V) * kTileN, s));
     return stored_backward(p, sh, w, H, idx, lse, grad_loss, dH, dW, s);
@@ -668,6 +708,7 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
     if (one_plan) KD_TRY(launch_plan(idx, 0, p->N, p->K, p->V, w.plan_off, w.plan_ent, s));
     KD_TRY(launch_teacher_prob(tlog, sh.tlog, 0, p->N, p->K, p->T, w.pt, s));
     KD_TRY(launch_transpose(sh.act, W, p->d, p->V, p->d, w.WT, n_vtiles(p->V) * kTileN, 0, n_vtiles(p->V) * kTileN, s));
+    if (w.Wt) KD_TRY(launch_tile_rows(sh.act, W, p->d, p->V, p->d, w.Wt, s));
     int64_t ci = 0;
     int n_blk = 0;
     bool dw_written = false;
@@ -680,8 +721,8 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
         Shape shc = sh;
         shc.N = cc;
         const int nvs = fwd_vsplits(cc, p->V);
-        KD_TRY(launch_fwd(shc, (const char*)H + c0 * p->d * es, W, c_off, w.plan_ent, nvs, w.part, w.zk + c0 * p->K,
-                          w.zt, w.ldzt, s));
+        st = stored_forward(p, sh, w, H, W, c0, cc, c_off, nvs, w.zk + c0 * p->K, w.zt, s);
+        if (st != KD_OK) return st;
         int nb = 0;
         KD_TRY(launch_combine(shc, w.part, 2 * nvs, w.zk + c0 * p->K, (const char*)tlog + c0 * p->K * ets, lse + c0,
                               row_kl ? row_kl + c0 : nullptr, w.blk_sum + n_blk, &nb, s));

@@ -2021,14 +2021,18 @@ hipError_t launch_fwd(const Shape& sh, const void* H, const void* W, const int32
     const dim3 blk(64 * kFwdWaves);
     const bool t = tiled_S > 0;
     if (sh.act == Dt::BF16) {
-        if (zt)
+        if (zt && t)
+            KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, true, kFwdWaves, kTiled>), dim3(grid), blk, 0, s, a);
+        else if (zt)
             KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, true, kFwdWaves, kRow>), dim3(grid), blk, 0, s, a);
         else if (t)
             KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, false, kFwdWaves, kTiled>), dim3(grid), blk, 0, s, a);
         else
             KD_LAUNCH(kKindFwd, s, (k_fwd<bf16_t, false, kFwdWaves, kRow>), dim3(grid), blk, 0, s, a);
     } else {
-        if (zt)
+        if (zt && t)
+            KD_LAUNCH(kKindFwd, s, (k_fwd<float, true, kFwdWaves, kTiled>), dim3(grid), blk, 0, s, a);
+        else if (zt)
             KD_LAUNCH(kKindFwd, s, (k_fwd<float, true, kFwdWaves, kRow>), dim3(grid), blk, 0, s, a);
         else if (t)
             KD_LAUNCH(kKindFwd, s, (k_fwd<float, false, kFwdWaves, kTiled>), dim3(grid), blk, 0, s, a);
