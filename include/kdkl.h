@@ -113,13 +113,13 @@ typedef enum kd_dtype {
 #define KD_SKIP_DW       0x4u /* kd_fused_kl_bwd computes dH only (dW may be NULL): for a frozen head.
                                  Ignored by kd_fused_kl_fwd; KD_ERR_VALUE for the other calls and
                                  together with KD_ACCUMULATE_DW */
-#define KD_LOW_MEMORY    0x8u /* memory-lean fused backward: of the default backward's buffers the
+#define KD_LOW_MEMORY    0x8u /* memory-lean fused calls: of the default backward's buffers the
                                  workspace keeps the chunk's gradient tile G_c [chunk, V], and none
-                                 of the transposed copies of W, G_c and H_c; dH and dW then read
+                                 of the transposed or stage-tiled copies of W, G_c and H_c (nor the
+                                 forward's stage-tiled copies of W and H); dH and dW then read
                                  their operands as stored, on a slower GEMM path, with one dW pass
                                  per chunk. Same results up to rounding order. Changes
-                                 kd_fused_workspace_bytes; ignored by kd_fused_kl_fwd; KD_ERR_VALUE
-                                 for the other loss calls */
+                                 kd_fused_workspace_bytes; KD_ERR_VALUE for the other loss calls */
 
 /*
  * Problem descriptor (host memory).
@@ -159,8 +159,11 @@ int kd_abi_version(void);
 const char* kd_status_str(kd_status s);
 
 /* Workspace bytes for kd_fused_kl_fwd and kd_fused_kl_bwd (one query serves both). Grows
- * with N only through O(N*K) and O(N) terms; the rest is O(chunk * V + V). Returns 0 if p is
- * NULL or invalid. */
+ * with N only through O(N*K) and O(N) terms; the rest is O(chunk * V + V * d). From N = 8192
+ * rows (without KD_LOW_MEMORY) it includes copies of W and of a chunk of rows of H in a
+ * stage-tiled layout, which the kernels read faster than W and H as stored (V * d elements of
+ * the act dtype for W: 1.16 GB at V = 201,088, d = 2880 in bf16). Returns 0 if p is NULL or
+ * invalid. */
 size_t kd_fused_workspace_bytes(const kd_problem* p);
 
 /*
