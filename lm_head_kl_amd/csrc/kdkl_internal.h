@@ -122,9 +122,11 @@ hipError_t launch_tile_rows(Dt dt, const void* src, int64_t ld, int64_t rows, in
 // Transpose of src [rows][lds] (cols used) into a stage-tiled operand with row blocks of 320 and
 // kdst K columns (kdst/SW stages): result row c < cols holds src[r][c] at K column k0 + r for r <
 // rows, zero for rows <= r < rows_pad. cols, lds and rows_pad multiples of 8; kdst and k0
-// multiples of 32. The result takes round_up(cols, 320) * kdst elements.
+// multiples of 32. The result takes round_up(cols, 320) * kdst elements. With tiled_copy not
+// null, src is also copied as launch_tile_rows would (rows_pad rows, a multiple of 256).
 hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst,
-                            int64_t kdst, int64_t k0, int64_t rows_pad, hipStream_t s);
+                            int64_t kdst, int64_t k0, int64_t rows_pad, hipStream_t s,
+                            void* tiled_copy = nullptr);
 
 // dH rows [c0, c0+cc) = G_c W. With WT not null, G_c is the stage-tiled tile written by
 // launch_bwd_grad and WT is W^T from launch_transpose (kdst = Vp); with WT null, W is read as stored

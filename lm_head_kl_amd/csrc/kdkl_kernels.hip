@@ -857,12 +857,13 @@ __global__ __launch_bounds__(256, 2) void k_grad_z(GradArgs a) {
 // Transpose into a stage-tiled operand with row blocks of 320 (engine.h, kTiled), for the wide
 // dH and dW tiles: result row c (c < cols) at K column k0 + r holds src[r*lds + c] for r < rows
 // and zero for rows <= r < rows_pad; the result has S stages per row block. 64 x 64 tiles
-// through LDS.
+// through LDS. With dst2 not null the source is also copied, untransposed, into a stage-tiled
+// operand with row blocks of 256 and S2 stages (the k_tile_rows layout), from the same loads.
 
 template <typename T>
 __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, int64_t lds, int64_t rows,
                                                    int64_t cols, T* __restrict__ dst, int64_t S, int64_t k0,
-                                                   int64_t rows_pad) {
+                                                   int64_t rows_pad, T* __restrict__ dst2, int64_t S2) {
     // 16-byte global accesses: VEC elements of a source row per load, VEC consecutive rows of
     // one column per store. cols, lds and rows_pad are multiples of VEC and k0 of the stage
     // width, so a vector never leaves its row or its stage. The LDS tile is padded to an odd word
@@ -879,6 +880,7 @@ __global__ __launch_bounds__(256) void k_transpose(const T* __restrict__ src, in
         const int64_t gr = r0 + r, gc = c0 + cv;
         u32x4 v = {0u, 0u, 0u, 0u};
         if (gr < rows && gc < cols) v = *(const u32x4*)(src + gr * lds + gc);
+        if (dst2 && gr < rows_pad && gc < S2 * 4 * VEC) *(u32x4*)(dst2 + tiled_at<T, kTileM>(gr, gc, S2)) = v;
         const T* e = (const T*)&v;
 #pragma unroll
         for (int u = 0; u < VEC; ++u) tile[r][cv + u] = e[u];
@@ -2184,16 +2186,19 @@ hipError_t launch_topk(Dt dt, const void* X, int64_t ld, int64_t N, int64_t V, i
 }
 
 hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, int64_t cols, void* dst, int64_t kdst,
-                            int64_t k0, int64_t rows_pad, hipStream_t s) {
+                            int64_t k0, int64_t rows_pad, hipStream_t s, void* tiled_copy) {
     const int64_t sw = dt == Dt::BF16 ? 32 : 16;
     if (kdst % sw != 0 || k0 % sw != 0 || k0 + rows_pad > kdst) return hipErrorInvalidValue;
+    // the untransposed copy needs every row block of 256 covered: rows_pad a multiple of 256
+    if (tiled_copy && rows_pad % kTileM != 0) return hipErrorInvalidValue;
+    const int64_t S2 = tiled_stages(dt, cols);
     const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows_pad + 63) / 64));
     if (dt == Dt::BF16)
         KD_LAUNCH(kKindTranspose, s, k_transpose<bf16_t>, grid, dim3(NTHR), 0, s, (const bf16_t*)src, lds, rows, cols,
-                  (bf16_t*)dst, kdst / sw, k0, rows_pad);
+                  (bf16_t*)dst, kdst / sw, k0, rows_pad, (bf16_t*)tiled_copy, S2);
     else
         KD_LAUNCH(kKindTranspose, s, k_transpose<float>, grid, dim3(NTHR), 0, s, (const float*)src, lds, rows, cols,
-                  (float*)dst, kdst / sw, k0, rows_pad);
+                  (float*)dst, kdst / sw, k0, rows_pad, (float*)tiled_copy, S2);
     return hipGetLastError();
 }
 

@@ -55,7 +55,7 @@ def test_small_bf16(path):
 @pytest.mark.parametrize("dtype,N,d,V,chunk", [("fp32", 8200, 136, 2100, 1024), ("bf16", 8448, 1032, 4100, 768)])
 def test_stage_tiled_forward_full(path, dtype, N, d, V, chunk):
     """From 8192 rows the forward of both paths reads W and H through stage-tiled copies (in
-    launches of 8192 rows for the forward-chunked path, one chunk for the single pass), with a
+    launches of up to 16384 rows for the forward-chunked path, one chunk for the single pass), with a
     ragged last launch, partial stages and ragged vocabulary tiles."""
     p = datagen.make("tiny", N=N, d=d, V=V, dtype=dtype, chunk=chunk)
     compare_full(path, p, p.chunk, TOL[dtype], label=f"tiled {dtype} N={N}")
