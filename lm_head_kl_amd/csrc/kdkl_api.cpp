@@ -147,6 +147,17 @@ int fwd_parts(const kd_problem* p) {
 
 bool low_memory(const kd_problem* p) { return (p->flags & KD_LOW_MEMORY) != 0; }
 
+// The wide dH tile reads W^T stage-tiled in blocks of 320 rows through one buffer descriptor
+// per tile: its last stage sits (Vp/SW - 1) * 320 * 64 bytes past the tile's first, which must
+// stay inside the descriptor's 32-bit range (an offset past it reads zero). That caps V at
+// 3,355,392 (bf16) or 1,677,568 (fp32) on every path that computes dH this way (all backward
+// paths but the memory-lean one); G_c's 256-row blocks allow more.
+constexpr int64_t kDescRange = 0x7FFFFFF0;
+bool wide_dh_fits(const kd_problem* p) {
+    const int64_t Vp = round_up(p->V, kTileN), sw = 64 / (int64_t)esize(p->act);
+    return (Vp / sw) * 320 * 64 - 16 < kDescRange;
+}
+
 // The forward and gradient kernels read W and H from stage-tiled copies (engine.h, kTiled):
 // the copies cost one pass over W and H per call, and W's size plus a row chunk of H's in the
 // workspace; the kernels' operand loads then fetch whole 128-byte lines, 7-11 % faster. Below
@@ -500,6 +511,7 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
     const bool want_dw = (p->flags & KD_SKIP_DW) == 0;
+    if (!low_memory(p) && !wide_dh_fits(p)) return KD_ERR_SHAPE;
     if (!H || !W || !idx || !tlog || !lse || !dH || (want_dw && !dW) || !ws) return KD_ERR_NULL;
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || (want_dw && !aligned(dW, 16))) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_fused_workspace_bytes(p)) return KD_ERR_WORKSPACE;
@@ -646,6 +658,7 @@ kd_status kd_chunked_kl(const kd_problem* p, const void* H, const void* W, const
     if (st != KD_OK) return st;
     // only the fused backward can leave dW out or run memory-lean
     if (p->flags & (KD_SKIP_DW | KD_LOW_MEMORY)) return KD_ERR_VALUE;
+    if (!wide_dh_fits(p)) return KD_ERR_SHAPE;
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_chunked_workspace_bytes(p)) return KD_ERR_WORKSPACE;
@@ -689,6 +702,7 @@ kd_status kd_fused_kl_fwdbwd(const kd_problem* p, const void* H, const void* W, 
     if (st != KD_OK) return st;
     // only the fused backward can leave dW out or run memory-lean
     if (p->flags & (KD_SKIP_DW | KD_LOW_MEMORY)) return KD_ERR_VALUE;
+    if (!wide_dh_fits(p)) return KD_ERR_SHAPE;
     if (!H || !W || !idx || !tlog || !loss || !lse || !dH || !dW || !ws) return KD_ERR_NULL;
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || !aligned(dW, 16)) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_fused_fwdbwd_workspace_bytes(p)) return KD_ERR_WORKSPACE;

@@ -230,6 +230,25 @@ def test_low_memory_workspace():
 
 
 @nogpu
+def test_wide_dh_vocabulary_limit():
+    """The backward paths that read W^T stage-tiled in 320-row blocks stop where its last stage
+    would leave a buffer descriptor's 32-bit range: V = 3,355,392 in bf16, 1,677,568 in fp32
+    (KD_ERR_SHAPE before anything is enqueued); the memory-lean backward and the forward go on."""
+    L = _lib.lib()
+    for act, vmax in ((KD_BF16, 3355392), (KD_FP32, 1677568)):
+        for V, ok in ((vmax, True), (vmax + 256, False)):
+            p = prob(N=256, d=8, V=V, K=4, chunk=256, act=act, tlogit=act)
+            code = bwd(p, nbytes=1)  # too small a workspace: past the shape check it is error 5
+            assert code == (5 if ok else 2), (act, V, code)
+            for fn in ("kd_chunked_kl", "kd_fused_kl_fwdbwd"):
+                assert (getattr(L, fn)(ctypes.byref(p), F, F, F, F, None, F, F, None, F, F, F, 1, None)
+                        == (5 if ok else 2)), (fn, act, V)
+            lean = prob(N=256, d=8, V=V, K=4, chunk=256, act=act, tlogit=act, flags=_lib.KD_LOW_MEMORY)
+            assert bwd(lean, nbytes=1) == 5
+            assert fwd(p, nbytes=1) == 5
+
+
+@nogpu
 def test_low_memory_flag_rules():
     """KD_LOW_MEMORY belongs to the fused calls; the other loss calls reject it."""
     L = _lib.lib()
