@@ -16,17 +16,19 @@
 //     32x32x16 blocks.
 // Operands reach LDS straight from memory (buffer_load ... lds) in 16-byte chunks, XOR-swizzled
 // by row so that fragment reads are free of bank conflicts, four stages of half a K step deep.
-// Every operand of the fast path is K contiguous. Where the natural layout is not, a copy is
-// made: W^T once per backward call (K-blocked, for dH = G W), H_c^T per chunk and G_c^T from the
-// gradient tile (for dW = G^T H). The dense and memory-lean paths read M/N-contiguous operands
-// through registers instead (8 x 8 bf16 blocks transposed on the way to LDS).
+// Every operand of the fast path is stage-tiled (engine.h, kTiled): each 64-byte K step of a
+// tile's rows is one contiguous block, so its loads fetch whole 128-byte lines. The copies are
+// made here: W and row chunks of H (k_tile_rows) for the forward and gradient kernels, W^T once
+// per backward call and H_c^T per chunk (k_transpose) for dH = G W and dW = G^T H, and G_c and
+// G_c^T written by the gradient kernels. The dense and memory-lean paths read row-major or
+// M/N-contiguous operands (through registers, 8 x 8 bf16 blocks transposed on the way to LDS).
 //
 // Epilogues:
 //   forward   logit tiles are computed transposed (vocabulary x tokens), so each lane keeps the
 //             running (max, sum) of its token columns in the log2 domain without shuffles; the
 //             gather of z at the cached ids goes through an LDS-staged half tile;
 //   backward  G = g*T/n_norm*(softmax(z/T) - P_t), P_t subtracted in the LDS-staged tile, then
-//             stored twice in the activation dtype: K-blocked G_c for dH and G_c^T for dW;
+//             stored twice in the activation dtype, stage-tiled: G_c for dH and G_c^T for dW;
 //   dH        fp32 split-K partials, reduced in a fixed order, or a direct store;
 //   dW        fp32 read-modify-write through LDS.
 // Hand-offs of staged LDS data inside an epilogue use an LDS-only barrier: a full workgroup
