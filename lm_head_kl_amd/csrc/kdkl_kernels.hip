@@ -514,8 +514,9 @@ __global__ __launch_bounds__(256) void k_sum_rows(const double* __restrict__ v, 
 // Like the forward, the tile is computed transposed (rows: vocabulary entries, columns:
 // tokens), so each lane needs the lse of only its 4 token columns, kept in registers. The
 // tile leaves through LDS in two passes of 128 vocabulary rows, which lets both copies be
-// written in whole 128-byte lines: G row-major (a token's 64 consecutive entries per group)
-// and G^T (a vocabulary entry's 256 consecutive tokens).
+// written in whole 128-byte lines: G (a token's entries of the pass, 64 bytes in each of four
+// stage blocks, the neighbouring token completing each line) and G^T (a vocabulary entry's 256
+// consecutive tokens).
 
 struct GradArgs {
     const void* H;  // row-major [N][d], or stage-tiled (ldh stages per row block)
@@ -559,8 +560,9 @@ __device__ __forceinline__ void store8(T* dst, const float (&x)[8]) {
 }
 
 // Second half of a gradient pass, once the pass's 128 vocabulary rows of gs*softmax are staged:
-// subtract gs*p_t at the cached ids that fall in the pass, then write the rows of G (K-blocked)
-// and of G^T. Ends with a barrier, so the stage may be refilled.
+// subtract gs*p_t at the cached ids that fall in the pass, then write the rows of G (stage-tiled,
+// or K-blocked for the memory-lean backward) and of G^T. Ends with a barrier, so the stage may be
+// refilled.
 // The plan fills each bucket in atomic order, so whether an entry is among the first NT (held
 // in registers) or comes from the loop changes between calls; both paths subtract with one
 // explicit fused multiply-add, so G does not depend on that order.
@@ -927,8 +929,8 @@ __global__ __launch_bounds__(256) void k_tile_rows(const T* __restrict__ src, in
 
 // ------------------------------------------------------------------------------------------
 // dH = G W. The dense path multiplies G [rows][ldg] (vocabulary contiguous) by W [V][d]
-// (d contiguous) on 256 x 256 tiles; the chunked paths use K-blocked G_c and W^T on
-// 256 x 320 tiles (k_dh_w).
+// (d contiguous) on 256 x 256 tiles, and so does the memory-lean backward with its K-blocked
+// G_c; the other chunked paths use stage-tiled G_c and W^T on 256 x 320 tiles (k_dh_w).
 
 struct DhArgs {
     const void* G;   // G_c [cc][ldg] row-major or K-blocked [Vp/256][cc][256]; stage-tiled with W^T
