@@ -759,7 +759,8 @@ struct KOperandW {
     template <typename Id>
     __device__ __forceinline__ void issue_one(u32x4* L, int stage, int t, int64_t k0, int64_t k_lim, bool full,
                                               bool live, const Id& id) const {
-        const bool in = live && dst[t] >= 0 && (full || (int64_t)chunk * VEC < k_lim - k0);
+        // off[t] is already out of range for a dummy instruction's lanes
+        const bool in = live && (full || (int64_t)chunk * VEC < k_lim - k0);
         u32x4* d = dst[t] >= 0 ? L + stage * WST + dst[t] : L + 4 * WST + 64 * (id.w & 3);
         if constexpr (BLK) {
             const __amdgpu_buffer_rsrc_t r = make_rsrc(base + (k0 >> 8) * blk_bytes);
