@@ -138,6 +138,28 @@ def test_low_memory_matches_default_and_flags():
     assert torch.equal(dH3.view(torch.int16), dH1.view(torch.int16))
 
 
+def test_stage_tiled_copies_change_no_bit_and_keep_the_flags():
+    """From 8192 rows the default calls read W and H through stage-tiled copies, the memory-lean
+    ones as stored. The forward's arithmetic is the same either way, so lse, zk, KL_n and the loss
+    agree bit for bit; on the tiled backward KD_SKIP_DW gives the same dH bit for bit and
+    KD_ACCUMULATE_DW adds into dW."""
+    p = datagen.make("tiny", N=8448, d=264, V=3000, dtype="bf16", chunk=768)
+    say("stage-tiled vs as stored, flags", f"N={p.N} d={p.d} V={p.V} K={p.K}")
+    H, W, idx, t = device_inputs(p)
+    f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=768, want_zk=True)
+    g = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=768, want_zk=True, flags=kd.KD_LOW_MEMORY)
+    torch.cuda.synchronize()
+    for a, b in ((f.loss, g.loss), (f.lse, g.lse), (f.zk, g.zk), (f.row_kl, g.row_kl)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    dH0, dW0 = kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=768)
+    dH1, none = kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=768, flags=kd.KD_SKIP_DW)
+    acc = dW0.clone()
+    kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=768, flags=kd.KD_ACCUMULATE_DW, dW=acc)
+    torch.cuda.synchronize()
+    assert none is None and torch.equal(dH1.view(torch.int16), dH0.view(torch.int16))
+    assert rel_l2(host(acc), 2 * host(dW0)) <= 1e-6
+
+
 def test_low_memory_gptoss_sampled():
     """The memory-lean backward at the gpt-oss head (N = 32768, chunk 2048): dH on 256 seeded
     rows against the oracle, 256 rows of the full-batch dW against oracle.dw_rows (from the
