@@ -92,14 +92,19 @@ def test_accumulate_dw(path):
     assert torch.equal(acc, dW1 + dW1)
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
-def test_agreement_with_fused_path(dtype):
+@pytest.mark.parametrize("dtype,case", [("fp32", "tiny"), ("bf16", "small"), ("bf16", "tiled")])
+def test_agreement_with_fused_path(dtype, case):
     """Same inputs, same chunk: the forward-chunked path reads the very logits the fused backward
     recomputes (same tiles, same summation order), so its gradients match bit for bit; the
-    single-pass path merges lse over different vocab splits, so it agrees to rounding."""
-    p = datagen.make("small", N=2048, dtype=dtype) if dtype == "bf16" else datagen.make("tiny", N=512, chunk=256)
-    chunk = 512 if dtype == "bf16" else 256
-    say("agreement with fused", dtype, f"N={p.N} chunk={chunk}")
+    single-pass path merges lse over different vocab splits, so it agrees to rounding. The "tiled"
+    case reads stage-tiled operands (8448 rows) and has about 870 cached ids per tile."""
+    if case == "tiny":
+        p, chunk = datagen.make("tiny", N=512, chunk=256), 256
+    elif case == "small":
+        p, chunk = datagen.make("small", N=2048, dtype=dtype), 512
+    else:
+        p, chunk = datagen.make("tiny", N=8448, d=264, V=3000, K=40, dtype=dtype, chunk=768), 768
+    say("agreement with fused", dtype, case, f"N={p.N} chunk={chunk}")
     H, W, idx, t = device_inputs(p)
     f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=chunk)
     dH0, dW0 = kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=chunk)
