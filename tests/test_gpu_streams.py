@@ -69,9 +69,17 @@ def test_concurrent_streams_match_sequential():
             assert same(x, y), f"stream 2, repeat {rep}"
 
 
-def test_graph_capture_and_replay():
-    say("fused forward + backward captured into a HIP graph, replayed")
-    p = datagen.make("small", N=1024)
+def make_case(case: str, seed: int | None = None) -> datagen.Problem:
+    if case == "small":
+        return datagen.make("small", N=1024, seed=seed)
+    # 8448 rows: the calls copy W and H into the stage-tiled layout first
+    return datagen.make("tiny", N=8448, d=264, V=3000, dtype="bf16", seed=seed)
+
+
+@pytest.mark.parametrize("case", ["small", "tiled"])
+def test_graph_capture_and_replay(case):
+    say("fused forward + backward captured into a HIP graph, replayed", case)
+    p = make_case(case)
     st = Step(p)
     eager = snapshot(st())
     torch.cuda.synchronize()
@@ -94,7 +102,7 @@ def test_graph_capture_and_replay():
         other()  # eager work of the program between replays
         torch.cuda.synchronize()
     # the graph reads its input buffers at replay: new values in place give the new results
-    p2 = datagen.make("small", N=1024, seed=99)
+    p2 = make_case(case, seed=99)
     st.H.copy_(to_torch(p2.H))
     st.t.copy_(to_torch(p2.tlog))
     st.idx.copy_(torch.from_numpy(p2.idx))
