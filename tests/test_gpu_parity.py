@@ -69,12 +69,14 @@ def test_small_bf16_full():
 
 
 @pytest.mark.parametrize("dtype,N,d,V,chunk", [("fp32", 8200, 136, 2100, 1024), ("bf16", 8192, 264, 3000, 2048),
-                                               ("bf16", 8448, 1032, 4100, 768)])
+                                               ("bf16", 8448, 1032, 4100, 768), ("fp32", 16500, 72, 1100, 2048),
+                                               ("bf16", 16640, 136, 2100, 4096)])
 def test_stage_tiled_operands_full(dtype, N, d, V, chunk):
     """From 8192 rows the forward and gradient kernels read W and H through stage-tiled copies.
     Full parity there: a ragged last row block, hidden sizes that leave a partial 64-byte stage
     and a partial 320-row block, ragged vocabulary tiles, and a chunk that is not a multiple of
-    256 (per-chunk plans, 32-column dW slots)."""
+    256 (per-chunk plans, 32-column dW slots). Past 16384 rows the forward runs in two launches,
+    the second ragged (116 or 256 rows)."""
     p = datagen.make("tiny", N=N, d=d, V=V, dtype=dtype, chunk=chunk)
     compare_full(p, p.chunk, TOL[dtype], label=f"tiled {dtype} N={N}")
 
