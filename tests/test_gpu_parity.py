@@ -81,6 +81,14 @@ def test_stage_tiled_operands_full(dtype, N, d, V, chunk):
     compare_full(p, p.chunk, TOL[dtype], label=f"tiled {dtype} N={N}")
 
 
+def test_stage_tiled_crowded_tiles():
+    """K = 1024 of V = 3000 at 8448 rows: about 22,000 cached ids per 256 x 256 tile, so the
+    forward's gather and the gradient tile's corrections run their loops past the entries held in
+    registers, on stage-tiled operands."""
+    p = datagen.make("tiny", N=8448, d=136, V=3000, K=1024, dtype="bf16", chunk=1024)
+    compare_full(p, p.chunk, TOL["bf16"], label="tiled, K = 1024")
+
+
 def test_small_bf16_dense_path():
     p = datagen.make("small", N=1024)
     say("dense path small bf16, 1024 rows")
