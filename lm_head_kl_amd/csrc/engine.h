@@ -40,6 +40,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kdkl_internal.h"
 
 namespace kdkl {
@@ -364,7 +366,11 @@ __device__ __forceinline__ int swz4(int r, int c) { return c ^ (((r >> 2) ^ (r >
 // as 64-byte pieces of separate 128-byte lines, the second half of each line following one stage
 // later; a stage-tiled operand gives it as one contiguous block, every line whole. At the
 // gpt-oss head the same mainloop runs 15-18 % faster on stage-tiled operands.
-enum Lay : int { kRow = 0, kKBlk = 1, kTiled = 2 };
+//   kTrans  M/N-contiguous (bf16, wide tile only): each source row holds one K index, and the
+//           tile's M or N entries are contiguous in it: element (mn, k) at src[k*ld + mn - mn0]
+//           for a src that the caller points at the tile's first column. Read through LDS
+//           transpose reads (see KOperandTR).
+enum Lay : int { kRow = 0, kKBlk = 1, kTiled = 2, kTrans = 3 };
 
 template <typename T, int LAY = kRow, int NW = 4>
 struct KOperand4 {
@@ -779,6 +785,67 @@ struct KOperandW {
     }
 };
 
+// An M/N-contiguous bf16 operand of the wide tile (kTrans). A stage holds its 32 K rows as
+// blocks of 32 columns, 2 KB each: [K half ks][16 rows][64 bytes], the half ks holding the K
+// indices 8g + 4ks + r (g, r = 0..3) as row 4g + r. Each DMA instruction fills one half of one
+// block, four lanes a 64-byte source row, so eight consecutive lanes read one whole 128-byte
+// line of a row pair. ds_read_b64_tr_b16 (gfx950) reads a 4 x 16 block of 16-bit values per
+// group of 16 lanes, lanes 4r .. 4r+3 supplying row r and lane j receiving column j (checked on
+// hardware); two such reads give a lane the 8 consecutive K values of its column that a
+// 16 x 16 x 32 MFMA operand needs. Plain 8-byte reads cost the loop about 19 % against the
+// 16-byte reads of K-contiguous operands, the transpose about 5 % more, so this mode serves the
+// paths that keep no transposed copy (the memory-lean backward).
+template <int NI, int ROWS>
+struct KOperandTR {
+    const bf16_t* src;  // the tile's first column; element (k, j) at src[k * ld + j]
+    int64_t ld;
+    uint32_t voff[NI];
+    int dst[NI];  // chunk index of the destination within a stage, or -1 (dummy)
+    int kk[NI];   // the lane's K row within the stage
+    bool ok[NI];
+    template <typename P, typename Id>
+    __device__ __forceinline__ void init(const P* s, int64_t ld_, int64_t mn0, int64_t mn_lim, int stage_off,
+                                         const Id& id) {
+        src = (const bf16_t*)s;
+        ld = ld_;
+        const int rs = id.lane >> 2, c = id.lane & 3, g = rs >> 2, r = rs & 3;
+#pragma unroll
+        for (int t = 0; t < NI; ++t) {
+            const int idx = 8 * t + id.w;  // instruction: block idx/2, K half idx%2
+            const bool real = idx < 2 * (ROWS / 32);
+            const int b = idx >> 1, ks = idx & 1;
+            const int k = 8 * g + 4 * ks + r, j = 32 * b + 8 * c;
+            voff[t] = (uint32_t)(((int64_t)k * ld + j) * 2);
+            kk[t] = k;
+            ok[t] = real && mn0 + j < mn_lim;
+            dst[t] = real ? stage_off + (2 * b + ks) * 64 : -1;
+        }
+    }
+    template <typename Id>
+    __device__ __forceinline__ void issue_one(u32x4* L, int stage, int t, int64_t k0, int64_t k_lim, bool, bool live,
+                                              const Id& id) const {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + k0 * ld);
+        const bool in = live && ok[t] && k0 + kk[t] < k_lim;
+        u32x4* d = dst[t] >= 0 ? L + stage * WST + dst[t] : L + 4 * WST + 64 * (id.w & 3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)d, 16, (int)(in ? voff[t] : kOOB), 0, 0, 0);
+    }
+};
+
+typedef short kd_v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) kd_v4s lds_v4s;
+
+// The MFMA operand of 16-column group c16 of a kTrans operand stage: lane l gets column l%16
+// at K 8*(l/16) .. +7.
+__device__ __forceinline__ u32x4 trfrag(const u32x4* S, int c16, int lane) {
+    const int b = c16 >> 1, h = c16 & 1, g = lane >> 4, x = lane & 15;
+    const char* p = (const char*)S + b * 2048 + (4 * g + (x >> 2)) * 64 + h * 32 + (x & 3) * 8;
+    const kd_v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+    const kd_v4s r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 1024));
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 a = __builtin_bit_cast(u2, r1), c = __builtin_bit_cast(u2, r2);
+    return u32x4{a[0], a[1], c[0], c[1]};
+}
+
 // Wide tile on 16 x 16 blocks: eight waves in a 2 x 4 grid, 128 x 80 per wave = 8 x 5 blocks,
 // acc[i][j] at tile rows wm*128 + 16i, columns wn*80 + 16j (WaveIdN<8>). The stage layout and
 // DMA are those above; the schedule is gemm_tile_kk16's: part 0 = A rows 0-3 while A rows 4-7
@@ -797,8 +864,9 @@ __device__ __forceinline__ void gemm_tile_w16(f32x4 (&acc)[8][5], u32x4* L, cons
         for (int j = 0; j < 5; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nk = (int)((k_end - k_begin + BKH - 1) / BKH);
     if (nk <= 0) return;
-    KOperandW<T, BA, 2, kTileM> opA;
-    KOperandW<T, BB, 3, kWideN> opB;
+    static_assert((BA != kTrans && BB != kTrans) || sizeof(T) == 2, "kTrans operands are bf16");
+    typename std::conditional<BA == kTrans, KOperandTR<2, kTileM>, KOperandW<T, BA, 2, kTileM>>::type opA;
+    typename std::conditional<BB == kTrans, KOperandTR<3, kWideN>, KOperandW<T, BB, 3, kWideN>>::type opB;
     opA.init(A, lda, m0, m_lim, 0, id);
     opB.init(B, ldb, n0, n_lim, kTileM * NCH4, id);
     auto kof = [&](int s) { return k_begin + (int64_t)s * BKH; };
@@ -814,13 +882,19 @@ __device__ __forceinline__ void gemm_tile_w16(f32x4 (&acc)[8][5], u32x4* L, cons
     auto rdA = [&](int i0, int s) {
         const u32x4* S = L + (s & 3) * WST;
 #pragma unroll
-        for (int i = i0; i < i0 + 4; ++i) fa[i] = frag16(S, id.wm * 128 + 16 * i, id.lane);
+        for (int i = i0; i < i0 + 4; ++i)
+            fa[i] = BA == kTrans ? trfrag(S, id.wm * 8 + i, id.lane) : frag16(S, id.wm * 128 + 16 * i, id.lane);
     };
     auto rdB = [&](u32x4 (&b)[5], int s) {
         const u32x4* S = L + (s & 3) * WST + kTileM * NCH4;
 #pragma unroll
-        for (int j = 0; j < 5; ++j) b[j] = frag16(S, id.wn * 80 + 16 * j, id.lane);
+        for (int j = 0; j < 5; ++j)
+            b[j] = BB == kTrans ? trfrag(S, id.wn * 5 + j, id.lane) : frag16(S, id.wn * 80 + 16 * j, id.lane);
     };
+    // LDS reads per fragment: two for a kTrans operand
+    constexpr int RA = BA == kTrans ? 2 : 1, RB = BB == kTrans ? 2 : 1;
+    constexpr int NRD1 = 4 * RA + 5 * RB;                 // reads under part 1's 15 MFMAs
+    constexpr int RDG = NRD1 <= 15 ? NRD1 : (NRD1 + 1) / 2, RDPER = NRD1 <= 15 ? 1 : 2;
     auto stage = [&](int k, const u32x4 (&bc)[5], u32x4 (&bn)[5], bool more) {
         KD_SCHED_FENCE();
         rdA(4, k);
@@ -831,7 +905,7 @@ __device__ __forceinline__ void gemm_tile_w16(f32x4 (&acc)[8][5], u32x4* L, cons
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 4 * MM, 0);
-            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, RA, 0);
         }
         __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 4 * MM, 0);
         KD_SCHED_FENCE();
@@ -851,18 +925,18 @@ __device__ __forceinline__ void gemm_tile_w16(f32x4 (&acc)[8][5], u32x4* L, cons
 #pragma unroll
             for (int j = 0; j < 5; ++j) mma16<T>(acc[i][j], fa[i], bc[j]);
         if (more) {
-            // 20 MFMAs carry 5 DMA issues and 9 fragment reads
+            // 20 MFMAs carry 5 DMA issues and the fragment reads (9 from K-contiguous operands)
 #pragma unroll
             for (int q = 0; q < 5; ++q) {
                 __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, MM, 1);
                 __builtin_amdgcn_sched_group_barrier(KD_SG_VMEM_RD, 1, 1);
             }
 #pragma unroll
-            for (int q = 0; q < 9; ++q) {
+            for (int q = 0; q < RDG; ++q) {
                 __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, MM, 1);
-                __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, 1, 1);
+                __builtin_amdgcn_sched_group_barrier(KD_SG_DS_RD, RDPER, 1);
             }
-            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, 6 * MM, 1);
+            __builtin_amdgcn_sched_group_barrier(KD_SG_MFMA, (15 - RDG) * MM, 1);
         }
         KD_SCHED_FENCE();
     };

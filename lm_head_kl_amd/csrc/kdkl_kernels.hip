@@ -986,8 +986,10 @@ __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
         }
 }
 
-// Same product on 256 x 320 tiles (tokens x hidden) with stage-tiled G_c and W^T.
-template <typename T>
+// Same product on 256 x 320 tiles (tokens x hidden): with stage-tiled G_c and W^T (GL = kTiled),
+// or, in the memory-lean backward (bf16), with the K-blocked G_c and W as stored, whose rows run
+// along V and so reach the MFMAs through LDS transpose reads (GL = kKBlk).
+template <typename T, int GL>
 __global__ __launch_bounds__(512, 1) void k_dh_w(DhArgs a) {
     constexpr int SW = 64 / (int)sizeof(T);
     __shared__ u32x4 L[WIDE_LDS_CHUNKS];
@@ -1001,8 +1003,12 @@ __global__ __launch_bounds__(512, 1) void k_dh_w(DhArgs a) {
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kWideN;
     const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
     f32x4 acc[8][5];
-    gemm_tile_w16<T, kTiled, kTiled>(acc, L, id, (const T*)a.G, a.Vp / SW, m0, a.cc, k_end, (const T*)a.W, a.Vp / SW,
-                                     n0, a.d, k_end, k_begin, k_end);
+    if constexpr (GL == kKBlk)
+        gemm_tile_w16<T, kKBlk, kTrans>(acc, L, id, (const T*)a.G, a.cc, m0, a.cc, k_end, (const T*)a.W + n0, a.d, n0,
+                                        a.d, min(a.V, k_end), k_begin, k_end);
+    else
+        gemm_tile_w16<T, kTiled, kTiled>(acc, L, id, (const T*)a.G, a.Vp / SW, m0, a.cc, k_end, (const T*)a.W,
+                                         a.Vp / SW, n0, a.d, k_end, k_begin, k_end);
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -1143,7 +1149,10 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
 // per pass, in two batches; old values are requested ahead of the LDS work that hides them.
 constexpr int kWSS = 324;
 
-template <typename T>
+// GL = kTiled: G_c^T and H_c^T stage-tiled over a group of chunks. GL = kKBlk (the memory-lean
+// backward, bf16): one chunk's K-blocked G_c and H as stored, both M/N-contiguous for this
+// product (their rows run along the tokens), through LDS transpose reads.
+template <typename T, int GL>
 __global__ __launch_bounds__(512, 1) void k_dw_w(DwArgs a) {
     constexpr int NT = 512, IB = 5;  // items per thread per batch; 2 batches x 512 x 5 = 64 rows x 80
     constexpr int SW = 64 / (int)sizeof(T);
@@ -1155,8 +1164,12 @@ __global__ __launch_bounds__(512, 1) void k_dw_w(DwArgs a) {
     const int mt = (int)(t / a.n_nt), nt = (int)(t % a.n_nt);
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kWideN;
     f32x4 acc[8][5];
-    gemm_tile_w16<T, kTiled, kTiled>(acc, L, id, (const T*)a.G, a.ldg / SW, m0, a.Vp, a.ccp, (const T*)a.H, a.ldh / SW,
-                                     n0, a.d, a.ccp, 0, a.ccp);
+    if constexpr (GL == kKBlk)
+        gemm_tile_w16<T, kTrans, kTrans>(acc, L, id, (const T*)a.G + (m0 / kTileM) * a.cc * kTileM, kTileM, m0, a.Vp,
+                                         a.cc, (const T*)a.H + a.c0 * a.ldh + n0, a.ldh, n0, a.d, a.cc, 0, a.cc);
+    else
+        gemm_tile_w16<T, kTiled, kTiled>(acc, L, id, (const T*)a.G, a.ldg / SW, m0, a.Vp, a.ccp, (const T*)a.H,
+                                         a.ldh / SW, n0, a.d, a.ccp, 0, a.ccp);
     const WaveIdN<8> ie = id.fresh();
     float* stage = (float*)L;
     // dW is addressed through a descriptor at the tile origin with 32-bit offsets (d <= 2^20
@@ -2243,19 +2256,21 @@ hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W
     a.kper = round_up((a.Vp + n_split - 1) / n_split, 64);
     a.part = part;
     a.dH = dH;
-    a.n_nt = (int)((sh.d + (WT ? kWideN : kTileN) - 1) / (WT ? kWideN : kTileN));
+    // the wide tile: from W^T, or (bf16) from the K-blocked G_c and W as stored
+    const bool wide = WT || (g_blocked && sh.act == Dt::BF16);
+    a.n_nt = (int)((sh.d + (wide ? kWideN : kTileN) - 1) / (wide ? kWideN : kTileN));
     a.n_mt = (int)((cc + kTileM - 1) / kTileM);
     const dim3 grid(grid_xcd((int64_t)n_split * a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16) {
         if (WT)
-            KD_LAUNCH(kKindDh, s, k_dh_w<bf16_t>, grid, dim3(512), 0, s, a);
+            KD_LAUNCH(kKindDh, s, (k_dh_w<bf16_t, kTiled>), grid, dim3(512), 0, s, a);
         else if (g_blocked)
-            KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, true>), grid, dim3(NTHR), 0, s, a);
+            KD_LAUNCH(kKindDh, s, (k_dh_w<bf16_t, kKBlk>), grid, dim3(512), 0, s, a);
         else
             KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, false>), grid, dim3(NTHR), 0, s, a);
     } else {
         if (WT)
-            KD_LAUNCH(kKindDh, s, k_dh_w<float>, grid, dim3(512), 0, s, a);
+            KD_LAUNCH(kKindDh, s, (k_dh_w<float, kTiled>), grid, dim3(512), 0, s, a);
         else if (g_blocked)
             KD_LAUNCH(kKindDh, s, (k_dh<float, true>), grid, dim3(NTHR), 0, s, a);
         else
@@ -2288,8 +2303,15 @@ hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H
     a.ccp = cc;
     a.accumulate = accumulate ? 1 : 0;
     a.dW = dW;
-    a.n_nt = (int)((sh.d + kTileN - 1) / kTileN);
     a.n_mt = (int)(a.Vp / kTileM);
+    if (g_blocked && sh.act == Dt::BF16) {
+        // the memory-lean backward: 256 x 320 tiles on the K-blocked G_c and H as stored
+        a.n_nt = (int)((sh.d + kWideN - 1) / kWideN);
+        const dim3 grid(grid_xcd((int64_t)a.n_nt * a.n_mt));
+        KD_LAUNCH(kKindDw, s, (k_dw_w<bf16_t, kKBlk>), grid, dim3(512), 0, s, a);
+        return hipGetLastError();
+    }
+    a.n_nt = (int)((sh.d + kTileN - 1) / kTileN);
     const dim3 grid(grid_xcd((int64_t)a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16)
         KD_LAUNCH(kKindDw, s, k_dw<bf16_t>, grid, dim3(NTHR), 0, s, a);
@@ -2318,9 +2340,9 @@ hipError_t launch_dw_t(const Shape& sh, const void* GT, int64_t ldgt, const void
     a.n_mt = (int)(a.Vp / kTileM);
     const dim3 grid(grid_xcd((int64_t)a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16)
-        KD_LAUNCH(kKindDw, s, k_dw_w<bf16_t>, grid, dim3(512), 0, s, a);
+        KD_LAUNCH(kKindDw, s, (k_dw_w<bf16_t, kTiled>), grid, dim3(512), 0, s, a);
     else
-        KD_LAUNCH(kKindDw, s, k_dw_w<float>, grid, dim3(512), 0, s, a);
+        KD_LAUNCH(kKindDw, s, (k_dw_w<float, kTiled>), grid, dim3(512), 0, s, a);
     return hipGetLastError();
 }
 
