@@ -370,7 +370,12 @@ __device__ __forceinline__ int swz4(int r, int c) { return c ^ (((r >> 2) ^ (r >
 //           tile's M or N entries are contiguous in it: element (mn, k) at src[k*ld + mn - mn0]
 //           for a src that the caller points at the tile's first column. Read through LDS
 //           transpose reads (see KOperandTR).
-enum Lay : int { kRow = 0, kKBlk = 1, kTiled = 2, kTrans = 3 };
+//   kTransT the same, stage-tiled with the roles of rows and columns exchanged: K runs along
+//           the rows (blocks of 256), M/N along the 64-byte stages: element (mn, k) at
+//           src[((k/256)*ld + (mn-mn0)/32)*8192 + (k%256)*32 + (mn-mn0)%32], src at the tile's
+//           first column, ld the stages per row block. Each stage's 32 K rows of a 32-column
+//           block are then one contiguous 2 KB piece.
+enum Lay : int { kRow = 0, kKBlk = 1, kTiled = 2, kTrans = 3, kTransT = 4 };
 
 template <typename T, int LAY = kRow, int NW = 4>
 struct KOperand4 {
@@ -795,9 +800,9 @@ struct KOperandW {
 // 16 x 16 x 32 MFMA operand needs. Plain 8-byte reads cost the loop about 19 % against the
 // 16-byte reads of K-contiguous operands, the transpose about 5 % more, so this mode serves the
 // paths that keep no transposed copy (the memory-lean backward).
-template <int NI, int ROWS>
+template <int NI, int ROWS, bool TILED = false>
 struct KOperandTR {
-    const bf16_t* src;  // the tile's first column; element (k, j) at src[k * ld + j]
+    const bf16_t* src;  // the tile's first column (kTrans: element (k, j) at src[k * ld + j])
     int64_t ld;
     uint32_t voff[NI];
     int dst[NI];  // chunk index of the destination within a stage, or -1 (dummy)
@@ -815,7 +820,7 @@ struct KOperandTR {
             const bool real = idx < 2 * (ROWS / 32);
             const int b = idx >> 1, ks = idx & 1;
             const int k = 8 * g + 4 * ks + r, j = 32 * b + 8 * c;
-            voff[t] = (uint32_t)(((int64_t)k * ld + j) * 2);
+            voff[t] = TILED ? (uint32_t)((b * 8192 + k * 32 + 8 * c) * 2) : (uint32_t)(((int64_t)k * ld + j) * 2);
             kk[t] = k;
             ok[t] = real && mn0 + j < mn_lim;
             dst[t] = real ? stage_off + (2 * b + ks) * 64 : -1;
@@ -824,7 +829,8 @@ struct KOperandTR {
     template <typename Id>
     __device__ __forceinline__ void issue_one(u32x4* L, int stage, int t, int64_t k0, int64_t k_lim, bool, bool live,
                                               const Id& id) const {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(src + k0 * ld);
+        const __amdgpu_buffer_rsrc_t rs =
+            make_rsrc(TILED ? src + ((k0 >> 8) * ld * 8192 + (k0 & 255) * 32) : src + k0 * ld);
         const bool in = live && ok[t] && k0 + kk[t] < k_lim;
         u32x4* d = dst[t] >= 0 ? L + stage * WST + dst[t] : L + 4 * WST + 64 * (id.w & 3);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)d, 16, (int)(in ? voff[t] : kOOB), 0, 0, 0);
@@ -864,9 +870,10 @@ __device__ __forceinline__ void gemm_tile_w16(f32x4 (&acc)[8][5], u32x4* L, cons
         for (int j = 0; j < 5; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int nk = (int)((k_end - k_begin + BKH - 1) / BKH);
     if (nk <= 0) return;
-    static_assert((BA != kTrans && BB != kTrans) || sizeof(T) == 2, "kTrans operands are bf16");
-    typename std::conditional<BA == kTrans, KOperandTR<2, kTileM>, KOperandW<T, BA, 2, kTileM>>::type opA;
-    typename std::conditional<BB == kTrans, KOperandTR<3, kWideN>, KOperandW<T, BB, 3, kWideN>>::type opB;
+    constexpr bool TA = BA == kTrans || BA == kTransT, TB = BB == kTrans || BB == kTransT;
+    static_assert((!TA && !TB) || sizeof(T) == 2, "kTrans and kTransT operands are bf16");
+    typename std::conditional<TA, KOperandTR<2, kTileM, BA == kTransT>, KOperandW<T, BA, 2, kTileM>>::type opA;
+    typename std::conditional<TB, KOperandTR<3, kWideN, BB == kTransT>, KOperandW<T, BB, 3, kWideN>>::type opB;
     opA.init(A, lda, m0, m_lim, 0, id);
     opB.init(B, ldb, n0, n_lim, kTileM * NCH4, id);
     auto kof = [&](int s) { return k_begin + (int64_t)s * BKH; };
@@ -883,16 +890,16 @@ __device__ __forceinline__ void gemm_tile_w16(f32x4 (&acc)[8][5], u32x4* L, cons
         const u32x4* S = L + (s & 3) * WST;
 #pragma unroll
         for (int i = i0; i < i0 + 4; ++i)
-            fa[i] = BA == kTrans ? trfrag(S, id.wm * 8 + i, id.lane) : frag16(S, id.wm * 128 + 16 * i, id.lane);
+            fa[i] = TA ? trfrag(S, id.wm * 8 + i, id.lane) : frag16(S, id.wm * 128 + 16 * i, id.lane);
     };
     auto rdB = [&](u32x4 (&b)[5], int s) {
         const u32x4* S = L + (s & 3) * WST + kTileM * NCH4;
 #pragma unroll
         for (int j = 0; j < 5; ++j)
-            b[j] = BB == kTrans ? trfrag(S, id.wn * 5 + j, id.lane) : frag16(S, id.wn * 80 + 16 * j, id.lane);
+            b[j] = TB ? trfrag(S, id.wn * 5 + j, id.lane) : frag16(S, id.wn * 80 + 16 * j, id.lane);
     };
     // LDS reads per fragment: two for a kTrans operand
-    constexpr int RA = BA == kTrans ? 2 : 1, RB = BB == kTrans ? 2 : 1;
+    constexpr int RA = TA ? 2 : 1, RB = TB ? 2 : 1;
     constexpr int NRD1 = 4 * RA + 5 * RB;                 // reads under part 1's 15 MFMAs
     constexpr int RDG = NRD1 <= 15 ? NRD1 : (NRD1 + 1) / 2, RDPER = NRD1 <= 15 ? 1 : 2;
     auto stage = [&](int k, const u32x4 (&bc)[5], u32x4 (&bn)[5], bool more) {

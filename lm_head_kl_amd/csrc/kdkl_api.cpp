@@ -116,7 +116,7 @@ struct FusedWs {
     int32_t* cplan_off;
     uint32_t* cplan_ent;
     float* pt;
-    void* Gc;   // stage-tiled (K-blocked [Vp/256][cc][256] in the memory-lean backward)
+    void* Gc;   // stage-tiled (K-blocked [Vp/256][cc][256] in the fp32 memory-lean backward)
     void* GT;   // G_c^T stage-tiled, ldgt K columns: a group of chunks side by side
     void* WT;   // W^T stage-tiled, Vp K columns, entries past V zero
     void* HT;   // H_c^T stage-tiled, ldgt K columns
@@ -547,9 +547,10 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
         // The chunk's row blocks in the plan; entry offsets in it are absolute.
         const int32_t* c_off = w.cplan_off + (one_plan ? (c0 / kTileM) * plan_stride : 0);
         if (lean) {
-            // G_c only; dH reads W as stored and dW reads G_c and H_c as they are.
+            // G_c only (stage-tiled for bf16, K-blocked for fp32); dH reads W as stored and dW reads
+            // G_c and H_c as they are.
             KD_TRY(launch_bwd_grad(sh, H, W, lse, w.pt + c0 * p->K, grad_loss, c0, cc, c_off, w.cplan_ent, w.Gc,
-                                   false, nullptr, 0, 0, s));
+                                   p->act == KD_BF16, nullptr, 0, 0, s));
             KD_TRY(launch_dh(sh, w.Gc, 0, W, nullptr, c0, cc, w.n_split, w.dh_part, dH, s, true));
             if (want_dw) {
                 KD_TRY(launch_dw(sh, w.Gc, 0, H, c0, cc, acc0 || dw_written, dW, s, true));

@@ -129,18 +129,19 @@ hipError_t launch_transpose(Dt dt, const void* src, int64_t lds, int64_t rows, i
                             void* tiled_copy = nullptr);
 
 // dH rows [c0, c0+cc) = G_c W. With WT not null, G_c is the stage-tiled tile written by
-// launch_bwd_grad and WT is W^T from launch_transpose (kdst = Vp); with WT null, W is read as stored
-// and G_c is either that K-blocked tile (g_blocked) or row-major [cc][ldg]. Split over the
-// vocabulary into n_split fp32 partials when n_split > 1 (part: [n_split][cc][d]), then
-// reduced in a fixed order.
+// launch_bwd_grad and WT is W^T from launch_transpose (kdst = Vp); with WT null, W is read as
+// stored and G_c is the memory-lean backward's tile (lean: stage-tiled for bf16, K-blocked for
+// fp32) or row-major [cc][ldg]. Split over the vocabulary into n_split fp32 partials when
+// n_split > 1 (part: [n_split][cc][d]), then reduced in a fixed order.
 hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, const void* WT,
                      int64_t c0, int64_t cc, int n_split, float* part, void* dH, hipStream_t s,
-                     bool g_blocked = false);
+                     bool lean = false);
 
 // dW (+)= G_c^T H[c0:c0+cc] from G_c and H, both M/N contiguous: G_c row-major [cc][ldg], or
-// the gradient kernel's K-blocked tile [Vp/256][cc][256] (g_blocked; ldg unused).
+// the memory-lean backward's tile (lean; ldg unused): stage-tiled for bf16 (wide tiles, LDS
+// transpose reads), K-blocked [Vp/256][cc][256] for fp32.
 hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H, int64_t c0,
-                     int64_t cc, bool accumulate, float* dW, hipStream_t s, bool g_blocked = false);
+                     int64_t cc, bool accumulate, float* dW, hipStream_t s, bool lean = false);
 // dW (+)= G_c^T H_c over K columns [0, cc) from stage-tiled G_c^T (launch_bwd_grad, ldgt K
 // columns) and H_c^T (launch_transpose, kdst = ldht).
 hipError_t launch_dw_t(const Shape& sh, const void* GT, int64_t ldgt, const void* HT, int64_t ldht,

@@ -944,9 +944,9 @@ struct DhArgs {
     void* dH;
 };
 
-// BLK: G_c is the K-blocked tile of the gradient kernel ([Vp/256][cc][256]) instead of
-// row-major [cc][ldg]; W is read as stored either way (the memory-lean backward, which keeps
-// no W^T).
+// BLK: G_c is the K-blocked tile of the gradient kernel ([Vp/256][cc][256], the fp32 memory-lean
+// backward, which keeps no W^T) instead of row-major [cc][ldg] (the dense path); W is read as
+// stored either way.
 template <typename T, bool BLK>
 __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
     __shared__ u32x4 L[LDS_CHUNKS];
@@ -986,10 +986,10 @@ __global__ __launch_bounds__(256, 1) void k_dh(DhArgs a) {
         }
 }
 
-// Same product on 256 x 320 tiles (tokens x hidden): with stage-tiled G_c and W^T (GL = kTiled),
-// or, in the memory-lean backward (bf16), with the K-blocked G_c and W as stored, whose rows run
-// along V and so reach the MFMAs through LDS transpose reads (GL = kKBlk).
-template <typename T, int GL>
+// Same product on 256 x 320 tiles (tokens x hidden) with stage-tiled G_c, and W^T stage-tiled
+// (BW = kTiled) or, in the memory-lean backward (bf16), W as stored, whose rows run along V and
+// so reach the MFMAs through LDS transpose reads (BW = kTrans).
+template <typename T, int BW>
 __global__ __launch_bounds__(512, 1) void k_dh_w(DhArgs a) {
     constexpr int SW = 64 / (int)sizeof(T);
     __shared__ u32x4 L[WIDE_LDS_CHUNKS];
@@ -1003,9 +1003,9 @@ __global__ __launch_bounds__(512, 1) void k_dh_w(DhArgs a) {
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kWideN;
     const int64_t k_begin = ks * a.kper, k_end = min(a.Vp, k_begin + a.kper);
     f32x4 acc[8][5];
-    if constexpr (GL == kKBlk)
-        gemm_tile_w16<T, kKBlk, kTrans>(acc, L, id, (const T*)a.G, a.cc, m0, a.cc, k_end, (const T*)a.W + n0, a.d, n0,
-                                        a.d, min(a.V, k_end), k_begin, k_end);
+    if constexpr (BW == kTrans)
+        gemm_tile_w16<T, kTiled, kTrans>(acc, L, id, (const T*)a.G, a.Vp / SW, m0, a.cc, k_end, (const T*)a.W + n0, a.d,
+                                         n0, a.d, min(a.V, k_end), k_begin, k_end);
     else
         gemm_tile_w16<T, kTiled, kTiled>(acc, L, id, (const T*)a.G, a.Vp / SW, m0, a.cc, k_end, (const T*)a.W,
                                          a.Vp / SW, n0, a.d, k_end, k_begin, k_end);
@@ -1149,8 +1149,8 @@ __global__ __launch_bounds__(256, 1) void k_dw(DwArgs a) {
 // per pass, in two batches; old values are requested ahead of the LDS work that hides them.
 constexpr int kWSS = 324;
 
-// GL = kTiled: G_c^T and H_c^T stage-tiled over a group of chunks. GL = kKBlk (the memory-lean
-// backward, bf16): one chunk's K-blocked G_c and H as stored, both M/N-contiguous for this
+// GL = kTiled: G_c^T and H_c^T stage-tiled over a group of chunks. GL = kTransT (the memory-lean
+// backward, bf16): one chunk's stage-tiled G_c and H as stored, both M/N-contiguous for this
 // product (their rows run along the tokens), through LDS transpose reads.
 template <typename T, int GL>
 __global__ __launch_bounds__(512, 1) void k_dw_w(DwArgs a) {
@@ -1164,9 +1164,9 @@ __global__ __launch_bounds__(512, 1) void k_dw_w(DwArgs a) {
     const int mt = (int)(t / a.n_nt), nt = (int)(t % a.n_nt);
     const int64_t m0 = (int64_t)mt * kTileM, n0 = (int64_t)nt * kWideN;
     f32x4 acc[8][5];
-    if constexpr (GL == kKBlk)
-        gemm_tile_w16<T, kTrans, kTrans>(acc, L, id, (const T*)a.G + (m0 / kTileM) * a.cc * kTileM, kTileM, m0, a.Vp,
-                                         a.cc, (const T*)a.H + a.c0 * a.ldh + n0, a.ldh, n0, a.d, a.cc, 0, a.cc);
+    if constexpr (GL == kTransT)
+        gemm_tile_w16<T, kTransT, kTrans>(acc, L, id, (const T*)a.G + (m0 / SW) * (kTileM * SW), a.Vp / SW, m0, a.Vp,
+                                          a.cc, (const T*)a.H + a.c0 * a.ldh + n0, a.ldh, n0, a.d, a.cc, 0, a.cc);
     else
         gemm_tile_w16<T, kTiled, kTiled>(acc, L, id, (const T*)a.G, a.ldg / SW, m0, a.Vp, a.ccp, (const T*)a.H,
                                          a.ldh / SW, n0, a.d, a.ccp, 0, a.ccp);
@@ -2242,7 +2242,7 @@ hipError_t launch_tile_rows(Dt dt, const void* src, int64_t ld, int64_t rows, in
 }
 
 hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W, const void* WT, int64_t c0,
-                     int64_t cc, int n_split, float* part, void* dH, hipStream_t s, bool g_blocked) {
+                     int64_t cc, int n_split, float* part, void* dH, hipStream_t s, bool lean) {
     DhArgs a;
     a.G = Gc;
     a.ldg = ldg;
@@ -2256,22 +2256,22 @@ hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W
     a.kper = round_up((a.Vp + n_split - 1) / n_split, 64);
     a.part = part;
     a.dH = dH;
-    // the wide tile: from W^T, or (bf16) from the K-blocked G_c and W as stored
-    const bool wide = WT || (g_blocked && sh.act == Dt::BF16);
+    // the wide tile: from W^T, or (the memory-lean backward, bf16) from W as stored
+    const bool wide = WT || (lean && sh.act == Dt::BF16);
     a.n_nt = (int)((sh.d + (wide ? kWideN : kTileN) - 1) / (wide ? kWideN : kTileN));
     a.n_mt = (int)((cc + kTileM - 1) / kTileM);
     const dim3 grid(grid_xcd((int64_t)n_split * a.n_nt * a.n_mt));
     if (sh.act == Dt::BF16) {
         if (WT)
             KD_LAUNCH(kKindDh, s, (k_dh_w<bf16_t, kTiled>), grid, dim3(512), 0, s, a);
-        else if (g_blocked)
-            KD_LAUNCH(kKindDh, s, (k_dh_w<bf16_t, kKBlk>), grid, dim3(512), 0, s, a);
+        else if (lean)  // bf16: G_c stage-tiled
+            KD_LAUNCH(kKindDh, s, (k_dh_w<bf16_t, kTrans>), grid, dim3(512), 0, s, a);
         else
             KD_LAUNCH(kKindDh, s, (k_dh<bf16_t, false>), grid, dim3(NTHR), 0, s, a);
     } else {
         if (WT)
             KD_LAUNCH(kKindDh, s, (k_dh_w<float, kTiled>), grid, dim3(512), 0, s, a);
-        else if (g_blocked)
+        else if (lean)  // fp32: G_c K-blocked
             KD_LAUNCH(kKindDh, s, (k_dh<float, true>), grid, dim3(NTHR), 0, s, a);
         else
             KD_LAUNCH(kKindDh, s, (k_dh<float, false>), grid, dim3(NTHR), 0, s, a);
@@ -2288,11 +2288,11 @@ hipError_t launch_dh(const Shape& sh, const void* Gc, int64_t ldg, const void* W
 }
 
 hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H, int64_t c0, int64_t cc,
-                     bool accumulate, float* dW, hipStream_t s, bool g_blocked) {
+                     bool accumulate, float* dW, hipStream_t s, bool lean) {
     DwArgs a;
     a.G = Gc;
     a.ldg = ldg;
-    a.g_blk = g_blocked ? 1 : 0;
+    a.g_blk = lean ? 1 : 0;  // the fp32 memory-lean G_c is K-blocked
     a.Vp = round_up(sh.V, kTileN);
     a.H = H;
     a.ldh = sh.d;
@@ -2304,11 +2304,11 @@ hipError_t launch_dw(const Shape& sh, const void* Gc, int64_t ldg, const void* H
     a.accumulate = accumulate ? 1 : 0;
     a.dW = dW;
     a.n_mt = (int)(a.Vp / kTileM);
-    if (g_blocked && sh.act == Dt::BF16) {
-        // the memory-lean backward: 256 x 320 tiles on the K-blocked G_c and H as stored
+    if (lean && sh.act == Dt::BF16) {
+        // the memory-lean backward: 256 x 320 tiles on the stage-tiled G_c and H as stored
         a.n_nt = (int)((sh.d + kWideN - 1) / kWideN);
         const dim3 grid(grid_xcd((int64_t)a.n_nt * a.n_mt));
-        KD_LAUNCH(kKindDw, s, (k_dw_w<bf16_t, kKBlk>), grid, dim3(512), 0, s, a);
+        KD_LAUNCH(kKindDw, s, (k_dw_w<bf16_t, kTransT>), grid, dim3(512), 0, s, a);
         return hipGetLastError();
     }
     a.n_nt = (int)((sh.d + kTileN - 1) / kTileN);
