@@ -126,7 +126,8 @@ typedef enum kd_dtype {
  *   N, d, V, K   sizes as above; limits: N >= 1, 8 <= d <= 1048576 and d % 8 == 0, 1 <= V <= 4194304,
  *                1 <= K <= min(V, 1024), N * K < 2^31, N * d < 2^31, V * d < 2^31. The backward
  *                calls (kd_fused_kl_bwd without KD_LOW_MEMORY, kd_chunked_kl, kd_fused_kl_fwdbwd)
- *                also need V <= 3355392 (bf16) or V <= 1677568 (fp32): KD_ERR_SHAPE otherwise.
+ *                also need V <= 3355392 (bf16) or V <= 1677568 (fp32), and kd_fused_kl_bwd with
+ *                KD_LOW_MEMORY in bf16 V <= 4194048: KD_ERR_SHAPE otherwise.
  *   chunk        rows per backward chunk (>= 1; N need not be a multiple). It bounds the
  *                backward's per-chunk gradient tile G_c [chunk, V] in the workspace. The
  *                forward keeps each projected tile in registers only, so its memory does not

@@ -157,6 +157,12 @@ bool wide_dh_fits(const kd_problem* p) {
     const int64_t Vp = round_up(p->V, kTileN), sw = 64 / (int64_t)esize(p->act);
     return (Vp / sw) * 320 * 64 - 16 < kDescRange;
 }
+// The bf16 memory-lean backward's dH reads the stage-tiled G_c (256-row blocks) the same way:
+// V up to 4,194,048.
+bool lean_dh_fits(const kd_problem* p) {
+    const int64_t Vp = round_up(p->V, kTileN), sw = 64 / (int64_t)esize(p->act);
+    return p->act != KD_BF16 || (Vp / sw) * 256 * 64 - 16 < kDescRange;
+}
 
 // The forward and gradient kernels read W and H from stage-tiled copies (engine.h, kTiled):
 // the copies cost one pass over W and H per call, and W's size plus a row chunk of H's in the
@@ -512,7 +518,7 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
     kd_status st = check_problem(p);
     if (st != KD_OK) return st;
     const bool want_dw = (p->flags & KD_SKIP_DW) == 0;
-    if (!low_memory(p) && !wide_dh_fits(p)) return KD_ERR_SHAPE;
+    if (low_memory(p) ? !lean_dh_fits(p) : !wide_dh_fits(p)) return KD_ERR_SHAPE;
     if (!H || !W || !idx || !tlog || !lse || !dH || (want_dw && !dW) || !ws) return KD_ERR_NULL;
     if (!aligned(H, 16) || !aligned(W, 16) || !aligned(dH, 16) || (want_dw && !aligned(dW, 16))) return KD_ERR_VALUE;
     if (!aligned(ws, kAlign) || ws_bytes < kd_fused_workspace_bytes(p)) return KD_ERR_WORKSPACE;

@@ -233,7 +233,8 @@ def test_low_memory_workspace():
 def test_wide_dh_vocabulary_limit():
     """The backward paths that read W^T stage-tiled in 320-row blocks stop where its last stage
     would leave a buffer descriptor's 32-bit range: V = 3,355,392 in bf16, 1,677,568 in fp32
-    (KD_ERR_SHAPE before anything is enqueued); the memory-lean backward and the forward go on."""
+    (KD_ERR_SHAPE before anything is enqueued); the memory-lean backward and the forward go on,
+    the bf16 memory-lean backward up to V = 4,194,048."""
     L = _lib.lib()
     for act, vmax in ((KD_BF16, 3355392), (KD_FP32, 1677568)):
         for V, ok in ((vmax, True), (vmax + 256, False)):
@@ -246,6 +247,11 @@ def test_wide_dh_vocabulary_limit():
             lean = prob(N=256, d=8, V=V, K=4, chunk=256, act=act, tlogit=act, flags=_lib.KD_LOW_MEMORY)
             assert bwd(lean, nbytes=1) == 5
             assert fwd(p, nbytes=1) == 5
+    # the bf16 memory-lean backward reads its stage-tiled G_c (256-row blocks) the same way: up to
+    # V = 4,194,048; fp32 goes on to the largest vocabulary the calls take
+    for act, V, ok in ((KD_BF16, 4194048, True), (KD_BF16, 4194304, False), (KD_FP32, 4194304, True)):
+        lean = prob(N=256, d=8, V=V, K=4, chunk=256, act=act, tlogit=act, flags=_lib.KD_LOW_MEMORY)
+        assert bwd(lean, nbytes=1) == (5 if ok else 2), (act, V)
 
 
 @nogpu
