@@ -1,6 +1,6 @@
 """Seeded random problems: sizes, dtype, temperature, teacher recipe, id recipe, chunk,
-normaliser and upstream weight are drawn per case, and each of the four formulations is
-compared in full with the fp64 oracle at the stated tolerances. The fixed edge list
+normaliser and upstream weight are drawn per case, and each of the four formulations (and the
+memory-lean fused backward) is compared in full with the fp64 oracle at the stated tolerances. The fixed edge list
 elsewhere names the boundaries one at a time; here they are combined the way a caller might
 combine them (a ragged chunk with K near its maximum, d just past a hidden tile, V below one
 vocab tile).
@@ -89,6 +89,12 @@ def test_fuzz_case(i):
     torch.cuda.synchronize()
     assert torch.equal(dH1, dH) and torch.equal(dW1, dW), "the backward is not reproducible"
 
+    # memory-lean backward (its own G_c layout and GEMM paths), against the oracle
+    dHl, dWl = kd.fused_kl_bwd(H, W, idx, t, f.lse, grad_loss=gt, T=p.T, chunk=c["chunk"], n_norm=c["n_norm"],
+                               flags=kd.KD_LOW_MEMORY)
+    torch.cuda.synchronize()
+    check("fused low-memory", c, ref, f.loss, f.lse, f.row_kl, dHl, dWl)
+
     # frozen head: the same dH, dW left alone
     dH2, none = kd.fused_kl_bwd(H, W, idx, t, f.lse, grad_loss=gt, T=p.T, chunk=c["chunk"], n_norm=c["n_norm"],
                                 flags=kd.KD_SKIP_DW)
@@ -175,4 +181,11 @@ def test_fuzz_medium(i):
     want = oracle.dw_rows(Hf, Wf, p.idx, tl, p.T, vocab, ref["lse"], n_norm=p.N)
     e_dw = rel_l2(host(dW[torch.from_numpy(vocab).to(dW.device)]), want)
     say(f"  dH relL2 {e_dh:.2e}  dW rows relL2 {e_dw:.2e}")
+    assert e_dh <= tol["grad"] and e_dw <= tol["grad"]
+    # the memory-lean backward on the same shapes
+    dHl, dWl = kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=c["chunk"], flags=kd.KD_LOW_MEMORY)
+    torch.cuda.synchronize()
+    e_dh = rel_l2(host(dHl), ref["dH"])
+    e_dw = rel_l2(host(dWl[torch.from_numpy(vocab).to(dWl.device)]), want)
+    say(f"  low-memory: dH relL2 {e_dh:.2e}  dW rows relL2 {e_dw:.2e}")
     assert e_dh <= tol["grad"] and e_dw <= tol["grad"]
