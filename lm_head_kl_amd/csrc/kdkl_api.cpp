@@ -179,7 +179,7 @@ FusedWs layout_fused(const kd_problem* p, void* ws, bool fwd_tiles = true) {
     const int64_t n_vt = n_vtiles(V), Vp = n_vt * kTileN;
     const int64_t C = chunk_rows(p);
     const bool lean = low_memory(p);
-    // dH on the wide tile except in the fp32 memory-lean backward (bf16 lean: K-blocked G_c, W as stored)
+    // dH on the wide tile except in the fp32 memory-lean backward (bf16 lean: stage-tiled G_c, W as stored)
     w.n_split = dh_splits(C, d, V, !lean || p->act == KD_BF16);
     Carve f(ws);
     w.status = (uint32_t*)f.take(kAlign);

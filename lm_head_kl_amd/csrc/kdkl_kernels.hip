@@ -561,7 +561,7 @@ __device__ __forceinline__ void store8(T* dst, const float (&x)[8]) {
 
 // Second half of a gradient pass, once the pass's 128 vocabulary rows of gs*softmax are staged:
 // subtract gs*p_t at the cached ids that fall in the pass, then write the rows of G (stage-tiled,
-// or K-blocked for the memory-lean backward) and of G^T. Ends with a barrier, so the stage may be
+// or K-blocked for the fp32 memory-lean backward) and of G^T. Ends with a barrier, so the stage may be
 // refilled.
 // The plan fills each bucket in atomic order, so whether an entry is among the first NT (held
 // in registers) or comes from the loop changes between calls; both paths subtract with one
@@ -929,8 +929,9 @@ __global__ __launch_bounds__(256) void k_tile_rows(const T* __restrict__ src, in
 
 // ------------------------------------------------------------------------------------------
 // dH = G W. The dense path multiplies G [rows][ldg] (vocabulary contiguous) by W [V][d]
-// (d contiguous) on 256 x 256 tiles, and so does the memory-lean backward with its K-blocked
-// G_c; the other chunked paths use stage-tiled G_c and W^T on 256 x 320 tiles (k_dh_w).
+// (d contiguous) on 256 x 256 tiles, and so does the fp32 memory-lean backward with its K-blocked
+// G_c; the other chunked paths use stage-tiled G_c on 256 x 320 tiles (k_dh_w), with W^T, or
+// (the bf16 memory-lean backward) with W as stored.
 
 struct DhArgs {
     const void* G;   // G_c [cc][ldg] row-major or K-blocked [Vp/256][cc][256]; stage-tiled with W^T
@@ -2110,7 +2111,7 @@ hipError_t launch_bwd_grad(const Shape& sh, const void* H, const void* W, const 
     // workgroups stay in lockstep and so issue their tile stores all at once.
     const dim3 grid(grid_xcd((int64_t)a.n_vt * a.n_rbc));
     const dim3 blk(64 * kGradWaves);
-    // Operand layouts: H and W stage-tiled or as stored; G_c stage-tiled, or K-blocked (the
+    // Operand layouts: H and W stage-tiled or as stored; G_c stage-tiled, or K-blocked (the fp32
     // memory-lean backward, which reads H and W as stored).
     if (tiled_S > 0 && !g_tiled) return hipErrorInvalidValue;
     if (sh.act == Dt::BF16) {
