@@ -92,15 +92,20 @@ def producer(dev, stream, N: int, V: int, K: int, seed: int, reps: int = 5) -> d
             "frac_of_hbm_peak": read_gb / (ms / 1e3) / PEAK_HBM_GBS}
 
 
-def kernel_sources_sha() -> str:
-    """Hash of the kernel sources; a traffic figure measured on other sources is stale."""
+def kernel_sources_sha(csrc: str | None = None) -> str:
+    """Hash of the kernel sources' code, with comments and layout whitespace dropped: a traffic
+    figure measured on other code is stale."""
     import hashlib
+    import re
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "lm_head_kl_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "lm_head_kl_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+            with open(os.path.join(csrc, name), encoding="utf-8") as f:
+                text = f.read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+            h.update(name.encode() + b"\0" + " ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
