@@ -34,3 +34,16 @@ def test_traffic_summary_lookup(tmp_path, monkeypatch):
     assert bench.measured_traffic("cfg", "dh") is None        # measured on other sources
     assert bench.measured_traffic("cfg", "fwd") is None       # not measured
     assert bench.measured_traffic("other", "bwd_grad") is None
+
+
+def test_sources_hash_follows_code_not_comments(tmp_path):
+    """A comment or reflowed line leaves the kernel-code hash (and so a measured traffic figure)
+    as it is; a change to the code gives a new hash."""
+    src = tmp_path / "csrc"
+    src.mkdir()
+    (src / "k.hip").write_text("__global__ void k(int* p) { p[0] = 1; }\n")
+    base = bench.kernel_sources_sha(str(src))
+    (src / "k.hip").write_text("// writes one\n__global__ void k(int* p) {\n    p[0] = 1;  /* one */\n}\n")
+    assert bench.kernel_sources_sha(str(src)) == base
+    (src / "k.hip").write_text("__global__ void k(int* p) { p[0] = 2; }\n")
+    assert bench.kernel_sources_sha(str(src)) != base
