@@ -564,12 +564,15 @@ kd_status kd_fused_kl_bwd(const kd_problem* p, const void* H, const void* W, con
             }
             continue;
         }
-        // H_c^T into its slot, so that dW = G^T H reads both operands with the rows contiguous
+        // H_c^T into its slot, so that dW = G^T H reads both operands with the rows contiguous.
+        // For whole row blocks the same loads also write the chunk's stage-tiled copy of H_c.
+        const char* Hc = (const char*)H + c0 * p->d * es;
+        const bool one_pass = want_dw && w.cHt && cc % kTileM == 0;
         if (want_dw)
-            KD_TRY(launch_transpose(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d, w.HT, w.ldgt, slot * SC,
-                                    round_up(cc, 32), s));
+            KD_TRY(launch_transpose(sh.act, Hc, p->d, cc, p->d, w.HT, w.ldgt, slot * SC, round_up(cc, 32), s,
+                                    one_pass ? w.cHt : nullptr));
         // Without dW, G^T is not needed: the gradient kernel skips those stores.
-        if (w.cHt) KD_TRY(launch_tile_rows(sh.act, (const char*)H + c0 * p->d * es, p->d, cc, p->d, w.cHt, s));
+        if (w.cHt && !one_pass) KD_TRY(launch_tile_rows(sh.act, Hc, p->d, cc, p->d, w.cHt, s));
         KD_TRY(launch_bwd_grad(sh, w.cHt ? w.cHt : H, w.cWt ? w.cWt : W, lse, w.pt + c0 * p->K, grad_loss, c0, cc,
                                c_off, w.cplan_ent, w.Gc, true, want_dw ? w.GT : nullptr, w.ldgt, slot * SC, s,
                                w.cWt ? w.tS : 0));
