@@ -136,27 +136,32 @@ __device__ __forceinline__ int st_row(int c) { return (c >> 7) * 64 + (c & 63); 
 // ------------------------------------------------------------------------------------------
 // Plan: bucket cached ids by (row block of 256, vocab tile of 256).
 
-__global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ idx, int64_t row0, int64_t row1,
-                                              int K, int64_t V, int n_vt, int32_t* __restrict__ off,
-                                              uint32_t* __restrict__ ent) {
+// One workgroup of kPlanThreads per row block: the grid is only N / 256 workgroups, so each
+// one is wide, and the bucket offsets come from a shuffle scan rather than a serial one.
+constexpr int kPlanThreads = 1024;
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan(const int32_t* __restrict__ idx, int64_t row0,
+                                                       int64_t row1, int K, int64_t V, int n_vt,
+                                                       int32_t* __restrict__ off, uint32_t* __restrict__ ent) {
+    constexpr int PT = kPlanThreads, PW = PT / 64;
     __shared__ int cnt[kMaxVTiles];
-    __shared__ int part[NTHR];
-    const int tid = threadIdx.x;
+    __shared__ int wsum[PW];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int rb = blockIdx.x;
     const int64_t r0 = row0 + (int64_t)rb * kTileM;
     const int rows = (int)min<int64_t>(kTileM, row1 - r0);
     const int64_t base = (int64_t)rb * kTileM * K;
-    for (int t = tid; t < n_vt; t += NTHR) cnt[t] = 0;
+    for (int t = tid; t < n_vt; t += PT) cnt[t] = 0;
     __syncthreads();
     const int n_e = rows * K;
     // Entries go in batches of PB per thread, all loaded before any is used, so the loads'
     // latency is paid once per batch rather than once per entry.
     constexpr int PB = 8;
-    for (int i0 = 0; i0 < n_e; i0 += NTHR * PB) {
+    for (int i0 = 0; i0 < n_e; i0 += PT * PB) {
         int v[PB];
 #pragma unroll
         for (int u = 0; u < PB; ++u) {
-            const int i = i0 + u * NTHR + tid;
+            const int i = i0 + u * PT + tid;
             v[u] = i < n_e ? idx[r0 * K + i] : -1;
         }
 #pragma unroll
@@ -164,23 +169,32 @@ __global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ idx, i
             if (v[u] >= 0 && v[u] < V) atomicAdd(&cnt[v[u] >> 8], 1);
     }
     __syncthreads();
-    // exclusive scan of cnt[0..n_vt): each thread owns a contiguous segment
-    const int seg = (n_vt + NTHR - 1) / NTHR;
+    // Exclusive scan of cnt[0..n_vt): each thread owns a contiguous segment; the segment sums
+    // are scanned within each wave by shuffles, then across the PW wave totals.
+    const int seg = (n_vt + PT - 1) / PT;
     const int s0 = min(n_vt, tid * seg), s1 = min(n_vt, s0 + seg);
     int sum = 0;
     for (int t = s0; t < s1; ++t) sum += cnt[t];
-    part[tid] = sum;
+    int incl = sum;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const int y = __shfl_up(incl, m);
+        if (lane >= m) incl += y;
+    }
+    if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int t = 0; t < NTHR; ++t) {
-            const int x = part[t];
-            part[t] = run;
-            run += x;
+    if (tid < 64) {
+        const int x = lane < PW ? wsum[lane] : 0;
+        int wi = x;
+#pragma unroll
+        for (int m = 1; m < PW; m <<= 1) {
+            const int y = __shfl_up(wi, m);
+            if (lane >= m) wi += y;
         }
+        if (lane < PW) wsum[lane] = wi - x;
     }
     __syncthreads();
-    int run = part[tid];
+    int run = wsum[w] + incl - sum;
     int32_t* o = off + (int64_t)rb * (n_vt + 1);
     for (int t = s0; t < s1; ++t) {
         const int x = cnt[t];
@@ -188,19 +202,19 @@ __global__ __launch_bounds__(256) void k_plan(const int32_t* __restrict__ idx, i
         o[t] = (int32_t)(base + run);
         run += x;
     }
-    if (tid == NTHR - 1) o[n_vt] = (int32_t)(base + run);  // the last segment ends at the total
+    if (tid == PT - 1) o[n_vt] = (int32_t)(base + run);  // the last segment ends at the total
     __syncthreads();
-    for (int i0 = 0; i0 < n_e; i0 += NTHR * PB) {
+    for (int i0 = 0; i0 < n_e; i0 += PT * PB) {
         int v[PB];
 #pragma unroll
         for (int u = 0; u < PB; ++u) {
-            const int i = i0 + u * NTHR + tid;
+            const int i = i0 + u * PT + tid;
             v[u] = i < n_e ? idx[r0 * K + i] : -1;
         }
 #pragma unroll
         for (int u = 0; u < PB; ++u) {
             if (v[u] >= 0 && v[u] < V) {
-                const int i = i0 + u * NTHR + tid;
+                const int i = i0 + u * PT + tid;
                 const int pos = atomicAdd(&cnt[v[u] >> 8], 1);
                 const int r = i / K, k = i - r * K;
                 ent[base + pos] = (uint32_t)r | ((uint32_t)(v[u] & 255) << 8) | ((uint32_t)k << 16);
@@ -427,7 +441,7 @@ __global__ __launch_bounds__(64 * NW, 1) void k_fwd(FwdArgs a) {
 // ------------------------------------------------------------------------------------------
 // Combine: lse_n from the partials, KL_n from the cached teacher and zk, block sums in fp64.
 
-constexpr int kCombRows = 16;  // rows per workgroup (4 per wave)
+constexpr int kCombRows = 4;  // rows per workgroup (one per wave: each row is a chain of dependent reductions)
 
 __global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ part, int n_part, int64_t N, int K,
                                                  float T, const float* __restrict__ zk,
@@ -439,6 +453,19 @@ __global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ part
     for (int rr = 0; rr < kCombRows / 4; ++rr) {
         const int64_t n = (int64_t)blockIdx.x * kCombRows + w * (kCombRows / 4) + rr;
         if (n >= N) break;
+        const void* tl = tlog;
+        auto tval = [&](int k) { return (double)load_t(tl, tdt, n * K + k) / T; };
+        // The row's first 128 cached entries are loaded once, up front, beside the partials;
+        // entries past 128 (K > 128) are read in each pass. Every sum runs in the same order
+        // over k either way.
+        double tv[2];
+        float zv[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int k = lane + 64 * j;
+            tv[j] = k < K ? tval(k) : 0.0;
+            zv[j] = k < K ? zk[n * K + k] : 0.f;
+        }
         float m = -INFINITY, s = 0.f;
         for (int sl = lane; sl < n_part; sl += 64) {
             const float2 v = part[(int64_t)sl * N + n];
@@ -450,20 +477,29 @@ __global__ __launch_bounds__(256) void k_combine(const float2* __restrict__ part
             ms_merge(m, s, m2, s2);
         }
         const double lse_d = ((double)m + log2((double)s)) * kLn2;
-        const void* tl = tlog;
         double mx = -INFINITY;
-        for (int k = lane; k < K; k += 64) mx = fmax(mx, (double)load_t(tl, tdt, n * K + k) / T);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (lane + 64 * j < K) mx = fmax(mx, tv[j]);
+        for (int k = lane + 128; k < K; k += 64) mx = fmax(mx, tval(k));
         mx = wave_max_d(mx);
         double se = 0.0;
-        for (int k = lane; k < K; k += 64) se += exp((double)load_t(tl, tdt, n * K + k) / T - mx);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (lane + 64 * j < K) se += exp(tv[j] - mx);
+        for (int k = lane + 128; k < K; k += 64) se += exp(tval(k) - mx);
         const double lz = mx + log(wave_sum_d(se));
         // An entry whose teacher logit is -inf has p_t = 0 and adds nothing (0 log 0 = 0).
         double term = 0.0;
-        for (int k = lane; k < K; k += 64) {
-            const double lp = (double)load_t(tl, tdt, n * K + k) / T - lz;
+        auto add_term = [&](double t, float z) {
+            const double lp = t - lz;
             const double pk = exp(lp);
-            if (pk > 0.0) term += pk * (lp - (double)zk[n * K + k] / T + lse_d);
-        }
+            if (pk > 0.0) term += pk * (lp - (double)z / T + lse_d);
+        };
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (lane + 64 * j < K) add_term(tv[j], zv[j]);
+        for (int k = lane + 128; k < K; k += 64) add_term(tval(k), zk[n * K + k]);
         const double kl = wave_sum_d(term);
         if (lane == 0) {
             lse[n] = (float)lse_d;
@@ -1996,7 +2032,7 @@ hipError_t launch_plan(const int32_t* idx, int64_t row0, int64_t row1, int64_t K
                        uint32_t* ent, hipStream_t s) {
     const int n_rb = (int)((row1 - row0 + kTileM - 1) / kTileM);
     const int n_vt = (int)((V + kTileN - 1) / kTileN);
-    KD_LAUNCH(kKindPlan, s, k_plan, dim3(n_rb), dim3(NTHR), 0, s, idx, row0, row1, (int)K, V, n_vt, off, ent);
+    KD_LAUNCH(kKindPlan, s, k_plan, dim3(n_rb), dim3(kPlanThreads), 0, s, idx, row0, row1, (int)K, V, n_vt, off, ent);
     return hipGetLastError();
 }
 
