@@ -16,7 +16,7 @@ Prints one JSON line. Along with the throughput it carries:
     backward, and the autograd term with an fp32 dW accumulator, on the same inputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config gptoss] [--chunk C]
-       [--no-cpu-baseline] [--no-dense] [--no-formulations]
+       [--no-cpu-baseline] [--no-dense] [--no-formulations] [--low-memory]
        python bench.py --sweep   (per-config timings and the peak-memory sweep over S; not the
                                   headline line)
 """
@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--sweep", action="store_true",
                     help="time the fused path at every timed config (small, the Qwen-like head over its "
                          "chunk sweep, gpt-oss, the pages' full shape) and sweep S for peak memory")
+    ap.add_argument("--low-memory", action="store_true",
+                    help="time the fused step with the memory-lean backward (KD_LOW_MEMORY) as the step "
+                         "(for its kernel trace; the default step is the headline)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device-to-device once (reference for the HBM byte counters)")
     ap.add_argument("--producer", action="store_true",
@@ -295,7 +298,8 @@ def main():
     print(f"[bench] inputs {args.config} N={p.N} d={p.d} V={p.V} K={p.K} chunk={chunk} ready in "
           f"{time.perf_counter() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
-    prob = kd.make_problem(H, W, idx, t, p.T, chunk)
+    step_flags = kd.KD_LOW_MEMORY if args.low_memory else 0
+    prob = kd.make_problem(H, W, idx, t, p.T, chunk, flags=step_flags)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats(dev)
     inputs_mem = torch.cuda.memory_allocated(dev)
@@ -306,10 +310,10 @@ def main():
     def step(ev=None):
         if ev:
             ev[0].record(stream)
-        f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=chunk, want_row_kl=True, workspace=ws)
+        f = kd.fused_kl_fwd(H, W, idx, t, T=p.T, chunk=chunk, want_row_kl=True, flags=step_flags, workspace=ws)
         if ev:
             ev[1].record(stream)
-        kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=chunk, dW=dW, workspace=ws)
+        kd.fused_kl_bwd(H, W, idx, t, f.lse, T=p.T, chunk=chunk, flags=step_flags, dW=dW, workspace=ws)
         if ev:
             ev[2].record(stream)
         return f
@@ -368,7 +372,7 @@ def main():
         "data": "synthetic (seeded; bf16 H ~ N(0,1), W ~ N(0,1/d), top-K cache peaked/flat mix)",
         "config": {
             "workload": f"{args.config}: LM-head fused chunked top-K KL, N={N}, d={d}, V={V}, K={p.K}, "
-                        f"chunk={chunk}, T={p.T}",
+                        f"chunk={chunk}, T={p.T}" + (", memory-lean backward" if args.low_memory else ""),
             "N": N, "d": d, "V": V, "K": p.K, "chunk": chunk, "T": p.T,
         },
         "pct_bf16_peak": 100.0 * flops_step / (ms_step / 1e3) / (PEAK_BF16_TFLOPS * 1e12),
@@ -385,7 +389,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved / PEAK_BF16_TFLOPS,
-            "traffic": measured_traffic(args.config, dom),
+            # the committed counters are for the default step's kernels
+            "traffic": None if args.low_memory else measured_traffic(args.config, dom),
         },
     }
 
