@@ -4,21 +4,26 @@
 // registers. Four variants:
 //   gemm_tile       256 x 256, four waves (2 x 2, 128 x 128 each as 4 x 4 blocks of
 //                   v_mfma_f32_32x32x16_bf16 / 32x32x2_f32, accumulators in AGPRs), two LDS
-//                   stages of a full K step; takes M/N-contiguous operands (dense path).
+//                   stages of a full K step; takes M/N-contiguous operands (dense path, fp32
+//                   memory-lean backward).
 //   gemm_tile_kk    same tile on K-contiguous operands, four LDS stages of half a K step,
 //                   four or eight waves (dense logits).
 //   gemm_tile_kk16  same tile and stages, eight waves (2 x 4, 128 x 64 each as 8 x 4 blocks of
 //                   v_mfma_f32_16x16x32_bf16 / 16x16x4_f32): forward and gradient kernels.
-//   gemm_tile_w16   256 x 320, eight waves (2 x 4, 128 x 80 each as 8 x 5 16x16 blocks): dH, dW.
+//   gemm_tile_w16   256 x 320, eight waves (2 x 4, 128 x 80 each as 8 x 5 16x16 blocks): dH, dW;
+//                   either operand may also be M/N contiguous (kTrans, kTransT), reaching the
+//                   MFMAs through LDS transpose reads (bf16 memory-lean backward).
 //
 // Operands reach LDS in 16-byte chunks:
 //   - K contiguous (element (mn, k) at src[mn*ld + k]): buffer_load_dwordx4 with the LDS
 //     destination bit, straight from memory into LDS. No VGPRs and no ds_write are used.
 //     A wave instruction fills 64 consecutive LDS chunks, so each lane fetches the global
 //     chunk that belongs at its destination under the stage's swizzle.
-//   - M/N contiguous (element (mn, k) at src[k*ld + mn], gemm_tile only): buffer loads of
+//   - M/N contiguous (element (mn, k) at src[k*ld + mn]) in gemm_tile: buffer loads of
 //     8 x 8 (bf16) or 4 x 4 (fp32) blocks into VGPRs, transposed in registers and written with
-//     ds_write_b128.
+//     ds_write_b128;
+//   - M/N contiguous in gemm_tile_w16 (bf16): the same LDS DMA as K-contiguous operands, rows of
+//     k into LDS as they lie, and ds_read_b64_tr_b16 pairs transpose them into fragments.
 // Rows and k beyond the operand's limits are read through an out-of-range offset of the
 // buffer descriptor. The hardware returns zeros for those, so the loop has no branches.
 //

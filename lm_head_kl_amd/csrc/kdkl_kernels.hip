@@ -11,17 +11,21 @@
 // tile of C = A B^T with its accumulators in registers:
 //   - forward and gradient kernels: 256 x 256, eight 64-wide waves in a 2 x 4 grid, each wave
 //     128 x 64 as 8 x 4 blocks of v_mfma_f32_16x16x32_bf16 (v_mfma_f32_16x16x4_f32 for fp32);
-//   - dH and dW: 256 x 320 (the hidden size on the 320 side), eight waves of 128 x 80;
-//   - the dense comparison path and the memory-lean backward: 256 x 256 on four waves of
+//   - dH and dW: 256 x 320 (the hidden size on the 320 side), eight waves of 128 x 80, also
+//     in the bf16 memory-lean backward;
+//   - the dense comparison path and the fp32 memory-lean backward: 256 x 256 on four waves of
 //     32x32x16 blocks.
 // Operands reach LDS straight from memory (buffer_load ... lds) in 16-byte chunks, XOR-swizzled
 // by row so that fragment reads are free of bank conflicts, four stages of half a K step deep.
 // Every operand of the fast path is stage-tiled (engine.h, kTiled): each 64-byte K step of a
 // tile's rows is one contiguous block, so its loads fetch whole 128-byte lines. The copies are
-// made here: W and row chunks of H (k_tile_rows) for the forward and gradient kernels, W^T once
-// per backward call and H_c^T per chunk (k_transpose) for dH = G W and dW = G^T H, and G_c and
-// G_c^T written by the gradient kernels. The dense and memory-lean paths read row-major or
-// M/N-contiguous operands (through registers, 8 x 8 bf16 blocks transposed on the way to LDS).
+// made here: for the forward, W and each launch's rows of H (k_tile_rows); for the backward,
+// W^T once per call and H_c^T per chunk (k_transpose), whose loads also write the gradient
+// kernel's stage-tiled W and H_c; and G_c and G_c^T, written by the gradient kernels. The bf16
+// memory-lean backward makes no copy: dH and dW read W, H and the stage-tiled G_c through LDS
+// transpose reads (engine.h, kTrans / kTransT). The dense path and the fp32 memory-lean
+// backward read row-major or M/N-contiguous operands through registers (8 x 8 blocks transposed
+// on the way to LDS).
 //
 // Epilogues:
 //   forward   logit tiles are computed transposed (vocabulary x tokens), so each lane keeps the
