@@ -43,5 +43,25 @@ def max_rel(a, b) -> float:
     return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), 1e-30)))
 
 
+def lse_err(a, b, T: float) -> float:
+    """Largest lse error in units of max(|lse_n|, 1) + 4/T, to be held to the lse tolerance tol.
+    lse_n is the log-sum-exp of the row's tempered logits, so its error is at most theirs; the
+    logits (zk) are held to tol relative plus 4*tol absolute, which gives lse_n a bound of
+    tol*(|lse_n| + 4/T). Where lse_n is far from 0 (at the configured heads it is near log V
+    or above) this is the relative error with a small absolute slack; where it nears 0 (V = 1:
+    lse_n is the one tempered logit) a purely relative bound would be undefined."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b) / (np.maximum(np.abs(b), 1.0) + 4.0 / T)))
+
+
+def zero_kl_bound(ref: dict, T: float, tol_lse: float) -> np.ndarray:
+    """Per-row bound on |KL_n| for a problem whose exact KL_n are all 0 (V = 1: student and
+    teacher both put all mass on the one token), where a relative bound is undefined. The GPU
+    forms KL_n = sum_k p_k (log p_k - zk_nk / T + lse_n) from lse and zk, each held to tol_lse
+    relative, so its error is at most tol_lse * (|lse_n| + max_k |zk_nk| / T)."""
+    return tol_lse * (np.abs(ref["lse"]) + np.abs(ref["zk"]).max(axis=1) / T)
+
+
 def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)

@@ -7,6 +7,8 @@ vocab tile).
 
 The draws are fixed by the case number, so a failing case is reproduced by its id."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -14,11 +16,12 @@ import torch
 import datagen
 import oracle
 import lm_head_kl_amd as kd
-from gpu_helpers import TOL, device_inputs, host, max_rel, rel_l2, say
+from gpu_helpers import TOL, device_inputs, host, max_rel, rel_l2, say, lse_err, zero_kl_bound
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 32
+# More cases (new draws, same recipe) with KD_FUZZ_CASES=<n>.
+N_CASES = int(os.environ.get("KD_FUZZ_CASES", "32"))
 
 
 def draw_case(i: int) -> dict:
@@ -48,10 +51,17 @@ def make_problem(c: dict) -> datagen.Problem:
 def check(label, c, ref, loss, lse, row_kl, dH, dW=None, zk=None):
     tol = TOL[c["dtype"]]
     got = float(loss.item()) * c["grad"]  # the oracle's loss carries the upstream weight
-    assert abs(got - ref["loss"]) <= tol["loss"] * max(abs(ref["loss"]), 1e-30), (label, got, ref["loss"])
-    assert max_rel(host(lse), ref["lse"]) <= tol["lse"], label
-    scale = max(np.abs(ref["row_kl"]).max(), 1e-30)
-    assert np.max(np.abs(host(row_kl) - ref["row_kl"])) <= tol["loss"] * scale, label
+    assert lse_err(host(lse), ref["lse"], c["T"]) <= tol["lse"], label
+    if not np.any(ref["row_kl"]):
+        # every KL_n is exactly 0 (V = 1): held to the bound the lse tolerance implies
+        b = zero_kl_bound(ref, c["T"], tol["lse"])
+        ls = abs(c["grad"]) * c["T"] ** 2 / (c["n_norm"] or c["N"])
+        assert abs(got) <= ls * b.sum(), (label, got)
+        assert np.all(np.abs(host(row_kl)) <= b), label
+    else:
+        assert abs(got - ref["loss"]) <= tol["loss"] * abs(ref["loss"]), (label, got, ref["loss"])
+        scale = np.abs(ref["row_kl"]).max()
+        assert np.max(np.abs(host(row_kl) - ref["row_kl"])) <= tol["loss"] * scale, label
     if zk is not None:
         np.testing.assert_allclose(host(zk), ref["zk"], rtol=tol["lse"], atol=tol["lse"] * 4, err_msg=label)
     e_dh = rel_l2(host(dH), ref["dH"])
