@@ -55,12 +55,21 @@ def lse_err(a, b, T: float) -> float:
     return float(np.max(np.abs(a - b) / (np.maximum(np.abs(b), 1.0) + 4.0 / T)))
 
 
-def zero_kl_bound(ref: dict, T: float, tol_lse: float) -> np.ndarray:
-    """Per-row bound on |KL_n| for a problem whose exact KL_n are all 0 (V = 1: student and
-    teacher both put all mass on the one token), where a relative bound is undefined. The GPU
-    forms KL_n = sum_k p_k (log p_k - zk_nk / T + lse_n) from lse and zk, each held to tol_lse
-    relative, so its error is at most tol_lse * (|lse_n| + max_k |zk_nk| / T)."""
+def kl_input_bound(ref: dict, T: float, tol_lse: float) -> np.ndarray:
+    """Per-row bound on the error of KL_n carried in from its inputs: the GPU forms
+    KL_n = sum_k p_k (log p_k - zk_nk / T + lse_n) from lse and zk, each held to tol_lse
+    relative, so KL_n may be off by tol_lse * (|lse_n| + max_k |zk_nk| / T) whatever its own
+    size. It decides where KL_n is much smaller than the terms it cancels from (a flat
+    teacher against a near-uniform student; V = 1, where every KL_n is exactly 0)."""
     return tol_lse * (np.abs(ref["lse"]) + np.abs(ref["zk"]).max(axis=1) / T)
+
+
+def row_kl_err(got, ref: dict, T: float, tol: dict) -> float:
+    """Largest per-row KL error over its bar, max(tol * max_m |KL_m|, the input bound); <= 1
+    passes."""
+    got = np.asarray(got, np.float64)
+    bar = np.maximum(tol["loss"] * np.abs(ref["row_kl"]).max(), kl_input_bound(ref, T, tol["lse"]))
+    return float(np.max(np.abs(got - ref["row_kl"]) / bar))
 
 
 def host(t: torch.Tensor) -> np.ndarray:
