@@ -55,6 +55,35 @@ def lse_err(a, b, T: float) -> float:
     return float(np.max(np.abs(a - b) / (np.maximum(np.abs(b), 1.0) + 4.0 / T)))
 
 
+def zk_dot_bound(H, W, idx) -> np.ndarray:
+    """Forward error bound of each gathered logit z_nk = sum_i h_ni w_(idx_nk)i accumulated in
+    fp32, with products exact (bf16 inputs) or rounded once (fp32 inputs), in any summation
+    order: |fl(z) - z| <= gamma_(d+1) * sum_i |h_ni w_(idx_nk)i|, gamma_m = m u / (1 - m u),
+    u = 2^-24 (the standard bound for a floating-point dot product; Higham, Accuracy and
+    Stability of Numerical Algorithms, section 3.1). H and W as fp64 arrays, idx [N, K]."""
+    d = H.shape[1]
+    u = 2.0 ** -24
+    g = (d + 1) * u / (1.0 - (d + 1) * u)
+    aW = np.abs(W)
+    out = np.empty(idx.shape)
+    for r0 in range(0, H.shape[0], 256):
+        s = np.abs(H[r0:r0 + 256]) @ aW.T
+        out[r0:r0 + 256] = np.take_along_axis(s, np.asarray(idx[r0:r0 + 256], np.int64), axis=1)
+    return g * out
+
+
+def assert_zk(got, ref_zk, tol_lse: float, H, W, idx):
+    """zk against the oracle: within tol relative plus 4*tol absolute, or else within the fp32
+    dot-product bound (zk_dot_bound), which no correct gather and accumulation exceeds."""
+    got = np.asarray(got, np.float64)
+    err = np.abs(got - ref_zk)
+    ok = err <= tol_lse * np.abs(ref_zk) + 4.0 * tol_lse
+    if not ok.all():
+        bad = ~ok
+        bound = zk_dot_bound(H, W, idx)
+        assert np.all(err[bad] <= bound[bad]), (err[bad].max(), bound[bad].min())
+
+
 def kl_input_bound(ref: dict, T: float, tol_lse: float) -> np.ndarray:
     """Per-row bound on the error of KL_n carried in from its inputs: the GPU forms
     KL_n = sum_k p_k (log p_k - zk_nk / T + lse_n) from lse and zk, each held to tol_lse

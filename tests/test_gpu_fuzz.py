@@ -16,7 +16,7 @@ import torch
 import datagen
 import oracle
 import lm_head_kl_amd as kd
-from gpu_helpers import TOL, device_inputs, host, max_rel, rel_l2, say, lse_err, kl_input_bound, row_kl_err
+from gpu_helpers import TOL, device_inputs, host, max_rel, rel_l2, say, lse_err, kl_input_bound, row_kl_err, assert_zk
 
 pytestmark = pytest.mark.gpu
 
@@ -142,7 +142,7 @@ def test_fuzz_draws_cover_the_boundaries():
 # Medium shapes: more tiles than the chip has workgroup slots, so the persistent loops, the
 # forward's vocabulary split and the dW chunk groups all take their general paths. Every row's
 # lse, zk, KL_n and dH row is compared; dW on 64 vocabulary rows (ids 0-3, V-1 and seeded).
-N_MEDIUM = 6
+N_MEDIUM = int(os.environ.get("KD_FUZZ_MEDIUM", "6"))  # more with KD_FUZZ_MEDIUM=<n>
 
 
 def draw_medium(i: int) -> dict:
@@ -180,9 +180,9 @@ def test_fuzz_medium(i):
     ref = {k: np.concatenate(v) for k, v in ref.items()}
     loss = p.T * p.T / p.N * float(np.sum(ref["row_kl"]))
     assert abs(f.loss.item() - loss) <= tol["loss"] * abs(loss)
-    assert max_rel(host(f.lse), ref["lse"]) <= tol["lse"]
-    assert np.max(np.abs(host(f.row_kl) - ref["row_kl"])) <= tol["loss"] * np.abs(ref["row_kl"]).max()
-    np.testing.assert_allclose(host(f.zk), ref["zk"], rtol=tol["lse"], atol=tol["lse"] * 4)
+    assert lse_err(host(f.lse), ref["lse"], p.T) <= tol["lse"]
+    assert row_kl_err(host(f.row_kl), ref, p.T, tol) <= 1.0
+    assert_zk(host(f.zk), ref["zk"], tol["lse"], Hf, Wf, p.idx)
     e_dh = rel_l2(host(dH), ref["dH"])
     vocab = datagen.sample_vocab(p.V, 64, c["seed"])
     want = oracle.dw_rows(Hf, Wf, p.idx, tl, p.T, vocab, ref["lse"], n_norm=p.N)
