@@ -2,6 +2,8 @@
 ids and values, on random rows, rows full of ties, signed zeros and infinities, K at its limits,
 padded rows, and rows at the gpt-oss vocabulary size."""
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -164,7 +166,10 @@ def draw_rows(g: np.random.Generator, N: int, V: int, K: int) -> np.ndarray:
     return x
 
 
-@pytest.mark.parametrize("i", range(24))
+N_RANDOM = int(os.environ.get("KD_TOPK_CASES", "24"))  # more with KD_TOPK_CASES=<n>
+
+
+@pytest.mark.parametrize("i", range(N_RANDOM))
 def test_random_shapes(i):
     """Seeded random (N, V, K, row stride, dtype, row kinds); ids and values bit for bit."""
     g = np.random.Generator(np.random.PCG64([4244, i]))
@@ -221,7 +226,26 @@ def single_read_rows(g: np.random.Generator, N: int, V: int, K: int) -> np.ndarr
 def test_single_read_pass(dtype, V, K, N, pad):
     """kd_topk_cache at the row lengths where a whole row is held on chip and read once, with the
     rows it cannot settle redone by the exact kernel; ids and values bit for bit."""
-    g = np.random.Generator(np.random.PCG64([4245, V, K]))
+    run_single_read(np.random.Generator(np.random.PCG64([4245, V, K])), dtype, V, K, N, pad)
+
+
+# Seeded draws over the row lengths and widths the single-read pass takes (more with
+# KD_TOPK_SINGLE_CASES=<n>).
+N_SINGLE = int(os.environ.get("KD_TOPK_SINGLE_CASES", "6"))
+
+
+@pytest.mark.parametrize("i", range(N_SINGLE))
+def test_single_read_random(i):
+    g = np.random.Generator(np.random.PCG64([4246, i]))
+    dtype = "bf16" if i % 2 == 0 else "fp32"
+    V = int(g.integers(68272, 204801)) if dtype == "bf16" else int(g.integers(34136, 102401))
+    K = int(g.choice([1, int(g.integers(1, 129)), 128]))
+    N = int(g.integers(1, 300))
+    pad = int(g.choice([0, 0, int(g.integers(1, 16))]))
+    run_single_read(g, dtype, V, K, N, pad)
+
+
+def run_single_read(g: np.random.Generator, dtype: str, V: int, K: int, N: int, pad: int) -> None:
     x = single_read_rows(g, N, V, K)
     xs = datagen.bf16_bits(x) if dtype == "bf16" else x  # what the device holds
     xv = datagen.bf16_to_f32(xs) if dtype == "bf16" else x
