@@ -449,3 +449,48 @@ def test_truncation_terms_identities():
     # more cached entries never lose mass
     m = [oracle.truncation_terms(H, W, t, k)["mass"] for k in (1, 5, 20, 50)]
     assert all(np.all(a <= b + 1e-15) for a, b in zip(m, m[1:]))
+
+
+@pytest.mark.parametrize("T", [0.5, 2.0])
+def test_one_token_head_is_exactly_zero(T):
+    """V = 1 (so K = 1): student and teacher both put all mass on the one token, so every KL_n,
+    the loss and every gradient are exactly 0, in each formulation (closed form)."""
+    g = np.random.default_rng(31)
+    N, d = 40, 24
+    H, W = g.standard_normal((N, d)), g.standard_normal((1, d))
+    idx = np.zeros((N, 1), np.int64)
+    t = g.standard_normal((N, 1))
+    for ref in (oracle.kl_dense(H, W, idx, t, T), oracle.kl_chunked(H, W, idx, t, T, chunk=16),
+                oracle.kl_fused(H, W, idx, t, T, chunk=16, vtile=1)):
+        assert ref["loss"] == 0.0 and not np.any(ref["row_kl"])
+        assert not np.any(ref["dH"]) and not np.any(ref["dW"])
+        np.testing.assert_allclose(ref["lse"], (H @ W.T)[:, 0] / T, rtol=1e-14)
+
+
+def test_fp32_dot_product_bound_holds():
+    """The GPU tests' fallback bound for gathered logits, gamma_(d+1) * sum |h_i w_i| with
+    u = 2^-24, bounds fp32 dot products computed from fp32 inputs in several summation orders
+    (numpy's fp32 matmul, a sequential fp32 loop, pairwise sums) against the exact fp64 value."""
+    from gpu_helpers import zk_dot_bound
+    g = np.random.default_rng(32)
+    N, d, V, K = 64, 700, 300, 8
+    H = g.standard_normal((N, d)).astype(np.float32)
+    W = (g.standard_normal((V, d)) / np.sqrt(d)).astype(np.float32)
+    idx = np.stack([g.choice(V, K, replace=False) for _ in range(N)])
+    Hd, Wd = H.astype(np.float64), W.astype(np.float64)
+    exact = np.take_along_axis(Hd @ Wd.T, idx, axis=1)
+    bound = zk_dot_bound(Hd, Wd, idx)
+    z_mm = np.take_along_axis((H @ W.T).astype(np.float64), idx, axis=1)
+    prod = H[:, None, :] * W[idx]                       # fp32 products, [N, K, d]
+    z_seq = np.zeros((N, K), np.float32)
+    for i in range(d):                                  # left-to-right fp32 accumulation
+        z_seq = (z_seq + prod[:, :, i]).astype(np.float32)
+    z_pair = prod.astype(np.float32)
+    while z_pair.shape[2] > 1:                          # pairwise fp32 accumulation
+        if z_pair.shape[2] % 2:
+            z_pair = np.concatenate([z_pair, np.zeros_like(z_pair[:, :, :1])], axis=2)
+        z_pair = (z_pair[:, :, 0::2] + z_pair[:, :, 1::2]).astype(np.float32)
+    for z in (z_mm, z_seq.astype(np.float64), z_pair[:, :, 0].astype(np.float64)):
+        err = np.abs(z - exact)
+        assert np.all(err <= bound), float((err / bound).max())
+        assert (err / bound).max() > 0.0
